@@ -1,0 +1,38 @@
+"""Plain, slow CPU oracle of the DeepSeek-V4-Flash-Vision encoder hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+path (no kernels, headers, tables or helpers); the only thing both sides see
+is the seeded input arrays.
+
+Everything is computed with numpy in float64 (pass ``dtype=np.float32`` for the
+single-precision reading) as the plain definition of each step, one step after
+another, with no blocking, fusion or reordering.  Each function names the page
+passage it follows.  Readings taken where the pages are silent or garbled are
+listed in ``vit.READINGS``.
+
+Parity pins: every function here is pinned by ``tests/test_oracle.py`` against
+closed forms, hand-derived golden values, brute-force loops or invariants.
+"""
+from .vit import (  # noqa: F401
+    READINGS,
+    aligner,
+    aligner_gather,
+    aligner_perm,
+    apply_rope,
+    attention,
+    attention_probs,
+    block,
+    encode,
+    encode_varlen,
+    linear,
+    mlp,
+    nlayout,
+    patch_embed,
+    patchify,
+    rmsnorm,
+    rope_freqs,
+    rope_table,
+    tower,
+)

@@ -1,0 +1,291 @@
+"""Oracle steps of the vision encoder (test infrastructure only; see package doc).
+
+Sources (web pages):
+  [VIS]  NeMo Automodel API docs, ``nemo_automodel.components.models.deepseek_v4.vision``
+         (classes DeepseekV4VisionPatchEmbed, RMSNorm, Attention, MLP, Block,
+         Transformer, Aligner; functions apply_vision_rotary, get_vision_cos_sin).
+  [MOD]  NeMo Automodel API docs, ``...deepseek_v4.model`` (DeepseekV4Model.encode_image,
+         forward arguments ``pixel_values`` / ``image_grid_hws``; image sentinel
+         parameters image_start / image_newline / image_pad / image_end).
+  [PR]   NVIDIA-NeMo/Automodel PR #3772 (Changelog; Validation: vision-only parity
+         table with grids and "N-layout" / "Permutation" columns).
+  [HF]   summary page of the HF DeepSeek-V4-Flash-Vision-Exp text model (the
+         ``rotate_half`` pattern computed in fp32 and cast back).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Readings taken where the pages leave a step open (same list as the design notes).
+READINGS = {
+    "rope_freq": "each half of a head is a 1D rotary of width D/2 with f_k = theta^(-k/(D/4)), k < D/4",
+    "rope_pairing": "rotate_half pairing inside each half: element i pairs with i + D/4",
+    "rope_axes": "first D/2 dims rotated by the patch row index, last D/2 by the column index",
+    "positions": "0-based integer (row, col) with p = row*gw + col, restarting for every image",
+    "attention": "scale 1/sqrt(D), no mask inside an image, images never see each other",
+    "wqkv": "rows ordered [q; k; v], each head-major (head h owns rows h*D .. h*D+D-1)",
+    "bias": "no bias in patch embed, wqkv, out-proj, MLP or aligner",
+    "rmsnorm": "y = w * x / sqrt(mean(x^2) + eps), eps inside the root, fp32 scale w",
+    "final_norm": "applied once after the last block, before the aligner",
+    "patch_order": "patch (r, c) flattens img[:, 14r:14r+14, 14c:14c+14] in C order [3,14,14]",
+    "swiglu": "silu(x Wg^T) * (x Wu^T), then Wd; no clamp",
+    "aligner": "2x2 groups row-major over (gh/2, gw/2); inside a group TL,TR,BL,BR concatenated "
+               "along features; one bias-free linear to the LLM width",
+    "odd_grid": "the aligner needs an even grid; odd grids are rejected",
+    "nlayout": "per image: [START] + per merged row (w' IMAGE, NEWLINE) + [END]; "
+               "types START=0 IMAGE=1 NEWLINE=2 END=3; src = merged token index or -1",
+}
+
+NL_START, NL_IMAGE, NL_NEWLINE, NL_END = 0, 1, 2, 3
+
+
+def _f(a, dtype):
+    return np.asarray(a, dtype=dtype)
+
+
+def linear(x, w, dtype=np.float64):
+    """Bias-free linear map with a PyTorch-style weight ``[out, in]``: y = x W^T.
+
+    [VIS] every projection (patch_embed.proj, wqkv, out-proj, MLP, aligner) is a
+    linear map; the MLP page calls it bias-free and no bias is named elsewhere.
+    """
+    return _f(x, dtype) @ _f(w, dtype).T
+
+
+def patchify(img, patch_size=14):
+    """Cut a ``[3, gh*ps, gw*ps]`` image into ``[gh*gw, 3*ps*ps]`` row-major patches.
+
+    [VIS] DeepseekV4VisionTransformer.forward takes patches ``[n_h*n_w, 3, ps, ps]``;
+    patch p = r*gw + c holds pixels rows ps*r.., cols ps*c.. flattened in C order.
+    """
+    img = np.asarray(img)
+    C, Hpx, Wpx = img.shape
+    gh, gw = Hpx // patch_size, Wpx // patch_size
+    out = np.empty((gh * gw, C * patch_size * patch_size), dtype=img.dtype)
+    for r in range(gh):
+        for c in range(gw):
+            tile = img[:, r * patch_size:(r + 1) * patch_size, c * patch_size:(c + 1) * patch_size]
+            out[r * gw + c] = tile.reshape(-1)
+    return out
+
+
+def patch_embed(patches, w, dtype=np.float64):
+    """[VIS] DeepseekV4VisionPatchEmbed: project flattened RGB patches to vision_dim."""
+    p = _f(patches, dtype).reshape(len(patches), -1)
+    return linear(p, w, dtype)
+
+
+def rmsnorm(x, w, eps=1e-6, dtype=np.float64):
+    """[VIS] DeepseekV4VisionRMSNorm(dim, eps=1e-6) with an fp32 scale parameter.
+
+    y = w * x / sqrt(mean(x^2 over the last axis) + eps).
+    """
+    x = _f(x, dtype)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return _f(w, dtype) * (x / np.sqrt(ms + eps))
+
+
+def rope_freqs(head_dim, theta=10000.0):
+    """Rotary frequencies of one half of a head (width D/2): f_k = theta^(-k/(D/4)).
+
+    [VIS] apply_vision_rotary is a "half-split 2D" rotary whose tables have width
+    head_dim/2; the theta is the transformer's ``rope_theta``.  Each half is read as
+    a standard 1D rotary of width D/2 (reading "rope_freq").
+    """
+    q = head_dim // 4
+    return np.array([theta ** (-(k / q)) for k in range(q)], dtype=np.float64)
+
+
+def rope_table(gh, gw, head_dim, theta=10000.0, origin=(0, 0)):
+    """Cos/sin tables ``[gh*gw, D/2]`` = [row-angle part D/4 | column-angle part D/4].
+
+    [VIS] get_vision_cos_sin(n_h, n_w, dim, theta) builds the 2D table for one image;
+    patch p sits at row p // gw and column p % gw.  ``origin`` shifts every position
+    by the same offset (used only by the shift-invariance pin).  Built in float64.
+    """
+    f = rope_freqs(head_dim, theta)
+    P = gh * gw
+    cos = np.empty((P, head_dim // 2), dtype=np.float64)
+    sin = np.empty((P, head_dim // 2), dtype=np.float64)
+    q = head_dim // 4
+    for p in range(P):
+        r = p // gw + origin[0]
+        c = p % gw + origin[1]
+        cos[p, :q] = np.cos(r * f)
+        sin[p, :q] = np.sin(r * f)
+        cos[p, q:] = np.cos(c * f)
+        sin[p, q:] = np.sin(c * f)
+    return cos, sin
+
+
+def apply_rope(x, cos, sin, dtype=np.float64):
+    """Half-split 2D rotary on ``[P, H, D]``.
+
+    [VIS] apply_vision_rotary: the first half A = x[:D/2] of each head rotates with
+    the row angles, the second half B = x[D/2:] with the column angles.  Inside a
+    half, [a1 | a2] (quarters) maps to [a1 cos - a2 sin | a2 cos + a1 sin], the
+    rotate_half pattern ([HF]: x*cos + rotate_half(x)*sin with
+    rotate_half([a1|a2]) = [-a2|a1]).
+    """
+    x = _f(x, dtype)
+    P, H, D = x.shape
+    q = D // 4
+    out = np.empty_like(x)
+    for half in range(2):
+        lo = half * (D // 2)
+        c = _f(cos[:, half * q:(half + 1) * q], dtype)[:, None, :]
+        s = _f(sin[:, half * q:(half + 1) * q], dtype)[:, None, :]
+        a1 = x[:, :, lo:lo + q]
+        a2 = x[:, :, lo + q:lo + 2 * q]
+        out[:, :, lo:lo + q] = a1 * c - a2 * s
+        out[:, :, lo + q:lo + 2 * q] = a2 * c + a1 * s
+    return out
+
+
+def attention_probs(q, k, dtype=np.float64):
+    """Softmax(Q K^T / sqrt(D)) per head for one image: ``[H, P, P]``.
+
+    [VIS] DeepseekV4VisionAttention: full bidirectional patch attention over one
+    image (no mask).  Scale 1/sqrt(head_dim) (reading "attention").
+    """
+    q = _f(q, dtype)
+    k = _f(k, dtype)
+    P, H, D = q.shape
+    out = np.empty((H, P, k.shape[0]), dtype=dtype)
+    for h in range(H):
+        s = (q[:, h, :] @ k[:, h, :].T) / np.sqrt(D)
+        s = s - s.max(axis=-1, keepdims=True)
+        e = np.exp(s)
+        out[h] = e / e.sum(axis=-1, keepdims=True)
+    return out
+
+
+def attention(q, k, v, dtype=np.float64):
+    """O = softmax(Q K^T / sqrt(D)) V per head for one image; ``[P, H, D]``.
+
+    One head at a time (same arithmetic as ``attention_probs``, less memory).
+    """
+    q, k, v = _f(q, dtype), _f(k, dtype), _f(v, dtype)
+    out = np.empty_like(v)
+    for h in range(q.shape[1]):
+        a = attention_probs(q[:, h:h + 1], k[:, h:h + 1], dtype)[0]
+        out[:, h, :] = a @ v[:, h, :]
+    return out
+
+
+def mlp(x, w_gate, w_up, w_down, dtype=np.float64):
+    """[VIS] DeepseekV4VisionMLP: bias-free SwiGLU, silu(x Wg^T) * (x Wu^T), then Wd."""
+    g = linear(x, w_gate, dtype)
+    u = linear(x, w_up, dtype)
+    return linear((g / (1.0 + np.exp(-g))) * u, w_down, dtype)
+
+
+def block(x, blk, cos, sin, n_heads, eps=1e-6, dtype=np.float64):
+    """[VIS] DeepseekV4VisionBlock: x += attn(norm1(x)); x += mlp(norm2(x)).
+
+    Inside attn ([VIS] DeepseekV4VisionAttention): wqkv -> q, k, v ``[P, H, D]``,
+    rotary on q and k, full attention, out-projection ``wo``.
+    """
+    x = _f(x, dtype)
+    P, d = x.shape
+    D = d // n_heads
+    n = rmsnorm(x, blk["norm1"], eps, dtype)
+    qkv = linear(n, blk["wqkv"], dtype)
+    q = qkv[:, 0:d].reshape(P, n_heads, D)
+    k = qkv[:, d:2 * d].reshape(P, n_heads, D)
+    v = qkv[:, 2 * d:3 * d].reshape(P, n_heads, D)
+    q = apply_rope(q, cos, sin, dtype)
+    k = apply_rope(k, cos, sin, dtype)
+    o = attention(q, k, v, dtype).reshape(P, d)
+    x = x + linear(o, blk["wo"], dtype)
+    n2 = rmsnorm(x, blk["norm2"], eps, dtype)
+    return x + mlp(n2, blk["w_gate"], blk["w_up"], blk["w_down"], dtype)
+
+
+def tower(patches, gh, gw, weights, n_heads, eps=1e-6, theta=10000.0, dtype=np.float64,
+          origin=(0, 0)):
+    """[VIS] DeepseekV4VisionTransformer.forward for one image: embed, blocks, final norm."""
+    x = patch_embed(patches, weights["patch_embed"], dtype)
+    d = x.shape[1]
+    cos, sin = rope_table(gh, gw, d // n_heads, theta, origin)
+    for blk in weights["blocks"]:
+        x = block(x, blk, cos, sin, n_heads, eps, dtype)
+    return rmsnorm(x, weights["final_norm"], eps, dtype)
+
+
+def aligner_perm(gh, gw, merge=2):
+    """Source patch of every slot of the merged layout, ``[gh*gw]`` int32.
+
+    [VIS] DeepseekV4VisionAligner spatially downsamples (downsample_ratio = 2) and
+    [PR] reports the permutation as exact; reading "aligner": merged token
+    t = i*(gw/2) + j gathers the 2x2 group at rows 2i..2i+1, cols 2j..2j+1 in
+    row-major order TL, TR, BL, BR.
+    """
+    if gh % merge or gw % merge:
+        raise ValueError("aligner needs a grid divisible by the merge size")
+    perm = []
+    for i in range(gh // merge):
+        for j in range(gw // merge):
+            for a in range(merge):
+                for b in range(merge):
+                    perm.append((merge * i + a) * gw + (merge * j + b))
+    return np.array(perm, dtype=np.int32)
+
+
+def aligner_gather(x, gh, gw, merge=2):
+    """G[t] = concat of x over the group of merged token t: ``[P/4, 4d]``."""
+    x = np.asarray(x)
+    perm = aligner_perm(gh, gw, merge)
+    m2 = merge * merge
+    return x[perm].reshape(len(perm) // m2, m2 * x.shape[1])
+
+
+def aligner(x, gh, gw, w, merge=2, dtype=np.float64):
+    """[VIS] DeepseekV4VisionAligner.forward: 2x2 gather, then the linear map to LLM width."""
+    return linear(aligner_gather(_f(x, dtype), gh, gw, merge), w, dtype)
+
+
+def nlayout(gh, gw, merge=2):
+    """Newline layout of one image span in the LLM stream: (types, src) int32.
+
+    [PR] names the released "N-layout pseudo-token expansion"; [MOD] names the
+    sentinels image_start / image_newline / image_end.  Reading "nlayout": the span
+    is [START], then for each merged row i its gw/2 IMAGE tokens followed by one
+    NEWLINE, then [END].  ``src`` holds the merged token index of IMAGE slots and
+    -1 for sentinels.
+    """
+    hh, ww = gh // merge, gw // merge
+    types, src = [NL_START], [-1]
+    t = 0
+    for _ in range(hh):
+        for _ in range(ww):
+            types.append(NL_IMAGE)
+            src.append(t)
+            t += 1
+        types.append(NL_NEWLINE)
+        src.append(-1)
+    types.append(NL_END)
+    src.append(-1)
+    return np.array(types, dtype=np.int32), np.array(src, dtype=np.int32)
+
+
+def encode(patches, gh, gw, weights, n_heads, eps=1e-6, theta=10000.0, with_aligner=True,
+           dtype=np.float64):
+    """[MOD] DeepseekV4Model.encode_image: the vision tower, then the aligner."""
+    x = tower(patches, gh, gw, weights, n_heads, eps, theta, dtype)
+    if not with_aligner:
+        return x
+    return aligner(x, gh, gw, weights["aligner"], dtype=dtype)
+
+
+def encode_varlen(patches, grids, weights, n_heads, eps=1e-6, theta=10000.0, with_aligner=True,
+                  dtype=np.float64):
+    """Concatenated images ([MOD] pixel_values + image_grid_hws): each image alone, in order."""
+    outs = []
+    off = 0
+    for gh, gw in grids:
+        P = gh * gw
+        outs.append(encode(patches[off:off + P], gh, gw, weights, n_heads, eps, theta,
+                           with_aligner, dtype))
+        off += P
+    return np.concatenate(outs, axis=0)
