@@ -1,0 +1,217 @@
+"""Throughput of the MI355X encoder hot path (one GPU).
+
+One step = one vit_encode_varlen call over the whole batch: patch embedding,
+every block (RMSNorm, wqkv, rotary, attention, out-projection, RMSNorm, SwiGLU
+gate/up, down) and the final norm, plus the aligner when the workload has one.
+Inputs and weights are resident in HBM before the timed region.
+
+Prints one JSON line (metric, value in patches/s, roofline of the dominant
+kernel measured with HIP events inside the timed region, cpu_baseline of the
+oracle on a bounded sample on the host cores).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "patches/sec through ViT stack + aligner (bf16), % of MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "ragged_varlen_4img"
+
+# kernel class -> source file of its kernel (for the counter-traffic freshness check)
+KERNEL_SOURCE = {"qkv": "gemm_bf16.hip", "outproj": "gemm_bf16.hip", "gateup": "gemm_bf16.hip",
+                 "down": "gemm_bf16.hip", "embed": "gemm_bf16.hip", "aligner": "gemm_bf16.hip",
+                 "attn": "attention.hip", "rmsnorm": "elementwise.hip", "rope": "elementwise.hip",
+                 "gather": "elementwise.hip"}
+
+
+def class_flops(cfg):
+    """Algorithmic FLOPs per launch of each MFMA-bound kernel class."""
+    P, d, h = cfg.total_patches, cfg.vision_dim, cfg.mlp_hidden
+    f = {"qkv": 6.0 * P * d * d, "outproj": 2.0 * P * d * d, "gateup": 4.0 * P * d * h,
+         "down": 2.0 * P * d * h, "attn": sum(4.0 * d * p * p for p in cfg.seqlens),
+         "embed": 2.0 * P * cfg.patch_dim * d}
+    if cfg.aligner:
+        f["aligner"] = 2.0 * P * d * cfg.llm_dim
+    return f
+
+
+def class_bytes(cfg):
+    """Algorithmic HBM bytes per launch of the bandwidth-bound classes (bf16 activations)."""
+    P, d, D, H = cfg.total_patches, cfg.vision_dim, cfg.head_dim, cfg.n_heads
+    return {"rmsnorm": P * d * 4 + P * d * 2 + d * 4,        # fp32 residual in, bf16 out, scale
+            "rope": 2 * (2 * P * H * D * 2) + P * (D // 2) * 8,  # q,k read+write, table read
+            "gather": 2 * P * d * 2}
+
+
+def source_sha(kernel_class):
+    p = os.path.join(ROOT, "vision_transformer_encoder_image_amd", "csrc", KERNEL_SOURCE[kernel_class])
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+
+
+def counter_traffic(kernel_class, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_class}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != source_sha(kernel_class):
+        return None  # the kernel changed since the counters were taken
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, budget_s=30.0):
+    """Time the oracle (as is) on a bounded sample of the workload on host cores."""
+    import numpy as np  # noqa: F401
+    import threadpoolctl
+
+    import oracle
+
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    # sample: whole images, in order, until the estimated cost fits the budget; the
+    # ragged 4-image batch runs whole (~15 s on 8 cores)
+    grids = list(cfg.grids)
+    take = []
+    for g in grids:
+        take.append(g)
+        if sum(a * b for a, b in take) >= 4096:
+            break
+    P = sum(a * b for a, b in take)
+    t0 = time.perf_counter()
+    oracle.encode_varlen(inp["patches"][:P], take, inp["weights"], cfg.n_heads, cfg.rms_eps,
+                         cfg.rope_theta, with_aligner=cfg.aligner)
+    dt = time.perf_counter() - t0
+    return {"value": P / dt, "unit": "patches/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(take)} of {len(grids)} images ({P} patches, {cfg.n_blocks} blocks, "
+                      f"float64 numpy oracle, one pass, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="also time every kernel class")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the encoder shards "
+              "by image across GPUs with no exchange, so run one process per GPU instead.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from vision_transformer_encoder_image_amd import api, configs, synth
+
+    cfg = configs.get(args.workload)
+    idx = [c.name for c in configs.CONFIGS].index(cfg.name)
+    inp = synth.make_inputs(cfg, seed=idx)
+    dev = "cuda:0"
+    w = api.DeviceWeights(cfg, inp["weights"], device=dev)
+    x = torch.from_numpy(inp["patches"]).to(dev, torch.bfloat16 if cfg.dtype == "bf16" else torch.float32)
+    enc = api.Encoder(cfg, w, cfg.grids, aligner=cfg.aligner, device=dev)
+    out = torch.empty(enc.out_shape, dtype=x.dtype, device=dev)
+
+    flops = class_flops(cfg)
+    for _ in range(max(args.warmup, 1)):
+        enc(x, out)
+    torch.cuda.synchronize()
+
+    # which kernel dominates: one profiled step per class (not part of the timing)
+    per_class = {}
+    for k in flops:
+        api.profile_enable(k, True)
+    enc(x, out)
+    torch.cuda.synchronize()
+    for k in flops:
+        ms, n = api.profile_read(k)
+        api.profile_enable(k, False)
+        per_class[k] = ms
+    dominant = max(per_class, key=per_class.get)
+
+    # timed region: K steps, HIP events around every launch of the dominant kernel
+    api.profile_enable(dominant, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        enc(x, out)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dom_ms, dom_n = api.profile_read(dominant)
+    api.profile_enable(dominant, False)
+
+    P = cfg.total_patches
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = P * args.steps / elapsed
+    peak = PEAK_TFLOPS[cfg.dtype]
+    avg_launch_s = dom_ms / 1e3 / max(dom_n, 1)
+    achieved = flops[dominant] / avg_launch_s / 1e12
+    traffic = counter_traffic(dominant, cfg.name)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "patches/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "grids": [list(g) for g in cfg.grids], "patches": P,
+                   "vision_dim": cfg.vision_dim, "heads": cfg.n_heads, "head_dim": cfg.head_dim,
+                   "mlp_hidden": cfg.mlp_hidden, "blocks": cfg.n_blocks,
+                   "aligner": cfg.llm_dim if cfg.aligner else None},
+        "mfma_frac_step": round(cfg.total_flops() / (ms_per_step / 1e3) / (peak * 1e12), 4),
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                     "launches": dom_n, "flops_per_launch": flops[dominant]},
+    }
+    if args.breakdown:
+        bd = {}
+        for k in list(flops) + ["rmsnorm", "rope", "gather"]:
+            if k == "gather" and not cfg.aligner:
+                continue
+            api.profile_enable(k, True)
+        for _ in range(5):
+            enc(x, out)
+        torch.cuda.synchronize()
+        byts = class_bytes(cfg)
+        for k in list(flops) + ["rmsnorm", "rope", "gather"]:
+            if k == "gather" and not cfg.aligner:
+                continue
+            ms, n = api.profile_read(k)
+            api.profile_enable(k, False)
+            if n == 0:
+                continue
+            us = ms * 1e3 / n
+            e = {"avg_us": round(us, 2), "launches_per_step": n // 5}
+            if k in flops:
+                e["tflops"] = round(flops[k] / (us * 1e-6) / 1e12, 1)
+                e["mfma_frac"] = round(flops[k] / (us * 1e-6) / 1e12 / peak, 4)
+            else:
+                e["gbs"] = round(byts[k] / (us * 1e-6) / 1e9, 1)
+                e["hbm_frac"] = round(byts[k] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            bd[k] = e
+        result["breakdown"] = bd
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+/*
+ * vitenc.h - C ABI of the MI355X (gfx950) encoder for DeepSeek-V4-Flash-Vision images.
+ *
+ * The library computes the hot path of the vision encoder described on the NeMo
+ * Automodel API page "nemo_automodel.components.models.deepseek_v4.vision":
+ * patch embedding (DeepseekV4VisionPatchEmbed), a stack of pre-norm blocks
+ * (DeepseekV4VisionBlock: fp32-scale RMSNorm, wqkv, half-split 2D rotary, full
+ * bidirectional patch attention, out-projection, bias-free SwiGLU MLP), the final
+ * RMSNorm (DeepseekV4VisionTransformer.norm) and the 2x2 spatial-downsampling
+ * aligner (DeepseekV4VisionAligner), as chained by DeepseekV4Model.encode_image on
+ * the "...deepseek_v4.model" page.  Batches of images of different grids are
+ * concatenated as in that page's ``pixel_values`` / ``image_grid_hws`` arguments.
+ *
+ * Conventions shared by every entry point
+ *  - Device pointers are HIP device addresses; "host" marks the few host arrays.
+ *  - Matrices are row-major with a PyTorch-style weight layout [out, in].
+ *  - Activations and weights are bfloat16 (VIT_BF16) or float32 (VIT_F32) as
+ *    chosen by vit_config.dtype; norm scales are always float32.
+ *  - The caller owns every buffer (inputs, weights, outputs, workspace).  The
+ *    library never allocates or frees device memory, never writes inputs or
+ *    weights, and enqueues all work asynchronously on ``stream`` (a hipStream_t;
+ *    NULL = the null stream).  Host arrays are read before the call returns.
+ *  - Errors are returned as vit_status; no exception crosses the ABI.
+ *    vit_last_error() gives a human-readable detail of the last failure on the
+ *    calling thread.  NaN in gives NaN out (no NaN checks).
+ *  - Results are deterministic: no floating-point atomics.
+ *  - Calls on different streams must use different workspaces.
+ */
+#ifndef VITENC_H
+#define VITENC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VIT_OK = 0,
+  VIT_E_ARG = -1,        /* null pointer or invalid enum/flag */
+  VIT_E_SHAPE = -2,      /* inconsistent or unsupported dimensions */
+  VIT_E_ODD_GRID = -3,   /* aligner requested on a grid not divisible by merge */
+  VIT_E_WORKSPACE = -4,  /* workspace smaller than vit_workspace_bytes() */
+  VIT_E_HIP = -5,        /* a HIP launch or runtime call failed */
+} vit_status;
+
+typedef enum { VIT_BF16 = 0, VIT_F32 = 1 } vit_dtype;
+
+/* flags for vit_encode / vit_encode_varlen / vit_workspace_bytes */
+enum {
+  VIT_NO_ALIGNER = 1,  /* stop after the final norm: out is [sum P, vision_dim] */
+  VIT_OUT_NLAYOUT = 2, /* aligner rows land at their newline-layout slots (see
+                          vit_aligner_layout); sentinel rows are not written */
+};
+
+/* Upper bound on images per varlen call (descriptors travel as kernel args). */
+#define VIT_MAX_IMAGES 128
+
+/* Encoder shape.  head_dim must equal vision_dim / n_heads (the page's
+ * DeepseekV4VisionAttention.head_dim) and be a multiple of 4 (two halves, each
+ * split in rotate_half quarters); bf16 mode supports head_dim 64 and 72.
+ * patch_dim = 3 * patch_size^2 (588 for 14x14 RGB patches).  merge is the
+ * aligner's downsample_ratio (2).  rms_eps is 1e-6 on the page's
+ * DeepseekV4VisionRMSNorm.  rope_theta is DeepseekV4VisionTransformer.rope_theta. */
+typedef struct {
+  int32_t vision_dim;
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t mlp_hidden;
+  int32_t n_blocks;
+  int32_t patch_dim;
+  int32_t merge;
+  int32_t llm_dim;
+  float rope_theta;
+  float rms_eps;
+  int32_t dtype; /* vit_dtype */
+} vit_config;
+
+/* Weights (device pointers; the per-block arrays are HOST arrays of n_blocks
+ * device pointers).  dtype = cfg.dtype except the norm scales (float32).
+ *   patch_embed [d, patch_dim]     DeepseekV4VisionPatchEmbed.proj
+ *   wqkv[b]     [3d, d]            rows [q; k; v], each head-major
+ *   wo[b]       [d, d]             attention out-projection
+ *   w_gate[b], w_up[b] [h, d]      SwiGLU gate and up
+ *   w_down[b]   [d, h]
+ *   norm1[b], norm2[b], final_norm [d] float32
+ *   aligner     [llm_dim, merge^2 * d] (may be NULL with VIT_NO_ALIGNER) */
+typedef struct {
+  const void* patch_embed;
+  const void* const* wqkv;
+  const void* const* wo;
+  const void* const* w_gate;
+  const void* const* w_up;
+  const void* const* w_down;
+  const float* const* norm1;
+  const float* const* norm2;
+  const float* final_norm;
+  const void* aligner;
+} vit_weights;
+
+/* Text for a status code (static storage). */
+const char* vit_status_str(int32_t status);
+/* Detail of the last failing call on this thread ("" if none). */
+const char* vit_last_error(void);
+
+/* Workspace bytes needed by vit_encode_varlen (and vit_encode, n_images = 1) for
+ * these grids (host array [n_images, 2] of (rows, cols)).  Returns 0 when the
+ * arguments are invalid. */
+size_t vit_workspace_bytes(const vit_config* cfg, const int32_t* grid_hw_host, int32_t n_images,
+                           int32_t flags);
+
+/* Encode one image: DeepseekV4Model.encode_image on the "...deepseek_v4.model" page
+ * (vision tower, then aligner unless VIT_NO_ALIGNER).
+ *   in   [grid_h * grid_w, patch_dim] patches, row-major over the grid, each patch
+ *        flattened in [3, ps, ps] C order (DeepseekV4VisionTransformer.forward).
+ *   out  aligner on: [(grid_h/merge)*(grid_w/merge), llm_dim], merged tokens
+ *        row-major over the merged grid (or newline-layout rows with
+ *        VIT_OUT_NLAYOUT: [(h'*(w'+1)+2), llm_dim]);
+ *        aligner off: [grid_h*grid_w, vision_dim].  dtype = cfg.dtype.
+ *   ws   device workspace of ws_bytes >= vit_workspace_bytes(); contents scratch.
+ * Errors: VIT_E_ARG (null pointer), VIT_E_SHAPE (dims), VIT_E_ODD_GRID (aligner
+ * on an odd grid), VIT_E_WORKSPACE, VIT_E_HIP.  out must not alias in or ws. */
+vit_status vit_encode(const vit_config* cfg, const vit_weights* w, const void* in, int32_t grid_h,
+                      int32_t grid_w, int32_t flags, void* out, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* Encode a batch of images packed back to back (the page's pixel_values with
+ * image_grid_hws [n_images, 2]).  Each image attends only to itself (block-
+ * diagonal attention) with rotary positions restarting at (0, 0).  Outputs are
+ * concatenated in image order with the per-image layouts of vit_encode.
+ * grid_hw_host is a HOST array [n_images, 2]; 1 <= n_images <= VIT_MAX_IMAGES. */
+vit_status vit_encode_varlen(const vit_config* cfg, const vit_weights* w, const void* in,
+                             const int32_t* grid_hw_host, int32_t n_images, int32_t flags,
+                             void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Index arrays of one image's aligner layout (the "permutation" and "N-layout"
+ * columns of the PR #3772 parity table).  All device int32:
+ *   perm    [grid_h*grid_w]: slot 4t+s of merged token t holds patch perm[4t+s];
+ *           token t = i*(grid_w/2)+j covers rows 2i..2i+1, cols 2j..2j+1 in the
+ *           order TL, TR, BL, BR.
+ *   nl_type [h'*(w'+1)+2]: 0 START, 1 IMAGE, 2 NEWLINE, 3 END for the span
+ *           [START] + per merged row (w' IMAGE, NEWLINE) + [END].
+ *   nl_src  [same]: merged token index of IMAGE slots, -1 for sentinels.
+ * Any of the three pointers may be NULL (skipped).  merge must be 2. */
+vit_status vit_aligner_layout(int32_t grid_h, int32_t grid_w, int32_t merge, int32_t* perm,
+                              int32_t* nl_type, int32_t* nl_src, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Step entry points: the single steps of the path, for per-step parity tests.
+ * ------------------------------------------------------------------------- */
+
+/* RMSNorm (DeepseekV4VisionRMSNorm): out[r] = w * x[r] / sqrt(mean(x[r]^2) + eps),
+ * computed in fp32.  x [rows, dim] float32, w [dim] float32, out [rows, dim] of
+ * out_dtype.  dim must be a multiple of 4. */
+vit_status vit_rmsnorm(const float* x, const float* w, float eps, int64_t rows, int32_t dim,
+                       int32_t out_dtype, void* out, void* stream);
+
+/* Rotary table for a batch of grids (get_vision_cos_sin on the vision page):
+ * table [sum P, head_dim/2] of float2 (cos, sin); entries k < head_dim/4 use the
+ * patch row angle row * theta^(-k/(head_dim/4)), the rest the column angle. */
+vit_status vit_rope_table(const int32_t* grid_hw_host, int32_t n_images, int32_t head_dim,
+                          float theta, void* table, void* stream);
+
+/* Half-split 2D rotary (apply_vision_rotary) in place on the q and k parts of a
+ * packed qkv buffer [P, 3*n_heads*head_dim] of dtype, fp32 math, using a table
+ * from vit_rope_table. */
+vit_status vit_rope(int32_t dtype, void* qkv, const void* table, int64_t P, int32_t n_heads,
+                    int32_t head_dim, void* stream);
+
+/* Full bidirectional attention per image and head (DeepseekV4VisionAttention):
+ * out[p, h*D:(h+1)*D] = softmax(q k^T / sqrt(D)) v over the patches of p's image.
+ * qkv [P, 3*n_heads*D] (rows [q|k|v], rotary already applied), out [P, n_heads*D]. */
+vit_status vit_attention_varlen(int32_t dtype, const void* qkv, const int32_t* grid_hw_host,
+                                int32_t n_images, int32_t n_heads, int32_t head_dim, void* out,
+                                void* stream);
+
+/* GEMM epilogues for vit_gemm */
+enum {
+  VIT_EPI_STORE = 0,     /* C (dtype)   = A B^T                      */
+  VIT_EPI_STORE_F32 = 1, /* C (float32) = A B^T                      */
+  VIT_EPI_ADD_F32 = 2,   /* C (float32) += A B^T (residual, in place)  */
+  VIT_EPI_SWIGLU = 3,    /* C (dtype)   = silu(A B^T) * (A B2^T)      */
+};
+
+/* C[M, N] = epilogue(A[M, K] . B[N, K]^T): the bias-free linear maps of the block
+ * (wqkv, out-projection, SwiGLU gate/up, down) and of the aligner.  Leading
+ * dimensions are in elements.  bf16: K, lda, ldb multiple of 8 and 16-byte aligned
+ * A/B.  B2 is only read by VIT_EPI_SWIGLU. */
+vit_status vit_gemm(int32_t dtype, int32_t epilogue, const void* A, int64_t lda, const void* B,
+                    const void* B2, int64_t ldb, void* C, int64_t ldc, int64_t M, int64_t N,
+                    int64_t K, void* stream);
+
+/* 2x2 aligner gather for a batch: G[t_i + t, s*d:(s+1)*d] = x[off_i + perm_i[4t+s]]
+ * with x [sum P, d] and G [sum P/4, 4d] of dtype (DeepseekV4VisionAligner). */
+vit_status vit_aligner_gather(int32_t dtype, const void* x, const int32_t* grid_hw_host,
+                              int32_t n_images, int32_t d, void* G, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Kernel timing with HIP events (for measurement tools).  When enabled for a
+ * kernel class, every launch of that class inside vit_encode(_varlen) is
+ * bracketed by events on the call's stream; vit_profile_read synchronises them
+ * and returns the summed duration and the launch count, then resets.
+ * ------------------------------------------------------------------------- */
+enum {
+  VIT_K_EMBED = 0,
+  VIT_K_RMSNORM = 1,
+  VIT_K_QKV = 2,
+  VIT_K_ROPE = 3,
+  VIT_K_ATTN = 4,
+  VIT_K_OUTPROJ = 5,
+  VIT_K_GATEUP = 6,
+  VIT_K_DOWN = 7,
+  VIT_K_GATHER = 8,
+  VIT_K_ALIGNER = 9,
+  VIT_K_COUNT = 10,
+};
+vit_status vit_profile_enable(int32_t kernel_class, int32_t on);
+vit_status vit_profile_read(int32_t kernel_class, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VITENC_H */

@@ -1,0 +1,102 @@
+"""CPU tier: the C ABI library loads, exports every symbol declared in the
+header, and rejects bad arguments on the host before any GPU work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from vision_transformer_encoder_image_amd import _lib, api, configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vitenc.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vit_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libvitenc.so is not built; run __graft_entry__.build() first")
+    return _lib.load()
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    for n in ("vit_encode", "vit_encode_varlen", "vit_workspace_bytes", "vit_aligner_layout",
+              "vit_status_str", "vit_rmsnorm", "vit_rope", "vit_attention_varlen", "vit_gemm"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in vitenc.h but not exported"
+        assert n in _lib.SIGNATURES, f"{n} has no ctypes signature"
+
+
+def test_status_strings(lib):
+    assert lib.vit_status_str(0) == b"ok"
+    assert b"workspace" in lib.vit_status_str(-4)
+    assert lib.vit_status_str(12345) == b"unknown status"
+
+
+def test_config_struct_layout():
+    assert ctypes.sizeof(_lib.VitConfig) == 44
+    assert ctypes.sizeof(_lib.VitWeights) == 10 * ctypes.sizeof(ctypes.c_void_p)
+
+
+def test_host_validation_errors(lib):
+    cfg = api.c_config(configs.get(1))
+    g = _lib.grid_array([(28, 28)])
+    # null config / weights / buffers -> VIT_E_ARG, before any device work
+    assert lib.vit_encode(None, None, None, 28, 28, 0, None, None, 0, None) == _lib.VIT_E_ARG
+    assert lib.vit_encode(ctypes.byref(cfg), None, None, 28, 28, 0, None, None, 0, None) == _lib.VIT_E_ARG
+    # odd grid with the aligner on
+    assert lib.vit_aligner_layout(27, 37, 2, None, None, None, None) == _lib.VIT_E_ODD_GRID
+    assert lib.vit_workspace_bytes(ctypes.byref(cfg), _lib.grid_array([(27, 37)]), 1, 0) == 0
+    assert b"not divisible" in lib.vit_last_error()
+    # the same grid is fine without the aligner
+    assert lib.vit_workspace_bytes(ctypes.byref(cfg), _lib.grid_array([(27, 37)]), 1,
+                                   _lib.VIT_NO_ALIGNER) > 0
+    # bad shapes
+    bad = api.c_config(configs.get(1))
+    bad.head_dim = 60
+    assert lib.vit_workspace_bytes(ctypes.byref(bad), g, 1, 0) == 0
+    bad = api.c_config(configs.get(1))
+    bad.n_heads = 8  # 8 * 64 != 1024
+    assert lib.vit_workspace_bytes(ctypes.byref(bad), g, 1, 0) == 0
+    # image count limits
+    assert lib.vit_workspace_bytes(ctypes.byref(cfg), g, 0, 0) == 0
+    many = _lib.grid_array([(2, 2)] * (_lib.VIT_MAX_IMAGES + 1))
+    assert lib.vit_workspace_bytes(ctypes.byref(cfg), many, _lib.VIT_MAX_IMAGES + 1, 0) == 0
+    ok = _lib.grid_array([(2, 2)] * _lib.VIT_MAX_IMAGES)
+    assert lib.vit_workspace_bytes(ctypes.byref(cfg), ok, _lib.VIT_MAX_IMAGES, 0) > 0
+    # GEMM argument checks (host side)
+    assert lib.vit_gemm(0, 0, None, 8, None, None, 8, None, 8, 1, 1, 8, None) == _lib.VIT_E_ARG
+    assert lib.vit_gemm(0, 9, 16, 8, 16, None, 8, 16, 8, 1, 1, 8, None) == _lib.VIT_E_ARG
+    assert lib.vit_gemm(0, 0, 16, 12, 16, None, 12, 16, 8, 1, 1, 12, None) == _lib.VIT_E_SHAPE
+    assert lib.vit_gemm(0, 0, 8, 16, 16, None, 16, 16, 8, 1, 1, 16, None) == _lib.VIT_E_ARG  # misaligned
+
+
+def test_workspace_grows_with_patches(lib):
+    c = configs.get(2)
+    small = api.workspace_bytes(c, [(8, 8)], aligner=False)
+    big = api.workspace_bytes(c, list(c.grids), aligner=False)
+    assert big > small > 0
+    # the plan holds at least the fp32 residual stream and the qkv buffer
+    P = c.total_patches
+    assert big >= P * c.vision_dim * 4 + P * 3 * c.vision_dim * 2
+
+
+def test_configs_flops_match_hand_count():
+    c = configs.get(2)
+    assert c.total_patches == 3562  # 999 + 999 + 780 + 784
+    P, d, h = 3562, 1024, 2816
+    attn = 4 * d * (999 ** 2 * 2 + 780 ** 2 + 784 ** 2)
+    assert c.block_flops() == 8 * P * d * d + 6 * P * d * h + attn

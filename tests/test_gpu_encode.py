@@ -1,0 +1,148 @@
+"""GPU tier, whole path: vit_encode / vit_encode_varlen against the oracle on the
+five seeded workloads, plus determinism, newline-layout output and error paths."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_util import TOL, global_rel_err, rowwise_rel_err, to_np
+from vision_transformer_encoder_image_amd import _lib, api, configs, synth
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+_cache = {}
+
+
+def _setup(idx):
+    if idx not in _cache:
+        cfg = configs.get(idx)
+        inp = synth.make_inputs(cfg, seed=idx)
+        w = api.DeviceWeights(cfg, inp["weights"])
+        x = torch.from_numpy(inp["patches"]).to("cuda", torch.bfloat16 if cfg.dtype == "bf16"
+                                                  else torch.float32)
+        _cache.clear()
+        _cache[idx] = (cfg, inp, w, x)
+    return _cache[idx]
+
+
+def _oracle(cfg, inp, grids=None, patches=None):
+    return oracle.encode_varlen(inp["patches"] if patches is None else patches,
+                                inp["grids"] if grids is None else grids, inp["weights"],
+                                cfg.n_heads, cfg.rms_eps, cfg.rope_theta, with_aligner=cfg.aligner)
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_workload_full_parity(idx):
+    cfg, inp, w, x = _setup(idx)
+    got = to_np(api.Encoder(cfg, w, cfg.grids, aligner=cfg.aligner)(x))
+    ref = _oracle(cfg, inp)
+    assert got.shape == ref.shape
+    err = rowwise_rel_err(got, ref)
+    print(f"{cfg.name}: row-wise rel err {err:.3e}, global {global_rel_err(got, ref):.3e}")
+    assert err < TOL[cfg.dtype], err
+
+
+def test_highres_full_tower_against_stored_oracle():
+    """64x64 grid, 32 blocks, head_dim 72: rows sampled from the stored oracle run."""
+    path = os.path.join(GOLDEN, "expected_highres_64x64_full_tower.npz")
+    ref = np.load(path)
+    cfg, inp, w, x = _setup(3)
+    got = to_np(api.Encoder(cfg, w, cfg.grids, aligner=True)(x))
+    assert tuple(ref["shape"]) == got.shape
+    err = rowwise_rel_err(got[ref["rows"]], ref["values"])
+    print(f"{cfg.name}: row-wise rel err {err:.3e} on {len(ref['rows'])} rows")
+    assert err < TOL["bf16"], err
+
+
+def test_throughput_batch_sampled_images():
+    """16 x 48x48 images: images are independent, so the oracle runs on two of them."""
+    cfg, inp, w, x = _setup(4)
+    got = to_np(api.Encoder(cfg, w, cfg.grids, aligner=True)(x))
+    P, T = 48 * 48, 24 * 24
+    for i in (0, 15):
+        ref = _oracle(cfg, inp, grids=[(48, 48)], patches=inp["patches"][i * P:(i + 1) * P])
+        err = rowwise_rel_err(got[i * T:(i + 1) * T], ref)
+        print(f"{cfg.name} image {i}: row-wise rel err {err:.3e}")
+        assert err < TOL["bf16"], err
+
+
+def test_single_image_entry_matches_varlen_bitwise():
+    cfg, inp, w, x = _setup(1)
+    a = api.encode(x, cfg.grids[0], w, aligner=True)
+    b = api.encode_varlen(x, cfg.grids, w, aligner=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_deterministic_run_to_run():
+    cfg, inp, w, x = _setup(2)
+    enc = api.Encoder(cfg, w, cfg.grids, aligner=False)
+    a = enc(x).clone()
+    b = enc(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_varlen_equals_per_image_runs():
+    cfg, inp, w, x = _setup(2)
+    whole = to_np(api.Encoder(cfg, w, cfg.grids, aligner=False)(x))
+    off = 0
+    for gh, gw in cfg.grids:
+        P = gh * gw
+        one = to_np(api.encode(x[off:off + P].contiguous(), (gh, gw), w, aligner=False))
+        np.testing.assert_array_equal(one, whole[off:off + P])
+        off += P
+
+
+def test_newline_layout_output():
+    cfg, inp, w, x = _setup(1)
+    plain = api.encode(x, cfg.grids[0], w, aligner=True)
+    nl = api.encode(x, cfg.grids[0], w, aligner=True, nlayout=True)
+    torch.cuda.synchronize()
+    types, src = oracle.nlayout(*cfg.grids[0])
+    img = types == 1
+    assert nl.shape[0] == len(types)
+    assert torch.equal(nl[torch.from_numpy(np.nonzero(img)[0]).cuda()], plain[torch.from_numpy(src[img]).long().cuda()])
+    assert (nl[torch.from_numpy(np.nonzero(~img)[0]).cuda()] == 0).all()  # sentinel rows untouched
+
+
+def test_tiny_and_ragged_edge_grids():
+    """1x1, 1xN and tall grids in one bf16 batch (encoder only), against the oracle."""
+    cfg = configs.VitConfig("edge", ((1, 1), (1, 17), (33, 2), (5, 5)), 256, 4, 704, 2, 0, "bf16")
+    inp = synth.make_inputs(cfg, seed=99)
+    w = api.DeviceWeights(cfg, inp["weights"])
+    x = torch.from_numpy(inp["patches"]).to("cuda", torch.bfloat16)
+    got = to_np(api.Encoder(cfg, w, cfg.grids, aligner=False)(x))
+    ref = _oracle(cfg, inp)
+    assert rowwise_rel_err(got, ref) < TOL["bf16"]
+
+
+def test_max_images_per_call():
+    cfg = configs.VitConfig("many", tuple([(2, 2)] * _lib.VIT_MAX_IMAGES), 256, 4, 704, 1, 512, "bf16")
+    inp = synth.make_inputs(cfg, seed=98)
+    w = api.DeviceWeights(cfg, inp["weights"])
+    x = torch.from_numpy(inp["patches"]).to("cuda", torch.bfloat16)
+    got = to_np(api.Encoder(cfg, w, cfg.grids, aligner=True)(x))
+    for i in (0, 77, _lib.VIT_MAX_IMAGES - 1):
+        ref = _oracle(cfg, inp, grids=[(2, 2)], patches=inp["patches"][4 * i:4 * i + 4])
+        assert rowwise_rel_err(got[i:i + 1], ref) < TOL["bf16"]
+
+
+def test_error_paths_on_device():
+    cfg, inp, w, x = _setup(1)
+    enc = api.Encoder(cfg, w, cfg.grids, aligner=True)
+    lib = _lib.load()
+    out = torch.empty(enc.out_shape, dtype=torch.bfloat16, device="cuda")
+    st = lib.vit_encode(ctypes.byref(enc.c_cfg), ctypes.byref(w.c), x.data_ptr(), 27, 37, 0,
+                        out.data_ptr(), enc.ws.data_ptr(), enc.ws_bytes,
+                        torch.cuda.current_stream().cuda_stream)
+    assert st == _lib.VIT_E_ODD_GRID
+    out = torch.empty(enc.out_shape, dtype=torch.bfloat16, device="cuda")
+    st = lib.vit_encode_varlen(ctypes.byref(enc.c_cfg), ctypes.byref(w.c), x.data_ptr(), enc.c_grids,
+                               1, enc.flags, out.data_ptr(), enc.ws.data_ptr(), enc.ws_bytes - 256,
+                               torch.cuda.current_stream().cuda_stream)
+    assert st == _lib.VIT_E_WORKSPACE

@@ -1,0 +1,211 @@
+"""GPU tier, per step: every kernel of the path against the oracle on the same
+seeded inputs, through the C ABI.  Sizes span several tiles and ragged tails."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_util import TOL, rowwise_rel_err, to_np
+from vision_transformer_encoder_image_amd import _lib, api, synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _dev(a, dtype="f32"):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV, TDT[dtype])
+
+
+# ---------------------------------------------------------------- GEMM
+GEMM_SHAPES = [(1, 8, 8), (130, 136, 72), (257, 200, 640), (300, 4304, 1152), (64, 1024, 4304),
+               (1000, 3072, 1024)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", GEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("epi", ["store", "store_f32", "add_f32", "swiglu"])
+def test_gemm_epilogues(dtype, shape, epi):
+    M, N, K = shape
+    if dtype == "f32" and M * N * K > 2e8:
+        pytest.skip("fp32 vector GEMM only serves the small single-precision workload")
+    bf = dtype == "bf16"
+    A = synth.random_array((M, K), 1, bf16=bf)
+    B = synth.random_array((N, K), 2, std=0.05, bf16=bf)
+    B2 = synth.random_array((N, K), 3, std=0.05, bf16=bf)
+    C0 = synth.random_array((M, N), 4)
+    code = {"store": _lib.VIT_EPI_STORE, "store_f32": _lib.VIT_EPI_STORE_F32,
+            "add_f32": _lib.VIT_EPI_ADD_F32, "swiglu": _lib.VIT_EPI_SWIGLU}[epi]
+    C = _dev(C0) if epi == "add_f32" else None
+    got = api.gemm(_dev(A, dtype), _dev(B, dtype), code, B2=_dev(B2, dtype) if epi == "swiglu" else None,
+                   C=C)
+    torch.cuda.synchronize()
+    if epi == "swiglu":
+        ref = oracle.mlp(A, B, B2, np.eye(N))
+    else:
+        ref = oracle.linear(A, B)
+    if epi == "add_f32":
+        ref = ref + C0
+    err = rowwise_rel_err(to_np(got), ref)
+    # fp32 outputs carry only accumulation error; bf16 outputs one rounding (2^-9)
+    tol = 1e-4 if (dtype == "f32" or epi in ("store_f32", "add_f32")) else 8e-3
+    assert err < tol, err
+
+
+def test_gemm_full_qkv_shape_sampled_rows():
+    """wqkv at the ragged-batch size (M=3562, N=3072, K=1024), rows sampled."""
+    M, N, K = 3562, 3072, 1024
+    A = synth.random_array((M, K), 5, bf16=True)
+    B = synth.random_array((N, K), 6, std=0.02, bf16=True)
+    got = to_np(api.gemm(_dev(A, "bf16"), _dev(B, "bf16")))
+    rows = np.r_[0:5, 1791:1795, M - 40:M]
+    assert rowwise_rel_err(got[rows], oracle.linear(A[rows], B)) < 8e-3
+
+
+# ---------------------------------------------------------------- RMSNorm
+@pytest.mark.parametrize("dim", [256, 1024, 1152])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_rmsnorm(dim, out_dtype):
+    rows = 777
+    x = synth.random_array((rows, dim), 7)
+    x *= np.exp(synth.random_array((rows, 1), 8)).astype(np.float32)  # varied row scales
+    w = 1 + synth.random_array((dim,), 9, std=0.02)
+    got = to_np(api.rmsnorm(_dev(x), _dev(w), 1e-6, out_dtype))
+    ref = oracle.rmsnorm(x, w, 1e-6)
+    assert rowwise_rel_err(got, ref) < (1e-5 if out_dtype == "f32" else 8e-3)
+
+
+def test_rmsnorm_zero_rows_are_zero():
+    x = np.zeros((4, 256), dtype=np.float32)
+    got = to_np(api.rmsnorm(_dev(x), _dev(np.ones(256)), 1e-6, "f32"))
+    assert (got == 0).all()
+
+
+# ---------------------------------------------------------------- rotary
+ROPE_GRIDS = [[(1, 1)], [(8, 8)], [(27, 37), (37, 27), (10, 78), (112, 7)], [(3, 5), (64, 64)]]
+
+
+@pytest.mark.parametrize("grids", ROPE_GRIDS, ids=lambda g: "_".join(f"{a}x{b}" for a, b in g))
+@pytest.mark.parametrize("D", [64, 72])
+def test_rope_table(grids, D):
+    t = to_np(api.rope_table(grids, D))
+    off = 0
+    for gh, gw in grids:
+        cos, sin = oracle.rope_table(gh, gw, D)
+        P = gh * gw
+        assert np.abs(t[off:off + P, :, 0] - cos).max() < 1e-6
+        assert np.abs(t[off:off + P, :, 1] - sin).max() < 1e-6
+        off += P
+
+
+@pytest.mark.parametrize("grids", ROPE_GRIDS, ids=lambda g: "_".join(f"{a}x{b}" for a, b in g))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 72])
+def test_rope_apply(grids, dtype, D):
+    H = 4
+    d = H * D
+    P = sum(a * b for a, b in grids)
+    qkv = synth.random_array((P, 3 * d), 10, bf16=dtype == "bf16")
+    t = api.rope_table(grids, D)
+    got = to_np(api.rope_(_dev(qkv, dtype), t, H, D))
+    off = 0
+    for gh, gw in grids:
+        cos, sin = oracle.rope_table(gh, gw, D)
+        sl = slice(off, off + gh * gw)
+        for part in range(2):
+            x = qkv[sl, part * d:(part + 1) * d].reshape(-1, H, D)
+            ref = oracle.apply_rope(x, cos, sin).reshape(-1, d)
+            err = rowwise_rel_err(got[sl, part * d:(part + 1) * d], ref)
+            assert err < (1e-6 if dtype == "f32" else 8e-3), (part, err)
+        # v untouched, and position (0, 0) of every image is the identity (bitwise)
+        np.testing.assert_array_equal(got[sl, 2 * d:], qkv[sl, 2 * d:])
+        np.testing.assert_array_equal(got[off, :2 * d], qkv[off, :2 * d])
+        off += gh * gw
+
+
+def test_rope_preserves_pair_norms_on_gpu():
+    grids, D, H = [(40, 30)], 64, 2
+    d = H * D
+    qkv = synth.random_array((1200, 3 * d), 11)
+    got = to_np(api.rope_(_dev(qkv), api.rope_table(grids, D), H, D))
+    for part in range(2):
+        x = qkv[:, part * d:(part + 1) * d].reshape(-1, H, 4, D // 4)
+        y = got[:, part * d:(part + 1) * d].reshape(-1, H, 4, D // 4)
+        for half in range(2):
+            n_in = x[:, :, 2 * half] ** 2 + x[:, :, 2 * half + 1] ** 2
+            n_out = y[:, :, 2 * half] ** 2 + y[:, :, 2 * half + 1] ** 2
+            np.testing.assert_allclose(n_out, n_in, rtol=1e-5, atol=1e-6)
+
+
+# ---------------------------------------------------------------- attention
+ATTN_GRIDS = [[(1, 1)], [(3, 5)], [(8, 8)], [(2, 3), (1, 1), (9, 15), (1, 130)],
+              [(27, 37), (37, 27), (10, 78), (112, 7)]]
+
+
+def _attn_ref(qkv, grids, H, D):
+    d = H * D
+    out = np.empty((qkv.shape[0], d))
+    off = 0
+    for gh, gw in grids:
+        sl = slice(off, off + gh * gw)
+        q = qkv[sl, 0:d].reshape(-1, H, D)
+        k = qkv[sl, d:2 * d].reshape(-1, H, D)
+        v = qkv[sl, 2 * d:].reshape(-1, H, D)
+        out[sl] = oracle.attention(q, k, v).reshape(-1, d)
+        off += gh * gw
+    return out
+
+
+@pytest.mark.parametrize("grids", ATTN_GRIDS, ids=lambda g: "_".join(f"{a}x{b}" for a, b in g))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 72])
+def test_attention_varlen(grids, dtype, D):
+    H = 4 if sum(a * b for a, b in grids) > 1000 else 3
+    P = sum(a * b for a, b in grids)
+    qkv = synth.random_array((P, 3 * H * D), 12, bf16=dtype == "bf16")
+    got = to_np(api.attention_varlen(_dev(qkv, dtype), grids, H, D))
+    ref = _attn_ref(qkv, grids, H, D)
+    err = rowwise_rel_err(got, ref)
+    assert err < (1e-5 if dtype == "f32" else 1e-2), err
+
+
+def test_attention_single_patch_returns_v():
+    H, D = 2, 64
+    qkv = synth.random_array((1, 3 * H * D), 13, bf16=True)
+    got = to_np(api.attention_varlen(_dev(qkv, "bf16"), [(1, 1)], H, D))
+    np.testing.assert_array_equal(got[0], qkv[0, 2 * H * D:])
+
+
+def test_attention_large_logits_stay_finite():
+    """Scaled-up q/k (logits ~ +-100) exercise the running max of the online softmax."""
+    H, D, grids = 2, 64, [(20, 20)]
+    qkv = synth.random_array((400, 3 * H * D), 14, std=4.0, bf16=True)
+    got = to_np(api.attention_varlen(_dev(qkv, "bf16"), grids, H, D))
+    assert np.isfinite(got).all()
+    assert rowwise_rel_err(got, _attn_ref(qkv, grids, H, D)) < 2e-2
+
+
+# ---------------------------------------------------------------- aligner layout / gather
+@pytest.mark.parametrize("grid", [(2, 2), (4, 6), (28, 28), (64, 64), (10, 78), (112, 8)])
+def test_aligner_layout_bit_exact(grid):
+    gh, gw = grid
+    perm, t, s = api.aligner_layout(gh, gw)
+    rt, rs = oracle.nlayout(gh, gw)
+    np.testing.assert_array_equal(perm.cpu().numpy(), oracle.aligner_perm(gh, gw))
+    np.testing.assert_array_equal(t.cpu().numpy(), rt)
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_aligner_gather_bitwise(dtype):
+    grids = [(4, 6), (28, 28), (2, 2), (10, 78)]
+    d = 1024 if dtype == "bf16" else 256
+    P = sum(a * b for a, b in grids)
+    x = synth.random_array((P, d), 15, bf16=dtype == "bf16")
+    got = to_np(api.aligner_gather(_dev(x, dtype), grids))
+    ref, off = [], 0
+    for gh, gw in grids:
+        ref.append(oracle.aligner_gather(x[off:off + gh * gw], gh, gw))
+        off += gh * gw
+    np.testing.assert_array_equal(got, np.concatenate(ref))

@@ -1,0 +1,100 @@
+"""ctypes view of ``libvitenc.so`` (declarations mirror ``include/vitenc.h``).
+
+Loading fails loudly when the library has not been built: there is no fallback
+path, every step of the encoder runs in the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvitenc.so")
+
+VIT_OK, VIT_E_ARG, VIT_E_SHAPE, VIT_E_ODD_GRID, VIT_E_WORKSPACE, VIT_E_HIP = 0, -1, -2, -3, -4, -5
+VIT_BF16, VIT_F32 = 0, 1
+VIT_NO_ALIGNER, VIT_OUT_NLAYOUT = 1, 2
+VIT_MAX_IMAGES = 128
+VIT_EPI_STORE, VIT_EPI_STORE_F32, VIT_EPI_ADD_F32, VIT_EPI_SWIGLU = 0, 1, 2, 3
+KERNEL_CLASSES = ["embed", "rmsnorm", "qkv", "rope", "attn", "outproj", "gateup", "down",
+                  "gather", "aligner"]
+
+c_i32, c_i64, c_f32, c_vp, c_size = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                     ctypes.c_void_p, ctypes.c_size_t)
+P_i32 = ctypes.POINTER(ctypes.c_int32)
+
+
+class VitConfig(ctypes.Structure):
+    _fields_ = [("vision_dim", c_i32), ("n_heads", c_i32), ("head_dim", c_i32),
+                ("mlp_hidden", c_i32), ("n_blocks", c_i32), ("patch_dim", c_i32),
+                ("merge", c_i32), ("llm_dim", c_i32), ("rope_theta", c_f32),
+                ("rms_eps", c_f32), ("dtype", c_i32)]
+
+
+class VitWeights(ctypes.Structure):
+    _fields_ = [("patch_embed", c_vp), ("wqkv", ctypes.POINTER(c_vp)),
+                ("wo", ctypes.POINTER(c_vp)), ("w_gate", ctypes.POINTER(c_vp)),
+                ("w_up", ctypes.POINTER(c_vp)), ("w_down", ctypes.POINTER(c_vp)),
+                ("norm1", ctypes.POINTER(c_vp)), ("norm2", ctypes.POINTER(c_vp)),
+                ("final_norm", c_vp), ("aligner", c_vp)]
+
+
+# name -> (restype, argtypes); every function declared in include/vitenc.h
+SIGNATURES = {
+    "vit_status_str": (ctypes.c_char_p, [c_i32]),
+    "vit_last_error": (ctypes.c_char_p, []),
+    "vit_workspace_bytes": (c_size, [ctypes.POINTER(VitConfig), P_i32, c_i32, c_i32]),
+    "vit_encode": (c_i32, [ctypes.POINTER(VitConfig), ctypes.POINTER(VitWeights), c_vp, c_i32,
+                           c_i32, c_i32, c_vp, c_vp, c_size, c_vp]),
+    "vit_encode_varlen": (c_i32, [ctypes.POINTER(VitConfig), ctypes.POINTER(VitWeights), c_vp,
+                                  P_i32, c_i32, c_i32, c_vp, c_vp, c_size, c_vp]),
+    "vit_aligner_layout": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),
+    "vit_rmsnorm": (c_i32, [c_vp, c_vp, c_f32, c_i64, c_i32, c_i32, c_vp, c_vp]),
+    "vit_rope_table": (c_i32, [P_i32, c_i32, c_i32, c_f32, c_vp, c_vp]),
+    "vit_rope": (c_i32, [c_i32, c_vp, c_vp, c_i64, c_i32, c_i32, c_vp]),
+    "vit_attention_varlen": (c_i32, [c_i32, c_vp, P_i32, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "vit_gemm": (c_i32, [c_i32, c_i32, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64,
+                         c_i64, c_vp]),
+    "vit_aligner_gather": (c_i32, [c_i32, c_vp, P_i32, c_i32, c_i32, c_vp, c_vp]),
+    "vit_profile_enable": (c_i32, [c_i32, c_i32]),
+    "vit_profile_read": (c_i32, [c_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class VitError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({detail})")
+
+
+def load() -> ctypes.CDLL:
+    """Load the built HIP library (raises if it is missing: no CPU fallback exists)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build the HIP library first "
+                    "(python -c 'import __graft_entry__ as g; g.build()')")
+            lib = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+        return _lib
+
+
+def check(status: int, where: str) -> None:
+    if status != VIT_OK:
+        lib = load()
+        detail = lib.vit_last_error().decode() or lib.vit_status_str(status).decode()
+        raise VitError(status, where, detail)
+
+
+def grid_array(grids):
+    flat = [int(v) for g in grids for v in g]
+    return (ctypes.c_int32 * len(flat))(*flat)

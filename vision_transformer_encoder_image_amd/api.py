@@ -1,0 +1,243 @@
+"""Python binding of the gfx950 encoder library (argument marshalling only).
+
+PyTorch provides device memory and the current HIP stream; every step of the
+encoder runs inside ``libvitenc.so``.  Names follow the C ABI in
+``include/vitenc.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import _lib
+from .configs import VitConfig
+
+_TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
+_CODE = {"bf16": _lib.VIT_BF16, "f32": _lib.VIT_F32}
+
+
+def _stream(device=None) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _require_cuda(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors passed to the HIP library must live on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors passed to the HIP library must be contiguous")
+
+
+def c_config(cfg: VitConfig) -> _lib.VitConfig:
+    return _lib.VitConfig(cfg.vision_dim, cfg.n_heads, cfg.head_dim, cfg.mlp_hidden, cfg.n_blocks,
+                          cfg.patch_dim, cfg.merge, cfg.llm_dim, cfg.rope_theta, cfg.rms_eps,
+                          _CODE[cfg.dtype])
+
+
+class DeviceWeights:
+    """Encoder weights resident on the GPU plus the C struct pointing at them."""
+
+    def __init__(self, cfg: VitConfig, host: Dict, device="cuda"):
+        dt = _TORCH_DTYPE[cfg.dtype]
+
+        def mat(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device=device, dtype=dt)
+
+        def vec(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device=device)
+
+        self.cfg = cfg
+        self.patch_embed = mat(host["patch_embed"])
+        self.blocks = []
+        for b in host["blocks"]:
+            self.blocks.append({k: (vec(v) if k.startswith("norm") else mat(v)) for k, v in b.items()})
+        self.final_norm = vec(host["final_norm"])
+        self.aligner = mat(host["aligner"]) if host.get("aligner") is not None else None
+        n = len(self.blocks)
+
+        def arr(key):
+            return (ctypes.c_void_p * max(n, 1))(*[b[key].data_ptr() for b in self.blocks])
+
+        self._arrays = {k: arr(k) for k in ("wqkv", "wo", "w_gate", "w_up", "w_down", "norm1", "norm2")}
+        self.c = _lib.VitWeights(
+            self.patch_embed.data_ptr(), self._arrays["wqkv"], self._arrays["wo"],
+            self._arrays["w_gate"], self._arrays["w_up"], self._arrays["w_down"],
+            self._arrays["norm1"], self._arrays["norm2"], self.final_norm.data_ptr(),
+            None if self.aligner is None else self.aligner.data_ptr())
+
+
+def output_rows(cfg: VitConfig, grids: Sequence[Tuple[int, int]], aligner: bool, nlayout: bool) -> int:
+    if not aligner:
+        return sum(h * w for h, w in grids)
+    m = cfg.merge
+    if nlayout:
+        return sum((h // m) * (w // m + 1) + 2 for h, w in grids)
+    return sum((h // m) * (w // m) for h, w in grids)
+
+
+def workspace_bytes(cfg: VitConfig, grids, aligner=True, nlayout=False) -> int:
+    lib = _lib.load()
+    flags = (0 if aligner else _lib.VIT_NO_ALIGNER) | (_lib.VIT_OUT_NLAYOUT if nlayout else 0)
+    c = c_config(cfg)
+    n = lib.vit_workspace_bytes(ctypes.byref(c), _lib.grid_array(grids), len(grids), flags)
+    if n == 0:
+        _lib.check(_lib.VIT_E_SHAPE, "vit_workspace_bytes")
+    return n
+
+
+class Encoder:
+    """Reusable encoder call: keeps the workspace for one set of grids."""
+
+    def __init__(self, cfg: VitConfig, weights: DeviceWeights, grids, aligner=True, nlayout=False,
+                 device="cuda"):
+        self.cfg, self.w = cfg, weights
+        self.grids = [tuple(int(v) for v in g) for g in grids]
+        self.aligner, self.nlayout = aligner, nlayout
+        self.flags = (0 if aligner else _lib.VIT_NO_ALIGNER) | (_lib.VIT_OUT_NLAYOUT if nlayout else 0)
+        self.ws_bytes = workspace_bytes(cfg, self.grids, aligner, nlayout)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.c_cfg = c_config(cfg)
+        self.c_grids = _lib.grid_array(self.grids)
+        cols = cfg.llm_dim if aligner else cfg.vision_dim
+        self.out_shape = (output_rows(cfg, self.grids, aligner, nlayout), cols)
+        self.device = device
+
+    def __call__(self, patches: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        _require_cuda(patches)
+        if out is None:
+            alloc = torch.zeros if self.nlayout else torch.empty
+            out = alloc(self.out_shape, dtype=_TORCH_DTYPE[self.cfg.dtype], device=self.device)
+        _require_cuda(out)
+        lib = _lib.load()
+        st = lib.vit_encode_varlen(ctypes.byref(self.c_cfg), ctypes.byref(self.w.c),
+                                   patches.data_ptr(), self.c_grids, len(self.grids), self.flags,
+                                   out.data_ptr(), self.ws.data_ptr(), self.ws_bytes,
+                                   _stream(patches.device))
+        _lib.check(st, "vit_encode_varlen")
+        return out
+
+
+def encode(patches: torch.Tensor, grid: Tuple[int, int], weights: DeviceWeights, aligner=True,
+           nlayout=False) -> torch.Tensor:
+    """vit_encode: one image [gh*gw, patch_dim] -> aligned tokens (or encoded patches)."""
+    cfg = weights.cfg
+    _require_cuda(patches)
+    ws_bytes = workspace_bytes(cfg, [grid], aligner, nlayout)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=patches.device)
+    cols = cfg.llm_dim if aligner else cfg.vision_dim
+    rows = output_rows(cfg, [grid], aligner, nlayout)
+    out = (torch.zeros if nlayout else torch.empty)((rows, cols), dtype=_TORCH_DTYPE[cfg.dtype],
+                                                     device=patches.device)
+    flags = (0 if aligner else _lib.VIT_NO_ALIGNER) | (_lib.VIT_OUT_NLAYOUT if nlayout else 0)
+    c = c_config(cfg)
+    lib = _lib.load()
+    st = lib.vit_encode(ctypes.byref(c), ctypes.byref(weights.c), patches.data_ptr(), grid[0],
+                        grid[1], flags, out.data_ptr(), ws.data_ptr(), ws_bytes,
+                        _stream(patches.device))
+    _lib.check(st, "vit_encode")
+    return out
+
+
+def encode_varlen(patches: torch.Tensor, grids, weights: DeviceWeights, aligner=True,
+                  nlayout=False) -> torch.Tensor:
+    """vit_encode_varlen: packed images with block-diagonal attention."""
+    return Encoder(weights.cfg, weights, grids, aligner, nlayout, patches.device)(patches)
+
+
+def aligner_layout(grid_h: int, grid_w: int, merge: int = 2, device="cuda"):
+    """vit_aligner_layout -> (perm, nl_type, nl_src) int32 tensors."""
+    P = grid_h * grid_w
+    L = (grid_h // merge) * (grid_w // merge + 1) + 2
+    perm = torch.empty(P, dtype=torch.int32, device=device)
+    nl_type = torch.empty(L, dtype=torch.int32, device=device)
+    nl_src = torch.empty(L, dtype=torch.int32, device=device)
+    st = _lib.load().vit_aligner_layout(grid_h, grid_w, merge, perm.data_ptr(), nl_type.data_ptr(),
+                                        nl_src.data_ptr(), _stream(device))
+    _lib.check(st, "vit_aligner_layout")
+    return perm, nl_type, nl_src
+
+
+# ---------------------------------------------------------------- step entry points
+def rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, out_dtype="bf16") -> torch.Tensor:
+    _require_cuda(x, w)
+    assert x.dtype == torch.float32 and w.dtype == torch.float32
+    out = torch.empty(x.shape, dtype=_TORCH_DTYPE[out_dtype], device=x.device)
+    st = _lib.load().vit_rmsnorm(x.data_ptr(), w.data_ptr(), eps, x.shape[0], x.shape[1],
+                                 _CODE[out_dtype], out.data_ptr(), _stream(x.device))
+    _lib.check(st, "vit_rmsnorm")
+    return out
+
+
+def rope_table(grids, head_dim: int, theta: float = 10000.0, device="cuda") -> torch.Tensor:
+    P = sum(h * w for h, w in grids)
+    table = torch.empty((P, head_dim // 2, 2), dtype=torch.float32, device=device)
+    st = _lib.load().vit_rope_table(_lib.grid_array(grids), len(grids), head_dim, theta,
+                                    table.data_ptr(), _stream(device))
+    _lib.check(st, "vit_rope_table")
+    return table
+
+
+def rope_(qkv: torch.Tensor, table: torch.Tensor, n_heads: int, head_dim: int) -> torch.Tensor:
+    _require_cuda(qkv, table)
+    code = _lib.VIT_BF16 if qkv.dtype == torch.bfloat16 else _lib.VIT_F32
+    st = _lib.load().vit_rope(code, qkv.data_ptr(), table.data_ptr(), qkv.shape[0], n_heads,
+                              head_dim, _stream(qkv.device))
+    _lib.check(st, "vit_rope")
+    return qkv
+
+
+def attention_varlen(qkv: torch.Tensor, grids, n_heads: int, head_dim: int) -> torch.Tensor:
+    _require_cuda(qkv)
+    code = _lib.VIT_BF16 if qkv.dtype == torch.bfloat16 else _lib.VIT_F32
+    out = torch.empty((qkv.shape[0], n_heads * head_dim), dtype=qkv.dtype, device=qkv.device)
+    st = _lib.load().vit_attention_varlen(code, qkv.data_ptr(), _lib.grid_array(grids), len(grids),
+                                          n_heads, head_dim, out.data_ptr(), _stream(qkv.device))
+    _lib.check(st, "vit_attention_varlen")
+    return out
+
+
+def gemm(A: torch.Tensor, B: torch.Tensor, epilogue: int = _lib.VIT_EPI_STORE,
+         B2: Optional[torch.Tensor] = None, C: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """vit_gemm: C = epilogue(A . B^T) (A [M, K], B/B2 [N, K])."""
+    _require_cuda(A, B, B2, C)
+    code = _lib.VIT_BF16 if A.dtype == torch.bfloat16 else _lib.VIT_F32
+    M, K = A.shape
+    N = B.shape[0]
+    if C is None:
+        odt = torch.float32 if epilogue in (_lib.VIT_EPI_STORE_F32, _lib.VIT_EPI_ADD_F32) else A.dtype
+        C = torch.zeros((M, N), dtype=odt, device=A.device)
+    st = _lib.load().vit_gemm(code, epilogue, A.data_ptr(), A.stride(0), B.data_ptr(), _ptr(B2),
+                              B.stride(0), C.data_ptr(), C.stride(0), M, N, K, _stream(A.device))
+    _lib.check(st, "vit_gemm")
+    return C
+
+
+def aligner_gather(x: torch.Tensor, grids, merge: int = 2) -> torch.Tensor:
+    _require_cuda(x)
+    code = _lib.VIT_BF16 if x.dtype == torch.bfloat16 else _lib.VIT_F32
+    T = sum(h * w for h, w in grids) // (merge * merge)
+    G = torch.empty((T, merge * merge * x.shape[1]), dtype=x.dtype, device=x.device)
+    st = _lib.load().vit_aligner_gather(code, x.data_ptr(), _lib.grid_array(grids), len(grids),
+                                        x.shape[1], G.data_ptr(), _stream(x.device))
+    _lib.check(st, "vit_aligner_gather")
+    return G
+
+
+def profile_enable(kernel: str, on: bool = True) -> None:
+    _lib.check(_lib.load().vit_profile_enable(_lib.KERNEL_CLASSES.index(kernel), int(on)),
+               "vit_profile_enable")
+
+
+def profile_read(kernel: str) -> Tuple[float, int]:
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _lib.check(_lib.load().vit_profile_read(_lib.KERNEL_CLASSES.index(kernel), ctypes.byref(ms),
+                                            ctypes.byref(n)), "vit_profile_read")
+    return ms.value, n.value

@@ -1,0 +1,460 @@
+// C ABI of the encoder library: argument validation, workspace plan, launch
+// sequence of the vision tower + aligner, per-step entry points, event timing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+vit_status fail(vit_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+vit_status fail(vit_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+vit_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return VIT_OK;
+  return fail(VIT_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define VIT_TRY(expr)                    \
+  do {                                   \
+    vit_status _st = (expr);             \
+    if (_st != VIT_OK) return _st;       \
+  } while (0)
+#define VIT_HIP(expr, what) VIT_TRY(hip_check((expr), (what)))
+
+// ---------------------------------------------------------------- event timing
+struct Prof {
+  std::mutex mu;
+  bool on[VIT_K_COUNT] = {};
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[VIT_K_COUNT];
+  size_t used[VIT_K_COUNT] = {};
+};
+Prof& prof() {
+  static Prof p;
+  return p;
+}
+
+struct ProfScope {
+  int cls;
+  hipStream_t s;
+  hipEvent_t end = nullptr;
+  ProfScope(int c, hipStream_t st) : cls(c), s(st) {
+    Prof& p = prof();
+    std::lock_guard<std::mutex> lk(p.mu);
+    if (!p.on[cls]) return;
+    if (p.used[cls] == p.ev[cls].size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return;
+      if (hipEventCreate(&b) != hipSuccess) {
+        (void)hipEventDestroy(a);
+        return;
+      }
+      p.ev[cls].emplace_back(a, b);
+    }
+    auto& pr = p.ev[cls][p.used[cls]++];
+    (void)hipEventRecord(pr.first, s);
+    end = pr.second;
+  }
+  ~ProfScope() {
+    if (end) (void)hipEventRecord(end, s);
+  }
+};
+
+// ---------------------------------------------------------------- shapes
+size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+size_t esize(int dtype) { return dtype == VIT_BF16 ? 2 : 4; }
+
+vit_status check_config(const vit_config* c) {
+  if (!c) return fail(VIT_E_ARG, "config is NULL");
+  if (c->dtype != VIT_BF16 && c->dtype != VIT_F32) return fail(VIT_E_ARG, "bad dtype %d", c->dtype);
+  if (c->vision_dim <= 0 || c->n_heads <= 0 || c->head_dim <= 0 || c->mlp_hidden <= 0 ||
+      c->n_blocks < 0 || c->patch_dim <= 0 || c->merge <= 0)
+    return fail(VIT_E_SHAPE, "non-positive dimension in config");
+  if (c->vision_dim != c->n_heads * c->head_dim)
+    return fail(VIT_E_SHAPE, "vision_dim %d != n_heads %d * head_dim %d", c->vision_dim,
+                c->n_heads, c->head_dim);
+  if (c->head_dim % 4) return fail(VIT_E_SHAPE, "head_dim %d not a multiple of 4", c->head_dim);
+  if (c->head_dim != 64 && c->head_dim != 72)
+    return fail(VIT_E_SHAPE, "head_dim %d unsupported (64 or 72)", c->head_dim);
+  if (c->vision_dim % 8 || c->mlp_hidden % 8 || c->patch_dim % 4)
+    return fail(VIT_E_SHAPE, "vision_dim and mlp_hidden must be multiples of 8, patch_dim of 4");
+  if (c->merge != 2) return fail(VIT_E_SHAPE, "merge %d unsupported (2)", c->merge);
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail(VIT_E_SHAPE, "bad eps/theta");
+  return VIT_OK;
+}
+
+vit_status build_desc(const int32_t* grid_hw, int32_t n_images, int q_tile, bool need_even,
+                      int merge, VarlenDesc* d) {
+  if (!grid_hw) return fail(VIT_E_ARG, "grid_hw is NULL");
+  if (n_images < 1 || n_images > VIT_MAX_IMAGES)
+    return fail(VIT_E_SHAPE, "n_images %d outside [1, %d]", n_images, VIT_MAX_IMAGES);
+  std::memset(d, 0, sizeof(*d));
+  d->n_images = n_images;
+  int64_t total = 0, tiles = 0;
+  for (int i = 0; i < n_images; ++i) {
+    const int gh = grid_hw[2 * i], gw = grid_hw[2 * i + 1];
+    if (gh <= 0 || gw <= 0) return fail(VIT_E_SHAPE, "image %d has grid %dx%d", i, gh, gw);
+    if (need_even && (gh % merge || gw % merge))
+      return fail(VIT_E_ODD_GRID, "image %d grid %dx%d not divisible by merge %d", i, gh, gw,
+                  merge);
+    d->cu_seqlens[i] = (int32_t)total;
+    d->cu_tiles[i] = (int32_t)tiles;
+    d->grid_w[i] = gw;
+    total += (int64_t)gh * gw;
+    tiles += ((int64_t)gh * gw + q_tile - 1) / q_tile;
+    if (total > (1 << 24)) return fail(VIT_E_SHAPE, "more than 2^24 patches in one call");
+  }
+  d->cu_seqlens[n_images] = (int32_t)total;
+  d->cu_tiles[n_images] = (int32_t)tiles;
+  d->total = (int32_t)total;
+  return VIT_OK;
+}
+
+struct Plan {
+  int64_t P = 0, tokens = 0, Kp = 0;
+  size_t table = 0, xpad = 0, wpe = 0, x = 0, n = 0, qkv = 0, act = 0, G = 0, rowmap = 0;
+  size_t total = 0;
+};
+
+Plan make_plan(const vit_config& c, int64_t P, int flags) {
+  Plan p;
+  const size_t es = esize(c.dtype);
+  const bool aligner = !(flags & VIT_NO_ALIGNER);
+  const int64_t d = c.vision_dim, h = c.mlp_hidden, m2 = (int64_t)c.merge * c.merge;
+  p.P = P;
+  p.tokens = aligner ? P / m2 : 0;
+  p.Kp = c.dtype == VIT_BF16 ? round_up(c.patch_dim, 64) : c.patch_dim;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  p.table = take((size_t)P * (c.head_dim / 2) * sizeof(float2));
+  if (c.dtype == VIT_BF16) {
+    p.xpad = take((size_t)P * p.Kp * es);
+    p.wpe = take((size_t)d * p.Kp * es);
+  }
+  p.x = take((size_t)P * d * sizeof(float));
+  p.n = take((size_t)P * d * es);  // also holds the attention output
+  p.qkv = take((size_t)P * 3 * d * es);
+  p.act = take((size_t)P * h * es);
+  if (aligner) p.G = take((size_t)p.tokens * m2 * d * es);
+  if (aligner && (flags & VIT_OUT_NLAYOUT)) p.rowmap = take((size_t)p.tokens * sizeof(int32_t));
+  p.total = off;
+  return p;
+}
+
+vit_status gemm(int dtype, int epi, const void* A, int64_t lda, const void* B, const void* B2,
+                int64_t ldb, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                const int32_t* rowmap, hipStream_t s) {
+  GemmArgs g;
+  g.A = A;
+  g.B = B;
+  g.B2 = B2;
+  g.C = C;
+  g.rowmap = rowmap;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.ldc = ldc;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  const hipError_t e = dtype == VIT_BF16 ? launch_gemm_bf16(epi, g, s) : launch_gemm_f32(epi, g, s);
+  return hip_check(e, "gemm launch");
+}
+
+vit_status check_weights(const vit_config& c, const vit_weights* w, bool aligner) {
+  if (!w) return fail(VIT_E_ARG, "weights is NULL");
+  if (!w->patch_embed || !w->final_norm) return fail(VIT_E_ARG, "patch_embed/final_norm NULL");
+  if (c.n_blocks > 0 &&
+      (!w->wqkv || !w->wo || !w->w_gate || !w->w_up || !w->w_down || !w->norm1 || !w->norm2))
+    return fail(VIT_E_ARG, "per-block weight array NULL");
+  for (int b = 0; b < c.n_blocks; ++b)
+    if (!w->wqkv[b] || !w->wo[b] || !w->w_gate[b] || !w->w_up[b] || !w->w_down[b] ||
+        !w->norm1[b] || !w->norm2[b])
+      return fail(VIT_E_ARG, "block %d has a NULL weight", b);
+  if (aligner && !w->aligner) return fail(VIT_E_ARG, "aligner weight NULL");
+  return VIT_OK;
+}
+
+vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* in,
+                       const int32_t* grid_hw, int32_t n_images, int32_t flags, void* out,
+                       void* ws, size_t ws_bytes, hipStream_t s) {
+  VIT_TRY(check_config(cfg));
+  const vit_config& c = *cfg;
+  if (flags & ~(VIT_NO_ALIGNER | VIT_OUT_NLAYOUT)) return fail(VIT_E_ARG, "unknown flags %d", flags);
+  const bool aligner = !(flags & VIT_NO_ALIGNER);
+  if (aligner && c.llm_dim <= 0) return fail(VIT_E_SHAPE, "llm_dim must be positive with aligner");
+  if (aligner && c.llm_dim % 8 && c.dtype == VIT_BF16)
+    return fail(VIT_E_SHAPE, "llm_dim must be a multiple of 8");
+  if (!in || !out) return fail(VIT_E_ARG, "in/out is NULL");
+  VIT_TRY(check_weights(c, w, aligner));
+  VarlenDesc desc;
+  VIT_TRY(build_desc(grid_hw, n_images, attention_q_tile(c.dtype, c.head_dim), aligner, c.merge,
+                     &desc));
+  const Plan p = make_plan(c, desc.total, flags);
+  if (!ws || ws_bytes < p.total)
+    return fail(VIT_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0,
+                p.total);
+  char* base = (char*)ws;
+  void* table = base + p.table;
+  float* x = (float*)(base + p.x);
+  void* n = base + p.n;
+  void* qkv = base + p.qkv;
+  void* act = base + p.act;
+  const int dt = c.dtype;
+  const int64_t P = p.P, d = c.vision_dim, h = c.mlp_hidden;
+  const bool final_to_out = !aligner;
+
+  // patch embedding: x (fp32 residual stream) = patches . Wpe^T
+  {
+    ProfScope ps(VIT_K_EMBED, s);
+    if (dt == VIT_BF16) {
+      void* xpad = base + p.xpad;
+      void* wpe = base + p.wpe;
+      VIT_HIP(launch_pad_rows(dt, in, P, c.patch_dim, p.Kp, xpad, s), "pad patches");
+      VIT_HIP(launch_pad_rows(dt, w->patch_embed, d, c.patch_dim, p.Kp, wpe, s), "pad weight");
+      VIT_TRY(gemm(dt, VIT_EPI_STORE_F32, xpad, p.Kp, wpe, nullptr, p.Kp, x, d, P, d, p.Kp,
+                   nullptr, s));
+    } else {
+      VIT_TRY(gemm(dt, VIT_EPI_STORE_F32, in, c.patch_dim, w->patch_embed, nullptr, c.patch_dim,
+                   x, d, P, d, c.patch_dim, nullptr, s));
+    }
+  }
+  VIT_HIP(launch_rope_table(desc, c.head_dim, c.rope_theta, table, s), "rope table");
+
+  for (int b = 0; b < c.n_blocks; ++b) {
+    {
+      ProfScope ps(VIT_K_RMSNORM, s);
+      VIT_HIP(launch_rmsnorm(x, w->norm1[b], c.rms_eps, P, (int)d, dt, n, s), "norm1");
+    }
+    {
+      ProfScope ps(VIT_K_QKV, s);
+      VIT_TRY(gemm(dt, VIT_EPI_STORE, n, d, w->wqkv[b], nullptr, d, qkv, 3 * d, P, 3 * d, d,
+                   nullptr, s));
+    }
+    {
+      ProfScope ps(VIT_K_ROPE, s);
+      VIT_HIP(launch_rope(dt, qkv, table, P, c.n_heads, c.head_dim, s), "rope");
+    }
+    {
+      ProfScope ps(VIT_K_ATTN, s);
+      VIT_HIP(launch_attention(dt, qkv, desc, c.n_heads, c.head_dim, n, s), "attention");
+    }
+    {
+      ProfScope ps(VIT_K_OUTPROJ, s);
+      VIT_TRY(gemm(dt, VIT_EPI_ADD_F32, n, d, w->wo[b], nullptr, d, x, d, P, d, d, nullptr, s));
+    }
+    {
+      ProfScope ps(VIT_K_RMSNORM, s);
+      VIT_HIP(launch_rmsnorm(x, w->norm2[b], c.rms_eps, P, (int)d, dt, n, s), "norm2");
+    }
+    {
+      ProfScope ps(VIT_K_GATEUP, s);
+      VIT_TRY(gemm(dt, VIT_EPI_SWIGLU, n, d, w->w_gate[b], w->w_up[b], d, act, h, P, h, d,
+                   nullptr, s));
+    }
+    {
+      ProfScope ps(VIT_K_DOWN, s);
+      VIT_TRY(gemm(dt, VIT_EPI_ADD_F32, act, h, w->w_down[b], nullptr, h, x, d, P, d, h, nullptr,
+                   s));
+    }
+  }
+  {
+    ProfScope ps(VIT_K_RMSNORM, s);
+    VIT_HIP(launch_rmsnorm(x, w->final_norm, c.rms_eps, P, (int)d, dt, final_to_out ? out : n, s),
+            "final norm");
+  }
+  if (!aligner) return VIT_OK;
+
+  void* G = base + p.G;
+  const int64_t m2 = (int64_t)c.merge * c.merge;
+  {
+    ProfScope ps(VIT_K_GATHER, s);
+    VIT_HIP(launch_gather(dt, n, desc, (int)d, c.merge, G, s), "aligner gather");
+  }
+  int32_t* rowmap = nullptr;
+  if (flags & VIT_OUT_NLAYOUT) {
+    rowmap = (int32_t*)(base + p.rowmap);
+    VIT_HIP(launch_nl_rowmap(desc, c.merge, rowmap, s), "newline row map");
+  }
+  {
+    ProfScope ps(VIT_K_ALIGNER, s);
+    VIT_TRY(gemm(dt, VIT_EPI_STORE, G, m2 * d, w->aligner, nullptr, m2 * d, out, c.llm_dim,
+                 p.tokens, c.llm_dim, m2 * d, rowmap, s));
+  }
+  return VIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vit_status_str(int32_t st) {
+  switch (st) {
+    case VIT_OK: return "ok";
+    case VIT_E_ARG: return "invalid argument";
+    case VIT_E_SHAPE: return "invalid or unsupported shape";
+    case VIT_E_ODD_GRID: return "grid not divisible by the aligner merge size";
+    case VIT_E_WORKSPACE: return "workspace too small";
+    case VIT_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* vit_last_error(void) { return g_last_error.c_str(); }
+
+size_t vit_workspace_bytes(const vit_config* cfg, const int32_t* grid_hw_host, int32_t n_images,
+                           int32_t flags) {
+  if (check_config(cfg) != VIT_OK) return 0;
+  VarlenDesc d;
+  const bool aligner = !(flags & VIT_NO_ALIGNER);
+  if (build_desc(grid_hw_host, n_images, attention_q_tile(cfg->dtype, cfg->head_dim), aligner,
+                 cfg->merge, &d) != VIT_OK)
+    return 0;
+  return make_plan(*cfg, d.total, flags).total;
+}
+
+vit_status vit_encode(const vit_config* cfg, const vit_weights* w, const void* in, int32_t grid_h,
+                      int32_t grid_w, int32_t flags, void* out, void* ws, size_t ws_bytes,
+                      void* stream) {
+  const int32_t g[2] = {grid_h, grid_w};
+  return encode_impl(cfg, w, in, g, 1, flags, out, ws, ws_bytes, (hipStream_t)stream);
+}
+
+vit_status vit_encode_varlen(const vit_config* cfg, const vit_weights* w, const void* in,
+                             const int32_t* grid_hw_host, int32_t n_images, int32_t flags,
+                             void* out, void* ws, size_t ws_bytes, void* stream) {
+  return encode_impl(cfg, w, in, grid_hw_host, n_images, flags, out, ws, ws_bytes,
+                     (hipStream_t)stream);
+}
+
+vit_status vit_aligner_layout(int32_t grid_h, int32_t grid_w, int32_t merge, int32_t* perm,
+                              int32_t* nl_type, int32_t* nl_src, void* stream) {
+  if (merge != 2) return fail(VIT_E_SHAPE, "merge %d unsupported (2)", merge);
+  if (grid_h <= 0 || grid_w <= 0 || (int64_t)grid_h * grid_w > (1 << 24))
+    return fail(VIT_E_SHAPE, "bad grid %dx%d", grid_h, grid_w);
+  if (grid_h % merge || grid_w % merge)
+    return fail(VIT_E_ODD_GRID, "grid %dx%d not divisible by %d", grid_h, grid_w, merge);
+  return hip_check(launch_layout(grid_h, grid_w, merge, perm, nl_type, nl_src,
+                                 (hipStream_t)stream),
+                   "layout");
+}
+
+vit_status vit_rmsnorm(const float* x, const float* w, float eps, int64_t rows, int32_t dim,
+                       int32_t out_dtype, void* out, void* stream) {
+  if (!x || !w || !out) return fail(VIT_E_ARG, "NULL pointer");
+  if (out_dtype != VIT_BF16 && out_dtype != VIT_F32) return fail(VIT_E_ARG, "bad dtype");
+  if (rows < 0 || dim <= 0 || dim % 4) return fail(VIT_E_SHAPE, "bad rows/dim");
+  return hip_check(launch_rmsnorm(x, w, eps, rows, dim, out_dtype, out, (hipStream_t)stream),
+                   "rmsnorm");
+}
+
+vit_status vit_rope_table(const int32_t* grid_hw_host, int32_t n_images, int32_t head_dim,
+                          float theta, void* table, void* stream) {
+  if (!table) return fail(VIT_E_ARG, "table is NULL");
+  if (head_dim <= 0 || head_dim % 4) return fail(VIT_E_SHAPE, "bad head_dim");
+  VarlenDesc d;
+  VIT_TRY(build_desc(grid_hw_host, n_images, 1, false, 2, &d));
+  return hip_check(launch_rope_table(d, head_dim, theta, table, (hipStream_t)stream), "rope table");
+}
+
+vit_status vit_rope(int32_t dtype, void* qkv, const void* table, int64_t P, int32_t n_heads,
+                    int32_t head_dim, void* stream) {
+  if (!qkv || !table) return fail(VIT_E_ARG, "NULL pointer");
+  if (dtype != VIT_BF16 && dtype != VIT_F32) return fail(VIT_E_ARG, "bad dtype");
+  if (P < 0 || n_heads <= 0 || head_dim <= 0 || head_dim % 4) return fail(VIT_E_SHAPE, "bad dims");
+  return hip_check(launch_rope(dtype, qkv, table, P, n_heads, head_dim, (hipStream_t)stream),
+                   "rope");
+}
+
+vit_status vit_attention_varlen(int32_t dtype, const void* qkv, const int32_t* grid_hw_host,
+                                int32_t n_images, int32_t n_heads, int32_t head_dim, void* out,
+                                void* stream) {
+  if (!qkv || !out) return fail(VIT_E_ARG, "NULL pointer");
+  if (dtype != VIT_BF16 && dtype != VIT_F32) return fail(VIT_E_ARG, "bad dtype");
+  if (n_heads <= 0 || (head_dim != 64 && head_dim != 72))
+    return fail(VIT_E_SHAPE, "head_dim %d unsupported (64 or 72)", head_dim);
+  VarlenDesc d;
+  VIT_TRY(build_desc(grid_hw_host, n_images, attention_q_tile(dtype, head_dim), false, 2, &d));
+  return hip_check(launch_attention(dtype, qkv, d, n_heads, head_dim, out, (hipStream_t)stream),
+                   "attention");
+}
+
+vit_status vit_gemm(int32_t dtype, int32_t epilogue, const void* A, int64_t lda, const void* B,
+                    const void* B2, int64_t ldb, void* C, int64_t ldc, int64_t M, int64_t N,
+                    int64_t K, void* stream) {
+  if (dtype != VIT_BF16 && dtype != VIT_F32) return fail(VIT_E_ARG, "bad dtype");
+  if (epilogue < VIT_EPI_STORE || epilogue > VIT_EPI_SWIGLU) return fail(VIT_E_ARG, "bad epilogue");
+  if (!A || !B || !C || (epilogue == VIT_EPI_SWIGLU && !B2)) return fail(VIT_E_ARG, "NULL pointer");
+  if (M < 0 || N < 0 || K <= 0 || lda < K || ldb < K || ldc < N)
+    return fail(VIT_E_SHAPE, "bad GEMM dims");
+  if (M >= (1LL << 31) || N >= (1LL << 31) || K >= (1LL << 31))
+    return fail(VIT_E_SHAPE, "GEMM dims must stay below 2^31");
+  if (dtype == VIT_BF16) {
+    if (K % 8 || lda % 8 || ldb % 8) return fail(VIT_E_SHAPE, "bf16 GEMM needs K, lda, ldb % 8 == 0");
+    if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)(B2 ? B2 : B)) & 15)
+      return fail(VIT_E_ARG, "bf16 GEMM operands must be 16-byte aligned");
+  }
+  return gemm(dtype, epilogue, A, lda, B, B2, ldb, C, ldc, M, N, K, nullptr, (hipStream_t)stream);
+}
+
+vit_status vit_aligner_gather(int32_t dtype, const void* x, const int32_t* grid_hw_host,
+                              int32_t n_images, int32_t d, void* G, void* stream) {
+  if (!x || !G) return fail(VIT_E_ARG, "NULL pointer");
+  if (dtype != VIT_BF16 && dtype != VIT_F32) return fail(VIT_E_ARG, "bad dtype");
+  if (d <= 0 || (d * (int)esize(dtype)) % 16) return fail(VIT_E_SHAPE, "row bytes must be % 16");
+  VarlenDesc desc;
+  VIT_TRY(build_desc(grid_hw_host, n_images, 1, true, 2, &desc));
+  return hip_check(launch_gather(dtype, x, desc, d, 2, G, (hipStream_t)stream), "gather");
+}
+
+vit_status vit_profile_enable(int32_t cls, int32_t on) {
+  if (cls < 0 || cls >= VIT_K_COUNT) return fail(VIT_E_ARG, "bad kernel class %d", cls);
+  Prof& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  p.on[cls] = on != 0;
+  p.used[cls] = 0;
+  return VIT_OK;
+}
+
+vit_status vit_profile_read(int32_t cls, double* total_ms, int64_t* launches) {
+  if (cls < 0 || cls >= VIT_K_COUNT) return fail(VIT_E_ARG, "bad kernel class %d", cls);
+  if (!total_ms || !launches) return fail(VIT_E_ARG, "NULL pointer");
+  Prof& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  double sum = 0.0;
+  for (size_t i = 0; i < p.used[cls]; ++i) {
+    auto& pr = p.ev[cls][i];
+    VIT_HIP(hipEventSynchronize(pr.second), "event sync");
+    float ms = 0.f;
+    VIT_HIP(hipEventElapsedTime(&ms, pr.first, pr.second), "event elapsed");
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (int64_t)p.used[cls];
+  p.used[cls] = 0;
+  return VIT_OK;
+}
+
+}  // extern "C"

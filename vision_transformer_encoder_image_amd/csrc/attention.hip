@@ -1,0 +1,311 @@
+// Full bidirectional patch attention over packed images of different grids
+// (NeMo Automodel vision page, DeepseekV4VisionAttention: every patch of an image
+// attends to every patch of the same image; images are independent, i.e. the
+// batch is block-diagonal).  Flash-style single pass with an online softmax, so
+// the P_i x P_i score matrix never leaves registers.
+//
+// bf16 kernel (gfx950 MFMA).  One workgroup = 128 queries of one (image, head),
+// 4 waves x 32 queries.  Per 64-key tile:
+//   S^T = K . Q^T  on v_mfma_f32_16x16x32_bf16 with K from LDS (A operand, rows =
+//        keys) and Q held in registers for the whole kernel (B operand, columns =
+//        queries).  Transposing S puts one query per lane column, so the row max
+//        of the online softmax is a serial max over the lane's 16 values plus two
+//        cross-lane steps, and the running sum needs no cross-lane work until the
+//        end.
+//   O^T += V^T . P^T  with P^T taken straight from the S^T accumulators (the
+//        MFMA k-slots are permuted identically in both operands, so no shuffle
+//        is needed) and V^T read from an LDS tile stored key-contiguous.
+// Softmax in base 2 with the 1/sqrt(D) scale folded into log2(e); fp32 state.
+// The next K/V tile is prefetched into registers during the current one.
+//
+// fp32 kernel (vector ALU): one thread per query, K/V tiles in LDS, same online
+// softmax in base e.  Used by the single-precision mode.
+#include <math.h>
+
+#include "common.h"
+
+namespace {
+
+constexpr int BQ = 128, BKV = 64;
+constexpr int kThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __restrict__ qkv,
+                                                                VarlenDesc desc, int H,
+                                                                bf16* __restrict__ out,
+                                                                float scale_log2) {
+  constexpr int DP = (D + 31) / 32 * 32;  // QK contraction length padded to the MFMA k
+  constexpr int DO = (D + 15) / 16 * 16;  // output rows padded to the MFMA block
+  constexpr int NDS = DP / 32;
+  constexpr int NDB = DO / 16;
+  constexpr int KS = DP + 8;    // LDS row stride of K (elements), skews banks
+  constexpr int VS = BKV + 8;   // LDS row stride of V^T
+  constexpr int KCH = DP / 8;   // 16-byte chunks per K row (zero beyond D)
+  constexpr int VCH = D / 8;    // 16-byte chunks per V row
+  constexpr int KLD = (BKV * KCH + kThreads - 1) / kThreads;
+  constexpr int VLD = (BKV * VCH + kThreads - 1) / kThreads;
+  __shared__ __attribute__((aligned(16))) bf16 sK[BKV * KS];
+  __shared__ __attribute__((aligned(16))) bf16 sVt[DO * VS];
+
+  const int tile = blockIdx.x, h = blockIdx.y;
+  int img = 0;
+  while (img + 1 < desc.n_images && tile >= desc.cu_tiles[img + 1]) ++img;
+  const int seq0 = desc.cu_seqlens[img], seq1 = desc.cu_seqlens[img + 1];
+  const int q0 = seq0 + (tile - desc.cu_tiles[img]) * BQ;
+  const int64_t ld = 3 * (int64_t)H * D;
+  const bf16* Qb = qkv + h * D;
+  const bf16* Kb = qkv + (int64_t)H * D + h * D;
+  const bf16* Vb = qkv + 2 * (int64_t)H * D + h * D;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, fk = lane >> 4;
+
+  bf16x8 qf[2][NDS];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = q0 + wave * 32 + qb * 16 + fr;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const int d0 = ds * 32 + fk * 8;
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (qrow < seq1 && d0 < D) v = ld16(Qb + qrow * ld + d0);
+      qf[qb][ds] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  // K/V staging registers (fully unrolled; KLD, VLD <= 3)
+  u32x4 rk[KLD], rv[VLD];
+#define VIT_GLOAD(kv0)                                                           \
+  do {                                                                           \
+    _Pragma("unroll") for (int i = 0; i < KLD; ++i) {                            \
+      const int c = tid + kThreads * i;                                          \
+      const int key = c / KCH, kc = c % KCH;                                     \
+      const int kidx = (kv0) + key;                                              \
+      if (c < BKV * KCH && kidx < seq1 && kc * 8 < D)                            \
+        rk[i] = ld16(Kb + kidx * ld + kc * 8);                                   \
+      else                                                                       \
+        rk[i] = u32x4{0, 0, 0, 0};                                               \
+    }                                                                            \
+    _Pragma("unroll") for (int i = 0; i < VLD; ++i) {                            \
+      const int c = tid + kThreads * i;                                          \
+      const int key = c / VCH, vc = c % VCH;                                     \
+      const int kidx = (kv0) + key;                                              \
+      if (c < BKV * VCH && kidx < seq1)                                          \
+        rv[i] = ld16(Vb + kidx * ld + vc * 8);                                   \
+      else                                                                       \
+        rv[i] = u32x4{0, 0, 0, 0};                                               \
+    }                                                                            \
+  } while (0)
+#define VIT_LSTORE()                                                             \
+  do {                                                                           \
+    _Pragma("unroll") for (int i = 0; i < KLD; ++i) {                            \
+      const int c = tid + kThreads * i;                                          \
+      if (c < BKV * KCH) st16(&sK[(c / KCH) * KS + (c % KCH) * 8], rk[i]);        \
+    }                                                                            \
+    _Pragma("unroll") for (int i = 0; i < VLD; ++i) {                            \
+      const int c = tid + kThreads * i;                                          \
+      if (c < BKV * VCH) {                                                       \
+        const int key = c / VCH, vc = c % VCH;                                   \
+        const bf16x8 v = __builtin_bit_cast(bf16x8, rv[i]);                      \
+        _Pragma("unroll") for (int j = 0; j < 8; ++j) sVt[(vc * 8 + j) * VS + key] = v[j]; \
+      }                                                                          \
+    }                                                                            \
+  } while (0)
+
+  f32x4 o[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrow[2] = {-INFINITY, -INFINITY};
+  float lsum[2] = {0.f, 0.f};
+
+  const int nkv = (seq1 - seq0 + BKV - 1) / BKV;
+  VIT_GLOAD(seq0);
+  VIT_LSTORE();
+  __syncthreads();
+  for (int t = 0; t < nkv; ++t) {
+    const int kv0 = seq0 + t * BKV;
+    if (t + 1 < nkv) VIT_GLOAD(kv0 + BKV);
+
+    f32x4 s[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(&sK[(kb * 16 + fr) * KS + ds * 32 + fk * 8]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ds], s[kb][qb], 0, 0, 0);
+      }
+
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kv0 + kb * 16 + fk * 4 + i;
+          const float v = key < seq1 ? s[kb][qb][i] * scale_log2 : -INFINITY;
+          s[kb][qb][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(mrow[qb], mx);
+      const float alpha = exp2f(mrow[qb] - mnew);
+      mrow[qb] = mnew;
+      float ls = lsum[qb] * alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[db][qb][i] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2f(s[kb][qb][i] - mnew);
+          ls += p;
+          s[kb][qb][i] = p;
+        }
+      lsum[qb] = ls;
+    }
+
+#pragma unroll
+    for (int ks = 0; ks < BKV / 32; ++ks) {
+      bf16x8 pf[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pf[qb][i] = f2bf(s[2 * ks][qb][i]);
+          pf[qb][4 + i] = f2bf(s[2 * ks + 1][qb][i]);
+        }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const bf16* vr = &sVt[(db * 16 + fr) * VS + ks * 32 + fk * 4];
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
+        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], o[db][qb], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+    if (t + 1 < nkv) {
+      VIT_LSTORE();
+      __syncthreads();
+    }
+  }
+
+  const int64_t ldo = (int64_t)H * D;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float l = lsum[qb];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float inv = 1.0f / l;
+    const int query = q0 + wave * 32 + qb * 16 + fr;
+    if (query >= seq1) continue;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 16 + fk * 4;
+      if (d >= D) continue;
+      bf16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = f2bf(o[db][qb][i] * inv);
+      *reinterpret_cast<bf16x4*>(out + query * ldo + h * D + d) = v;
+    }
+  }
+#undef VIT_GLOAD
+#undef VIT_LSTORE
+}
+
+// ---------------------------------------------------------------------------
+constexpr int FQ = 64, FKV = 32;
+
+template <int D>
+__global__ __launch_bounds__(FQ) void attn_f32_kernel(const float* __restrict__ qkv,
+                                                      VarlenDesc desc, int H,
+                                                      float* __restrict__ out, float scale) {
+  __shared__ float sK[FKV][D];
+  __shared__ float sV[FKV][D];
+  const int tile = blockIdx.x, h = blockIdx.y;
+  int img = 0;
+  while (img + 1 < desc.n_images && tile >= desc.cu_tiles[img + 1]) ++img;
+  const int seq0 = desc.cu_seqlens[img], seq1 = desc.cu_seqlens[img + 1];
+  const int query = seq0 + (tile - desc.cu_tiles[img]) * FQ + threadIdx.x;
+  const int64_t ld = 3 * (int64_t)H * D;
+  const bool valid = query < seq1;
+  float q[D], o[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    q[e] = valid ? qkv[query * ld + h * D + e] : 0.f;
+    o[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int kv0 = seq0; kv0 < seq1; kv0 += FKV) {
+    for (int idx = threadIdx.x; idx < FKV * D; idx += FQ) {
+      const int j = idx / D, e = idx % D;
+      const int key = kv0 + j;
+      sK[j][e] = key < seq1 ? qkv[key * ld + (int64_t)H * D + h * D + e] : 0.f;
+      sV[j][e] = key < seq1 ? qkv[key * ld + 2 * (int64_t)H * D + h * D + e] : 0.f;
+    }
+    __syncthreads();
+    const int nj = min(FKV, seq1 - kv0);
+    for (int j = 0; j < nj; ++j) {
+      float sdot = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) sdot = fmaf(q[e], sK[j][e], sdot);
+      const float sc = sdot * scale;
+      const float mnew = fmaxf(m, sc);
+      const float a = expf(m - mnew);
+      const float p = expf(sc - mnew);
+      l = l * a + p;
+#pragma unroll
+      for (int e = 0; e < D; ++e) o[e] = o[e] * a + p * sV[j][e];
+      m = mnew;
+    }
+    __syncthreads();
+  }
+  if (!valid) return;
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int e = 0; e < D; ++e) out[query * (int64_t)H * D + h * D + e] = o[e] * inv;
+}
+
+}  // namespace
+
+int attention_q_tile(int dtype, int /*head_dim*/) { return dtype == VIT_BF16 ? BQ : FQ; }
+
+hipError_t launch_attention(int dtype, const void* qkv, const VarlenDesc& d, int n_heads,
+                            int head_dim, void* out, hipStream_t s) {
+  const int tiles = d.cu_tiles[d.n_images];
+  if (tiles == 0) return hipSuccess;
+  const dim3 grid((unsigned)tiles, (unsigned)n_heads);
+  if (dtype == VIT_BF16) {
+    const float sl2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+    if (head_dim == 64)
+      attn_bf16_kernel<64><<<grid, kThreads, 0, s>>>((const bf16*)qkv, d, n_heads, (bf16*)out, sl2);
+    else if (head_dim == 72)
+      attn_bf16_kernel<72><<<grid, kThreads, 0, s>>>((const bf16*)qkv, d, n_heads, (bf16*)out, sl2);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    const float sc = (float)(1.0 / sqrt((double)head_dim));
+    if (head_dim == 64)
+      attn_f32_kernel<64><<<grid, FQ, 0, s>>>((const float*)qkv, d, n_heads, (float*)out, sc);
+    else if (head_dim == 72)
+      attn_f32_kernel<72><<<grid, FQ, 0, s>>>((const float*)qkv, d, n_heads, (float*)out, sc);
+    else
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}

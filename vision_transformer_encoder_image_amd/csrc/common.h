@@ -1,0 +1,87 @@
+// Shared device/host helpers of the gfx950 encoder library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vitenc.h"
+
+#define VIT_DEV __device__ __forceinline__
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+// 16-byte global load of a native vector (no HIP struct temporaries).
+VIT_DEV u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+VIT_DEV void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Round-to-nearest-even float -> bf16 (finite values; NaN stays NaN).
+VIT_DEV bf16 f2bf(float f) { return (bf16)f; }
+VIT_DEV float bf2f(bf16 b) { return (float)b; }
+
+template <typename T> VIT_DEV T from_f32(float v);
+template <> VIT_DEV float from_f32<float>(float v) { return v; }
+template <> VIT_DEV bf16 from_f32<bf16>(float v) { return f2bf(v); }
+VIT_DEV float to_f32(float v) { return v; }
+VIT_DEV float to_f32(bf16 v) { return bf2f(v); }
+
+// Wave-wide (64 lanes) reductions through cross-lane shuffles.
+VIT_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+VIT_DEV float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// Per-image descriptors of a packed batch, passed by value as kernel arguments.
+struct VarlenDesc {
+  int32_t n_images;
+  int32_t total;                       // sum of P_i
+  int32_t cu_seqlens[VIT_MAX_IMAGES + 1];
+  int32_t grid_w[VIT_MAX_IMAGES];
+  int32_t cu_tiles[VIT_MAX_IMAGES + 1];  // prefix sum of q-tiles per image (attention)
+};
+
+VIT_DEV int find_image(const VarlenDesc& d, int p) {
+  int i = 0;
+  while (i + 1 < d.n_images && p >= d.cu_seqlens[i + 1]) ++i;
+  return i;
+}
+
+// Host-side launch helpers (defined in the .hip files, called by api.cpp).
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  const void* B2;
+  void* C;
+  const int32_t* rowmap;  // optional output row remap (aligner newline layout)
+  int64_t lda, ldb, ldc;
+  int64_t M, N, K;
+};
+
+hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_f32(int epilogue, const GemmArgs& g, hipStream_t s);
+hipError_t launch_rmsnorm(const float* x, const float* w, float eps, int64_t rows, int dim,
+                          int out_dtype, void* out, hipStream_t s);
+hipError_t launch_rope_table(const VarlenDesc& d, int head_dim, float theta, void* table,
+                             hipStream_t s);
+hipError_t launch_rope(int dtype, void* qkv, const void* table, int64_t P, int n_heads,
+                       int head_dim, hipStream_t s);
+hipError_t launch_attention(int dtype, const void* qkv, const VarlenDesc& d, int n_heads,
+                            int head_dim, void* out, hipStream_t s);
+int attention_q_tile(int dtype, int head_dim);
+hipError_t launch_gather(int dtype, const void* x, const VarlenDesc& d, int dim, int merge,
+                         void* G, hipStream_t s);
+hipError_t launch_pad_rows(int dtype, const void* src, int64_t rows, int64_t cols, int64_t ld_dst,
+                           void* dst, hipStream_t s);
+hipError_t launch_layout(int grid_h, int grid_w, int merge, int32_t* perm, int32_t* nl_type,
+                         int32_t* nl_src, hipStream_t s);
+hipError_t launch_nl_rowmap(const VarlenDesc& d, int merge, int32_t* rowmap, hipStream_t s);

@@ -1,0 +1,262 @@
+// Bandwidth-bound passes of the encoder on gfx950: RMSNorm, rotary table and
+// rotary application, 2x2 aligner gather, row padding, layout index arrays.
+#include <math.h>
+
+#include "common.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------------------
+// RMSNorm (NeMo Automodel vision page, DeepseekV4VisionRMSNorm: fp32 scale,
+// eps 1e-6): one wavefront per row, fp32 sum of squares reduced across the
+// wave, then y = w * (x * rsqrt(mean + eps)) cast once to the output type.
+template <typename TO>
+__global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const float* __restrict__ x,
+                                                           const float* __restrict__ w, float eps,
+                                                           int64_t rows, int dim,
+                                                           TO* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float4* xr = reinterpret_cast<const float4*>(x + row * dim);
+  const float4* w4 = reinterpret_cast<const float4*>(w);
+  const int n4 = dim >> 2;
+  float ss = 0.f;
+  for (int c = lane; c < n4; c += 64) {
+    float4 v = xr[c];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  const float rstd = 1.0f / sqrtf(ss / (float)dim + eps);
+  for (int c = lane; c < n4; c += 64) {
+    float4 v = xr[c];
+    float4 s = w4[c];
+    TO* o = out + row * dim + 4 * c;
+    o[0] = from_f32<TO>(s.x * (v.x * rstd));
+    o[1] = from_f32<TO>(s.y * (v.y * rstd));
+    o[2] = from_f32<TO>(s.z * (v.z * rstd));
+    o[3] = from_f32<TO>(s.w * (v.w * rstd));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Rotary table (vision page, get_vision_cos_sin): entry (p, k), k < D/2, holds
+// (cos, sin) of row * theta^(-k/(D/4)) for k < D/4 and of
+// col * theta^(-(k-D/4)/(D/4)) otherwise; row/col restart at every image.
+// Built in double precision, stored as float2.
+__global__ void rope_table_kernel(VarlenDesc d, int head_dim, double theta, float2* table) {
+  const int half = head_dim / 2, q4 = head_dim / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)d.total * half) return;
+  const int p = (int)(idx / half);
+  const int k = (int)(idx % half);
+  const int img = find_image(d, p);
+  const int local = p - d.cu_seqlens[img];
+  const int gw = d.grid_w[img];
+  const int pos = (k < q4) ? local / gw : local % gw;
+  const int kk = (k < q4) ? k : k - q4;
+  const double f = pow(theta, -(double)kk / (double)q4);
+  double s, c;
+  sincos((double)pos * f, &s, &c);
+  table[idx] = make_float2((float)c, (float)s);
+}
+
+// ---------------------------------------------------------------------------
+// Half-split 2D rotary (vision page, apply_vision_rotary) on the q and k parts of
+// a packed [P, 3*H*D] qkv buffer, in place, fp32 math.  One thread per rotated
+// pair (i, i + D/4) inside one half of one head.
+template <typename T>
+__global__ void rope_kernel(T* qkv, const float2* __restrict__ table, int64_t P, int H, int D) {
+  const int q4 = D / 4;
+  const int d = H * D;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= P * d) return;  // d pairs per row: 2 parts * H heads * 2 halves * D/4
+  const int64_t p = idx / d;
+  int j = (int)(idx % d);
+  const int kk = j % q4;
+  j /= q4;
+  const int half = j & 1;
+  j >>= 1;
+  const int h = j % H;
+  const int part = j / H;  // 0 = q, 1 = k
+  T* row = qkv + p * (3 * (int64_t)d) + part * d + h * D + half * (D / 2);
+  const float2 cs = table[p * (D / 2) + half * q4 + kk];
+  const float a1 = to_f32(row[kk]);
+  const float a2 = to_f32(row[kk + q4]);
+  row[kk] = from_f32<T>(a1 * cs.x - a2 * cs.y);
+  row[kk + q4] = from_f32<T>(a2 * cs.x + a1 * cs.y);
+}
+
+// ---------------------------------------------------------------------------
+// 2x2 aligner gather (vision page, DeepseekV4VisionAligner): merged token t of
+// image i concatenates patches TL, TR, BL, BR of its group.  One thread per
+// 16-byte chunk of the output.
+template <typename T>
+__global__ void gather_kernel(const T* __restrict__ x, VarlenDesc d, int dim, int merge,
+                              T* __restrict__ G) {
+  constexpr int V = 16 / sizeof(T);
+  const int m2 = merge * merge;
+  const int64_t row_chunks = (int64_t)m2 * dim / V;
+  const int64_t tokens = d.total / m2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= tokens * row_chunks) return;
+  const int64_t t = idx / row_chunks;
+  const int col = (int)(idx % row_chunks) * V;
+  const int s = col / dim;
+  const int e = col % dim;
+  // image of merged token t: token offsets are cu_seqlens / m2
+  int img = 0;
+  while (img + 1 < d.n_images && t >= d.cu_seqlens[img + 1] / m2) ++img;
+  const int tl = (int)(t - d.cu_seqlens[img] / m2);
+  const int gw = d.grid_w[img];
+  const int wq = gw / merge;
+  const int gi = tl / wq, gj = tl % wq;
+  const int src = d.cu_seqlens[img] + (merge * gi + s / merge) * gw + merge * gj + s % merge;
+  st16(G + t * (int64_t)m2 * dim + col, ld16(x + (int64_t)src * dim + e));
+}
+
+// Copy rows [rows, cols] into [rows, ld_dst] zero-padding columns cols..ld_dst-1.
+// cols and ld_dst multiples of 4; one thread per 4 elements.
+template <typename T>
+__global__ void pad_rows_kernel(const T* __restrict__ src, int64_t rows, int64_t cols,
+                                int64_t ld_dst, T* __restrict__ dst) {
+  const int64_t q = ld_dst / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * q) return;
+  const int64_t r = idx / q;
+  const int64_t c = (idx % q) * 4;
+  T v[4];
+  if (c < cols) {
+    const T* s = src + r * cols + c;
+    for (int k = 0; k < 4; ++k) v[k] = s[k];
+  } else {
+    for (int k = 0; k < 4; ++k) v[k] = from_f32<T>(0.f);
+  }
+  T* o = dst + r * ld_dst + c;
+  for (int k = 0; k < 4; ++k) o[k] = v[k];
+}
+
+// Aligner layout arrays of one image (permutation and newline layout).
+__global__ void layout_kernel(int gh, int gw, int merge, int32_t* perm, int32_t* nl_type,
+                              int32_t* nl_src) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int m2 = merge * merge;
+  const int hq = gh / merge, wq = gw / merge;
+  if (perm && idx < gh * gw) {
+    const int t = idx / m2, s = idx % m2;
+    const int gi = t / wq, gj = t % wq;
+    perm[idx] = (merge * gi + s / merge) * gw + merge * gj + s % merge;
+  }
+  const int L = hq * (wq + 1) + 2;
+  if (idx < L) {
+    int type, src;
+    if (idx == 0) {
+      type = 0; src = -1;
+    } else if (idx == L - 1) {
+      type = 3; src = -1;
+    } else {
+      const int q = idx - 1;
+      const int r = q / (wq + 1), c = q % (wq + 1);
+      if (c == wq) { type = 2; src = -1; } else { type = 1; src = r * wq + c; }
+    }
+    if (nl_type) nl_type[idx] = type;
+    if (nl_src) nl_src[idx] = src;
+  }
+}
+
+// Output row of every merged token when the aligner writes newline-layout spans.
+__global__ void nl_rowmap_kernel(VarlenDesc d, int merge, int32_t* rowmap) {
+  const int m2 = merge * merge;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= d.total / m2) return;
+  int img = 0, base = 0;
+  while (img + 1 < d.n_images && t >= d.cu_seqlens[img + 1] / m2) {
+    const int P = d.cu_seqlens[img + 1] - d.cu_seqlens[img];
+    const int wq = d.grid_w[img] / merge, hq = P / d.grid_w[img] / merge;
+    base += hq * (wq + 1) + 2;
+    ++img;
+  }
+  const int tl = t - d.cu_seqlens[img] / m2;
+  const int wq = d.grid_w[img] / merge;
+  rowmap[t] = base + 1 + (tl / wq) * (wq + 1) + tl % wq;
+}
+
+inline unsigned blocks_for(int64_t n, int t = kThreads) { return (unsigned)((n + t - 1) / t); }
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const float* x, const float* w, float eps, int64_t rows, int dim,
+                          int out_dtype, void* out, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((rows + 3) / 4);
+  if (out_dtype == VIT_BF16)
+    rmsnorm_kernel<bf16><<<grid, kThreads, 0, s>>>(x, w, eps, rows, dim, (bf16*)out);
+  else
+    rmsnorm_kernel<float><<<grid, kThreads, 0, s>>>(x, w, eps, rows, dim, (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(const VarlenDesc& d, int head_dim, float theta, void* table,
+                             hipStream_t s) {
+  const int64_t n = (int64_t)d.total * (head_dim / 2);
+  if (n == 0) return hipSuccess;
+  rope_table_kernel<<<blocks_for(n), kThreads, 0, s>>>(d, head_dim, (double)theta,
+                                                        (float2*)table);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope(int dtype, void* qkv, const void* table, int64_t P, int n_heads,
+                       int head_dim, hipStream_t s) {
+  const int64_t n = P * n_heads * head_dim;
+  if (n == 0) return hipSuccess;
+  if (dtype == VIT_BF16)
+    rope_kernel<bf16><<<blocks_for(n), kThreads, 0, s>>>((bf16*)qkv, (const float2*)table, P,
+                                                         n_heads, head_dim);
+  else
+    rope_kernel<float><<<blocks_for(n), kThreads, 0, s>>>((float*)qkv, (const float2*)table, P,
+                                                          n_heads, head_dim);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(int dtype, const void* x, const VarlenDesc& d, int dim, int merge,
+                         void* G, hipStream_t s) {
+  const int esz = dtype == VIT_BF16 ? 2 : 4;
+  const int64_t n = (int64_t)d.total * dim * esz / 16;
+  if (n == 0) return hipSuccess;
+  if (dtype == VIT_BF16)
+    gather_kernel<bf16><<<blocks_for(n), kThreads, 0, s>>>((const bf16*)x, d, dim, merge,
+                                                           (bf16*)G);
+  else
+    gather_kernel<float><<<blocks_for(n), kThreads, 0, s>>>((const float*)x, d, dim, merge,
+                                                            (float*)G);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_rows(int dtype, const void* src, int64_t rows, int64_t cols, int64_t ld_dst,
+                           void* dst, hipStream_t s) {
+  const int64_t n = rows * (ld_dst / 4);
+  if (n == 0) return hipSuccess;
+  if (dtype == VIT_BF16)
+    pad_rows_kernel<bf16><<<blocks_for(n), kThreads, 0, s>>>((const bf16*)src, rows, cols,
+                                                             ld_dst, (bf16*)dst);
+  else
+    pad_rows_kernel<float><<<blocks_for(n), kThreads, 0, s>>>((const float*)src, rows, cols,
+                                                              ld_dst, (float*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_layout(int grid_h, int grid_w, int merge, int32_t* perm, int32_t* nl_type,
+                         int32_t* nl_src, hipStream_t s) {
+  const int n = grid_h * grid_w + 2 * grid_h + 2;  // >= both array lengths
+  layout_kernel<<<blocks_for(n), kThreads, 0, s>>>(grid_h, grid_w, merge, perm, nl_type, nl_src);
+  return hipGetLastError();
+}
+
+hipError_t launch_nl_rowmap(const VarlenDesc& d, int merge, int32_t* rowmap, hipStream_t s) {
+  const int n = d.total / (merge * merge);
+  if (n == 0) return hipSuccess;
+  nl_rowmap_kernel<<<blocks_for(n), kThreads, 0, s>>>(d, merge, rowmap);
+  return hipGetLastError();
+}

@@ -1,0 +1,231 @@
+// bf16 MFMA GEMM for gfx950: C[M,N] = epilogue(A[M,K] . B[N,K]^T).
+//
+// Both operands are K-contiguous (activations [tokens, in], weights [out, in]),
+// so every lane fetches 16-byte runs along K for both MFMA operands.  Tile
+// 128x128x64, 256 threads = 4 waves in a 2x2 arrangement, each wave owning a
+// 64x64 sub-tile as 4x4 v_mfma_f32_16x16x32_bf16 blocks with fp32 accumulators.
+// A and B tiles are double-buffered in LDS (XOR-swizzled 16-byte chunks) and the
+// next K-tile is prefetched into registers while the current one is multiplied.
+// Workgroups are remapped so that the tiles running on one XCD (workgroup ids
+// are dealt round-robin over the 8 XCDs) form a contiguous band of the grouped
+// tile order, which keeps shared A rows / B panels inside that XCD's L2.
+//
+// Epilogues: store bf16, store fp32, fp32 residual add in place, and the SwiGLU
+// pair (two B matrices; the B tile holds 32 gate rows then 32 up rows for each
+// wave column so that silu(gate) * up meets in the same lane).
+#include "common.h"
+
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int kThreads = 256;
+constexpr int kGroupM = 8;              // m-tiles per band of the grouped order
+constexpr int kXcds = 8;
+
+VIT_DEV int swz(int row, int kc) { return row * BK + ((kc ^ (row & 7)) << 3); }
+
+VIT_DEV float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// Logical tile index of this workgroup after the XCD remap.
+VIT_DEV int xcd_remap(int bid, int ntiles) {
+  const int per = ntiles / kXcds, rem = ntiles % kXcds;
+  const int xcd = bid % kXcds, idx = bid / kXcds;
+  return xcd * per + min(xcd, rem) + idx;
+}
+
+// Source of LDS B-tile row r.  SwiGLU tiles interleave the two weight matrices:
+// rows 64c..64c+31 are gate rows n0+32c.., rows 64c+32..64c+63 the matching up rows.
+template <bool DUAL>
+VIT_DEV const bf16* b_row_src(const bf16* B, const bf16* B2, int n0, int N, int64_t ldb, int r,
+                              int kc) {
+  int brow = n0 + r;
+  const bf16* base = B;
+  if (DUAL) {
+    const int wc = r >> 6, within = r & 63;
+    brow = n0 + wc * 32 + (within & 31);
+    base = (within >> 5) ? B2 : B;
+  }
+  return base + (int64_t)min(brow, N - 1) * ldb + kc * 8;
+}
+
+template <int EPI, bool DUAL>
+__global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) bf16 sA[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16 sB[2][BN * BK];
+
+  const bf16* __restrict__ A = (const bf16*)g.A;
+  const bf16* __restrict__ B = (const bf16*)g.B;
+  const bf16* __restrict__ B2 = (const bf16*)g.B2;
+  const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
+  constexpr int BNO = DUAL ? BN / 2 : BN;  // output columns per tile
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (N + BNO - 1) / BNO;
+  const int ntiles = tiles_m * tiles_n;
+
+  // grouped order: bands of kGroupM m-tiles, n-major inside a band
+  const int L = xcd_remap(blockIdx.x, ntiles);
+  const int band = kGroupM * tiles_n;
+  const int first_m = (L / band) * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int tm = first_m + (L % band) % gm;
+  const int tn = (L % band) / gm;
+  const int m0 = tm * BM, n0 = tn * BNO;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // global -> register staging: each thread moves 4 chunks of A and 4 of B per
+  // K-tile (rows ld_row + 32 i, 16-byte chunk ld_kc)
+  const int ld_row = tid >> 3;
+  const int ld_kc = tid & 7;
+  const bf16* a_src0 = A + (int64_t)min(m0 + ld_row, M - 1) * g.lda + ld_kc * 8;
+  const bf16* a_src1 = A + (int64_t)min(m0 + ld_row + 32, M - 1) * g.lda + ld_kc * 8;
+  const bf16* a_src2 = A + (int64_t)min(m0 + ld_row + 64, M - 1) * g.lda + ld_kc * 8;
+  const bf16* a_src3 = A + (int64_t)min(m0 + ld_row + 96, M - 1) * g.lda + ld_kc * 8;
+  const bf16* b_src0 = b_row_src<DUAL>(B, B2, n0, N, g.ldb, ld_row, ld_kc);
+  const bf16* b_src1 = b_row_src<DUAL>(B, B2, n0, N, g.ldb, ld_row + 32, ld_kc);
+  const bf16* b_src2 = b_row_src<DUAL>(B, B2, n0, N, g.ldb, ld_row + 64, ld_kc);
+  const bf16* b_src3 = b_row_src<DUAL>(B, B2, n0, N, g.ldb, ld_row + 96, ld_kc);
+  const int s_off0 = swz(ld_row, ld_kc), s_off1 = swz(ld_row + 32, ld_kc);
+  const int s_off2 = swz(ld_row + 64, ld_kc), s_off3 = swz(ld_row + 96, ld_kc);
+  u32x4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+
+#define VIT_LOAD_TILE(k0)                                      \
+  do {                                                         \
+    if (((k0) + ld_kc * 8) < K) {                              \
+      ra0 = ld16(a_src0 + (k0));                               \
+      ra1 = ld16(a_src1 + (k0));                               \
+      ra2 = ld16(a_src2 + (k0));                               \
+      ra3 = ld16(a_src3 + (k0));                               \
+      rb0 = ld16(b_src0 + (k0));                               \
+      rb1 = ld16(b_src1 + (k0));                               \
+      rb2 = ld16(b_src2 + (k0));                               \
+      rb3 = ld16(b_src3 + (k0));                               \
+    } else {                                                   \
+      ra0 = ra1 = ra2 = ra3 = rb0 = rb1 = rb2 = rb3 = u32x4{0, 0, 0, 0}; \
+    }                                                          \
+  } while (0)
+#define VIT_STORE_TILE(buf)                                       \
+  do {                                                            \
+    st16(&sA[buf][s_off0], ra0);            \
+    st16(&sA[buf][s_off1], ra1);            \
+    st16(&sA[buf][s_off2], ra2);            \
+    st16(&sA[buf][s_off3], ra3);            \
+    st16(&sB[buf][s_off0], rb0);            \
+    st16(&sB[buf][s_off1], rb1);            \
+    st16(&sB[buf][s_off2], rb2);            \
+    st16(&sB[buf][s_off3], rb3);            \
+  } while (0)
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (K + BK - 1) / BK;
+  VIT_LOAD_TILE(0);
+  VIT_STORE_TILE(0);
+  __syncthreads();
+
+  const int fr = lane & 15;   // fragment row inside a 16-row block
+  const int fk = lane >> 4;   // 8-element k-chunk inside a 32-wide k step
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) VIT_LOAD_TILE((kt + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 64 + i * 16 + fr;
+        af[i] = *reinterpret_cast<const bf16x8*>(&sA[cur][swz(r, ks * 4 + fk)]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = wn * 64 + j * 16 + fr;
+        bfr[j] = *reinterpret_cast<const bf16x8*>(&sB[cur][swz(r, ks * 4 + fk)]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) VIT_STORE_TILE(cur ^ 1);
+    __syncthreads();
+  }
+#undef VIT_LOAD_TILE
+#undef VIT_STORE_TILE
+
+  // epilogue: lane holds column (lane & 15) and rows 4*(lane >> 4) + r of each block
+  const int col_in = lane & 15;
+  const int row_in = (lane >> 4) * 4;
+  if (DUAL) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn * 32 + j * 16 + col_in;
+        if (n >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm * 64 + i * 16 + row_in + r;
+          if (m >= M) continue;
+          const float v = silu(acc[i][j][r]) * acc[i][j + 2][r];
+          ((bf16*)g.C)[(int64_t)m * g.ldc + n] = f2bf(v);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn * 64 + j * 16 + col_in;
+        if (n >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm * 64 + i * 16 + row_in + r;
+          if (m >= M) continue;
+          const int64_t orow = g.rowmap ? (int64_t)g.rowmap[m] : (int64_t)m;
+          const float v = acc[i][j][r];
+          if (EPI == VIT_EPI_STORE) {
+            ((bf16*)g.C)[orow * g.ldc + n] = f2bf(v);
+          } else if (EPI == VIT_EPI_STORE_F32) {
+            ((float*)g.C)[orow * g.ldc + n] = v;
+          } else {  // VIT_EPI_ADD_F32
+            float* c = (float*)g.C + orow * g.ldc + n;
+            *c = *c + v;
+          }
+        }
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s) {
+  if (g.M == 0 || g.N == 0) return hipSuccess;
+  const bool dual = epilogue == VIT_EPI_SWIGLU;
+  const int64_t bno = dual ? BN / 2 : BN;
+  const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + bno - 1) / bno);
+  const dim3 grid((unsigned)tiles);
+  switch (epilogue) {
+    case VIT_EPI_STORE:
+      gemm_bf16_kernel<VIT_EPI_STORE, false><<<grid, kThreads, 0, s>>>(g);
+      break;
+    case VIT_EPI_STORE_F32:
+      gemm_bf16_kernel<VIT_EPI_STORE_F32, false><<<grid, kThreads, 0, s>>>(g);
+      break;
+    case VIT_EPI_ADD_F32:
+      gemm_bf16_kernel<VIT_EPI_ADD_F32, false><<<grid, kThreads, 0, s>>>(g);
+      break;
+    case VIT_EPI_SWIGLU:
+      gemm_bf16_kernel<VIT_EPI_SWIGLU, true><<<grid, kThreads, 0, s>>>(g);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
