@@ -130,7 +130,7 @@ vit_status build_desc(const int32_t* grid_hw, int32_t n_images, int q_tile, bool
 }
 
 struct Plan {
-  int64_t P = 0, tokens = 0, Kp = 0;
+  int64_t P = 0, tokens = 0, Kp = 0, hp = 0;
   size_t table = 0, xpad = 0, wpe = 0, x = 0, n = 0, qkv = 0, act = 0, G = 0, rowmap = 0;
   size_t total = 0;
 };
@@ -143,6 +143,9 @@ Plan make_plan(const vit_config& c, int64_t P, int flags) {
   p.P = P;
   p.tokens = aligner ? P / m2 : 0;
   p.Kp = c.dtype == VIT_BF16 ? round_up(c.patch_dim, 64) : c.patch_dim;
+  // MLP activations keep a 64-multiple row stride in bf16 so the down GEMM runs
+  // whole 64-wide K tiles (the pad columns are zero)
+  p.hp = c.dtype == VIT_BF16 ? round_up(h, 64) : h;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -157,11 +160,31 @@ Plan make_plan(const vit_config& c, int64_t P, int flags) {
   p.x = take((size_t)P * d * sizeof(float));
   p.n = take((size_t)P * d * es);  // also holds the attention output
   p.qkv = take((size_t)P * 3 * d * es);
-  p.act = take((size_t)P * h * es);
+  p.act = take((size_t)P * p.hp * es);
   if (aligner) p.G = take((size_t)p.tokens * m2 * d * es);
   if (aligner && (flags & VIT_OUT_NLAYOUT)) p.rowmap = take((size_t)p.tokens * sizeof(int32_t));
   p.total = off;
   return p;
+}
+
+GemmArgs gemm_args(const void* A, int64_t lda, const void* B, const void* B2, int64_t ldb, void* C,
+                   int64_t ldc, int64_t M, int64_t N, int64_t K, const int32_t* rowmap) {
+  GemmArgs g;
+  g.A = A;
+  g.B = B;
+  g.B2 = B2;
+  g.C = C;
+  g.rowmap = rowmap;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.ldc = ldc;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.kb = K;
+  g.rope_table = nullptr;
+  g.rope_cols = 0;
+  return g;
 }
 
 vit_status gemm(int dtype, int epi, const void* A, int64_t lda, const void* B, const void* B2,
@@ -179,6 +202,9 @@ vit_status gemm(int dtype, int epi, const void* A, int64_t lda, const void* B, c
   g.M = M;
   g.N = N;
   g.K = K;
+  g.kb = K;
+  g.rope_table = nullptr;
+  g.rope_cols = 0;
   const hipError_t e = dtype == VIT_BF16 ? launch_gemm_bf16(epi, g, s) : launch_gemm_f32(epi, g, s);
   return hip_check(e, "gemm launch");
 }
@@ -242,6 +268,8 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
     }
   }
   VIT_HIP(launch_rope_table(desc, c.head_dim, c.rope_theta, table, s), "rope table");
+  if (p.hp > h)
+    VIT_HIP(launch_zero_cols(dt, act, P, p.hp, h, p.hp, s), "zero MLP pad columns");
 
   for (int b = 0; b < c.n_blocks; ++b) {
     {
@@ -249,13 +277,24 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
       VIT_HIP(launch_rmsnorm(x, w->norm1[b], c.rms_eps, P, (int)d, dt, n, s), "norm1");
     }
     {
-      ProfScope ps(VIT_K_QKV, s);
-      VIT_TRY(gemm(dt, VIT_EPI_STORE, n, d, w->wqkv[b], nullptr, d, qkv, 3 * d, P, 3 * d, d,
-                   nullptr, s));
-    }
-    {
-      ProfScope ps(VIT_K_ROPE, s);
-      VIT_HIP(launch_rope(dt, qkv, table, P, c.n_heads, c.head_dim, s), "rope");
+      // wqkv with the rotary fused into the epilogue when each wave column is one
+      // 64-wide head; otherwise a separate rotary pass
+      GemmArgs g = gemm_args(n, d, w->wqkv[b], nullptr, d, qkv, 3 * d, P, 3 * d, d, nullptr);
+      g.rope_table = table;
+      g.rope_cols = 2 * d;
+      const bool fuse = dt == VIT_BF16 && c.head_dim == 64 && gemm_bf16_can_fuse_rope(g);
+      {
+        ProfScope ps(VIT_K_QKV, s);
+        if (fuse)
+          VIT_HIP(launch_gemm_bf16(VIT_EPI_STORE_ROPE, g, s), "qkv+rope gemm");
+        else
+          VIT_TRY(gemm(dt, VIT_EPI_STORE, n, d, w->wqkv[b], nullptr, d, qkv, 3 * d, P, 3 * d, d,
+                       nullptr, s));
+      }
+      if (!fuse) {
+        ProfScope ps(VIT_K_ROPE, s);
+        VIT_HIP(launch_rope(dt, qkv, table, P, c.n_heads, c.head_dim, s), "rope");
+      }
     }
     {
       ProfScope ps(VIT_K_ATTN, s);
@@ -271,13 +310,16 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
     }
     {
       ProfScope ps(VIT_K_GATEUP, s);
-      VIT_TRY(gemm(dt, VIT_EPI_SWIGLU, n, d, w->w_gate[b], w->w_up[b], d, act, h, P, h, d,
+      VIT_TRY(gemm(dt, VIT_EPI_SWIGLU, n, d, w->w_gate[b], w->w_up[b], d, act, p.hp, P, h, d,
                    nullptr, s));
     }
     {
       ProfScope ps(VIT_K_DOWN, s);
-      VIT_TRY(gemm(dt, VIT_EPI_ADD_F32, act, h, w->w_down[b], nullptr, h, x, d, P, d, h, nullptr,
-                   s));
+      GemmArgs g = gemm_args(act, p.hp, w->w_down[b], nullptr, h, x, d, P, d, p.hp, nullptr);
+      g.kb = h;  // act is zero past column h; W_down rows are h wide
+      VIT_HIP(dt == VIT_BF16 ? launch_gemm_bf16(VIT_EPI_ADD_F32, g, s)
+                             : launch_gemm_f32(VIT_EPI_ADD_F32, g, s),
+              "down gemm");
     }
   }
   {

@@ -65,10 +65,18 @@ struct GemmArgs {
   const int32_t* rowmap;  // optional output row remap (aligner newline layout)
   int64_t lda, ldb, ldc;
   int64_t M, N, K;
+  int64_t kb;  // valid K of B (< K when A is zero-padded past B's width)
+  const void* rope_table;  // float2 [M, 32] (head_dim 64) for the rotary epilogue
+  int64_t rope_cols;       // columns [0, rope_cols) get the rotary (q and k)
 };
+
+// Internal epilogue: bf16 store with the half-split 2D rotary applied to the
+// q and k columns (head_dim 64 only; each wave owns whole heads).
+constexpr int VIT_EPI_STORE_ROPE = 4;
 
 hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_f32(int epilogue, const GemmArgs& g, hipStream_t s);
+bool gemm_bf16_can_fuse_rope(const GemmArgs& g);
 hipError_t launch_rmsnorm(const float* x, const float* w, float eps, int64_t rows, int dim,
                           int out_dtype, void* out, hipStream_t s);
 hipError_t launch_rope_table(const VarlenDesc& d, int head_dim, float theta, void* table,
@@ -82,6 +90,8 @@ hipError_t launch_gather(int dtype, const void* x, const VarlenDesc& d, int dim,
                          void* G, hipStream_t s);
 hipError_t launch_pad_rows(int dtype, const void* src, int64_t rows, int64_t cols, int64_t ld_dst,
                            void* dst, hipStream_t s);
+hipError_t launch_zero_cols(int dtype, void* buf, int64_t rows, int64_t ld, int64_t c0, int64_t c1,
+                            hipStream_t s);
 hipError_t launch_layout(int grid_h, int grid_w, int merge, int32_t* perm, int32_t* nl_type,
                          int32_t* nl_src, hipStream_t s);
 hipError_t launch_nl_rowmap(const VarlenDesc& d, int merge, int32_t* rowmap, hipStream_t s);

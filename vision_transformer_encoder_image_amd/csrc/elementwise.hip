@@ -138,6 +138,15 @@ __global__ void pad_rows_kernel(const T* __restrict__ src, int64_t rows, int64_t
   for (int k = 0; k < 4; ++k) o[k] = v[k];
 }
 
+// Zero columns [c0, c1) of every row of a [rows, ld] buffer.
+template <typename T>
+__global__ void zero_cols_kernel(T* buf, int64_t rows, int64_t ld, int64_t c0, int64_t c1) {
+  const int64_t w = c1 - c0;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * w) return;
+  buf[(idx / w) * ld + c0 + idx % w] = from_f32<T>(0.f);
+}
+
 // Aligner layout arrays of one image (permutation and newline layout).
 __global__ void layout_kernel(int gh, int gw, int merge, int32_t* perm, int32_t* nl_type,
                               int32_t* nl_src) {
@@ -244,6 +253,17 @@ hipError_t launch_pad_rows(int dtype, const void* src, int64_t rows, int64_t col
   else
     pad_rows_kernel<float><<<blocks_for(n), kThreads, 0, s>>>((const float*)src, rows, cols,
                                                               ld_dst, (float*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_cols(int dtype, void* buf, int64_t rows, int64_t ld, int64_t c0, int64_t c1,
+                            hipStream_t s) {
+  const int64_t n = rows * (c1 - c0);
+  if (n <= 0) return hipSuccess;
+  if (dtype == VIT_BF16)
+    zero_cols_kernel<bf16><<<blocks_for(n), kThreads, 0, s>>>((bf16*)buf, rows, ld, c0, c1);
+  else
+    zero_cols_kernel<float><<<blocks_for(n), kThreads, 0, s>>>((float*)buf, rows, ld, c0, c1);
   return hipGetLastError();
 }
 
