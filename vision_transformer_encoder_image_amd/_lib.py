@@ -52,7 +52,9 @@ SIGNATURES = {
     "vit_rmsnorm": (c_i32, [c_vp, c_vp, c_f32, c_i64, c_i32, c_i32, c_vp, c_vp]),
     "vit_rope_table": (c_i32, [P_i32, c_i32, c_i32, c_f32, c_vp, c_vp]),
     "vit_rope": (c_i32, [c_i32, c_vp, c_vp, c_i64, c_i32, c_i32, c_vp]),
-    "vit_attention_varlen": (c_i32, [c_i32, c_vp, P_i32, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "vit_attention_workspace_bytes": (c_size, [c_i32, P_i32, c_i32, c_i32, c_i32]),
+    "vit_attention_varlen": (c_i32, [c_i32, c_vp, P_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_size,
+                                     c_vp]),
     "vit_gemm": (c_i32, [c_i32, c_i32, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64,
                          c_i64, c_vp]),
     "vit_aligner_gather": (c_i32, [c_i32, c_vp, P_i32, c_i32, c_i32, c_vp, c_vp]),

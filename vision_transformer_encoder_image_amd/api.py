@@ -197,8 +197,12 @@ def attention_varlen(qkv: torch.Tensor, grids, n_heads: int, head_dim: int) -> t
     _require_cuda(qkv)
     code = _lib.VIT_BF16 if qkv.dtype == torch.bfloat16 else _lib.VIT_F32
     out = torch.empty((qkv.shape[0], n_heads * head_dim), dtype=qkv.dtype, device=qkv.device)
-    st = _lib.load().vit_attention_varlen(code, qkv.data_ptr(), _lib.grid_array(grids), len(grids),
-                                          n_heads, head_dim, out.data_ptr(), _stream(qkv.device))
+    lib = _lib.load()
+    g = _lib.grid_array(grids)
+    nbytes = lib.vit_attention_workspace_bytes(code, g, len(grids), n_heads, head_dim)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=qkv.device)
+    st = lib.vit_attention_varlen(code, qkv.data_ptr(), g, len(grids), n_heads, head_dim,
+                                  out.data_ptr(), ws.data_ptr(), nbytes, _stream(qkv.device))
     _lib.check(st, "vit_attention_varlen")
     return out
 

@@ -109,7 +109,7 @@ vit_status build_desc(const int32_t* grid_hw, int32_t n_images, int q_tile, bool
     return fail(VIT_E_SHAPE, "n_images %d outside [1, %d]", n_images, VIT_MAX_IMAGES);
   std::memset(d, 0, sizeof(*d));
   d->n_images = n_images;
-  int64_t total = 0, tiles = 0;
+  int64_t total = 0, tiles = 0, kv = 0;
   for (int i = 0; i < n_images; ++i) {
     const int gh = grid_hw[2 * i], gw = grid_hw[2 * i + 1];
     if (gh <= 0 || gw <= 0) return fail(VIT_E_SHAPE, "image %d has grid %dx%d", i, gh, gw);
@@ -118,13 +118,16 @@ vit_status build_desc(const int32_t* grid_hw, int32_t n_images, int q_tile, bool
                   merge);
     d->cu_seqlens[i] = (int32_t)total;
     d->cu_tiles[i] = (int32_t)tiles;
+    d->kv_off[i] = (int32_t)kv;
     d->grid_w[i] = gw;
     total += (int64_t)gh * gw;
+    kv += ((int64_t)gh * gw + VT_ALIGN - 1) / VT_ALIGN * VT_ALIGN;
     tiles += ((int64_t)gh * gw + q_tile - 1) / q_tile;
     if (total > (1 << 24)) return fail(VIT_E_SHAPE, "more than 2^24 patches in one call");
   }
   d->cu_seqlens[n_images] = (int32_t)total;
   d->cu_tiles[n_images] = (int32_t)tiles;
+  d->kv_off[n_images] = (int32_t)kv;
   d->total = (int32_t)total;
   return VIT_OK;
 }
@@ -132,10 +135,14 @@ vit_status build_desc(const int32_t* grid_hw, int32_t n_images, int q_tile, bool
 struct Plan {
   int64_t P = 0, tokens = 0, Kp = 0, hp = 0;
   size_t table = 0, xpad = 0, wpe = 0, x = 0, n = 0, qkv = 0, act = 0, G = 0, rowmap = 0;
+  size_t vt = 0, vpos = 0;
+  int64_t kv_total = 0;
+  bool use_vt = false;  // bf16, head_dim 64: V written transposed by the wqkv GEMM
   size_t total = 0;
 };
 
-Plan make_plan(const vit_config& c, int64_t P, int flags) {
+Plan make_plan(const vit_config& c, const VarlenDesc& desc, int flags) {
+  const int64_t P = desc.total;
   Plan p;
   const size_t es = esize(c.dtype);
   const bool aligner = !(flags & VIT_NO_ALIGNER);
@@ -161,6 +168,12 @@ Plan make_plan(const vit_config& c, int64_t P, int flags) {
   p.n = take((size_t)P * d * es);  // also holds the attention output
   p.qkv = take((size_t)P * 3 * d * es);
   p.act = take((size_t)P * p.hp * es);
+  p.use_vt = c.dtype == VIT_BF16 && c.head_dim == 64;
+  if (p.use_vt) {
+    p.kv_total = desc.kv_off[desc.n_images];
+    p.vt = take((size_t)d * p.kv_total * es);
+    p.vpos = take((size_t)P * sizeof(int32_t));
+  }
   if (aligner) p.G = take((size_t)p.tokens * m2 * d * es);
   if (aligner && (flags & VIT_OUT_NLAYOUT)) p.rowmap = take((size_t)p.tokens * sizeof(int32_t));
   p.total = off;
@@ -238,7 +251,7 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
   VarlenDesc desc;
   VIT_TRY(build_desc(grid_hw, n_images, attention_q_tile(c.dtype, c.head_dim), aligner, c.merge,
                      &desc));
-  const Plan p = make_plan(c, desc.total, flags);
+  const Plan p = make_plan(c, desc, flags);
   if (!ws || ws_bytes < p.total)
     return fail(VIT_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0,
                 p.total);
@@ -270,35 +283,47 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
   VIT_HIP(launch_rope_table(desc, c.head_dim, c.rope_theta, table, s), "rope table");
   if (p.hp > h)
     VIT_HIP(launch_zero_cols(dt, act, P, p.hp, h, p.hp, s), "zero MLP pad columns");
+  void* vt = p.use_vt ? base + p.vt : nullptr;
+  int32_t* vpos = p.use_vt ? (int32_t*)(base + p.vpos) : nullptr;
+  if (p.use_vt) {
+    VIT_HIP(launch_vpos(desc, vpos, s), "transposed-V positions");
+    VIT_HIP(launch_vt_zero_pads(desc, d, vt, p.kv_total, s), "transposed-V padding");
+  }
 
   for (int b = 0; b < c.n_blocks; ++b) {
     {
       ProfScope ps(VIT_K_RMSNORM, s);
       VIT_HIP(launch_rmsnorm(x, w->norm1[b], c.rms_eps, P, (int)d, dt, n, s), "norm1");
     }
+    // wqkv: with head_dim 64 in bf16 the epilogue applies the rotary to q, k
+    // (stored [P, 2d]) and writes v transposed per head for the attention
+    // kernel; otherwise plain [P, 3d] output and a separate rotary pass
+    GemmArgs g = gemm_args(n, d, w->wqkv[b], nullptr, d, qkv, 2 * d, P, 3 * d, d, nullptr);
+    g.rope_table = table;
+    g.rope_cols = 2 * d;
+    g.vt = vt;
+    g.vpos = vpos;
+    g.vt_ld = p.kv_total;
+    const bool fuse = p.use_vt && gemm_bf16_can_fuse_rope(g);
     {
-      // wqkv with the rotary fused into the epilogue when each wave column is one
-      // 64-wide head; otherwise a separate rotary pass
-      GemmArgs g = gemm_args(n, d, w->wqkv[b], nullptr, d, qkv, 3 * d, P, 3 * d, d, nullptr);
-      g.rope_table = table;
-      g.rope_cols = 2 * d;
-      const bool fuse = dt == VIT_BF16 && c.head_dim == 64 && gemm_bf16_can_fuse_rope(g);
-      {
-        ProfScope ps(VIT_K_QKV, s);
-        if (fuse)
-          VIT_HIP(launch_gemm_bf16(VIT_EPI_STORE_ROPE, g, s), "qkv+rope gemm");
-        else
-          VIT_TRY(gemm(dt, VIT_EPI_STORE, n, d, w->wqkv[b], nullptr, d, qkv, 3 * d, P, 3 * d, d,
-                       nullptr, s));
-      }
-      if (!fuse) {
-        ProfScope ps(VIT_K_ROPE, s);
-        VIT_HIP(launch_rope(dt, qkv, table, P, c.n_heads, c.head_dim, s), "rope");
-      }
+      ProfScope ps(VIT_K_QKV, s);
+      if (fuse)
+        VIT_HIP(launch_gemm_bf16(VIT_EPI_QKV_VT, g, s), "qkv+rope gemm");
+      else
+        VIT_TRY(gemm(dt, VIT_EPI_STORE, n, d, w->wqkv[b], nullptr, d, qkv, 3 * d, P, 3 * d, d,
+                     nullptr, s));
+    }
+    if (!fuse) {
+      ProfScope ps(VIT_K_ROPE, s);
+      VIT_HIP(launch_rope(dt, qkv, table, P, c.n_heads, c.head_dim, s), "rope");
     }
     {
       ProfScope ps(VIT_K_ATTN, s);
-      VIT_HIP(launch_attention(dt, qkv, desc, c.n_heads, c.head_dim, n, s), "attention");
+      if (fuse)
+        VIT_HIP(launch_attention_vt(qkv, 2 * d, vt, p.kv_total, desc, c.n_heads, n, s),
+                "attention");
+      else
+        VIT_HIP(launch_attention(dt, qkv, desc, c.n_heads, c.head_dim, n, s), "attention");
     }
     {
       ProfScope ps(VIT_K_OUTPROJ, s);
@@ -374,7 +399,7 @@ size_t vit_workspace_bytes(const vit_config* cfg, const int32_t* grid_hw_host, i
   if (build_desc(grid_hw_host, n_images, attention_q_tile(cfg->dtype, cfg->head_dim), aligner,
                  cfg->merge, &d) != VIT_OK)
     return 0;
-  return make_plan(*cfg, d.total, flags).total;
+  return make_plan(*cfg, d, flags).total;
 }
 
 vit_status vit_encode(const vit_config* cfg, const vit_weights* w, const void* in, int32_t grid_h,
@@ -430,17 +455,35 @@ vit_status vit_rope(int32_t dtype, void* qkv, const void* table, int64_t P, int3
                    "rope");
 }
 
+size_t vit_attention_workspace_bytes(int32_t dtype, const int32_t* grid_hw_host,
+                                     int32_t n_images, int32_t n_heads, int32_t head_dim) {
+  if (dtype != VIT_BF16 || head_dim != 64) return 0;
+  VarlenDesc d;
+  if (build_desc(grid_hw_host, n_images, attention_q_tile(dtype, head_dim), false, 2, &d) != VIT_OK)
+    return 0;
+  return (size_t)n_heads * head_dim * d.kv_off[n_images] * 2;
+}
+
 vit_status vit_attention_varlen(int32_t dtype, const void* qkv, const int32_t* grid_hw_host,
                                 int32_t n_images, int32_t n_heads, int32_t head_dim, void* out,
-                                void* stream) {
+                                void* ws, size_t ws_bytes, void* stream) {
   if (!qkv || !out) return fail(VIT_E_ARG, "NULL pointer");
   if (dtype != VIT_BF16 && dtype != VIT_F32) return fail(VIT_E_ARG, "bad dtype");
   if (n_heads <= 0 || (head_dim != 64 && head_dim != 72))
     return fail(VIT_E_SHAPE, "head_dim %d unsupported (64 or 72)", head_dim);
   VarlenDesc d;
   VIT_TRY(build_desc(grid_hw_host, n_images, attention_q_tile(dtype, head_dim), false, 2, &d));
-  return hip_check(launch_attention(dtype, qkv, d, n_heads, head_dim, out, (hipStream_t)stream),
-                   "attention");
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == VIT_BF16 && head_dim == 64) {
+    const size_t need = (size_t)n_heads * head_dim * d.kv_off[n_images] * 2;
+    if (!ws || ws_bytes < need)
+      return fail(VIT_E_WORKSPACE, "attention workspace %zu < %zu", ws ? ws_bytes : (size_t)0, need);
+    VIT_HIP(launch_vt_pack(qkv, d, n_heads, head_dim, ws, d.kv_off[n_images], s), "pack V");
+    return hip_check(launch_attention_vt(qkv, 3 * (int64_t)n_heads * head_dim, ws,
+                                         d.kv_off[n_images], d, n_heads, out, s),
+                     "attention");
+  }
+  return hip_check(launch_attention(dtype, qkv, d, n_heads, head_dim, out, s), "attention");
 }
 
 vit_status vit_gemm(int32_t dtype, int32_t epilogue, const void* A, int64_t lda, const void* B,

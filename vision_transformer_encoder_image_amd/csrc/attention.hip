@@ -228,6 +228,184 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
 #undef VIT_LSTORE
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16 kernel for head_dim 64 with V supplied transposed ([H*64, ld], each
+// image's keys starting 64-aligned, padding zero, and the keys of every
+// 16-key group stored in the order 0-3, 8-11, 4-7, 12-15: see vt_key_slot).
+// K tiles ([key][64]) and V^T tiles ([d][64 key slots]) are plain 128-byte rows,
+// copied straight into a 4-stage LDS ring with global_load_lds_dwordx4 (16-byte
+// chunks XOR-swizzled per row) with exact vmcnt waits, as in the GEMM.
+// Math on v_mfma_f32_32x32x16_bf16: each wave owns 32 queries; per 64-key tile
+//   S^T (2 blocks of 32 keys x 32 queries) = K . Q^T   (Q fragments in registers)
+//   O^T (2 blocks of 32 dims x 32 queries) += V^T . P^T
+// A lane holds one query (column) and 32 of the tile's 64 keys, so the row max
+// needs one exchange with lane ^ 32 and the running sum none until the end.
+// The k-slot order of P^T is the S^T accumulator order; the V^T key-slot
+// permutation makes the matching 8 keys of a lane one contiguous 16-byte read.
+// Software pipelining: the S^T MFMAs of tile t+1 are issued before the softmax
+// of tile t, so the exp/max/sum VALU work of one tile overlaps the matrix work
+// of the next.  The softmax reference max is raised only when some lane's max
+// grows by more than 2^8 (exact after the final 1/sum; p stays <= 256).
+constexpr int VT_BQ = 128, VT_BKV = 64, VT_STAGES = 4;
+constexpr float VT_RESCALE_LOG2 = 8.0f;
+
+VIT_DEV int vt_swz(int row) { return (row >> 1) & 7; }
+
+__global__ __launch_bounds__(256, 2) void attn_vt_kernel(const bf16* __restrict__ qk, int64_t ldq,
+                                                         const bf16* __restrict__ vt,
+                                                         int64_t vt_ld, VarlenDesc desc, int H,
+                                                         bf16* __restrict__ out, float c) {
+  __shared__ __attribute__((aligned(16))) bf16 sm[VT_STAGES][2][VT_BKV * 64];
+  const int tile = blockIdx.x, h = blockIdx.y;
+  int img = 0;
+  while (img + 1 < desc.n_images && tile >= desc.cu_tiles[img + 1]) ++img;
+  const int seq0 = desc.cu_seqlens[img];
+  const int P = desc.cu_seqlens[img + 1] - seq0;
+  const int q0 = (tile - desc.cu_tiles[img]) * VT_BQ;  // local query offset
+  const int kvo = desc.kv_off[img];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int fr = lane & 31, fh = lane >> 5;
+  const int64_t dm = (int64_t)H * 64;
+
+  // copies per stage: 8 x 1 KB of K rows then 8 x 1 KB of V^T rows; wave w
+  // issues copies w, w+4, w+8, w+12
+  const int crow = lane >> 3;
+  const int cpc = lane & 7;
+#define VIT_ATT_ISSUE(t)                                                                 \
+  do {                                                                                   \
+    const int kv0_ = (t) * VT_BKV;                                                       \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
+      const int q_ = wave + 4 * i;                                                       \
+      const int r_ = 8 * (q_ & 7) + crow;                                                \
+      const int kc_ = cpc ^ vt_swz(r_);                                                  \
+      const bf16* src_;                                                                  \
+      if (q_ < 8)                                                                        \
+        src_ = qk + (int64_t)(seq0 + min(kv0_ + r_, P - 1)) * ldq + dm + h * 64 + kc_ * 8; \
+      else                                                                               \
+        src_ = vt + (int64_t)(h * 64 + r_) * vt_ld + kvo + kv0_ + kc_ * 8;               \
+      copy16_to_lds(src_, &sm[(t) % VT_STAGES][q_ >> 3][(q_ & 7) * 512]);                \
+    }                                                                                    \
+  } while (0)
+#define VIT_ATT_QK(sacc, stage)                                                          \
+  do {                                                                                   \
+    const bf16* sK_ = sm[stage][0];                                                      \
+    sacc[0] = f32x16{};                                                                  \
+    sacc[1] = f32x16{};                                                                  \
+    _Pragma("unroll") for (int ks = 0; ks < 4; ++ks)                                     \
+    _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) {                                   \
+      const int r_ = kb * 32 + fr;                                                       \
+      const bf16x8 kf_ = *reinterpret_cast<const bf16x8*>(                               \
+          sK_ + r_ * 64 + (((2 * ks + fh) ^ vt_swz(r_)) << 3));                          \
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf_, qf[ks], sacc[kb], 0, 0, 0); \
+    }                                                                                    \
+  } while (0)
+
+  // Q^T fragments (B operand): query q0 + wave*32 + fr, dims 16 ks + 8 fh .. +7
+  bf16x8 qf[4];
+  {
+    const int qi = min(q0 + wave * 32 + fr, P - 1);
+    const bf16* qrow = qk + (int64_t)(seq0 + qi) * ldq + h * 64 + fh * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16(qrow + ks * 16));
+  }
+
+  f32x16 o[2] = {f32x16{}, f32x16{}};
+  f32x16 sc[2], sn[2];
+  float mref = -INFINITY, lsum = 0.f;
+  const int nkv = (P + VT_BKV - 1) / VT_BKV;
+  VIT_ATT_ISSUE(0);
+  if (nkv > 1) VIT_ATT_ISSUE(1);
+  if (nkv > 2) VIT_ATT_ISSUE(2);
+  if (nkv > 2)
+    wait_vmcnt<8>();
+  else if (nkv > 1)
+    wait_vmcnt<4>();
+  else
+    wait_vmcnt<0>();
+  lds_barrier();
+  VIT_ATT_QK(sc, 0);
+
+  for (int t = 0; t < nkv; ++t) {
+    // tile t+1 must have landed; the barrier also retires all reads of tile t-1,
+    // whose buffer the next copy overwrites
+    if (t + 1 < nkv) {
+      if (t + 2 < nkv)
+        wait_vmcnt<4>();
+      else
+        wait_vmcnt<0>();
+    }
+    lds_barrier();
+    if (t + 3 < nkv) VIT_ATT_ISSUE(t + 3);
+    if (t + 1 < nkv) VIT_ATT_QK(sn, (t + 1) % VT_STAGES);
+
+    const int kv0 = t * VT_BKV;
+    if (kv0 + VT_BKV > P) {  // ragged last tile of the image
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kv0 + kb * 32 + (i >> 2) * 8 + fh * 4 + (i & 3) >= P) sc[kb][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (__any((mx - mref) * c > VT_RESCALE_LOG2)) {
+      const float mnew = fmaxf(mref, mx);
+      const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * c);
+      mref = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) o[db] *= alpha;
+    }
+    const float nmc = -mref * c;
+    const bf16* sV = sm[t % VT_STAGES][1];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        bf16x8 pf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * ks2 + j], c, nmc));
+          lsum += p;
+          pf[j] = f2bf(p);
+        }
+        const int chunk = kb * 4 + ks2 * 2 + fh;  // key slots 32 kb + 16 ks2 + 8 fh .. +7
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const int vr = db * 32 + fr;
+          const bf16x8 vf =
+              *reinterpret_cast<const bf16x8*>(sV + vr * 64 + ((chunk ^ vt_swz(vr)) << 3));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
+        }
+      }
+    sc[0] = sn[0];
+    sc[1] = sn[1];
+  }
+#undef VIT_ATT_ISSUE
+#undef VIT_ATT_QK
+
+  const float l = lsum + __shfl_xor(lsum, 32, 64);
+  const float inv = 1.0f / l;
+  const int qi = q0 + wave * 32 + fr;
+  if (qi < P) {
+    bf16* orow = out + (int64_t)(seq0 + qi) * dm + h * 64;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = f2bf(o[db][4 * grp + r] * inv);
+        *reinterpret_cast<bf16x4*>(orow + db * 32 + grp * 8 + fh * 4) = v;
+      }
+  }
+}
+
 // ---------------------------------------------------------------------------
 constexpr int FQ = 64, FKV = 32;
 
@@ -284,6 +462,17 @@ __global__ __launch_bounds__(FQ) void attn_f32_kernel(const float* __restrict__ 
 }  // namespace
 
 int attention_q_tile(int dtype, int /*head_dim*/) { return dtype == VIT_BF16 ? BQ : FQ; }
+
+hipError_t launch_attention_vt(const void* qk, int64_t ld_qk, const void* vt, int64_t vt_ld,
+                               const VarlenDesc& d, int n_heads, void* out, hipStream_t s) {
+  static_assert(VT_BQ == BQ, "both bf16 kernels share the q-tile descriptor");
+  const int tiles = d.cu_tiles[d.n_images];
+  if (tiles == 0) return hipSuccess;
+  const float c = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
+  attn_vt_kernel<<<dim3((unsigned)tiles, (unsigned)n_heads), 256, 0, s>>>(
+      (const bf16*)qk, ld_qk, (const bf16*)vt, vt_ld, d, n_heads, (bf16*)out, c);
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(int dtype, const void* qkv, const VarlenDesc& d, int n_heads,
                             int head_dim, void* out, hipStream_t s) {

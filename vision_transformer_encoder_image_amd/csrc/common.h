@@ -41,6 +41,34 @@ VIT_DEV float wave_max(float v) {
   return v;
 }
 
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | expcnt[6:4]
+// | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+template <int N>
+VIT_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane i writes
+// bytes [16 i, 16 i + 16) after the wave-uniform LDS address.  The builtin only
+// exists for the gfx950 device pass, so the host pass sees an empty body.
+VIT_DEV void copy16_to_lds(const void* gptr, void* lptr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lptr, 16, 0, 0);
+#else
+  (void)gptr;
+  (void)lptr;
+#endif
+}
+
+// Workgroup barrier that keeps LDS accesses in program order without draining
+// the outstanding global->LDS copies (the exact vmcnt waits do that).
+VIT_DEV void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Per-image descriptors of a packed batch, passed by value as kernel arguments.
 struct VarlenDesc {
   int32_t n_images;
@@ -48,7 +76,17 @@ struct VarlenDesc {
   int32_t cu_seqlens[VIT_MAX_IMAGES + 1];
   int32_t grid_w[VIT_MAX_IMAGES];
   int32_t cu_tiles[VIT_MAX_IMAGES + 1];  // prefix sum of q-tiles per image (attention)
+  int32_t kv_off[VIT_MAX_IMAGES + 1];    // image starts in the transposed-V layout (64-aligned)
 };
+
+// Keys of one image start at a multiple of this in the transposed-V layout.
+constexpr int VT_ALIGN = 64;
+
+// Slot of key j inside its 16-key group of the transposed-V layout: the groups
+// of four keys are stored in the order 0-3, 8-11, 4-7, 12-15 (bits 2 and 3 of j
+// swapped), so that the 8 keys one MFMA lane needs for P.V are contiguous.  The
+// map is its own inverse.
+VIT_DEV int vt_key_slot(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
 
 VIT_DEV int find_image(const VarlenDesc& d, int p) {
   int i = 0;
@@ -68,11 +106,17 @@ struct GemmArgs {
   int64_t kb;  // valid K of B (< K when A is zero-padded past B's width)
   const void* rope_table;  // float2 [M, 32] (head_dim 64) for the rotary epilogue
   int64_t rope_cols;       // columns [0, rope_cols) get the rotary (q and k)
+  void* vt;                // transposed V [n_heads*64, vt_ld] (VIT_EPI_QKV_VT)
+  const int32_t* vpos;     // column of every row m in vt
+  int64_t vt_ld;
 };
 
 // Internal epilogue: bf16 store with the half-split 2D rotary applied to the
 // q and k columns (head_dim 64 only; each wave owns whole heads).
 constexpr int VIT_EPI_STORE_ROPE = 4;
+// Internal epilogue: as VIT_EPI_STORE_ROPE for the q, k columns (C holds [M, rope_cols])
+// while the v columns are written transposed, one row per (head, dim), into vt.
+constexpr int VIT_EPI_QKV_VT = 5;
 
 hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_f32(int epilogue, const GemmArgs& g, hipStream_t s);
@@ -86,6 +130,13 @@ hipError_t launch_rope(int dtype, void* qkv, const void* table, int64_t P, int n
 hipError_t launch_attention(int dtype, const void* qkv, const VarlenDesc& d, int n_heads,
                             int head_dim, void* out, hipStream_t s);
 int attention_q_tile(int dtype, int head_dim);
+hipError_t launch_attention_vt(const void* qk, int64_t ld_qk, const void* vt, int64_t vt_ld,
+                               const VarlenDesc& d, int n_heads, void* out, hipStream_t s);
+hipError_t launch_vpos(const VarlenDesc& d, int32_t* vpos, hipStream_t s);
+hipError_t launch_vt_zero_pads(const VarlenDesc& d, int64_t rows, void* vt, int64_t vt_ld,
+                               hipStream_t s);
+hipError_t launch_vt_pack(const void* qkv, const VarlenDesc& d, int n_heads, int head_dim,
+                          void* vt, int64_t vt_ld, hipStream_t s);
 hipError_t launch_gather(int dtype, const void* x, const VarlenDesc& d, int dim, int merge,
                          void* G, hipStream_t s);
 hipError_t launch_pad_rows(int dtype, const void* src, int64_t rows, int64_t cols, int64_t ld_dst,

@@ -138,6 +138,44 @@ __global__ void pad_rows_kernel(const T* __restrict__ src, int64_t rows, int64_t
   for (int k = 0; k < 4; ++k) o[k] = v[k];
 }
 
+// Column of every patch in the transposed-V layout (images start 64-aligned).
+__global__ void vpos_kernel(VarlenDesc d, int32_t* vpos) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= d.total) return;
+  const int img = find_image(d, p);
+  vpos[p] = d.kv_off[img] + vt_key_slot(p - d.cu_seqlens[img]);
+}
+
+// Zero the slots of vt that hold no key: in image i, every slot from the start
+// of the 16-key group containing key P_i up to kv_off_{i+1} whose key is >= P_i.
+__global__ void vt_zero_pads_kernel(VarlenDesc d, int64_t rows, bf16* vt, int64_t ld) {
+  const int64_t row = blockIdx.y;
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;  // offset from the last group start
+  if (row >= rows || c >= VT_ALIGN + 16) return;
+  for (int i = 0; i < d.n_images; ++i) {
+    const int P = d.cu_seqlens[i + 1] - d.cu_seqlens[i];
+    const int j = (P & ~15) + c;  // local slot
+    if (d.kv_off[i] + j < d.kv_off[i + 1] && vt_key_slot(j) >= P)
+      vt[row * ld + d.kv_off[i] + j] = f2bf(0.f);
+  }
+}
+
+// V part of a packed qkv buffer [P, 3*H*D] -> vt [H*D, ld] (images 64-aligned,
+// padding zeroed).  One thread per element of vt.
+__global__ void vt_pack_kernel(const bf16* __restrict__ qkv, VarlenDesc d, int H, int D,
+                               bf16* __restrict__ vt, int64_t ld) {
+  const int64_t row = blockIdx.y;  // h*D + e
+  const int col = blockIdx.x * blockDim.x + threadIdx.x;
+  if (col >= d.kv_off[d.n_images]) return;
+  int img = 0;
+  while (img + 1 < d.n_images && col >= d.kv_off[img + 1]) ++img;
+  const int key = vt_key_slot(col - d.kv_off[img]);
+  const int P = d.cu_seqlens[img + 1] - d.cu_seqlens[img];
+  bf16 v = f2bf(0.f);
+  if (key < P) v = qkv[(int64_t)(d.cu_seqlens[img] + key) * 3 * H * D + 2 * H * D + row];
+  vt[row * ld + col] = v;
+}
+
 // Zero columns [c0, c1) of every row of a [rows, ld] buffer.
 template <typename T>
 __global__ void zero_cols_kernel(T* buf, int64_t rows, int64_t ld, int64_t c0, int64_t c1) {
@@ -264,6 +302,29 @@ hipError_t launch_zero_cols(int dtype, void* buf, int64_t rows, int64_t ld, int6
     zero_cols_kernel<bf16><<<blocks_for(n), kThreads, 0, s>>>((bf16*)buf, rows, ld, c0, c1);
   else
     zero_cols_kernel<float><<<blocks_for(n), kThreads, 0, s>>>((float*)buf, rows, ld, c0, c1);
+  return hipGetLastError();
+}
+
+hipError_t launch_vpos(const VarlenDesc& d, int32_t* vpos, hipStream_t s) {
+  if (d.total == 0) return hipSuccess;
+  vpos_kernel<<<blocks_for(d.total), kThreads, 0, s>>>(d, vpos);
+  return hipGetLastError();
+}
+
+hipError_t launch_vt_zero_pads(const VarlenDesc& d, int64_t rows, void* vt, int64_t vt_ld,
+                               hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  vt_zero_pads_kernel<<<dim3(1, (unsigned)rows), VT_ALIGN + 16, 0, s>>>(d, rows, (bf16*)vt,
+                                                                        vt_ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_vt_pack(const void* qkv, const VarlenDesc& d, int n_heads, int head_dim,
+                          void* vt, int64_t vt_ld, hipStream_t s) {
+  const int cols = d.kv_off[d.n_images];
+  if (cols == 0) return hipSuccess;
+  vt_pack_kernel<<<dim3(blocks_for(cols), (unsigned)(n_heads * head_dim)), kThreads, 0, s>>>(
+      (const bf16*)qkv, d, n_heads, head_dim, (bf16*)vt, vt_ld);
   return hipGetLastError();
 }
 

@@ -245,15 +245,17 @@ bool pipe_eligible(const GemmArgs& g) {
 
 }  // namespace
 
-// Tile configuration by a wave-quantisation cost model: cost ~ (rounds of 256
-// workgroups) x (tile area / relative efficiency).  The 8-wave 256x128 tile is
-// ~1.3x more efficient per flop (measured on gfx950) but has half the tiles.
+// Tile configuration by a wave-quantisation cost model: cost ~ (rounds of one
+// workgroup per CU) x (tile area / relative efficiency).  The 8-wave tiles are
+// ~1.35x (256x128) and ~1.45x (256x256, BK 32) more efficient per flop than the
+// 4-wave 128x128 tile on gfx950 but give 2x / 4x fewer tiles.
 int gemm_pipe_choice(int epilogue, int64_t M, int64_t N, int64_t K) {
   (void)K;
   const bool dual = epilogue == VIT_EPI_SWIGLU;
   struct Opt { int cfg, bm, bn; double eff; };
   const Opt opts[] = {{GEMM_PIPE_128x128_S4, 128, 128, 1.0},
-                      {GEMM_PIPE_256x128_W8_S3, 256, 128, 1.3}};
+                      {GEMM_PIPE_256x128_W8_S3, 256, 128, 1.35},
+                      {GEMM_PIPE_256x256_W8_K32_S4, 256, 256, 1.45}};
   int best = GEMM_PIPE_128x128_S4;
   double best_cost = 1e300;
   for (const Opt& o : opts) {
@@ -273,11 +275,12 @@ bool gemm_bf16_can_fuse_rope(const GemmArgs& g) { return pipe_eligible(g); }
 
 hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
-  if (epilogue == VIT_EPI_STORE_ROPE) {
-    if (!pipe_eligible(g)) return hipErrorInvalidValue;
-    return launch_gemm_pipe(gemm_pipe_choice(VIT_EPI_STORE, g.M, g.N, g.K), epilogue, g, s);
+  const bool rope = epilogue == VIT_EPI_STORE_ROPE || epilogue == VIT_EPI_QKV_VT;
+  if (rope && !pipe_eligible(g)) return hipErrorInvalidValue;
+  if (pipe_eligible(g)) {
+    const int cfg = gemm_pipe_choice(rope ? VIT_EPI_STORE : epilogue, g.M, g.N, g.K);
+    if (cfg == GEMM_PIPE_128x128_S4) return launch_gemm_tile128(epilogue, g, s);
+    return launch_gemm_pipe(cfg, epilogue, g, s);
   }
-  if (pipe_eligible(g))
-    return launch_gemm_pipe(gemm_pipe_choice(epilogue, g.M, g.N, g.K), epilogue, g, s);
   return launch_simple(epilogue, g, s);
 }
