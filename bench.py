@@ -26,11 +26,12 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "ragged_varlen_4img"
 
-# kernel class -> source file of its kernel (for the counter-traffic freshness check)
-KERNEL_SOURCE = {"qkv": "gemm_bf16.hip", "outproj": "gemm_bf16.hip", "gateup": "gemm_bf16.hip",
-                 "down": "gemm_bf16.hip", "embed": "gemm_bf16.hip", "aligner": "gemm_bf16.hip",
-                 "attn": "attention.hip", "rmsnorm": "elementwise.hip", "rope": "elementwise.hip",
-                 "gather": "elementwise.hip"}
+# kernel class -> sources of its kernels (for the counter-traffic freshness check)
+_GEMM_SRC = ("common.h", "gemm_bf16.hip", "gemm_pipe.h", "gemm_pipe.hip", "gemm_tile.hip")
+KERNEL_SOURCE = {"qkv": _GEMM_SRC, "outproj": _GEMM_SRC, "gateup": _GEMM_SRC, "down": _GEMM_SRC,
+                 "embed": _GEMM_SRC, "aligner": _GEMM_SRC, "attn": ("common.h", "attention.hip"),
+                 "rmsnorm": ("common.h", "elementwise.hip"), "rope": ("common.h", "elementwise.hip"),
+                 "gather": ("common.h", "elementwise.hip")}
 
 
 def class_flops(cfg):
@@ -53,8 +54,10 @@ def class_bytes(cfg):
 
 
 def source_sha(kernel_class):
-    p = os.path.join(ROOT, "vision_transformer_encoder_image_amd", "csrc", KERNEL_SOURCE[kernel_class])
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCE[kernel_class]:
+        h.update(open(os.path.join(ROOT, "vision_transformer_encoder_image_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
 
 
 def counter_traffic(kernel_class, workload):
@@ -66,6 +69,49 @@ def counter_traffic(kernel_class, workload):
     if rec.get("source_sha256") != source_sha(kernel_class):
         return None  # the kernel changed since the counters were taken
     return rec.get("hbm_bytes_per_launch")
+
+
+# kernel-name patterns of each class in rocprofv3 output (SwiGLU is the only
+# dual-B GEMM instantiation, i.e. the template argument list ends in "true>")
+KERNEL_NAME_PATTERN = {"gateup": ("gemm_", ", true>("), "attn": ("attn_vt_kernel", ""),
+                       "rmsnorm": ("rmsnorm_kernel", "")}
+
+
+def _pmc_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def pmc_summary(fetch_dir, write_dir, kernel, workload, copy_mb, out_path=None):
+    """HBM bytes per launch of `kernel` from FETCH_SIZE / WRITE_SIZE runs, each scaled
+    by the bytes the same counter reports for a plain copy of known size."""
+    import statistics
+
+    pat, tail = KERNEL_NAME_PATTERN[kernel]
+    out = {"kernel": kernel, "workload": workload, "source_sha256": source_sha(kernel)}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _pmc_rows(d) if r["Counter_Name"] == counter]
+        sel = [float(r["Counter_Value"]) for r in rows
+               if pat in r["Kernel_Name"] and tail in r["Kernel_Name"]]
+        copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]
+                or "copy_kernel" in r["Kernel_Name"] or "elementwise" in r["Kernel_Name"]]
+        known_kib = copy_mb * 1024.0
+        scale = known_kib / max(copy) if copy else 1.0
+        kib = statistics.median(sel) if sel else float("nan")
+        out[counter.lower() + "_kib_raw"] = kib
+        out[counter.lower() + "_copy_kib_raw"] = max(copy) if copy else None
+        out[counter.lower() + "_scale"] = scale
+        out[counter.lower() + "_bytes_per_launch"] = kib * scale * 1024.0
+        out[counter.lower() + "_launches"] = len(sel)
+    out["hbm_bytes_per_launch"] = out["fetch_size_bytes_per_launch"] + out["write_size_bytes_per_launch"]
+    path = out_path or os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def cpu_baseline(cfg, inp, budget_s=30.0):
@@ -103,7 +149,19 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="after the timed steps, run a plain device copy of this many MiB "
+                         "(the reference kernel for HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "script into profiles/traffic_<kernel>_<workload>.json and exit")
+    ap.add_argument("--kernel", default="gateup", help="kernel class for --pmc-summary")
+    ap.add_argument("--pmc-out", default=None, help="output path for --pmc-summary")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.kernel, args.workload,
+                    args.copy_calibration_mb, args.pmc_out)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the encoder shards "
               "by image across GPUs with no exchange, so run one process per GPU instead.",
@@ -208,6 +266,14 @@ def main():
                 e["hbm_frac"] = round(byts[k] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
             bd[k] = e
         result["breakdown"] = bd
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(result), flush=True)

@@ -257,7 +257,15 @@ __global__ __launch_bounds__(256, 2) void attn_vt_kernel(const bf16* __restrict_
                                                          int64_t vt_ld, VarlenDesc desc, int H,
                                                          bf16* __restrict__ out, float c) {
   __shared__ __attribute__((aligned(16))) bf16 sm[VT_STAGES][2][VT_BKV * 64];
-  const int tile = blockIdx.x, h = blockIdx.y;
+  // 1D grid over (head, q-tile); workgroup ids are dealt round-robin to the 8
+  // XCDs, so give every XCD a contiguous range of work items: the q-tiles of one
+  // (image, head) then share that XCD's L2 copy of the image's K and V^T
+  const int ntiles = desc.cu_tiles[desc.n_images];
+  const int nitems = ntiles * H;
+  const int per = nitems / 8, rem = nitems % 8;
+  const int xcd = blockIdx.x % 8;
+  const int item = xcd * per + min(xcd, rem) + (int)blockIdx.x / 8;
+  const int h = item / ntiles, tile = item % ntiles;
   int img = 0;
   while (img + 1 < desc.n_images && tile >= desc.cu_tiles[img + 1]) ++img;
   const int seq0 = desc.cu_seqlens[img];
@@ -469,7 +477,7 @@ hipError_t launch_attention_vt(const void* qk, int64_t ld_qk, const void* vt, in
   const int tiles = d.cu_tiles[d.n_images];
   if (tiles == 0) return hipSuccess;
   const float c = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
-  attn_vt_kernel<<<dim3((unsigned)tiles, (unsigned)n_heads), 256, 0, s>>>(
+  attn_vt_kernel<<<dim3((unsigned)(tiles * n_heads)), 256, 0, s>>>(
       (const bf16*)qk, ld_qk, (const bf16*)vt, vt_ld, d, n_heads, (bf16*)out, c);
   return hipGetLastError();
 }
