@@ -27,7 +27,7 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "ragged_varlen_4img"
 
 # kernel class -> sources of its kernels (for the counter-traffic freshness check)
-_GEMM_SRC = ("common.h", "gemm_bf16.hip", "gemm_pipe.h", "gemm_pipe.hip", "gemm_tile.hip")
+_GEMM_SRC = ("common.h", "gemm_bf16.hip", "gemm_mfma.h", "gemm_mfma.hip")
 KERNEL_SOURCE = {"qkv": _GEMM_SRC, "outproj": _GEMM_SRC, "gateup": _GEMM_SRC, "down": _GEMM_SRC,
                  "embed": _GEMM_SRC, "aligner": _GEMM_SRC, "attn": ("common.h", "attention.hip"),
                  "rmsnorm": ("common.h", "elementwise.hip"), "rope": ("common.h", "elementwise.hip"),

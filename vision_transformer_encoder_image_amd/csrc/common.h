@@ -61,6 +61,20 @@ VIT_DEV void copy16_to_lds(const void* gptr, void* lptr) {
 #endif
 }
 
+// s_waitcnt with only lgkmcnt (LDS) constrained: at most N LDS operations of
+// this wave may still be outstanding.
+template <int N>
+VIT_DEV void wait_lgkmcnt() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (N << 8) | (0x3 << 14));
+}
+
+// Scheduling fence: the compiler may not move any instruction across it.  Used
+// to keep the LDS fragment reads of the next k-step ahead of the MFMAs of the
+// current one (otherwise they are sunk below the MFMAs and their latency is
+// exposed by an immediate wait).
+VIT_DEV void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Workgroup barrier that keeps LDS accesses in program order without draining
 // the outstanding global->LDS copies (the exact vmcnt waits do that).
 VIT_DEV void lds_barrier() {

@@ -14,7 +14,7 @@
 // pair (two B matrices; the B tile holds 32 gate rows then 32 up rows for each
 // wave column so that silu(gate) * up meets in the same lane).
 #include "common.h"
-#include "gemm_pipe.h"
+#include "gemm_mfma.h"
 
 namespace {
 
@@ -239,24 +239,28 @@ hipError_t launch_simple(int epilogue, const GemmArgs& g, hipStream_t s) {
 bool pipe_eligible(const GemmArgs& g) {
   const uintptr_t al = (uintptr_t)g.A | (uintptr_t)g.B | (uintptr_t)(g.B2 ? g.B2 : g.B) |
                        (uintptr_t)g.C;
+  // the copies address A and B with 32-bit byte offsets from the matrix base
+  const int64_t lim = (int64_t)1 << 32;
   return g.K % 64 == 0 && g.kb % 8 == 0 && g.kb <= g.K && g.N % 4 == 0 && g.ldc % 4 == 0 &&
-         g.lda % 8 == 0 && g.ldb % 8 == 0 && (al & 15) == 0;
+         g.lda % 8 == 0 && g.ldb % 8 == 0 && (al & 15) == 0 && g.M * g.lda * 2 < lim &&
+         g.N * g.ldb * 2 < lim;
 }
 
 }  // namespace
 
 // Tile configuration by a wave-quantisation cost model: cost ~ (rounds of one
-// workgroup per CU) x (tile area / relative efficiency).  The 8-wave tiles are
-// ~1.35x (256x128) and ~1.45x (256x256, BK 32) more efficient per flop than the
-// 4-wave 128x128 tile on gfx950 but give 2x / 4x fewer tiles.
-int gemm_pipe_choice(int epilogue, int64_t M, int64_t N, int64_t K) {
-  (void)K;
+// workgroup per CU) x (tile area / relative efficiency per flop).  Measured on
+// gfx950: the 8-wave 256x128 tile is ~1.35x and the 8-wave 256x256 tile ~1.5x
+// as efficient per flop as the 4-wave 128x128 tile, less so (1.1x / 1.25x) with
+// the fp32 read-modify-write epilogue, whose traffic grows with the tile.
+int gemm_mfma_choice(int epilogue, int64_t M, int64_t N) {
   const bool dual = epilogue == VIT_EPI_SWIGLU;
+  const bool rmw = epilogue == VIT_EPI_ADD_F32;
   struct Opt { int cfg, bm, bn; double eff; };
-  const Opt opts[] = {{GEMM_PIPE_128x128_S4, 128, 128, 1.0},
-                      {GEMM_PIPE_256x128_W8_S3, 256, 128, 1.35},
-                      {GEMM_PIPE_256x256_W8_K32_S4, 256, 256, 1.45}};
-  int best = GEMM_PIPE_128x128_S4;
+  const Opt opts[] = {{GEMM_MFMA_128x128, 128, 128, 1.0},
+                      {GEMM_MFMA_256x128_W8, 256, 128, rmw ? 1.1 : 1.35},
+                      {GEMM_MFMA_256x256_W8, 256, 256, rmw ? 1.25 : 1.5}};
+  int best = GEMM_MFMA_128x128;
   double best_cost = 1e300;
   for (const Opt& o : opts) {
     const int64_t bno = dual ? o.bn / 2 : o.bn;
@@ -278,9 +282,8 @@ hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s) {
   const bool rope = epilogue == VIT_EPI_STORE_ROPE || epilogue == VIT_EPI_QKV_VT;
   if (rope && !pipe_eligible(g)) return hipErrorInvalidValue;
   if (pipe_eligible(g)) {
-    const int cfg = gemm_pipe_choice(rope ? VIT_EPI_STORE : epilogue, g.M, g.N, g.K);
-    if (cfg == GEMM_PIPE_128x128_S4) return launch_gemm_tile128(epilogue, g, s);
-    return launch_gemm_pipe(cfg, epilogue, g, s);
+    const int cfg = gemm_mfma_choice(rope ? VIT_EPI_STORE : epilogue, g.M, g.N);
+    return launch_gemm_mfma(cfg, epilogue, g, s);
   }
   return launch_simple(epilogue, g, s);
 }

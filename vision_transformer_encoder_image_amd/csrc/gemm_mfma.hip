@@ -1,0 +1,461 @@
+// bf16 MFMA GEMM for gfx950: C[M,N] = epilogue(A[M,K] . B[N,K]^T), one
+// BM x BN output tile per workgroup of WM x WN waves (the hardware dispatcher
+// balances the tiles).
+//
+// Operands: both matrices K-contiguous.  Each BK-wide K-tile of A and B is
+// copied from global memory straight into LDS with global_load_lds_dwordx4 (no
+// register staging) into a ring of STAGES buffers: while the waves multiply
+// K-tile kt, the copies of kt+1 .. kt+STAGES-2 are in flight.  Waits are exact
+// (s_waitcnt vmcnt on the number of younger copies), and the one workgroup
+// barrier per K-tile is taken before its last 16-wide k-step, so the next
+// K-tile's first fragments are read while the last MFMAs of this one run.
+//
+// MFMA: v_mfma_f32_32x32x16_bf16 (32 cycles for 32K flops), issued as
+// C^T = B . A^T with the weight fragment in the A slot, so a lane owns 4 groups
+// of 4 consecutive output columns of one row.  Fragment reads are issued one
+// k-step ahead of the MFMAs that use them and retired (lgkmcnt 0) right after
+// those MFMAs have been issued, when they are long complete; no read is then
+// pending at a branch merge or the loop back-edge, where the compiler's own
+// wait counting falls back to a full wait in front of the MFMAs.
+//
+// LDS rows hold BK bf16; 16-byte chunks are XOR-swizzled on the global side of
+// the copy ((row >> 1) & 7 for BK 64, (row >> 2) & 3 for BK 32) so fragment
+// reads of 32 consecutive rows spread over all banks.
+//
+// Tile shapes: a wave that multiplies a TM x TN sub-tile reads (TM + TN) rows
+// of fragments per TM*TN/1024 MFMAs, so larger sub-tiles need less LDS
+// bandwidth per flop but give fewer tiles; the dispatcher weighs that against
+// wave quantisation over the 256 CUs.
+//
+// Epilogues: bf16 store, fp32 store, fp32 residual add, SwiGLU (gate and up rows
+// side by side in the B tile so silu(gate) * up meets in one lane), and the
+// half-split 2D rotary on the q and k columns (both rotate_half partners,
+// columns c and c+16 of a 32-wide block, sit in one lane), optionally with the
+// v columns written transposed for the attention kernel.  bf16 and fp32-store
+// outputs are staged through the idle LDS ring and written as row-contiguous
+// 16-byte stores.
+//
+// Requirements (checked by the dispatcher): K a multiple of BK for A (A may be
+// zero-padded past B's valid K), N a multiple of 4, 16-byte aligned rows, and
+// matrices addressable with 32-bit byte offsets.
+#include "common.h"
+#include "gemm_mfma.h"
+
+namespace {
+
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+
+template <int BK>
+VIT_DEV int chunk_swz(int row) {
+  return BK == 64 ? (row >> 1) & 7 : (row >> 2) & 3;
+}
+
+VIT_DEV float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool DUAL>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;  // wave sub-tile
+  constexpr int BI = TM / 32, BJ = TN / 32;  // 32x32 blocks per wave
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
+  constexpr int KSTEPS = BK / 16;
+  constexpr int CPR = BK / 8;    // 16-byte chunks per LDS row
+  constexpr int RPC = 64 / CPR;  // LDS rows filled by one 1 KB wave copy
+  constexpr int ROWS = BM + BN;  // LDS rows per stage (A then B)
+  constexpr int NI = ROWS / RPC / NW;
+  constexpr int BNO = DUAL ? BN / 2 : BN;  // output columns per tile
+  static_assert(STAGES >= 3, "stages");
+  static_assert(ROWS % (RPC * NW) == 0 && (TN / 2) % RPC == 0, "copy split");
+  static_assert(!DUAL || BJ % 2 == 0, "dual tile");
+  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+
+  const bf16* __restrict__ A = (const bf16*)g.A;
+  const bf16* __restrict__ B = (const bf16*)g.B;
+  const bf16* __restrict__ B2 = (const bf16*)g.B2;
+  const int M = (int)g.M, N = (int)g.N, K = (int)g.K, KB = (int)g.kb;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (N + BNO - 1) / BNO;
+  const int ntiles = tiles_m * tiles_n;
+  const int nk = K / BK;
+
+  // Workgroup ids go round-robin over the 8 XCDs; give each XCD a contiguous
+  // run of the grouped tile order (kGroupM tile rows share a column band), so
+  // the A rows and B columns one XCD touches stay in its own L2.
+  int L = blockIdx.x;
+  {
+    const int per = ntiles / kXcds, rem = ntiles % kXcds;
+    const int xcd = L % kXcds, idx = L / kXcds;
+    L = xcd * per + min(xcd, rem) + idx;
+  }
+  const int band = kGroupM * tiles_n;
+  const int first_m = (L / band) * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int m0 = (first_m + (L % band) % gm) * BM;
+  const int n0 = ((L % band) / gm) * BNO;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  // copy i of this wave fills LDS rows RPC*(wave + NW*i) .. +RPC-1 of a stage
+  // (copies i < NIA are A rows, the rest B rows).  voff is the lane's byte
+  // offset from the wave-uniform matrix base: for A it includes the lane's
+  // K chunk (the K-tile offset is added to the scalar base), for B only the
+  // row, because B's K index is clamped to its valid width per K-tile.
+  constexpr int NIA = BM / (RPC * NW);
+  static_assert(BM % (RPC * NW) == 0, "A/B copy split");
+  uint32_t voff[NI];
+  int kcol[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int q = wave + NW * i;
+    const int row = RPC * q + lane / CPR;
+    kcol[i] = ((lane % CPR) ^ chunk_swz<BK>(row)) * 8;
+    if (i < NIA) {
+      voff[i] = (uint32_t)(((int64_t)min(m0 + row, M - 1) * g.lda + kcol[i]) * 2);
+    } else {
+      const int r = row - BM;
+      int brow = n0 + r;
+      if (DUAL) brow = n0 + (r / TN) * (TN / 2) + (r % TN) % (TN / 2);
+      voff[i] = (uint32_t)((int64_t)min(brow, N - 1) * g.ldb * 2);
+    }
+  }
+  // copy K-tile kt_ into LDS buffer `stage` (a constant).  A may be zero-padded
+  // past B's valid K (KB); B's K index is clamped into [0, KB) so its reads
+  // stay inside its rows (the products with A's zero columns vanish).
+#define W_ISSUE(stage, kt_)                                                             \
+  do {                                                                                  \
+    /* readfirstlane keeps the K offset a scalar: strength reduction would */           \
+    /* otherwise turn every copy address into a 64-bit vector induction variable */     \
+    const int k0_ = __builtin_amdgcn_readfirstlane((kt_) * BK);                         \
+    bf16* dst_ = smem + (stage) * ROWS * BK;                                            \
+    _Pragma("unroll") for (int i = 0; i < NI; ++i) {                                    \
+      const int q_ = wave + NW * i;                                                     \
+      if (i < NIA) {                                                                    \
+        copy16_to_lds((const char*)A + 2 * (int64_t)k0_ + voff[i], dst_ + q_ * 512);    \
+      } else {                                                                          \
+        const char* b_ = (const char*)((DUAL && ((RPC * q_ - BM) % TN) >= TN / 2) ? B2 : B); \
+        copy16_to_lds(b_ + (voff[i] + 2u * (uint32_t)min(k0_ + kcol[i], KB - 8)),        \
+                      dst_ + q_ * 512);                                                 \
+      }                                                                                 \
+    }                                                                                   \
+  } while (0)
+
+  // fragment reads: lane row (lane & 31) of a 32-row block, 16-byte chunk
+  // 2*ks + (lane >> 5); the swizzle depends only on (lane & 31), so blocks of
+  // one wave differ by a constant offset
+  const int fr = lane & 31, fh = lane >> 5;
+  int a_off[KSTEPS], b_off[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const int ra = wm * TM + fr, rb = BM + wn * TN + fr;
+    a_off[ks] = ra * BK + (((2 * ks + fh) ^ chunk_swz<BK>(ra)) << 3);
+    b_off[ks] = rb * BK + (((2 * ks + fh) ^ chunk_swz<BK>(rb)) << 3);
+  }
+
+  f32x16 acc[BI][BJ];
+#pragma unroll
+  for (int i = 0; i < BI; ++i)
+#pragma unroll
+    for (int j = 0; j < BJ; ++j) acc[i][j] = f32x16{};
+
+  bf16x8 af[2][BI], bfr[2][BJ];
+#define W_LOAD_FRAGS(buf, stage, ks)                                                    \
+  do {                                                                                  \
+    const bf16* base_ = smem + (stage) * ROWS * BK;                                     \
+    _Pragma("unroll") for (int i = 0; i < BI; ++i) af[buf][i] =                         \
+        *reinterpret_cast<const bf16x8*>(base_ + a_off[ks] + i * 32 * BK);              \
+    _Pragma("unroll") for (int j = 0; j < BJ; ++j) bfr[buf][j] =                        \
+        *reinterpret_cast<const bf16x8*>(base_ + b_off[ks] + j * 32 * BK);              \
+  } while (0)
+#define W_MFMAS(buf)                                                                    \
+  do {                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < BI; ++i)                                      \
+    _Pragma("unroll") for (int j = 0; j < BJ; ++j) acc[i][j] =                          \
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][j], af[buf][i], acc[i][j], 0, 0, 0); \
+  } while (0)
+
+  // prologue: K-tiles 0..STAGES-2 in flight, wait for the first, first fragments
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) W_ISSUE(s, s);
+  if (nk > STAGES - 2)
+    wait_vmcnt<(STAGES - 2) * NI>();
+  else
+    wait_vmcnt<0>();
+  lds_barrier();
+  W_LOAD_FRAGS(0, 0, 0);
+  wait_lgkmcnt<0>();  // nothing pending on entry to the loop (see W_KTILE)
+  sched_fence();
+
+  // one K-tile (ring slot u, a constant): the fragments of each next k-step are
+  // read while the MFMAs of the current one run
+#define W_KTILE(u, kt)                                                                  \
+  do {                                                                                  \
+    _Pragma("unroll") for (int ks = 0; ks < KSTEPS - 1; ++ks) {                         \
+      W_LOAD_FRAGS((ks + 1) & 1, u, ks + 1);                                            \
+      sched_fence();                                                                    \
+      W_MFMAS(ks & 1);                                                                  \
+      sched_fence();                                                                    \
+      wait_lgkmcnt<0>(); /* free: see below */                                          \
+      sched_fence();                                                                    \
+    }                                                                                   \
+    /* K-tile kt+1 must have landed (younger copies may stay in flight); the */         \
+    /* barrier also retires every wave's reads of K-tile kt-1, whose buffer */          \
+    /* the next copy overwrites */                                                      \
+    if ((kt) + 1 < nk) {                                                                \
+      if ((kt) + STAGES - 1 < nk)                                                       \
+        wait_vmcnt<(STAGES - 3) * NI>();                                                \
+      else                                                                              \
+        wait_vmcnt<0>();                                                                \
+    }                                                                                   \
+    lds_barrier();                                                                      \
+    if ((kt) + STAGES - 1 < nk) W_ISSUE(((u) + STAGES - 1) % STAGES, (kt) + STAGES - 1); \
+    /* unconditional (after the last K-tile it reads a stale, in-bounds */              \
+    /* buffer), so the LDS wait counts stay exact */                                    \
+    W_LOAD_FRAGS(KSTEPS & 1, ((u) + 1) % STAGES, 0);                                    \
+    sched_fence();                                                                      \
+    W_MFMAS((KSTEPS - 1) & 1);                                                          \
+    sched_fence();                                                                      \
+    /* those reads are long done once the MFMA pipe has taken these MFMAs; */           \
+    /* waiting here leaves no read pending across branch merges and the loop */         \
+    /* back-edge, where the compiler's wait counting would otherwise fall back */       \
+    /* to lgkmcnt(0) right before the next MFMAs */                                     \
+    wait_lgkmcnt<0>();                                                                  \
+    sched_fence();                                                                      \
+  } while (0)
+
+  // whole turns of the ring without guards (exact wait counts in the hot
+  // loop), then the remaining K-tiles each under a guard (a guarded body, not
+  // a break: early exits from the unrolled ring make the register allocator
+  // duplicate the accumulators)
+  int kb0 = 0;
+  for (; kb0 + STAGES <= nk; kb0 += STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) W_KTILE(u, kb0 + u);
+  }
+#pragma unroll
+  for (int u = 0; u < STAGES - 1; ++u)
+    if (kb0 + u < nk) W_KTILE(u, kb0 + u);
+#undef W_KTILE
+#undef W_LOAD_FRAGS
+#undef W_MFMAS
+#undef W_ISSUE
+
+  // ---- epilogue: acc[i][j] lane holds row (lane & 31) of block i and, for
+  // gq = 0..3, columns 8gq + 4*(lane >> 5) .. +3 of block j ----
+  const int c4 = 4 * fh;
+  if constexpr (EPI == VIT_EPI_STORE_ROPE || EPI == VIT_EPI_QKV_VT) {
+    // each pair of 32-wide blocks (2h, 2h+1) is one 64-wide head: block 2h
+    // holds the row-angle half, block 2h+1 the column-angle half; the
+    // rotate_half partners (columns c and c+16 of a block) sit in one lane
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int m = min(m0 + wm * TM + i * 32 + fr, M - 1);
+      const float2* tab = (const float2*)g.rope_table + (int64_t)m * 32;
+#pragma unroll
+      for (int h = 0; h < BJ / 2; ++h) {
+        if (n0 + wn * TN + h * 64 >= g.rope_cols) continue;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int gq = 0; gq < 2; ++gq)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float2 cs = tab[half * 16 + 8 * gq + c4 + r];
+              const float a1 = acc[i][2 * h + half][4 * gq + r];
+              const float a2 = acc[i][2 * h + half][4 * (gq + 2) + r];
+              acc[i][2 * h + half][4 * gq + r] = a1 * cs.x - a2 * cs.y;
+              acc[i][2 * h + half][4 * (gq + 2) + r] = a2 * cs.x + a1 * cs.y;
+            }
+      }
+    }
+  }
+
+  // Staged store: the wave writes its output sub-tile into its own quarter of
+  // the (now idle) LDS ring, then reads it back one 16-byte chunk per lane in
+  // row order, so every global store instruction covers whole 128-byte lines
+  // (direct stores from the MFMA layout touch 32 rows per instruction).
+  constexpr bool kF32 = (EPI == VIT_EPI_STORE_F32 || EPI == VIT_EPI_ADD_F32);
+  constexpr int OB = kF32 ? 4 : 2;             // output bytes per element
+  constexpr int OTN = DUAL ? TN / 2 : TN;      // output columns per wave
+  constexpr int ROWB = OTN * OB;               // bytes per staged row
+  constexpr int CPRW = ROWB / 16;              // 16-byte chunks per staged row
+  constexpr int RPL = 256 / ROWB;              // staged rows per 256-byte bank line
+  constexpr int EPC = 16 / OB;                 // elements per chunk
+  constexpr bool kStaged = EPI != VIT_EPI_ADD_F32 && (ROWB == 64 || ROWB == 128 || ROWB == 256) &&
+                           TM * ROWB * NW <= STAGES * ROWS * BK * 2;
+  const bool v_wave = (EPI == VIT_EPI_QKV_VT) && (n0 + wn * TN >= g.rope_cols);
+  const bool staged = kStaged && (g.ldc * OB) % 16 == 0;  // 16-byte aligned output rows
+  if (staged) {
+    lds_barrier();  // every wave is done reading the ring
+    if (!v_wave) {
+      char* st = (char*)smem + wave * (TM * ROWB);
+      // chunk c16 (and 8-byte half h for bf16) of staged row r goes to
+      // chunk c16 ^ ((r / RPL) % CPRW), half h ^ ((r >> 4) & 1): conflict-free
+      // writes from the MFMA layout and conflict-free row-order reads
+#pragma unroll
+      for (int i = 0; i < BI; ++i) {
+        const int r = i * 32 + fr;
+        const int sw = (r / RPL) % CPRW;
+        char* row = st + r * ROWB;
+#pragma unroll
+        for (int j = 0; j < (DUAL ? BJ / 2 : BJ); ++j)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            if constexpr (kF32) {
+              const int c16 = j * 8 + 2 * gq + fh;
+              f32x4 v;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * gq + e];
+              *reinterpret_cast<f32x4*>(row + ((c16 ^ sw) << 4)) = v;
+            } else {
+              const int c16 = j * 4 + gq;
+              const int hh = fh ^ ((r >> 4) & 1);
+              bf16x4 b;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if constexpr (DUAL)
+                  b[e] = f2bf(silu_f(acc[i][j][4 * gq + e]) * acc[i][j + BJ / 2][4 * gq + e]);
+                else
+                  b[e] = f2bf(acc[i][j][4 * gq + e]);
+              }
+              *reinterpret_cast<bf16x4*>(row + ((c16 ^ sw) << 4) + (hh << 3)) = b;
+            }
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staged writes done
+      asm volatile("" ::: "memory");
+      constexpr int RPI = 64 / CPRW;  // staged rows per read instruction
+      const int cl = lane % CPRW;
+#pragma unroll 4
+      for (int it = 0; it < TM / RPI; ++it) {
+        const int R = it * RPI + lane / CPRW;
+        const int m = m0 + wm * TM + R;
+        u32x4 d = *reinterpret_cast<const u32x4*>(st + R * ROWB +
+                                                  ((cl ^ ((R / RPL) % CPRW)) << 4));
+        if (!kF32 && ((R >> 4) & 1)) {
+          const uint32_t t0 = d[0], t1 = d[1];
+          d[0] = d[2]; d[1] = d[3]; d[2] = t0; d[3] = t1;
+        }
+        const int n = n0 + wn * OTN + cl * EPC;
+        if (m >= M || n >= N) continue;
+        const int64_t orow = g.rowmap ? (int64_t)g.rowmap[m] : (int64_t)m;
+        char* dst = (char*)g.C + (orow * g.ldc + n) * OB;
+        if (n + EPC <= N) {
+          if constexpr (EPI == VIT_EPI_ADD_F32) {
+            const f32x4 c = *reinterpret_cast<const f32x4*>(dst);
+            *reinterpret_cast<f32x4*>(dst) = c + __builtin_bit_cast(f32x4, d);
+          } else {
+            *reinterpret_cast<u32x4*>(dst) = d;
+          }
+        } else {  // N % 8 == 4 tail of a bf16 row: the first 8 bytes
+          *reinterpret_cast<uint2*>(dst) = make_uint2(d[0], d[1]);
+        }
+      }
+    }
+  }
+  if (staged && !v_wave) return;
+
+  // direct stores (outputs too wide to stage, and the transposed v columns)
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int m = m0 + wm * TM + i * 32 + fr;
+    if (m >= M) continue;
+    const int64_t orow = g.rowmap ? (int64_t)g.rowmap[m] : (int64_t)m;
+    if constexpr (DUAL) {
+#pragma unroll
+      for (int j = 0; j < BJ / 2; ++j)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = n0 + wn * (TN / 2) + j * 32 + 8 * gq + c4;
+          if (n >= N) continue;
+          bf16x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            v[r] = f2bf(silu_f(acc[i][j][4 * gq + r]) * acc[i][j + BJ / 2][4 * gq + r]);
+          *reinterpret_cast<bf16x4*>((bf16*)g.C + orow * g.ldc + n) = v;
+          sched_fence();
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < BJ; ++j)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = n0 + wn * TN + j * 32 + 8 * gq + c4;
+          if (n >= N) continue;
+          f32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * gq + r];
+          if (EPI == VIT_EPI_QKV_VT && n >= g.rope_cols) {
+            // v column: row (head, dim) = n - rope_cols of the transposed layout
+            bf16* vt = (bf16*)g.vt + (int64_t)(n - g.rope_cols) * g.vt_ld + g.vpos[m];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) vt[r * g.vt_ld] = f2bf(v[r]);
+          } else if (EPI == VIT_EPI_STORE || EPI == VIT_EPI_STORE_ROPE ||
+                     EPI == VIT_EPI_QKV_VT) {
+            bf16x4 b;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) b[r] = f2bf(v[r]);
+            *reinterpret_cast<bf16x4*>((bf16*)g.C + orow * g.ldc + n) = b;
+          } else if (EPI == VIT_EPI_STORE_F32) {
+            *reinterpret_cast<f32x4*>((float*)g.C + orow * g.ldc + n) = v;
+          } else {  // VIT_EPI_ADD_F32
+            f32x4* c = reinterpret_cast<f32x4*>((float*)g.C + orow * g.ldc + n);
+            *c = *c + v;
+          }
+          sched_fence();  // convert and store block by block (bounds live registers)
+        }
+    }
+  }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool DUAL>
+hipError_t mfma_cfg(const GemmArgs& g, hipStream_t s) {
+  constexpr int BNO = DUAL ? BN / 2 : BN;
+  constexpr size_t lds = (size_t)STAGES * (BM + BN) * BK * sizeof(bf16);
+  auto kern = gemm_mfma_kernel<BM, BN, BK, WM, WN, STAGES, EPI, DUAL>;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BNO - 1) / BNO);
+  kern<<<dim3((unsigned)tiles), dim3(WM * WN * 64), lds, s>>>(g);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES>
+hipError_t mfma_epi(int epi, const GemmArgs& g, hipStream_t s) {
+  switch (epi) {
+    case VIT_EPI_STORE: return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_STORE, false>(g, s);
+    case VIT_EPI_STORE_F32:
+      return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_STORE_F32, false>(g, s);
+    case VIT_EPI_ADD_F32:
+      return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_ADD_F32, false>(g, s);
+    case VIT_EPI_SWIGLU: return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_SWIGLU, true>(g, s);
+    case VIT_EPI_STORE_ROPE:
+      if constexpr ((BN / WN) % 64 == 0)
+        return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_STORE_ROPE, false>(g, s);
+      return hipErrorInvalidValue;
+    case VIT_EPI_QKV_VT:
+      if constexpr ((BN / WN) % 64 == 0)
+        return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_QKV_VT, false>(g, s);
+      return hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_mfma(int cfg, int epi, const GemmArgs& g, hipStream_t s) {
+  switch (cfg) {
+    case GEMM_MFMA_128x128: return mfma_epi<128, 128, 64, 2, 2, 4>(epi, g, s);
+    case GEMM_MFMA_256x128_W8: return mfma_epi<256, 128, 64, 4, 2, 3>(epi, g, s);
+    case GEMM_MFMA_256x256_W8: return mfma_epi<256, 256, 32, 2, 4, 4>(epi, g, s);
+  }
+  return hipErrorInvalidValue;
+}
