@@ -243,9 +243,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
 // needs one exchange with lane ^ 32 and the running sum none until the end.
 // The k-slot order of P^T is the S^T accumulator order; the V^T key-slot
 // permutation makes the matching 8 keys of a lane one contiguous 16-byte read.
-// Software pipelining: the S^T MFMAs of tile t+1 are issued before the softmax
-// of tile t, so the exp/max/sum VALU work of one tile overlaps the matrix work
-// of the next.  The softmax reference max is raised only when some lane's max
+// Software pipelining: every step reads the K fragments of tile t+1 and the V^T
+// fragments of tile t from LDS, runs the softmax of tile t (whose S^T came from
+// the previous step) while those reads are in flight, then issues the S^T
+// MFMAs of tile t+1 and the O^T MFMAs of tile t as one interleaved run.  The softmax reference max is raised only when some lane's max
 // grows by more than 2^8 (exact after the final 1/sum; p stays <= 256).
 constexpr int VT_BQ = 128, VT_BKV = 64, VT_STAGES = 4;
 constexpr float VT_RESCALE_LOG2 = 8.0f;
@@ -295,17 +296,29 @@ __global__ __launch_bounds__(256, 2) void attn_vt_kernel(const bf16* __restrict_
       copy16_to_lds(src_, &sm[(t) % VT_STAGES][q_ >> 3][(q_ & 7) * 512]);                \
     }                                                                                    \
   } while (0)
-#define VIT_ATT_QK(sacc, stage)                                                          \
+  // fragments of one tile: kf[2 ks + kb] = K rows 32 kb + (lane & 31), dims
+  // 16 ks + 8 fh .. +7; vf[4 kb + 2 ks2 + db] = V^T rows (dims) 32 db + (lane & 31),
+  // key slots 32 kb + 16 ks2 + 8 fh .. +7
+#define VIT_ATT_LOADK(stage)                                                             \
   do {                                                                                   \
     const bf16* sK_ = sm[stage][0];                                                      \
-    sacc[0] = f32x16{};                                                                  \
-    sacc[1] = f32x16{};                                                                  \
     _Pragma("unroll") for (int ks = 0; ks < 4; ++ks)                                     \
     _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) {                                   \
       const int r_ = kb * 32 + fr;                                                       \
-      const bf16x8 kf_ = *reinterpret_cast<const bf16x8*>(                               \
+      kf[2 * ks + kb] = *reinterpret_cast<const bf16x8*>(                                \
           sK_ + r_ * 64 + (((2 * ks + fh) ^ vt_swz(r_)) << 3));                          \
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf_, qf[ks], sacc[kb], 0, 0, 0); \
+    }                                                                                    \
+  } while (0)
+#define VIT_ATT_LOADV(stage)                                                             \
+  do {                                                                                   \
+    const bf16* sV_ = sm[stage][1];                                                      \
+    _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                     \
+    _Pragma("unroll") for (int ks2 = 0; ks2 < 2; ++ks2)                                  \
+    _Pragma("unroll") for (int db = 0; db < 2; ++db) {                                   \
+      const int vr_ = db * 32 + fr;                                                      \
+      const int ch_ = kb * 4 + ks2 * 2 + fh;                                             \
+      vf[4 * kb + 2 * ks2 + db] =                                                        \
+          *reinterpret_cast<const bf16x8*>(sV_ + vr_ * 64 + ((ch_ ^ vt_swz(vr_)) << 3)); \
     }                                                                                    \
   } while (0)
 
@@ -320,6 +333,7 @@ __global__ __launch_bounds__(256, 2) void attn_vt_kernel(const bf16* __restrict_
 
   f32x16 o[2] = {f32x16{}, f32x16{}};
   f32x16 sc[2], sn[2];
+  bf16x8 kf[8], vf[8];
   float mref = -INFINITY, lsum = 0.f;
   const int nkv = (P + VT_BKV - 1) / VT_BKV;
   VIT_ATT_ISSUE(0);
@@ -332,7 +346,19 @@ __global__ __launch_bounds__(256, 2) void attn_vt_kernel(const bf16* __restrict_
   else
     wait_vmcnt<0>();
   lds_barrier();
-  VIT_ATT_QK(sc, 0);
+  VIT_ATT_LOADK(0);
+  // consume the scale here: its kernel-argument load would otherwise be waited
+  // for (lgkmcnt(0), which also drains the LDS reads) inside the loop
+  asm volatile("" : "+s"(c));
+  wait_lgkmcnt<0>();
+  sched_fence();
+  sc[0] = f32x16{};
+  sc[1] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * ks + kb], qf[ks], sc[kb], 0, 0, 0);
 
   for (int t = 0; t < nkv; ++t) {
     // tile t+1 must have landed; the barrier also retires all reads of tile t-1,
@@ -345,7 +371,13 @@ __global__ __launch_bounds__(256, 2) void attn_vt_kernel(const bf16* __restrict_
     }
     lds_barrier();
     if (t + 3 < nkv) VIT_ATT_ISSUE(t + 3);
-    if (t + 1 < nkv) VIT_ATT_QK(sn, (t + 1) % VT_STAGES);
+    // all LDS reads of this step go out first (K of tile t+1 -- after the last
+    // tile a stale, in-bounds buffer whose products are discarded -- and V of
+    // tile t); the softmax below covers their latency, and one wait then
+    // frees a run of 16 MFMAs
+    VIT_ATT_LOADK((t + 1) % VT_STAGES);
+    VIT_ATT_LOADV(t % VT_STAGES);
+    sched_fence();
 
     const int kv0 = t * VT_BKV;
     if (kv0 + VT_BKV > P) {  // ragged last tile of the image
@@ -360,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void attn_vt_kernel(const bf16* __restrict_
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = xor32_max(mx);
     if (__any((mx - mref) * c > VT_RESCALE_LOG2)) {
       const float mnew = fmaxf(mref, mx);
       const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * c);
@@ -370,32 +402,38 @@ __global__ __launch_bounds__(256, 2) void attn_vt_kernel(const bf16* __restrict_
       for (int db = 0; db < 2; ++db) o[db] *= alpha;
     }
     const float nmc = -mref * c;
-    const bf16* sV = sm[t % VT_STAGES][1];
+    bf16x8 pf[4];  // P^T fragment of key slots 32 kb + 16 ks2 + 8 fh .. +7
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        bf16x8 pf;
+      for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * ks2 + j], c, nmc));
           lsum += p;
-          pf[j] = f2bf(p);
+          pf[2 * kb + ks2][j] = f2bf(p);
         }
-        const int chunk = kb * 4 + ks2 * 2 + fh;  // key slots 32 kb + 16 ks2 + 8 fh .. +7
+    wait_lgkmcnt<0>();
+    sched_fence();
+    // four independent chains (S^T blocks of tile t+1, O^T blocks) interleaved
+    sn[0] = f32x16{};
+    sn[1] = f32x16{};
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const int vr = db * 32 + fr;
-          const bf16x8 vf =
-              *reinterpret_cast<const bf16x8*>(sV + vr * 64 + ((chunk ^ vt_swz(vr)) << 3));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
-        }
-      }
+    for (int x = 0; x < 4; ++x) {
+      const int kb = x >> 1, ks2 = x & 1;
+      sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * x], qf[x], sn[0], 0, 0, 0);
+      sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * x + 1], qf[x], sn[1], 0, 0, 0);
+      o[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 * kb + 2 * ks2], pf[x], o[0], 0, 0, 0);
+      o[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 * kb + 2 * ks2 + 1], pf[x], o[1], 0, 0,
+                                                     0);
+    }
+    sched_fence();
     sc[0] = sn[0];
     sc[1] = sn[1];
   }
 #undef VIT_ATT_ISSUE
-#undef VIT_ATT_QK
+#undef VIT_ATT_LOADK
+#undef VIT_ATT_LOADV
 
   const float l = lsum + __shfl_xor(lsum, 32, 64);
   const float inv = 1.0f / l;

@@ -69,6 +69,16 @@ VIT_DEV void wait_lgkmcnt() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (N << 8) | (0x3 << 14));
 }
 
+// max over lanes l and l ^ 32 without the LDS crossbar (a ds_bpermute would
+// count against lgkmcnt and wait for every LDS read issued before it):
+// v_permlane32_swap exchanges the upper half of one operand with the lower half
+// of the other, so with both operands = v the two results hold v[l] and v[l^32].
+VIT_DEV float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Scheduling fence: the compiler may not move any instruction across it.  Used
 // to keep the LDS fragment reads of the next k-step ahead of the MFMAs of the
 // current one (otherwise they are sunk below the MFMAs and their latency is
