@@ -135,9 +135,10 @@ vit_status build_desc(const int32_t* grid_hw, int32_t n_images, int q_tile, bool
 struct Plan {
   int64_t P = 0, tokens = 0, Kp = 0, hp = 0;
   size_t table = 0, xpad = 0, wpe = 0, x = 0, n = 0, qkv = 0, act = 0, G = 0, rowmap = 0;
-  size_t vt = 0, vpos = 0;
+  size_t vt = 0, vpos = 0, u = 0, ss = 0;
   int64_t kv_total = 0;
   bool use_vt = false;  // bf16, head_dim 64: V written transposed by the wqkv GEMM
+  bool fuse_norm = false;  // bf16, vision_dim % 64 == 0: RMSNorm folded into the GEMMs
   size_t total = 0;
 };
 
@@ -174,6 +175,11 @@ Plan make_plan(const vit_config& c, const VarlenDesc& desc, int flags) {
     p.vt = take((size_t)d * p.kv_total * es);
     p.vpos = take((size_t)P * sizeof(int32_t));
   }
+  p.fuse_norm = c.dtype == VIT_BF16 && d % 64 == 0 && d / 64 <= kMaxNormGroups && c.n_blocks > 0;
+  if (p.fuse_norm) {
+    p.u = take((size_t)P * d * es);                     // bf16(x * norm weight)
+    p.ss = take((size_t)P * round_up(d / 64, 4) * sizeof(float));  // partial sums of x^2
+  }
   if (aligner) p.G = take((size_t)p.tokens * m2 * d * es);
   if (aligner && (flags & VIT_OUT_NLAYOUT)) p.rowmap = take((size_t)p.tokens * sizeof(int32_t));
   p.total = off;
@@ -182,7 +188,7 @@ Plan make_plan(const vit_config& c, const VarlenDesc& desc, int flags) {
 
 GemmArgs gemm_args(const void* A, int64_t lda, const void* B, const void* B2, int64_t ldb, void* C,
                    int64_t ldc, int64_t M, int64_t N, int64_t K, const int32_t* rowmap) {
-  GemmArgs g;
+  GemmArgs g{};
   g.A = A;
   g.B = B;
   g.B2 = B2;
@@ -203,7 +209,7 @@ GemmArgs gemm_args(const void* A, int64_t lda, const void* B, const void* B2, in
 vit_status gemm(int dtype, int epi, const void* A, int64_t lda, const void* B, const void* B2,
                 int64_t ldb, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                 const int32_t* rowmap, hipStream_t s) {
-  GemmArgs g;
+  GemmArgs g{};
   g.A = A;
   g.B = B;
   g.B2 = B2;
@@ -265,6 +271,35 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
   const int64_t P = p.P, d = c.vision_dim, h = c.mlp_hidden;
   const bool final_to_out = !aligner;
 
+  // RMSNorm folded into the GEMMs: the GEMM that writes the residual stream x
+  // (patch embedding, out-projection, down-projection) also writes
+  // u = bf16(x * w_norm) and per-row partial sums of x^2; the GEMM that reads
+  // the normalised row (wqkv, gate/up) takes u and scales its output rows by
+  // 1/rms.  Only the final norm remains a pass of its own.
+  void* u = p.fuse_norm ? base + p.u : nullptr;
+  float* ss = p.fuse_norm ? (float*)(base + p.ss) : nullptr;
+  auto producer = [&](GemmArgs& g, const float* wn) {
+    g.norm_w = wn;
+    g.norm_out = u;
+    g.ss_out = ss;
+  };
+  auto consumer = [&](GemmArgs& g) {
+    g.ss_in = ss;
+    g.ss_groups = (int32_t)(d / 64);
+    g.rms_eps = c.rms_eps;
+    g.rms_inv_dim = 1.0f / (float)d;
+  };
+  bool fuse = p.fuse_norm;
+  if (fuse) {  // every GEMM of the stack must take the MFMA path
+    const GemmArgs chk[] = {
+        gemm_args(base + p.xpad, p.Kp, base + p.wpe, nullptr, p.Kp, x, d, P, d, p.Kp, nullptr),
+        gemm_args(u, d, w->wqkv[0], nullptr, d, qkv, 3 * d, P, 3 * d, d, nullptr),
+        gemm_args(n, d, w->wo[0], nullptr, d, x, d, P, d, d, nullptr),
+        gemm_args(u, d, w->w_gate[0], w->w_up[0], d, act, p.hp, P, h, d, nullptr),
+        gemm_args(act, p.hp, w->w_down[0], nullptr, h, x, d, P, d, p.hp, nullptr)};
+    for (const GemmArgs& g : chk) fuse = fuse && gemm_bf16_mfma_eligible(g);
+  }
+
   // patch embedding: x (fp32 residual stream) = patches . Wpe^T
   {
     ProfScope ps(VIT_K_EMBED, s);
@@ -273,8 +308,9 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
       void* wpe = base + p.wpe;
       VIT_HIP(launch_pad_rows(dt, in, P, c.patch_dim, p.Kp, xpad, s), "pad patches");
       VIT_HIP(launch_pad_rows(dt, w->patch_embed, d, c.patch_dim, p.Kp, wpe, s), "pad weight");
-      VIT_TRY(gemm(dt, VIT_EPI_STORE_F32, xpad, p.Kp, wpe, nullptr, p.Kp, x, d, P, d, p.Kp,
-                   nullptr, s));
+      GemmArgs g = gemm_args(xpad, p.Kp, wpe, nullptr, p.Kp, x, d, P, d, p.Kp, nullptr);
+      if (fuse) producer(g, w->norm1[0]);
+      VIT_HIP(launch_gemm_bf16(VIT_EPI_STORE_F32, g, s), "patch embedding gemm");
     } else {
       VIT_TRY(gemm(dt, VIT_EPI_STORE_F32, in, c.patch_dim, w->patch_embed, nullptr, c.patch_dim,
                    x, d, P, d, c.patch_dim, nullptr, s));
@@ -289,37 +325,44 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
     VIT_HIP(launch_vpos(desc, vpos, s), "transposed-V positions");
     VIT_HIP(launch_vt_zero_pads(desc, d, vt, p.kv_total, s), "transposed-V padding");
   }
+  void* a_in = fuse ? u : n;  // A operand of the GEMMs after a norm
 
   for (int b = 0; b < c.n_blocks; ++b) {
-    {
+    if (!fuse) {
       ProfScope ps(VIT_K_RMSNORM, s);
       VIT_HIP(launch_rmsnorm(x, w->norm1[b], c.rms_eps, P, (int)d, dt, n, s), "norm1");
     }
     // wqkv: with head_dim 64 in bf16 the epilogue applies the rotary to q, k
     // (stored [P, 2d]) and writes v transposed per head for the attention
     // kernel; otherwise plain [P, 3d] output and a separate rotary pass
-    GemmArgs g = gemm_args(n, d, w->wqkv[b], nullptr, d, qkv, 2 * d, P, 3 * d, d, nullptr);
+    GemmArgs g = gemm_args(a_in, d, w->wqkv[b], nullptr, d, qkv, 2 * d, P, 3 * d, d, nullptr);
     g.rope_table = table;
     g.rope_cols = 2 * d;
     g.vt = vt;
     g.vpos = vpos;
     g.vt_ld = p.kv_total;
-    const bool fuse = p.use_vt && gemm_bf16_can_fuse_rope(g);
+    if (fuse) consumer(g);
+    const bool fuse_rope = p.use_vt && gemm_bf16_can_fuse_rope(g);
     {
       ProfScope ps(VIT_K_QKV, s);
-      if (fuse)
+      if (fuse_rope) {
         VIT_HIP(launch_gemm_bf16(VIT_EPI_QKV_VT, g, s), "qkv+rope gemm");
-      else
+      } else if (dt == VIT_BF16) {
+        GemmArgs gp = gemm_args(a_in, d, w->wqkv[b], nullptr, d, qkv, 3 * d, P, 3 * d, d, nullptr);
+        if (fuse) consumer(gp);
+        VIT_HIP(launch_gemm_bf16(VIT_EPI_STORE, gp, s), "qkv gemm");
+      } else {
         VIT_TRY(gemm(dt, VIT_EPI_STORE, n, d, w->wqkv[b], nullptr, d, qkv, 3 * d, P, 3 * d, d,
                      nullptr, s));
+      }
     }
-    if (!fuse) {
+    if (!fuse_rope) {
       ProfScope ps(VIT_K_ROPE, s);
       VIT_HIP(launch_rope(dt, qkv, table, P, c.n_heads, c.head_dim, s), "rope");
     }
     {
       ProfScope ps(VIT_K_ATTN, s);
-      if (fuse)
+      if (fuse_rope)
         VIT_HIP(launch_attention_vt(qkv, 2 * d, vt, p.kv_total, desc, c.n_heads, n, s),
                 "attention");
       else
@@ -327,23 +370,36 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
     }
     {
       ProfScope ps(VIT_K_OUTPROJ, s);
-      VIT_TRY(gemm(dt, VIT_EPI_ADD_F32, n, d, w->wo[b], nullptr, d, x, d, P, d, d, nullptr, s));
+      if (dt == VIT_BF16) {
+        GemmArgs go = gemm_args(n, d, w->wo[b], nullptr, d, x, d, P, d, d, nullptr);
+        if (fuse) producer(go, w->norm2[b]);
+        VIT_HIP(launch_gemm_bf16(VIT_EPI_ADD_F32, go, s), "out-projection gemm");
+      } else {
+        VIT_TRY(gemm(dt, VIT_EPI_ADD_F32, n, d, w->wo[b], nullptr, d, x, d, P, d, d, nullptr, s));
+      }
     }
-    {
+    if (!fuse) {
       ProfScope ps(VIT_K_RMSNORM, s);
       VIT_HIP(launch_rmsnorm(x, w->norm2[b], c.rms_eps, P, (int)d, dt, n, s), "norm2");
     }
     {
       ProfScope ps(VIT_K_GATEUP, s);
-      VIT_TRY(gemm(dt, VIT_EPI_SWIGLU, n, d, w->w_gate[b], w->w_up[b], d, act, p.hp, P, h, d,
-                   nullptr, s));
+      if (dt == VIT_BF16) {
+        GemmArgs gg = gemm_args(a_in, d, w->w_gate[b], w->w_up[b], d, act, p.hp, P, h, d, nullptr);
+        if (fuse) consumer(gg);
+        VIT_HIP(launch_gemm_bf16(VIT_EPI_SWIGLU, gg, s), "gate/up gemm");
+      } else {
+        VIT_TRY(gemm(dt, VIT_EPI_SWIGLU, n, d, w->w_gate[b], w->w_up[b], d, act, p.hp, P, h, d,
+                     nullptr, s));
+      }
     }
     {
       ProfScope ps(VIT_K_DOWN, s);
-      GemmArgs g = gemm_args(act, p.hp, w->w_down[b], nullptr, h, x, d, P, d, p.hp, nullptr);
-      g.kb = h;  // act is zero past column h; W_down rows are h wide
-      VIT_HIP(dt == VIT_BF16 ? launch_gemm_bf16(VIT_EPI_ADD_F32, g, s)
-                             : launch_gemm_f32(VIT_EPI_ADD_F32, g, s),
+      GemmArgs gd = gemm_args(act, p.hp, w->w_down[b], nullptr, h, x, d, P, d, p.hp, nullptr);
+      gd.kb = h;  // act is zero past column h; W_down rows are h wide
+      if (fuse && b + 1 < c.n_blocks) producer(gd, w->norm1[b + 1]);
+      VIT_HIP(dt == VIT_BF16 ? launch_gemm_bf16(VIT_EPI_ADD_F32, gd, s)
+                             : launch_gemm_f32(VIT_EPI_ADD_F32, gd, s),
               "down gemm");
     }
   }

@@ -79,6 +79,13 @@ VIT_DEV float xor32_max(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// v[l] + v[l ^ 32] (identical in both lanes), through v_permlane32_swap.
+VIT_DEV float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Scheduling fence: the compiler may not move any instruction across it.  Used
 // to keep the LDS fragment reads of the next k-step ahead of the MFMAs of the
 // current one (otherwise they are sunk below the MFMAs and their latency is
@@ -133,7 +140,25 @@ struct GemmArgs {
   void* vt;                // transposed V [n_heads*64, vt_ld] (VIT_EPI_QKV_VT)
   const int32_t* vpos;     // column of every row m in vt
   int64_t vt_ld;
+  // RMSNorm folded into the GEMMs around it.  Producer (fp32 store / add
+  // epilogues, N a multiple of 64): besides the fp32 row x_new, write
+  // u = bf16(x_new * norm_w) to norm_out [M, N] and the sum of x_new^2 over each
+  // 64-column group k to ss_out[m * G4 + k] (G4 = N/64 rounded up to 4).
+  // Consumer (bf16 epilogues, ss_groups <= kMaxNormGroups): scale output row m by
+  // rstd = (sum over k < ss_groups of ss_in[m * G4 + k] * rms_inv_dim +
+  // rms_eps)^-1/2 before anything else, so u . W^T * rstd equals the GEMM of the
+  // normalised row.
+  const float* norm_w;
+  void* norm_out;
+  float* ss_out;
+  const float* ss_in;
+  int32_t ss_groups;
+  float rms_eps;
+  float rms_inv_dim;
 };
+
+// Largest number of 64-column groups (vision_dim / 64) the folded RMSNorm takes.
+constexpr int kMaxNormGroups = 24;
 
 // Internal epilogue: bf16 store with the half-split 2D rotary applied to the
 // q and k columns (head_dim 64 only; each wave owns whole heads).
@@ -145,6 +170,8 @@ constexpr int VIT_EPI_QKV_VT = 5;
 hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_f32(int epilogue, const GemmArgs& g, hipStream_t s);
 bool gemm_bf16_can_fuse_rope(const GemmArgs& g);
+// the MFMA GEMM path (rotary, transposed-V and RMSNorm epilogues) takes these arguments
+bool gemm_bf16_mfma_eligible(const GemmArgs& g);
 hipError_t launch_rmsnorm(const float* x, const float* w, float eps, int64_t rows, int dim,
                           int out_dtype, void* out, hipStream_t s);
 hipError_t launch_rope_table(const VarlenDesc& d, int head_dim, float theta, void* table,

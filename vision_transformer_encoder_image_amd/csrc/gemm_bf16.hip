@@ -277,10 +277,17 @@ int gemm_mfma_choice(int epilogue, int64_t M, int64_t N) {
 
 bool gemm_bf16_can_fuse_rope(const GemmArgs& g) { return pipe_eligible(g); }
 
+bool gemm_bf16_mfma_eligible(const GemmArgs& g) { return pipe_eligible(g); }
+
 hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   const bool rope = epilogue == VIT_EPI_STORE_ROPE || epilogue == VIT_EPI_QKV_VT;
-  if (rope && !pipe_eligible(g)) return hipErrorInvalidValue;
+  const bool norm = g.norm_w != nullptr || g.ss_in != nullptr;
+  if ((rope || norm) && !pipe_eligible(g)) return hipErrorInvalidValue;
+  if (g.ss_in && (g.ss_groups < 1 || g.ss_groups > kMaxNormGroups)) return hipErrorInvalidValue;
+  if (g.norm_w && (g.N % 64 != 0 || !g.norm_out || !g.ss_out ||
+                   (epilogue != VIT_EPI_STORE_F32 && epilogue != VIT_EPI_ADD_F32)))
+    return hipErrorInvalidValue;
   if (pipe_eligible(g)) {
     const int cfg = gemm_mfma_choice(rope ? VIT_EPI_STORE : epilogue, g.M, g.N);
     return launch_gemm_mfma(cfg, epilogue, g, s);

@@ -176,6 +176,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
         __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][j], af[buf][i], acc[i][j], 0, 0, 0); \
   } while (0)
 
+  // RMSNorm consumer: thread t < BM reads the partial sums of tile row t before
+  // the first copies are issued (the prologue's vmcnt wait then covers them)
+  // and leaves the row's rstd in LDS, past the ring, for the epilogue
+  float* s_rstd = (float*)((char*)smem + STAGES * ROWS * BK * 2);
+  const bool norm_in = g.ss_in != nullptr && threadIdx.x < BM;
+  f32x4 part[kMaxNormGroups / 4];
+  if (norm_in) {
+    const int ldss = (g.ss_groups + 3) & ~3;
+    const int m = min(m0 + (int)threadIdx.x, M - 1);
+    const f32x4* row = reinterpret_cast<const f32x4*>(g.ss_in + (int64_t)m * ldss);
+#pragma unroll
+    for (int q = 0; q < kMaxNormGroups / 4; ++q) part[q] = row[min(q, ldss / 4 - 1)];
+  }
+
   // prologue: K-tiles 0..STAGES-2 in flight, wait for the first, first fragments
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
@@ -184,6 +198,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
     wait_vmcnt<(STAGES - 2) * NI>();
   else
     wait_vmcnt<0>();
+  if (norm_in) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxNormGroups; ++k) t += k < g.ss_groups ? part[k / 4][k % 4] : 0.f;
+    s_rstd[threadIdx.x] = 1.0f / sqrtf(t * g.rms_inv_dim + g.rms_eps);
+  }
   lds_barrier();
   W_LOAD_FRAGS(0, 0, 0);
   wait_lgkmcnt<0>();  // nothing pending on entry to the loop (see W_KTILE)
@@ -246,6 +266,82 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
   // ---- epilogue: acc[i][j] lane holds row (lane & 31) of block i and, for
   // gq = 0..3, columns 8gq + 4*(lane >> 5) .. +3 of block j ----
   const int c4 = 4 * fh;
+  constexpr bool kF32Out = (EPI == VIT_EPI_STORE_F32 || EPI == VIT_EPI_ADD_F32);
+  if (!kF32Out && g.ss_in) {
+    // RMSNorm consumer: output rows times the rstd computed at kernel start
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const float rstd = s_rstd[wm * TM + i * 32 + fr];
+#pragma unroll
+      for (int j = 0; j < BJ; ++j) acc[i][j] *= rstd;
+    }
+  }
+  if (kF32Out && g.norm_w) {
+    // RMSNorm producer.  The wave's 64 columns are one group; lanes l and l^32
+    // hold the two halves of a row's group.  x_new goes straight back to the
+    // fp32 stream; u = bf16(x_new * w) is staged through the idle LDS ring (as
+    // the bf16 outputs below) and written as row-contiguous 16-byte stores.
+    static_assert(TN == 64, "one 64-column group per wave");
+    constexpr int UROWB = TN * 2;            // bytes per staged u row
+    constexpr int UCPR = UROWB / 16, URPL = 256 / UROWB;
+    static_assert(TM * UROWB * NW <= STAGES * ROWS * BK * 2, "u staging fits the ring");
+    const int n = n0 + wn * TN;
+    const bool cols_ok = n < N;
+    lds_barrier();  // every wave is done reading the ring
+    char* st = (char*)smem + wave * (TM * UROWB);
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int r = i * 32 + fr;
+      const int m = m0 + wm * TM + r;
+      const bool ok = cols_ok && m < M;
+      const int64_t orow = (ok && g.rowmap) ? (int64_t)g.rowmap[m] : (int64_t)m;
+      const int sw = (r / URPL) % UCPR;
+      float ssum = 0.f;
+#pragma unroll
+      for (int j = 0; j < BJ; ++j)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int nc = n + j * 32 + 8 * gq + c4;
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * gq + e];
+          if (ok) {
+            f32x4* c = reinterpret_cast<f32x4*>((float*)g.C + orow * g.ldc + nc);
+            if constexpr (EPI == VIT_EPI_ADD_F32) v = *c + v;
+            *c = v;
+          }
+          const f32x4 w = *reinterpret_cast<const f32x4*>(g.norm_w + min(nc, N - 4));
+          bf16x4 u;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            u[e] = f2bf(v[e] * w[e]);
+            ssum += v[e] * v[e];
+          }
+          const int c16 = j * 4 + gq, hh = fh ^ ((r >> 4) & 1);
+          *reinterpret_cast<bf16x4*>(st + r * UROWB + ((c16 ^ sw) << 4) + (hh << 3)) = u;
+          sched_fence();
+        }
+      ssum = xor32_sum(ssum);
+      if (ok && fh == 0) g.ss_out[(int64_t)m * ((N / 64 + 3) & ~3) + n / 64] = ssum;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staged writes done
+    asm volatile("" ::: "memory");
+    constexpr int URPI = 64 / UCPR;  // staged rows per read instruction
+    const int cl = lane % UCPR;
+#pragma unroll 4
+    for (int it = 0; it < TM / URPI; ++it) {
+      const int R = it * URPI + lane / UCPR;
+      const int m = m0 + wm * TM + R;
+      u32x4 dd = *reinterpret_cast<const u32x4*>(st + R * UROWB + ((cl ^ ((R / URPL) % UCPR)) << 4));
+      if ((R >> 4) & 1) {
+        const uint32_t t0 = dd[0], t1 = dd[1];
+        dd[0] = dd[2]; dd[1] = dd[3]; dd[2] = t0; dd[3] = t1;
+      }
+      if (!cols_ok || m >= M) continue;
+      *reinterpret_cast<u32x4*>((bf16*)g.norm_out + (int64_t)m * N + n + cl * 8) = dd;
+    }
+    return;
+  }
   if constexpr (EPI == VIT_EPI_STORE_ROPE || EPI == VIT_EPI_QKV_VT) {
     // each pair of 32-wide blocks (2h, 2h+1) is one 64-wide head: block 2h
     // holds the row-angle half, block 2h+1 the column-angle half; the
@@ -277,7 +373,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
   // the (now idle) LDS ring, then reads it back one 16-byte chunk per lane in
   // row order, so every global store instruction covers whole 128-byte lines
   // (direct stores from the MFMA layout touch 32 rows per instruction).
-  constexpr bool kF32 = (EPI == VIT_EPI_STORE_F32 || EPI == VIT_EPI_ADD_F32);
+  constexpr bool kF32 = kF32Out;
   constexpr int OB = kF32 ? 4 : 2;             // output bytes per element
   constexpr int OTN = DUAL ? TN / 2 : TN;      // output columns per wave
   constexpr int ROWB = OTN * OB;               // bytes per staged row
@@ -414,7 +510,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool DUAL>
 hipError_t mfma_cfg(const GemmArgs& g, hipStream_t s) {
   constexpr int BNO = DUAL ? BN / 2 : BN;
-  constexpr size_t lds = (size_t)STAGES * (BM + BN) * BK * sizeof(bf16);
+  // the ring, then BM floats of per-row RMSNorm scale
+  constexpr size_t lds = (size_t)STAGES * (BM + BN) * BK * sizeof(bf16) + BM * sizeof(float);
   auto kern = gemm_mfma_kernel<BM, BN, BK, WM, WN, STAGES, EPI, DUAL>;
   static bool attr = false;
   if (!attr) {
