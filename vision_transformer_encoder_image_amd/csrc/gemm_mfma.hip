@@ -38,6 +38,8 @@
 // Requirements (checked by the dispatcher): K a multiple of BK for A (A may be
 // zero-padded past B's valid K), N a multiple of 4, 16-byte aligned rows, and
 // matrices addressable with 32-bit byte offsets.
+#include <type_traits>
+
 #include "common.h"
 #include "gemm_mfma.h"
 
@@ -124,22 +126,26 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
   // copy K-tile kt_ into LDS buffer `stage` (a constant).  A may be zero-padded
   // past B's valid K (KB); B's K index is clamped into [0, KB) so its reads
   // stay inside its rows (the products with A's zero columns vanish).
+  // copy i of K-tile k0_/BK (k0_ a scalar) into the LDS buffer at dst_
+#define W_COPY1(k0_, dst_, i)                                                           \
+  do {                                                                                  \
+    const int q_ = wave + NW * (i);                                                     \
+    if ((i) < NIA) {                                                                    \
+      copy16_to_lds((const char*)A + 2 * (int64_t)(k0_) + voff[i], (dst_) + q_ * 512);  \
+    } else {                                                                            \
+      const char* b_ = (const char*)((DUAL && ((RPC * q_ - BM) % TN) >= TN / 2) ? B2 : B); \
+      copy16_to_lds(b_ + (voff[i] + 2u * (uint32_t)min((k0_) + kcol[i], KB - 8)),        \
+                    (dst_) + q_ * 512);                                                 \
+    }                                                                                   \
+  } while (0)
+  // all copies of K-tile kt_ into LDS buffer `stage` (a constant)
 #define W_ISSUE(stage, kt_)                                                             \
   do {                                                                                  \
     /* readfirstlane keeps the K offset a scalar: strength reduction would */           \
     /* otherwise turn every copy address into a 64-bit vector induction variable */     \
     const int k0_ = __builtin_amdgcn_readfirstlane((kt_) * BK);                         \
     bf16* dst_ = smem + (stage) * ROWS * BK;                                            \
-    _Pragma("unroll") for (int i = 0; i < NI; ++i) {                                    \
-      const int q_ = wave + NW * i;                                                     \
-      if (i < NIA) {                                                                    \
-        copy16_to_lds((const char*)A + 2 * (int64_t)k0_ + voff[i], dst_ + q_ * 512);    \
-      } else {                                                                          \
-        const char* b_ = (const char*)((DUAL && ((RPC * q_ - BM) % TN) >= TN / 2) ? B2 : B); \
-        copy16_to_lds(b_ + (voff[i] + 2u * (uint32_t)min(k0_ + kcol[i], KB - 8)),        \
-                      dst_ + q_ * 512);                                                 \
-      }                                                                                 \
-    }                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < NI; ++i) W_COPY1(k0_, dst_, i);               \
   } while (0)
 
   // fragment reads: lane row (lane & 31) of a 32-row block, 16-byte chunk
@@ -174,6 +180,25 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
     _Pragma("unroll") for (int i = 0; i < BI; ++i)                                      \
     _Pragma("unroll") for (int j = 0; j < BJ; ++j) acc[i][j] =                          \
         __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][j], af[buf][i], acc[i][j], 0, 0, 0); \
+  } while (0)
+  // the MFMAs of register set buf with the copies of K-tile kt_ (if it exists)
+  // into buffer `stage` spread evenly between them: issued as one burst right
+  // after the barrier, the copies of all waves queue at the texture unit and
+  // hold up the MFMAs behind them
+#define W_MFMAS_COPY(buf, stage, kt_)                                                   \
+  do {                                                                                  \
+    constexpr int NM_ = BI * BJ;                                                        \
+    const bool iss_ = (kt_) < nk;                                                       \
+    const int k0_ = __builtin_amdgcn_readfirstlane((kt_) * BK);                         \
+    bf16* dst_ = smem + (stage) * ROWS * BK;                                            \
+    _Pragma("unroll") for (int x = 0; x < NM_; ++x) {                                   \
+      acc[x / BJ][x % BJ] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                    \
+          bfr[buf][x % BJ], af[buf][x / BJ], acc[x / BJ][x % BJ], 0, 0, 0);             \
+      _Pragma("unroll") for (int c = 0; c < NI; ++c) {                                  \
+        if (c * NM_ / NI == x && iss_) W_COPY1(k0_, dst_, c);                           \
+      }                                                                                 \
+      sched_fence();                                                                    \
+    }                                                                                   \
   } while (0)
 
   // RMSNorm consumer: thread t < BM reads the partial sums of tile row t before
@@ -231,12 +256,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
         wait_vmcnt<0>();                                                                \
     }                                                                                   \
     lds_barrier();                                                                      \
-    if ((kt) + STAGES - 1 < nk) W_ISSUE(((u) + STAGES - 1) % STAGES, (kt) + STAGES - 1); \
     /* unconditional (after the last K-tile it reads a stale, in-bounds */              \
     /* buffer), so the LDS wait counts stay exact */                                    \
     W_LOAD_FRAGS(KSTEPS & 1, ((u) + 1) % STAGES, 0);                                    \
     sched_fence();                                                                      \
-    W_MFMAS((KSTEPS - 1) & 1);                                                          \
+    W_MFMAS_COPY((KSTEPS - 1) & 1, ((u) + STAGES - 1) % STAGES, (kt) + STAGES - 1);      \
     sched_fence();                                                                      \
     /* those reads are long done once the MFMA pipe has taken these MFMAs; */           \
     /* waiting here leaves no read pending across branch merges and the loop */         \
@@ -261,7 +285,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
 #undef W_KTILE
 #undef W_LOAD_FRAGS
 #undef W_MFMAS
+#undef W_MFMAS_COPY
 #undef W_ISSUE
+#undef W_COPY1
 
   // ---- epilogue: acc[i][j] lane holds row (lane & 31) of block i and, for
   // gq = 0..3, columns 8gq + 4*(lane >> 5) .. +3 of block j ----
@@ -276,6 +302,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
       for (int j = 0; j < BJ; ++j) acc[i][j] *= rstd;
     }
   }
+  // vmcnt also counts stores: a global load issued after stores is waited for
+  // together with them.  Every load of the epilogue (row map, fp32 rows to
+  // add to, norm weights, v positions) is therefore issued before the first
+  // store, and the paths are specialised on whether a row map is present (a
+  // load under a branch makes the compiler wait for all stores at its use).
+  const bool has_rowmap = g.rowmap != nullptr;
+
   if (kF32Out && g.norm_w) {
     // RMSNorm producer.  The wave's 64 columns are one group; lanes l and l^32
     // hold the two halves of a row's group.  x_new goes straight back to the
@@ -287,43 +320,73 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
     static_assert(TM * UROWB * NW <= STAGES * ROWS * BK * 2, "u staging fits the ring");
     const int n = n0 + wn * TN;
     const bool cols_ok = n < N;
-    lds_barrier();  // every wave is done reading the ring
     char* st = (char*)smem + wave * (TM * UROWB);
+    auto produce = [&](auto with_rowmap) __attribute__((always_inline)) {
+      int64_t orow[BI];
 #pragma unroll
-    for (int i = 0; i < BI; ++i) {
-      const int r = i * 32 + fr;
-      const int m = m0 + wm * TM + r;
-      const bool ok = cols_ok && m < M;
-      const int64_t orow = (ok && g.rowmap) ? (int64_t)g.rowmap[m] : (int64_t)m;
-      const int sw = (r / URPL) % UCPR;
-      float ssum = 0.f;
+      for (int i = 0; i < BI; ++i) {
+        const int m = min(m0 + wm * TM + i * 32 + fr, M - 1);
+        if constexpr (with_rowmap) orow[i] = g.rowmap[m]; else orow[i] = m;
+      }
+      f32x4 w[BJ][4];
 #pragma unroll
       for (int j = 0; j < BJ; ++j)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int nc = n + j * 32 + 8 * gq + c4;
-          f32x4 v;
+        for (int gq = 0; gq < 4; ++gq)
+          w[j][gq] = *reinterpret_cast<const f32x4*>(g.norm_w + min(n + j * 32 + 8 * gq + c4, N - 4));
+      lds_barrier();  // every wave is done reading the ring
+      constexpr int GI = BI < 2 ? BI : 2;  // row blocks per load/store group
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * gq + e];
-          if (ok) {
-            f32x4* c = reinterpret_cast<f32x4*>((float*)g.C + orow * g.ldc + nc);
-            if constexpr (EPI == VIT_EPI_ADD_F32) v = *c + v;
-            *c = v;
-          }
-          const f32x4 w = *reinterpret_cast<const f32x4*>(g.norm_w + min(nc, N - 4));
-          bf16x4 u;
+      for (int i0 = 0; i0 < BI; i0 += GI) {
+        // loads of the group (unconditional, clamped in bounds) before its stores
+        f32x4 v[GI][BJ][4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            u[e] = f2bf(v[e] * w[e]);
-            ssum += v[e] * v[e];
-          }
-          const int c16 = j * 4 + gq, hh = fh ^ ((r >> 4) & 1);
-          *reinterpret_cast<bf16x4*>(st + r * UROWB + ((c16 ^ sw) << 4) + (hh << 3)) = u;
-          sched_fence();
+        for (int ii = 0; ii < GI; ++ii)
+#pragma unroll
+          for (int j = 0; j < BJ; ++j)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int i = i0 + ii;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[ii][j][gq][e] = acc[i][j][4 * gq + e];
+              if constexpr (EPI == VIT_EPI_ADD_F32)
+                v[ii][j][gq] += *reinterpret_cast<const f32x4*>(
+                    (const float*)g.C + orow[i] * g.ldc + min(n + j * 32 + 8 * gq + c4, N - 4));
+            }
+#pragma unroll
+        for (int ii = 0; ii < GI; ++ii) {
+          const int i = i0 + ii;
+          const int r = i * 32 + fr;
+          const int m = m0 + wm * TM + r;
+          const bool ok = cols_ok && m < M;
+          const int sw = (r / URPL) % UCPR;
+          float ssum = 0.f;
+#pragma unroll
+          for (int j = 0; j < BJ; ++j)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              if (ok)
+                *reinterpret_cast<f32x4*>((float*)g.C + orow[i] * g.ldc + n + j * 32 + 8 * gq + c4) =
+                    v[ii][j][gq];
+              bf16x4 u;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                u[e] = f2bf(v[ii][j][gq][e] * w[j][gq][e]);
+                ssum += v[ii][j][gq][e] * v[ii][j][gq][e];
+              }
+              const int c16 = j * 4 + gq, hh = fh ^ ((r >> 4) & 1);
+              *reinterpret_cast<bf16x4*>(st + r * UROWB + ((c16 ^ sw) << 4) + (hh << 3)) = u;
+            }
+          ssum = xor32_sum(ssum);
+          if (ok && fh == 0) g.ss_out[(int64_t)m * ((N / 64 + 3) & ~3) + n / 64] = ssum;
         }
-      ssum = xor32_sum(ssum);
-      if (ok && fh == 0) g.ss_out[(int64_t)m * ((N / 64 + 3) & ~3) + n / 64] = ssum;
-    }
+        sched_fence();
+      }
+    };
+    if (has_rowmap)
+      produce(std::true_type{});
+    else
+      produce(std::false_type{});
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staged writes done
     asm volatile("" ::: "memory");
     constexpr int URPI = 64 / UCPR;  // staged rows per read instruction
@@ -425,86 +488,138 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
       asm volatile("" ::: "memory");
       constexpr int RPI = 64 / CPRW;  // staged rows per read instruction
       const int cl = lane % CPRW;
+      const int n = n0 + wn * OTN + cl * EPC;
+      auto flush = [&](auto with_rowmap) __attribute__((always_inline)) {
+        // with a row map, every map entry is read before the first store
+        int64_t dst_row[with_rowmap ? TM / RPI : 1];
+        if constexpr (with_rowmap) {
+#pragma unroll
+          for (int it = 0; it < TM / RPI; ++it)
+            dst_row[it] = g.rowmap[min(m0 + wm * TM + it * RPI + lane / CPRW, M - 1)];
+        }
 #pragma unroll 4
-      for (int it = 0; it < TM / RPI; ++it) {
-        const int R = it * RPI + lane / CPRW;
-        const int m = m0 + wm * TM + R;
-        u32x4 d = *reinterpret_cast<const u32x4*>(st + R * ROWB +
-                                                  ((cl ^ ((R / RPL) % CPRW)) << 4));
-        if (!kF32 && ((R >> 4) & 1)) {
-          const uint32_t t0 = d[0], t1 = d[1];
-          d[0] = d[2]; d[1] = d[3]; d[2] = t0; d[3] = t1;
-        }
-        const int n = n0 + wn * OTN + cl * EPC;
-        if (m >= M || n >= N) continue;
-        const int64_t orow = g.rowmap ? (int64_t)g.rowmap[m] : (int64_t)m;
-        char* dst = (char*)g.C + (orow * g.ldc + n) * OB;
-        if (n + EPC <= N) {
-          if constexpr (EPI == VIT_EPI_ADD_F32) {
-            const f32x4 c = *reinterpret_cast<const f32x4*>(dst);
-            *reinterpret_cast<f32x4*>(dst) = c + __builtin_bit_cast(f32x4, d);
-          } else {
+        for (int it = 0; it < TM / RPI; ++it) {
+          const int R = it * RPI + lane / CPRW;
+          const int m = m0 + wm * TM + R;
+          u32x4 d = *reinterpret_cast<const u32x4*>(st + R * ROWB +
+                                                    ((cl ^ ((R / RPL) % CPRW)) << 4));
+          if (!kF32 && ((R >> 4) & 1)) {
+            const uint32_t t0 = d[0], t1 = d[1];
+            d[0] = d[2]; d[1] = d[3]; d[2] = t0; d[3] = t1;
+          }
+          if (m >= M || n >= N) continue;
+          int64_t drow = m;
+          if constexpr (with_rowmap) drow = dst_row[it];
+          char* dst = (char*)g.C + (drow * g.ldc + n) * OB;
+          if (n + EPC <= N)
             *reinterpret_cast<u32x4*>(dst) = d;
-          }
-        } else {  // N % 8 == 4 tail of a bf16 row: the first 8 bytes
-          *reinterpret_cast<uint2*>(dst) = make_uint2(d[0], d[1]);
+          else  // N % 8 == 4 tail of a bf16 row: the first 8 bytes
+            *reinterpret_cast<uint2*>(dst) = make_uint2(d[0], d[1]);
         }
-      }
+      };
+      if (has_rowmap)
+        flush(std::true_type{});
+      else
+        flush(std::false_type{});
+      return;
     }
   }
-  if (staged && !v_wave) return;
 
-  // direct stores (outputs too wide to stage, and the transposed v columns)
+  // direct stores (fp32 residual add, outputs too wide to stage, the
+  // transposed v columns); all loads first, then all stores
+  auto direct = [&](auto with_rowmap) __attribute__((always_inline)) {
+    int64_t orow[BI];
+    int vpos_i[BI];
 #pragma unroll
-  for (int i = 0; i < BI; ++i) {
-    const int m = m0 + wm * TM + i * 32 + fr;
-    if (m >= M) continue;
-    const int64_t orow = g.rowmap ? (int64_t)g.rowmap[m] : (int64_t)m;
-    if constexpr (DUAL) {
-#pragma unroll
-      for (int j = 0; j < BJ / 2; ++j)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = n0 + wn * (TN / 2) + j * 32 + 8 * gq + c4;
-          if (n >= N) continue;
-          bf16x4 v;
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            v[r] = f2bf(silu_f(acc[i][j][4 * gq + r]) * acc[i][j + BJ / 2][4 * gq + r]);
-          *reinterpret_cast<bf16x4*>((bf16*)g.C + orow * g.ldc + n) = v;
-          sched_fence();
-        }
-    } else {
-#pragma unroll
-      for (int j = 0; j < BJ; ++j)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = n0 + wn * TN + j * 32 + 8 * gq + c4;
-          if (n >= N) continue;
-          f32x4 v;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * gq + r];
-          if (EPI == VIT_EPI_QKV_VT && n >= g.rope_cols) {
-            // v column: row (head, dim) = n - rope_cols of the transposed layout
-            bf16* vt = (bf16*)g.vt + (int64_t)(n - g.rope_cols) * g.vt_ld + g.vpos[m];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) vt[r * g.vt_ld] = f2bf(v[r]);
-          } else if (EPI == VIT_EPI_STORE || EPI == VIT_EPI_STORE_ROPE ||
-                     EPI == VIT_EPI_QKV_VT) {
-            bf16x4 b;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) b[r] = f2bf(v[r]);
-            *reinterpret_cast<bf16x4*>((bf16*)g.C + orow * g.ldc + n) = b;
-          } else if (EPI == VIT_EPI_STORE_F32) {
-            *reinterpret_cast<f32x4*>((float*)g.C + orow * g.ldc + n) = v;
-          } else {  // VIT_EPI_ADD_F32
-            f32x4* c = reinterpret_cast<f32x4*>((float*)g.C + orow * g.ldc + n);
-            *c = *c + v;
-          }
-          sched_fence();  // convert and store block by block (bounds live registers)
-        }
+    for (int i = 0; i < BI; ++i) {
+      const int m = min(m0 + wm * TM + i * 32 + fr, M - 1);
+      if constexpr (with_rowmap) orow[i] = g.rowmap[m]; else orow[i] = m;
+      if constexpr (EPI == VIT_EPI_QKV_VT) vpos_i[i] = g.vpos[m];
     }
-  }
+    if constexpr (EPI == VIT_EPI_ADD_F32) {
+      constexpr int GI = BI < 2 ? BI : 2;  // row blocks per load/store group
+#pragma unroll
+      for (int i0 = 0; i0 < BI; i0 += GI) {
+        // loads of the group (unconditional, clamped in bounds) before its stores
+        f32x4 c[GI][BJ][4];
+#pragma unroll
+        for (int ii = 0; ii < GI; ++ii)
+#pragma unroll
+          for (int j = 0; j < BJ; ++j)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int n = min(n0 + wn * TN + j * 32 + 8 * gq + c4, N - 4);
+              c[ii][j][gq] =
+                  *reinterpret_cast<const f32x4*>((const float*)g.C + orow[i0 + ii] * g.ldc + n);
+            }
+#pragma unroll
+        for (int ii = 0; ii < GI; ++ii)
+#pragma unroll
+          for (int j = 0; j < BJ; ++j)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int i = i0 + ii;
+              const int m = m0 + wm * TM + i * 32 + fr;
+              const int n = n0 + wn * TN + j * 32 + 8 * gq + c4;
+              if (m >= M || n >= N) continue;
+              f32x4 v = c[ii][j][gq];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) v[r] += acc[i][j][4 * gq + r];
+              *reinterpret_cast<f32x4*>((float*)g.C + orow[i] * g.ldc + n) = v;
+            }
+        sched_fence();
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int m = m0 + wm * TM + i * 32 + fr;
+      if (m >= M) continue;
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int j = 0; j < BJ / 2; ++j)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int n = n0 + wn * (TN / 2) + j * 32 + 8 * gq + c4;
+            if (n >= N) continue;
+            bf16x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              v[r] = f2bf(silu_f(acc[i][j][4 * gq + r]) * acc[i][j + BJ / 2][4 * gq + r]);
+            *reinterpret_cast<bf16x4*>((bf16*)g.C + orow[i] * g.ldc + n) = v;
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < BJ; ++j)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int n = n0 + wn * TN + j * 32 + 8 * gq + c4;
+            if (n >= N) continue;
+            f32x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * gq + r];
+            if (EPI == VIT_EPI_QKV_VT && n >= g.rope_cols) {
+              // v column: row (head, dim) = n - rope_cols of the transposed layout
+              bf16* vt = (bf16*)g.vt + (int64_t)(n - g.rope_cols) * g.vt_ld + vpos_i[i];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) vt[r * g.vt_ld] = f2bf(v[r]);
+            } else if (EPI == VIT_EPI_STORE_F32) {
+              *reinterpret_cast<f32x4*>((float*)g.C + orow[i] * g.ldc + n) = v;
+            } else {
+              bf16x4 b;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) b[r] = f2bf(v[r]);
+              *reinterpret_cast<bf16x4*>((bf16*)g.C + orow[i] * g.ldc + n) = b;
+            }
+          }
+      }
+      sched_fence();  // one row block at a time (bounds live registers)
+    }
+  };
+  if (has_rowmap)
+    direct(std::true_type{});
+  else
+    direct(std::false_type{});
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool DUAL>
