@@ -63,6 +63,39 @@ def test_gemm_full_qkv_shape_sampled_rows():
     assert rowwise_rel_err(got[rows], oracle.linear(A[rows], B)) < 8e-3
 
 
+# Larger shapes, rows sampled: chosen so that the tile cost model takes each of
+# its tile configurations (8-wave 256x128, 8-wave 256x256, 4-wave 192x256 with
+# the bf16 store, SwiGLU and fp32 residual-add epilogues), with partial tiles.
+BIG_GEMMS = [((2048, 2304, 1024), "store"), ((4096, 3456, 1152), "store"),
+             ((9216, 4096, 1024), "store"), ((4096, 4304, 1152), "swiglu"),
+             ((4096, 1152, 4352), "add_f32"), ((9216, 1024, 2816), "add_f32"),
+             ((3562, 2816, 1024), "swiglu")]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("shape,epi", BIG_GEMMS, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
+def test_gemm_tile_configs_sampled_rows(shape, epi):
+    M, N, K = shape
+    A = synth.random_array((M, K), 11, bf16=True)
+    B = synth.random_array((N, K), 12, std=0.03, bf16=True)
+    B2 = synth.random_array((N, K), 13, std=0.03, bf16=True)
+    C0 = synth.random_array((M, N), 14)
+    code = {"store": _lib.VIT_EPI_STORE, "swiglu": _lib.VIT_EPI_SWIGLU,
+            "add_f32": _lib.VIT_EPI_ADD_F32}[epi]
+    C = _dev(C0) if epi == "add_f32" else None
+    got = to_np(api.gemm(_dev(A, "bf16"), _dev(B, "bf16"), code,
+                         B2=_dev(B2, "bf16") if epi == "swiglu" else None, C=C))
+    rows = np.r_[0:3, 127:131, 191:194, 255:258, M // 2:M // 2 + 3, M - 70:M:7, M - 2:M]
+    if epi == "swiglu":
+        ref = oracle.mlp(A[rows], B, B2, np.eye(N))
+    else:
+        ref = oracle.linear(A[rows], B)
+    if epi == "add_f32":
+        ref = ref + C0[rows]
+    tol = 1e-4 if epi == "add_f32" else 8e-3
+    assert rowwise_rel_err(got[rows], ref) < tol
+
+
 # ---------------------------------------------------------------- RMSNorm
 @pytest.mark.parametrize("dim", [256, 1024, 1152])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f32"])

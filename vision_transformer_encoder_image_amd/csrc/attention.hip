@@ -27,6 +27,9 @@
 namespace {
 
 constexpr int BQ = 128, BKV = 64;
+// q-tile of the bf16 varlen descriptor: one transposed-V workgroup (8 waves x 32
+// queries), or two workgroups of the generic bf16 kernel
+constexpr int BQ_DESC = 256;
 constexpr int kThreads = 256;
 
 template <int D>
@@ -47,11 +50,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
   __shared__ __attribute__((aligned(16))) bf16 sK[BKV * KS];
   __shared__ __attribute__((aligned(16))) bf16 sVt[DO * VS];
 
-  const int tile = blockIdx.x, h = blockIdx.y;
+  const int tile = blockIdx.x >> 1, h = blockIdx.y;  // two workgroups per descriptor tile
   int img = 0;
   while (img + 1 < desc.n_images && tile >= desc.cu_tiles[img + 1]) ++img;
   const int seq0 = desc.cu_seqlens[img], seq1 = desc.cu_seqlens[img + 1];
-  const int q0 = seq0 + (tile - desc.cu_tiles[img]) * BQ;
+  const int q0 = seq0 + (tile - desc.cu_tiles[img]) * BQ_DESC + (blockIdx.x & 1) * BQ;
   const int64_t ld = 3 * (int64_t)H * D;
   const bf16* Qb = qkv + h * D;
   const bf16* Kb = qkv + (int64_t)H * D + h * D;
@@ -248,12 +251,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
 // the previous step) while those reads are in flight, then issues the S^T
 // MFMAs of tile t+1 and the O^T MFMAs of tile t as one interleaved run.  The softmax reference max is raised only when some lane's max
 // grows by more than 2^8 (exact after the final 1/sum; p stays <= 256).
-constexpr int VT_BQ = 128, VT_BKV = 64, VT_STAGES = 4;
+constexpr int VT_BQ = 256, VT_BKV = 64, VT_STAGES = 4, VT_WAVES = 8;
 constexpr float VT_RESCALE_LOG2 = 8.0f;
 
 VIT_DEV int vt_swz(int row) { return (row >> 1) & 7; }
 
-__global__ __launch_bounds__(256, 2) void attn_vt_kernel(const bf16* __restrict__ qk, int64_t ldq,
+__global__ __launch_bounds__(64 * VT_WAVES, 1) void attn_vt_kernel(const bf16* __restrict__ qk, int64_t ldq,
                                                          const bf16* __restrict__ vt,
                                                          int64_t vt_ld, VarlenDesc desc, int H,
                                                          bf16* __restrict__ out, float c) {
@@ -278,14 +281,14 @@ __global__ __launch_bounds__(256, 2) void attn_vt_kernel(const bf16* __restrict_
   const int64_t dm = (int64_t)H * 64;
 
   // copies per stage: 8 x 1 KB of K rows then 8 x 1 KB of V^T rows; wave w
-  // issues copies w, w+4, w+8, w+12
+  // issues copies w and w+8 (one K-row copy, one V^T-row copy)
   const int crow = lane >> 3;
   const int cpc = lane & 7;
 #define VIT_ATT_ISSUE(t)                                                                 \
   do {                                                                                   \
     const int kv0_ = (t) * VT_BKV;                                                       \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
-      const int q_ = wave + 4 * i;                                                       \
+    _Pragma("unroll") for (int i = 0; i < 16 / VT_WAVES; ++i) {                          \
+      const int q_ = wave + VT_WAVES * i;                                                \
       const int r_ = 8 * (q_ & 7) + crow;                                                \
       const int kc_ = cpc ^ vt_swz(r_);                                                  \
       const bf16* src_;                                                                  \
@@ -336,13 +339,14 @@ __global__ __launch_bounds__(256, 2) void attn_vt_kernel(const bf16* __restrict_
   bf16x8 kf[8], vf[8];
   float mref = -INFINITY, lsum = 0.f;
   const int nkv = (P + VT_BKV - 1) / VT_BKV;
+  constexpr int CPS = 16 / VT_WAVES;  // copies per stage per wave
   VIT_ATT_ISSUE(0);
   if (nkv > 1) VIT_ATT_ISSUE(1);
   if (nkv > 2) VIT_ATT_ISSUE(2);
   if (nkv > 2)
-    wait_vmcnt<8>();
+    wait_vmcnt<2 * CPS>();
   else if (nkv > 1)
-    wait_vmcnt<4>();
+    wait_vmcnt<CPS>();
   else
     wait_vmcnt<0>();
   lds_barrier();
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void attn_vt_kernel(const bf16* __restrict_
     // whose buffer the next copy overwrites
     if (t + 1 < nkv) {
       if (t + 2 < nkv)
-        wait_vmcnt<4>();
+        wait_vmcnt<CPS>();
       else
         wait_vmcnt<0>();
     }
@@ -507,15 +511,15 @@ __global__ __launch_bounds__(FQ) void attn_f32_kernel(const float* __restrict__ 
 
 }  // namespace
 
-int attention_q_tile(int dtype, int /*head_dim*/) { return dtype == VIT_BF16 ? BQ : FQ; }
+int attention_q_tile(int dtype, int /*head_dim*/) { return dtype == VIT_BF16 ? BQ_DESC : FQ; }
 
 hipError_t launch_attention_vt(const void* qk, int64_t ld_qk, const void* vt, int64_t vt_ld,
                                const VarlenDesc& d, int n_heads, void* out, hipStream_t s) {
-  static_assert(VT_BQ == BQ, "both bf16 kernels share the q-tile descriptor");
+  static_assert(VT_BQ == BQ_DESC && 2 * BQ == BQ_DESC, "both bf16 kernels share the q-tile descriptor");
   const int tiles = d.cu_tiles[d.n_images];
   if (tiles == 0) return hipSuccess;
   const float c = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
-  attn_vt_kernel<<<dim3((unsigned)(tiles * n_heads)), 256, 0, s>>>(
+  attn_vt_kernel<<<dim3((unsigned)(tiles * n_heads)), 64 * VT_WAVES, 0, s>>>(
       (const bf16*)qk, ld_qk, (const bf16*)vt, vt_ld, d, n_heads, (bf16*)out, c);
   return hipGetLastError();
 }
@@ -524,7 +528,8 @@ hipError_t launch_attention(int dtype, const void* qkv, const VarlenDesc& d, int
                             int head_dim, void* out, hipStream_t s) {
   const int tiles = d.cu_tiles[d.n_images];
   if (tiles == 0) return hipSuccess;
-  const dim3 grid((unsigned)tiles, (unsigned)n_heads);
+  // bf16: two 128-query workgroups per 256-query descriptor tile
+  const dim3 grid((unsigned)(dtype == VIT_BF16 ? 2 * tiles : tiles), (unsigned)n_heads);
   if (dtype == VIT_BF16) {
     const float sl2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
     if (head_dim == 64)

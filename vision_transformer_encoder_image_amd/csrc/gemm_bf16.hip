@@ -250,19 +250,23 @@ bool pipe_eligible(const GemmArgs& g) {
 
 // Tile configuration by a wave-quantisation cost model: cost ~ (rounds of one
 // workgroup per CU) x (tile area / relative efficiency per flop).  Measured on
-// gfx950: the 8-wave 256x128 tile is ~1.35x and the 8-wave 256x256 tile ~1.5x
-// as efficient per flop as the 4-wave 128x128 tile, less so (1.1x / 1.25x) with
-// the fp32 read-modify-write epilogue, whose traffic grows with the tile.
-int gemm_mfma_choice(int epilogue, int64_t M, int64_t N) {
+// gfx950 (many-round shapes): relative to the 4-wave 128x128 tile, the 8-wave
+// 256x128 tile is ~1.35x, the 4-wave 192x256 tile ~1.34x and the 8-wave
+// 256x256 tile ~1.5x as efficient per flop; with the fp32 read-modify-write
+// epilogue, whose traffic grows with the tile, 1.1x / 1.2x / 1.25x.  The
+// folded-RMSNorm producer needs 64-column wave sub-tiles (not 192x256).
+int gemm_mfma_choice(int epilogue, bool norm_producer, int64_t M, int64_t N) {
   const bool dual = epilogue == VIT_EPI_SWIGLU;
   const bool rmw = epilogue == VIT_EPI_ADD_F32;
-  struct Opt { int cfg, bm, bn; double eff; };
-  const Opt opts[] = {{GEMM_MFMA_128x128, 128, 128, 1.0},
-                      {GEMM_MFMA_256x128_W8, 256, 128, rmw ? 1.1 : 1.35},
-                      {GEMM_MFMA_256x256_W8, 256, 256, rmw ? 1.25 : 1.5}};
+  struct Opt { int cfg, bm, bn; double eff; bool ok; };
+  const Opt opts[] = {{GEMM_MFMA_128x128, 128, 128, 1.0, true},
+                      {GEMM_MFMA_256x128_W8, 256, 128, rmw ? 1.1 : 1.35, true},
+                      {GEMM_MFMA_256x256_W8, 256, 256, rmw ? 1.25 : 1.5, true},
+                      {GEMM_MFMA_192x256, 192, 256, rmw ? 1.2 : 1.34, !norm_producer}};
   int best = GEMM_MFMA_128x128;
   double best_cost = 1e300;
   for (const Opt& o : opts) {
+    if (!o.ok) continue;
     const int64_t bno = dual ? o.bn / 2 : o.bn;
     const int64_t tiles = ((M + o.bm - 1) / o.bm) * ((N + bno - 1) / bno);
     const double rounds = (double)((tiles + 255) / 256);
@@ -289,7 +293,7 @@ hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s) {
                    (epilogue != VIT_EPI_STORE_F32 && epilogue != VIT_EPI_ADD_F32)))
     return hipErrorInvalidValue;
   if (pipe_eligible(g)) {
-    const int cfg = gemm_mfma_choice(rope ? VIT_EPI_STORE : epilogue, g.M, g.N);
+    const int cfg = gemm_mfma_choice(rope ? VIT_EPI_STORE : epilogue, g.norm_w != nullptr, g.M, g.N);
     return launch_gemm_mfma(cfg, epilogue, g, s);
   }
   return launch_simple(epilogue, g, s);

@@ -309,12 +309,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
   // load under a branch makes the compiler wait for all stores at its use).
   const bool has_rowmap = g.rowmap != nullptr;
 
-  if (kF32Out && g.norm_w) {
-    // RMSNorm producer.  The wave's 64 columns are one group; lanes l and l^32
+  if constexpr (kF32Out && TN == 64) if (g.norm_w) {
+    // RMSNorm producer (64-column wave sub-tiles only; the dispatcher picks
+    // such a tile).  The wave's 64 columns are one group; lanes l and l^32
     // hold the two halves of a row's group.  x_new goes straight back to the
     // fp32 stream; u = bf16(x_new * w) is staged through the idle LDS ring (as
     // the bf16 outputs below) and written as row-contiguous 16-byte stores.
-    static_assert(TN == 64, "one 64-column group per wave");
     constexpr int UROWB = TN * 2;            // bytes per staged u row
     constexpr int UCPR = UROWB / 16, URPL = 256 / UROWB;
     static_assert(TM * UROWB * NW <= STAGES * ROWS * BK * 2, "u staging fits the ring");
@@ -668,6 +668,7 @@ hipError_t launch_gemm_mfma(int cfg, int epi, const GemmArgs& g, hipStream_t s) 
     case GEMM_MFMA_128x128: return mfma_epi<128, 128, 64, 2, 2, 4>(epi, g, s);
     case GEMM_MFMA_256x128_W8: return mfma_epi<256, 128, 64, 4, 2, 3>(epi, g, s);
     case GEMM_MFMA_256x256_W8: return mfma_epi<256, 256, 32, 2, 4, 4>(epi, g, s);
+    case GEMM_MFMA_192x256: return mfma_epi<192, 256, 32, 2, 2, 4>(epi, g, s);
   }
   return hipErrorInvalidValue;
 }
