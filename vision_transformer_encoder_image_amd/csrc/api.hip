@@ -300,31 +300,46 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
     for (const GemmArgs& g : chk) fuse = fuse && gemm_bf16_mfma_eligible(g);
   }
 
+  void* vt = p.use_vt ? base + p.vt : nullptr;
+  int32_t* vpos = p.use_vt ? (int32_t*)(base + p.vpos) : nullptr;
   // patch embedding: x (fp32 residual stream) = patches . Wpe^T
   {
     ProfScope ps(VIT_K_EMBED, s);
     if (dt == VIT_BF16) {
+      // one launch prepares everything the call needs before the first GEMM:
+      // patches and weight zero-padded to Kp, rotary table, transposed-V
+      // positions and padding
       void* xpad = base + p.xpad;
       void* wpe = base + p.wpe;
-      VIT_HIP(launch_pad_rows(dt, in, P, c.patch_dim, p.Kp, xpad, s), "pad patches");
-      VIT_HIP(launch_pad_rows(dt, w->patch_embed, d, c.patch_dim, p.Kp, wpe, s), "pad weight");
+      PrepArgs pa{};
+      pa.desc = desc;
+      pa.patches = in;
+      pa.xpad = xpad;
+      pa.w_pe = w->patch_embed;
+      pa.wpe = wpe;
+      pa.P = P;
+      pa.d = d;
+      pa.patch_dim = c.patch_dim;
+      pa.Kp = p.Kp;
+      pa.table = table;
+      pa.head_dim = c.head_dim;
+      pa.theta = (double)c.rope_theta;
+      pa.vpos = vpos;
+      pa.vt = vt;
+      pa.vt_rows = p.use_vt ? d : 0;
+      pa.vt_ld = p.kv_total;
+      VIT_HIP(launch_encode_prep(pa, s), "encode preparation");
       GemmArgs g = gemm_args(xpad, p.Kp, wpe, nullptr, p.Kp, x, d, P, d, p.Kp, nullptr);
       if (fuse) producer(g, w->norm1[0]);
       VIT_HIP(launch_gemm_bf16(VIT_EPI_STORE_F32, g, s), "patch embedding gemm");
     } else {
       VIT_TRY(gemm(dt, VIT_EPI_STORE_F32, in, c.patch_dim, w->patch_embed, nullptr, c.patch_dim,
                    x, d, P, d, c.patch_dim, nullptr, s));
+      VIT_HIP(launch_rope_table(desc, c.head_dim, c.rope_theta, table, s), "rope table");
     }
   }
-  VIT_HIP(launch_rope_table(desc, c.head_dim, c.rope_theta, table, s), "rope table");
   if (p.hp > h)
     VIT_HIP(launch_zero_cols(dt, act, P, p.hp, h, p.hp, s), "zero MLP pad columns");
-  void* vt = p.use_vt ? base + p.vt : nullptr;
-  int32_t* vpos = p.use_vt ? (int32_t*)(base + p.vpos) : nullptr;
-  if (p.use_vt) {
-    VIT_HIP(launch_vpos(desc, vpos, s), "transposed-V positions");
-    VIT_HIP(launch_vt_zero_pads(desc, d, vt, p.kv_total, s), "transposed-V padding");
-  }
   void* a_in = fuse ? u : n;  // A operand of the GEMMs after a norm
 
   for (int b = 0; b < c.n_blocks; ++b) {

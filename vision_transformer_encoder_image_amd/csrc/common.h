@@ -183,6 +183,25 @@ hipError_t launch_attention(int dtype, const void* qkv, const VarlenDesc& d, int
 int attention_q_tile(int dtype, int head_dim);
 hipError_t launch_attention_vt(const void* qk, int64_t ld_qk, const void* vt, int64_t vt_ld,
                                const VarlenDesc& d, int n_heads, void* out, hipStream_t s);
+// Per-call preparation of an encode (bf16): zero-padded patches and patch
+// weight (K padded to Kp), rotary table, transposed-V positions and padding.
+// A null destination skips its part; b[] is filled in by the launcher.
+struct PrepArgs {
+  VarlenDesc desc;
+  const void* patches;  // [P, patch_dim] -> xpad [P, Kp]
+  void* xpad;
+  const void* w_pe;     // [d, patch_dim] -> wpe [d, Kp]
+  void* wpe;
+  int64_t P, d, patch_dim, Kp;
+  void* table;          // float2 [P, head_dim / 2]
+  int32_t head_dim;
+  double theta;
+  int32_t* vpos;        // [P]
+  void* vt;             // [vt_rows, vt_ld]
+  int64_t vt_rows, vt_ld;
+  int64_t b[5];
+};
+hipError_t launch_encode_prep(PrepArgs a, hipStream_t s);
 hipError_t launch_vpos(const VarlenDesc& d, int32_t* vpos, hipStream_t s);
 hipError_t launch_vt_zero_pads(const VarlenDesc& d, int64_t rows, void* vt, int64_t vt_ld,
                                hipStream_t s);

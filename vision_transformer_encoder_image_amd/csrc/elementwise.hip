@@ -46,9 +46,9 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const float* __restri
 // (cos, sin) of row * theta^(-k/(D/4)) for k < D/4 and of
 // col * theta^(-(k-D/4)/(D/4)) otherwise; row/col restart at every image.
 // Built in double precision, stored as float2.
-__global__ void rope_table_kernel(VarlenDesc d, int head_dim, double theta, float2* table) {
+VIT_DEV void rope_table_elem(const VarlenDesc& d, int head_dim, double theta, float2* table,
+                             int64_t idx) {
   const int half = head_dim / 2, q4 = head_dim / 4;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)d.total * half) return;
   const int p = (int)(idx / half);
   const int k = (int)(idx % half);
@@ -61,6 +61,10 @@ __global__ void rope_table_kernel(VarlenDesc d, int head_dim, double theta, floa
   double s, c;
   sincos((double)pos * f, &s, &c);
   table[idx] = make_float2((float)c, (float)s);
+}
+
+__global__ void rope_table_kernel(VarlenDesc d, int head_dim, double theta, float2* table) {
+  rope_table_elem(d, head_dim, theta, table, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -120,10 +124,9 @@ __global__ void gather_kernel(const T* __restrict__ x, VarlenDesc d, int dim, in
 // Copy rows [rows, cols] into [rows, ld_dst] zero-padding columns cols..ld_dst-1.
 // cols and ld_dst multiples of 4; one thread per 4 elements.
 template <typename T>
-__global__ void pad_rows_kernel(const T* __restrict__ src, int64_t rows, int64_t cols,
-                                int64_t ld_dst, T* __restrict__ dst) {
+VIT_DEV void pad_rows_elem(const T* __restrict__ src, int64_t rows, int64_t cols, int64_t ld_dst,
+                           T* __restrict__ dst, int64_t idx) {
   const int64_t q = ld_dst / 4;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= rows * q) return;
   const int64_t r = idx / q;
   const int64_t c = (idx % q) * 4;
@@ -138,25 +141,62 @@ __global__ void pad_rows_kernel(const T* __restrict__ src, int64_t rows, int64_t
   for (int k = 0; k < 4; ++k) o[k] = v[k];
 }
 
+template <typename T>
+__global__ void pad_rows_kernel(const T* __restrict__ src, int64_t rows, int64_t cols,
+                                int64_t ld_dst, T* __restrict__ dst) {
+  pad_rows_elem(src, rows, cols, ld_dst, dst, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
 // Column of every patch in the transposed-V layout (images start 64-aligned).
-__global__ void vpos_kernel(VarlenDesc d, int32_t* vpos) {
-  const int p = blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= d.total) return;
+VIT_DEV void vpos_elem(const VarlenDesc& d, int32_t* vpos, int64_t idx) {
+  const int p = (int)idx;
+  if (idx >= d.total) return;
   const int img = find_image(d, p);
   vpos[p] = d.kv_off[img] + vt_key_slot(p - d.cu_seqlens[img]);
 }
 
+__global__ void vpos_kernel(VarlenDesc d, int32_t* vpos) {
+  vpos_elem(d, vpos, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
 // Zero the slots of vt that hold no key: in image i, every slot from the start
 // of the 16-key group containing key P_i up to kv_off_{i+1} whose key is >= P_i.
-__global__ void vt_zero_pads_kernel(VarlenDesc d, int64_t rows, bf16* vt, int64_t ld) {
-  const int64_t row = blockIdx.y;
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;  // offset from the last group start
+VIT_DEV void vt_zero_pads_elem(const VarlenDesc& d, int64_t rows, bf16* vt, int64_t ld,
+                               int64_t row, int c) {
+  // c: offset from the start of the 16-key group holding key P_i
   if (row >= rows || c >= VT_ALIGN + 16) return;
   for (int i = 0; i < d.n_images; ++i) {
     const int P = d.cu_seqlens[i + 1] - d.cu_seqlens[i];
     const int j = (P & ~15) + c;  // local slot
     if (d.kv_off[i] + j < d.kv_off[i + 1] && vt_key_slot(j) >= P)
       vt[row * ld + d.kv_off[i] + j] = f2bf(0.f);
+  }
+}
+
+__global__ void vt_zero_pads_kernel(VarlenDesc d, int64_t rows, bf16* vt, int64_t ld) {
+  vt_zero_pads_elem(d, rows, vt, ld, blockIdx.y, blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// Everything an encode call prepares before the patch embedding, in one
+// launch: block ranges [0, b[0]) pad the patches, [b[0], b[1]) pad the
+// patch-embedding weight, [b[1], b[2]) build the rotary table, [b[2], b[3])
+// the transposed-V positions and [b[3], b[4]) zero the transposed-V padding.
+__global__ __launch_bounds__(kThreads) void encode_prep_kernel(PrepArgs a) {
+  const int64_t b = blockIdx.x;
+  const int t = threadIdx.x;
+  if (b < a.b[0]) {
+    pad_rows_elem((const bf16*)a.patches, a.P, a.patch_dim, a.Kp, (bf16*)a.xpad, b * kThreads + t);
+  } else if (b < a.b[1]) {
+    pad_rows_elem((const bf16*)a.w_pe, a.d, a.patch_dim, a.Kp, (bf16*)a.wpe,
+                  (b - a.b[0]) * kThreads + t);
+  } else if (b < a.b[2]) {
+    rope_table_elem(a.desc, a.head_dim, a.theta, (float2*)a.table, (b - a.b[1]) * kThreads + t);
+  } else if (b < a.b[3]) {
+    vpos_elem(a.desc, a.vpos, (b - a.b[2]) * kThreads + t);
+  } else if (b < a.b[4]) {
+    const int64_t i = (b - a.b[3]) * kThreads + t;
+    vt_zero_pads_elem(a.desc, a.vt_rows, (bf16*)a.vt, a.vt_ld, i / (VT_ALIGN + 16),
+                      (int)(i % (VT_ALIGN + 16)));
   }
 }
 
@@ -302,6 +342,21 @@ hipError_t launch_zero_cols(int dtype, void* buf, int64_t rows, int64_t ld, int6
     zero_cols_kernel<bf16><<<blocks_for(n), kThreads, 0, s>>>((bf16*)buf, rows, ld, c0, c1);
   else
     zero_cols_kernel<float><<<blocks_for(n), kThreads, 0, s>>>((float*)buf, rows, ld, c0, c1);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_prep(PrepArgs a, hipStream_t s) {
+  const int64_t n[5] = {a.patches ? a.P * (a.Kp / 4) : 0, a.w_pe ? a.d * (a.Kp / 4) : 0,
+                        a.table ? (int64_t)a.desc.total * (a.head_dim / 2) : 0,
+                        a.vpos ? (int64_t)a.desc.total : 0,
+                        a.vt ? a.vt_rows * (VT_ALIGN + 16) : 0};
+  int64_t acc = 0;
+  for (int i = 0; i < 5; ++i) {
+    acc += (n[i] + kThreads - 1) / kThreads;
+    a.b[i] = acc;
+  }
+  if (acc == 0) return hipSuccess;
+  encode_prep_kernel<<<dim3((unsigned)acc), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
