@@ -52,6 +52,11 @@ enum {
   VIT_NO_ALIGNER = 1,  /* stop after the final norm: out is [sum P, vision_dim] */
   VIT_OUT_NLAYOUT = 2, /* aligner rows land at their newline-layout slots (see
                           vit_aligner_layout); sentinel rows are not written */
+  VIT_IN_PIXELS = 4,   /* `in` holds pixel images instead of patches: image i is
+                          [3, ps*grid_h, ps*grid_w] (C order, ps = patch size with
+                          patch_dim = 3*ps^2), images back to back; the library cuts
+                          them into patches (DeepseekV4VisionTransformer.forward
+                          takes [n_h*n_w, 3, ps, ps] patches of the image) */
 };
 
 /* Upper bound on images per varlen call (descriptors travel as kernel args). */
@@ -113,7 +118,9 @@ size_t vit_workspace_bytes(const vit_config* cfg, const int32_t* grid_hw_host, i
 /* Encode one image: DeepseekV4Model.encode_image on the "...deepseek_v4.model" page
  * (vision tower, then aligner unless VIT_NO_ALIGNER).
  *   in   [grid_h * grid_w, patch_dim] patches, row-major over the grid, each patch
- *        flattened in [3, ps, ps] C order (DeepseekV4VisionTransformer.forward).
+ *        flattened in [3, ps, ps] C order (DeepseekV4VisionTransformer.forward);
+ *        with VIT_IN_PIXELS the pixel image [3, ps*grid_h, ps*grid_w] instead
+ *        (patch_dim must then be 3*ps^2; VIT_E_SHAPE otherwise).
  *   out  aligner on: [(grid_h/merge)*(grid_w/merge), llm_dim], merged tokens
  *        row-major over the merged grid (or newline-layout rows with
  *        VIT_OUT_NLAYOUT: [(h'*(w'+1)+2), llm_dim]);

@@ -77,11 +77,30 @@ def test_host_validation_errors(lib):
     assert lib.vit_workspace_bytes(ctypes.byref(cfg), many, _lib.VIT_MAX_IMAGES + 1, 0) == 0
     ok = _lib.grid_array([(2, 2)] * _lib.VIT_MAX_IMAGES)
     assert lib.vit_workspace_bytes(ctypes.byref(cfg), ok, _lib.VIT_MAX_IMAGES, 0) > 0
+    # pixel input: patch_dim must be 3 * ps^2; unknown flags are refused
+    px = api.c_config(configs.get(1))
+    assert lib.vit_workspace_bytes(ctypes.byref(px), g, 1, _lib.VIT_IN_PIXELS) > 0
+    px.patch_dim = 592  # 3 * ps^2 has no integer ps
+    assert lib.vit_workspace_bytes(ctypes.byref(px), g, 1, _lib.VIT_IN_PIXELS) == 0
+    assert b"3*ps^2" in lib.vit_last_error()
+    assert lib.vit_encode(ctypes.byref(px), None, None, 28, 28, _lib.VIT_IN_PIXELS, None, None, 0,
+                          None) == _lib.VIT_E_SHAPE
+    assert lib.vit_workspace_bytes(ctypes.byref(cfg), g, 1, 64) == 0
     # GEMM argument checks (host side)
     assert lib.vit_gemm(0, 0, None, 8, None, None, 8, None, 8, 1, 1, 8, None) == _lib.VIT_E_ARG
     assert lib.vit_gemm(0, 9, 16, 8, 16, None, 8, 16, 8, 1, 1, 8, None) == _lib.VIT_E_ARG
     assert lib.vit_gemm(0, 0, 16, 12, 16, None, 12, 16, 8, 1, 1, 12, None) == _lib.VIT_E_SHAPE
     assert lib.vit_gemm(0, 0, 8, 16, 16, None, 16, 16, 8, 1, 1, 16, None) == _lib.VIT_E_ARG  # misaligned
+
+
+def test_pixel_input_workspace(lib):
+    # fp32 pixel input needs a buffer for the cut patches; bf16 reuses the padded one
+    tiny = configs.get(0)
+    assert api.workspace_bytes(tiny, list(tiny.grids), pixels=True) > \
+        api.workspace_bytes(tiny, list(tiny.grids))
+    c = configs.get(2)
+    assert api.workspace_bytes(c, list(c.grids), aligner=False, pixels=True) == \
+        api.workspace_bytes(c, list(c.grids), aligner=False)
 
 
 def test_workspace_grows_with_patches(lib):

@@ -78,6 +78,37 @@ def test_single_image_entry_matches_varlen_bitwise():
     assert torch.equal(a, b)
 
 
+def _unpatchify(patches, grids, ps=14):
+    """Pixel images [3, ps*gh, ps*gw] (flattened, back to back) whose patches are
+    the given rows; pinned against oracle.patchify below."""
+    out, off = [], 0
+    for gh, gw in grids:
+        P = gh * gw
+        img = (patches[off:off + P].reshape(gh, gw, 3, ps, ps).transpose(2, 0, 3, 1, 4)
+               .reshape(3, gh * ps, gw * ps))
+        np.testing.assert_array_equal(oracle.patchify(img, ps), patches[off:off + P])
+        out.append(img.reshape(-1))
+        off += P
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("idx", [0, 2])
+def test_pixel_input_matches_patch_input(idx):
+    """VIT_IN_PIXELS: the library cuts the pixel images into the patches the
+    oracle's patchify gives, so the result equals the patch-input call bitwise."""
+    cfg, inp, w, x = _setup(idx)
+    pix = _unpatchify(np.asarray(inp["patches"]), cfg.grids)
+    xp = torch.from_numpy(pix).to("cuda", x.dtype)
+    a = api.Encoder(cfg, w, cfg.grids, aligner=cfg.aligner)(x)
+    b = api.Encoder(cfg, w, cfg.grids, aligner=cfg.aligner, pixels=True)(xp)
+    c = api.encode(xp, cfg.grids[0], w, aligner=cfg.aligner, pixels=True) if len(cfg.grids) == 1 \
+        else None
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    if c is not None:
+        assert torch.equal(a, c)
+
+
 def test_deterministic_run_to_run():
     cfg, inp, w, x = _setup(2)
     enc = api.Encoder(cfg, w, cfg.grids, aligner=False)

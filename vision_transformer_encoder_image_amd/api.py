@@ -82,9 +82,14 @@ def output_rows(cfg: VitConfig, grids: Sequence[Tuple[int, int]], aligner: bool,
     return sum((h // m) * (w // m) for h, w in grids)
 
 
-def workspace_bytes(cfg: VitConfig, grids, aligner=True, nlayout=False) -> int:
+def _flags(aligner: bool, nlayout: bool, pixels: bool) -> int:
+    return ((0 if aligner else _lib.VIT_NO_ALIGNER) | (_lib.VIT_OUT_NLAYOUT if nlayout else 0)
+            | (_lib.VIT_IN_PIXELS if pixels else 0))
+
+
+def workspace_bytes(cfg: VitConfig, grids, aligner=True, nlayout=False, pixels=False) -> int:
     lib = _lib.load()
-    flags = (0 if aligner else _lib.VIT_NO_ALIGNER) | (_lib.VIT_OUT_NLAYOUT if nlayout else 0)
+    flags = _flags(aligner, nlayout, pixels)
     c = c_config(cfg)
     n = lib.vit_workspace_bytes(ctypes.byref(c), _lib.grid_array(grids), len(grids), flags)
     if n == 0:
@@ -96,12 +101,12 @@ class Encoder:
     """Reusable encoder call: keeps the workspace for one set of grids."""
 
     def __init__(self, cfg: VitConfig, weights: DeviceWeights, grids, aligner=True, nlayout=False,
-                 device="cuda"):
+                 device="cuda", pixels=False):
         self.cfg, self.w = cfg, weights
         self.grids = [tuple(int(v) for v in g) for g in grids]
         self.aligner, self.nlayout = aligner, nlayout
-        self.flags = (0 if aligner else _lib.VIT_NO_ALIGNER) | (_lib.VIT_OUT_NLAYOUT if nlayout else 0)
-        self.ws_bytes = workspace_bytes(cfg, self.grids, aligner, nlayout)
+        self.flags = _flags(aligner, nlayout, pixels)
+        self.ws_bytes = workspace_bytes(cfg, self.grids, aligner, nlayout, pixels)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         self.c_cfg = c_config(cfg)
         self.c_grids = _lib.grid_array(self.grids)
@@ -125,17 +130,18 @@ class Encoder:
 
 
 def encode(patches: torch.Tensor, grid: Tuple[int, int], weights: DeviceWeights, aligner=True,
-           nlayout=False) -> torch.Tensor:
-    """vit_encode: one image [gh*gw, patch_dim] -> aligned tokens (or encoded patches)."""
+           nlayout=False, pixels=False) -> torch.Tensor:
+    """vit_encode: one image [gh*gw, patch_dim] (or with pixels=True the pixel image
+    [3, ps*gh, ps*gw]) -> aligned tokens (or encoded patches)."""
     cfg = weights.cfg
     _require_cuda(patches)
-    ws_bytes = workspace_bytes(cfg, [grid], aligner, nlayout)
+    ws_bytes = workspace_bytes(cfg, [grid], aligner, nlayout, pixels)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=patches.device)
     cols = cfg.llm_dim if aligner else cfg.vision_dim
     rows = output_rows(cfg, [grid], aligner, nlayout)
     out = (torch.zeros if nlayout else torch.empty)((rows, cols), dtype=_TORCH_DTYPE[cfg.dtype],
                                                      device=patches.device)
-    flags = (0 if aligner else _lib.VIT_NO_ALIGNER) | (_lib.VIT_OUT_NLAYOUT if nlayout else 0)
+    flags = _flags(aligner, nlayout, pixels)
     c = c_config(cfg)
     lib = _lib.load()
     st = lib.vit_encode(ctypes.byref(c), ctypes.byref(weights.c), patches.data_ptr(), grid[0],
@@ -146,9 +152,10 @@ def encode(patches: torch.Tensor, grid: Tuple[int, int], weights: DeviceWeights,
 
 
 def encode_varlen(patches: torch.Tensor, grids, weights: DeviceWeights, aligner=True,
-                  nlayout=False) -> torch.Tensor:
-    """vit_encode_varlen: packed images with block-diagonal attention."""
-    return Encoder(weights.cfg, weights, grids, aligner, nlayout, patches.device)(patches)
+                  nlayout=False, pixels=False) -> torch.Tensor:
+    """vit_encode_varlen: packed images with block-diagonal attention (patches, or
+    with pixels=True the pixel images back to back)."""
+    return Encoder(weights.cfg, weights, grids, aligner, nlayout, patches.device, pixels)(patches)
 
 
 def aligner_layout(grid_h: int, grid_w: int, merge: int = 2, device="cuda"):

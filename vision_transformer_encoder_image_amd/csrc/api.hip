@@ -102,6 +102,13 @@ vit_status check_config(const vit_config* c) {
   return VIT_OK;
 }
 
+// Patch size ps with patch_dim = 3 * ps^2, or 0 if there is none.
+int patch_size_of(const vit_config& c) {
+  for (int ps = 1; 3 * ps * ps <= c.patch_dim; ++ps)
+    if (3 * ps * ps == c.patch_dim) return ps;
+  return 0;
+}
+
 vit_status build_desc(const int32_t* grid_hw, int32_t n_images, int q_tile, bool need_even,
                       int merge, VarlenDesc* d) {
   if (!grid_hw) return fail(VIT_E_ARG, "grid_hw is NULL");
@@ -151,6 +158,7 @@ Plan make_plan(const vit_config& c, const VarlenDesc& desc, int flags) {
   p.P = P;
   p.tokens = aligner ? P / m2 : 0;
   p.Kp = c.dtype == VIT_BF16 ? round_up(c.patch_dim, 64) : c.patch_dim;
+  const bool pixels = (flags & VIT_IN_PIXELS) != 0;
   // MLP activations keep a 64-multiple row stride in bf16 so the down GEMM runs
   // whole 64-wide K tiles (the pad columns are zero)
   p.hp = c.dtype == VIT_BF16 ? round_up(h, 64) : h;
@@ -164,6 +172,8 @@ Plan make_plan(const vit_config& c, const VarlenDesc& desc, int flags) {
   if (c.dtype == VIT_BF16) {
     p.xpad = take((size_t)P * p.Kp * es);
     p.wpe = take((size_t)d * p.Kp * es);
+  } else if (pixels) {
+    p.xpad = take((size_t)P * p.Kp * es);  // fp32 patches cut from the pixels
   }
   p.x = take((size_t)P * d * sizeof(float));
   p.n = take((size_t)P * d * es);  // also holds the attention output
@@ -247,7 +257,11 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
                        void* ws, size_t ws_bytes, hipStream_t s) {
   VIT_TRY(check_config(cfg));
   const vit_config& c = *cfg;
-  if (flags & ~(VIT_NO_ALIGNER | VIT_OUT_NLAYOUT)) return fail(VIT_E_ARG, "unknown flags %d", flags);
+  if (flags & ~(VIT_NO_ALIGNER | VIT_OUT_NLAYOUT | VIT_IN_PIXELS))
+    return fail(VIT_E_ARG, "unknown flags %d", flags);
+  const int pixel_ps = (flags & VIT_IN_PIXELS) ? patch_size_of(*cfg) : 0;
+  if ((flags & VIT_IN_PIXELS) && pixel_ps == 0)
+    return fail(VIT_E_SHAPE, "pixel input needs patch_dim = 3*ps^2 (got %d)", cfg->patch_dim);
   const bool aligner = !(flags & VIT_NO_ALIGNER);
   if (aligner && c.llm_dim <= 0) return fail(VIT_E_SHAPE, "llm_dim must be positive with aligner");
   if (aligner && c.llm_dim % 8 && c.dtype == VIT_BF16)
@@ -314,6 +328,7 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
       PrepArgs pa{};
       pa.desc = desc;
       pa.patches = in;
+      pa.pixel_ps = pixel_ps;
       pa.xpad = xpad;
       pa.w_pe = w->patch_embed;
       pa.wpe = wpe;
@@ -333,8 +348,13 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
       if (fuse) producer(g, w->norm1[0]);
       VIT_HIP(launch_gemm_bf16(VIT_EPI_STORE_F32, g, s), "patch embedding gemm");
     } else {
-      VIT_TRY(gemm(dt, VIT_EPI_STORE_F32, in, c.patch_dim, w->patch_embed, nullptr, c.patch_dim,
-                   x, d, P, d, c.patch_dim, nullptr, s));
+      const void* patches = in;
+      if (pixel_ps > 0) {
+        VIT_HIP(launch_patchify(dt, in, desc, pixel_ps, c.patch_dim, base + p.xpad, s), "patchify");
+        patches = base + p.xpad;
+      }
+      VIT_TRY(gemm(dt, VIT_EPI_STORE_F32, patches, c.patch_dim, w->patch_embed, nullptr,
+                   c.patch_dim, x, d, P, d, c.patch_dim, nullptr, s));
       VIT_HIP(launch_rope_table(desc, c.head_dim, c.rope_theta, table, s), "rope table");
     }
   }
@@ -465,6 +485,14 @@ const char* vit_last_error(void) { return g_last_error.c_str(); }
 size_t vit_workspace_bytes(const vit_config* cfg, const int32_t* grid_hw_host, int32_t n_images,
                            int32_t flags) {
   if (check_config(cfg) != VIT_OK) return 0;
+  if (flags & ~(VIT_NO_ALIGNER | VIT_OUT_NLAYOUT | VIT_IN_PIXELS)) {
+    fail(VIT_E_ARG, "unknown flags %d", flags);
+    return 0;
+  }
+  if ((flags & VIT_IN_PIXELS) && patch_size_of(*cfg) == 0) {
+    fail(VIT_E_SHAPE, "pixel input needs patch_dim = 3*ps^2 (got %d)", cfg->patch_dim);
+    return 0;
+  }
   VarlenDesc d;
   const bool aligner = !(flags & VIT_NO_ALIGNER);
   if (build_desc(grid_hw_host, n_images, attention_q_tile(cfg->dtype, cfg->head_dim), aligner,

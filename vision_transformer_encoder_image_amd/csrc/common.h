@@ -188,7 +188,8 @@ hipError_t launch_attention_vt(const void* qk, int64_t ld_qk, const void* vt, in
 // A null destination skips its part; b[] is filled in by the launcher.
 struct PrepArgs {
   VarlenDesc desc;
-  const void* patches;  // [P, patch_dim] -> xpad [P, Kp]
+  const void* patches;  // [P, patch_dim] -> xpad [P, Kp]; pixel images if pixel_ps > 0
+  int32_t pixel_ps;     // patch size of pixel input (0: `patches` holds patches)
   void* xpad;
   const void* w_pe;     // [d, patch_dim] -> wpe [d, Kp]
   void* wpe;
@@ -202,6 +203,9 @@ struct PrepArgs {
   int64_t b[5];
 };
 hipError_t launch_encode_prep(PrepArgs a, hipStream_t s);
+// pixel images (see VIT_IN_PIXELS) -> patches [P, ld_dst] (zero past 3*ps^2)
+hipError_t launch_patchify(int dtype, const void* pix, const VarlenDesc& d, int ps, int64_t ld_dst,
+                           void* dst, hipStream_t s);
 hipError_t launch_vpos(const VarlenDesc& d, int32_t* vpos, hipStream_t s);
 hipError_t launch_vt_zero_pads(const VarlenDesc& d, int64_t rows, void* vt, int64_t vt_ld,
                                hipStream_t s);

@@ -177,6 +177,42 @@ __global__ void vt_zero_pads_kernel(VarlenDesc d, int64_t rows, bf16* vt, int64_
   vt_zero_pads_elem(d, rows, vt, ld, blockIdx.y, blockIdx.x * blockDim.x + threadIdx.x);
 }
 
+// Patch (p, k) of a packed batch of pixel images (image i: [3, ps*gh_i, ps*gw_i]
+// C order, images back to back, so image i starts at element patch_dim *
+// cu_seqlens[i]): patch p = r*gw + c of its image holds pixel rows ps*r.., cols
+// ps*c.. flattened in [3, ps, ps] C order (the layout DeepseekV4VisionTransformer
+// .forward expects).  Columns k >= patch_dim of the padded row are zero.
+template <typename T>
+VIT_DEV void patchify_elem(const T* __restrict__ pix, const VarlenDesc& d, int ps, int64_t ld_dst,
+                           T* __restrict__ dst, int64_t idx) {
+  if (idx >= (int64_t)d.total * ld_dst) return;
+  const int p = (int)(idx / ld_dst);
+  const int k = (int)(idx % ld_dst);
+  const int pd = 3 * ps * ps;
+  T v = from_f32<T>(0.f);
+  if (k < pd) {
+    int lo = 0, hi = d.n_images - 1;  // image of patch p: last i with cu_seqlens[i] <= p
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (d.cu_seqlens[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    const int start = d.cu_seqlens[lo];
+    const int gw = d.grid_w[lo];
+    const int gh = (d.cu_seqlens[lo + 1] - start) / gw;
+    const int local = p - start, r = local / gw, c = local % gw;
+    const int ch = k / (ps * ps), y = (k % (ps * ps)) / ps, x = k % ps;
+    const int64_t W = (int64_t)gw * ps, Hh = (int64_t)gh * ps;
+    v = pix[(int64_t)pd * start + (ch * Hh + (int64_t)r * ps + y) * W + (int64_t)c * ps + x];
+  }
+  dst[idx] = v;
+}
+
+template <typename T>
+__global__ void patchify_kernel(const T* __restrict__ pix, VarlenDesc d, int ps, int64_t ld_dst,
+                                T* __restrict__ dst) {
+  patchify_elem(pix, d, ps, ld_dst, dst, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
 // Everything an encode call prepares before the patch embedding, in one
 // launch: block ranges [0, b[0]) pad the patches, [b[0], b[1]) pad the
 // patch-embedding weight, [b[1], b[2]) build the rotary table, [b[2], b[3])
@@ -185,7 +221,12 @@ __global__ __launch_bounds__(kThreads) void encode_prep_kernel(PrepArgs a) {
   const int64_t b = blockIdx.x;
   const int t = threadIdx.x;
   if (b < a.b[0]) {
-    pad_rows_elem((const bf16*)a.patches, a.P, a.patch_dim, a.Kp, (bf16*)a.xpad, b * kThreads + t);
+    if (a.pixel_ps > 0)
+      patchify_elem((const bf16*)a.patches, a.desc, a.pixel_ps, a.Kp, (bf16*)a.xpad,
+                    b * kThreads + t);
+    else
+      pad_rows_elem((const bf16*)a.patches, a.P, a.patch_dim, a.Kp, (bf16*)a.xpad,
+                    b * kThreads + t);
   } else if (b < a.b[1]) {
     pad_rows_elem((const bf16*)a.w_pe, a.d, a.patch_dim, a.Kp, (bf16*)a.wpe,
                   (b - a.b[0]) * kThreads + t);
@@ -346,7 +387,8 @@ hipError_t launch_zero_cols(int dtype, void* buf, int64_t rows, int64_t ld, int6
 }
 
 hipError_t launch_encode_prep(PrepArgs a, hipStream_t s) {
-  const int64_t n[5] = {a.patches ? a.P * (a.Kp / 4) : 0, a.w_pe ? a.d * (a.Kp / 4) : 0,
+  const int64_t n[5] = {a.patches ? a.P * (a.pixel_ps > 0 ? a.Kp : a.Kp / 4) : 0,
+                        a.w_pe ? a.d * (a.Kp / 4) : 0,
                         a.table ? (int64_t)a.desc.total * (a.head_dim / 2) : 0,
                         a.vpos ? (int64_t)a.desc.total : 0,
                         a.vt ? a.vt_rows * (VT_ALIGN + 16) : 0};
@@ -357,6 +399,19 @@ hipError_t launch_encode_prep(PrepArgs a, hipStream_t s) {
   }
   if (acc == 0) return hipSuccess;
   encode_prep_kernel<<<dim3((unsigned)acc), kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_patchify(int dtype, const void* pix, const VarlenDesc& d, int ps, int64_t ld_dst,
+                           void* dst, hipStream_t s) {
+  const int64_t n = (int64_t)d.total * ld_dst;
+  if (n == 0) return hipSuccess;
+  if (dtype == VIT_BF16)
+    patchify_kernel<bf16><<<blocks_for(n), kThreads, 0, s>>>((const bf16*)pix, d, ps, ld_dst,
+                                                             (bf16*)dst);
+  else
+    patchify_kernel<float><<<blocks_for(n), kThreads, 0, s>>>((const float*)pix, d, ps, ld_dst,
+                                                              (float*)dst);
   return hipGetLastError();
 }
 
