@@ -16,8 +16,13 @@ Parity pins: every function here is pinned by ``tests/test_oracle.py`` against
 closed forms, hand-derived golden values, brute-force loops or invariants.
 """
 from .vit import (  # noqa: F401
+    NL_END,
+    NL_IMAGE,
+    NL_NEWLINE,
+    NL_START,
     READINGS,
     aligner,
+    merge_image_embeddings,
     aligner_gather,
     aligner_perm,
     apply_rope,

@@ -34,6 +34,11 @@ READINGS = {
     "odd_grid": "the aligner needs an even grid; odd grids are rejected",
     "nlayout": "per image: [START] + per merged row (w' IMAGE, NEWLINE) + [END]; "
                "types START=0 IMAGE=1 NEWLINE=2 END=3; src = merged token index or -1",
+    "merge_embeddings": "positions are visited batch-major, sequence-minor; IMAGE positions "
+                        "take the aligned tokens in that order (the images' concatenation "
+                        "order), START/NEWLINE/END take the image_start/image_newline/"
+                        "image_end embeddings, -1 (text) and any other type stay as they are; "
+                        "image_pad is not used by this layout",
 }
 
 NL_START, NL_IMAGE, NL_NEWLINE, NL_END = 0, 1, 2, 3
@@ -267,6 +272,29 @@ def nlayout(gh, gw, merge=2):
     types.append(NL_END)
     src.append(-1)
     return np.array(types, dtype=np.int32), np.array(src, dtype=np.int32)
+
+
+def merge_image_embeddings(embeds, types, tokens, sentinels):
+    """[MOD] DeepseekV4Model.merge_image_embeddings: replace pseudo-token embeddings.
+
+    ``embeds`` [..., L] text embeddings (any leading shape, e.g. [batch, seq]),
+    ``types`` the matching pseudo-token types (-1 text), ``tokens`` [T, L] the
+    aligned image tokens in image order, ``sentinels`` [3, L] the image_start,
+    image_newline and image_end embeddings.  Reading "merge_embeddings".
+    """
+    out = np.array(embeds, copy=True)
+    flat = out.reshape(-1, out.shape[-1])
+    kinds = np.asarray(types).reshape(-1)
+    sentinel_row = {NL_START: 0, NL_NEWLINE: 1, NL_END: 2}
+    t = 0
+    for pos in range(len(kinds)):
+        kind = int(kinds[pos])
+        if kind == NL_IMAGE:
+            flat[pos] = tokens[t]
+            t += 1
+        elif kind in sentinel_row:
+            flat[pos] = sentinels[sentinel_row[kind]]
+    return out
 
 
 def encode(patches, gh, gw, weights, n_heads, eps=1e-6, theta=10000.0, with_aligner=True,

@@ -501,3 +501,55 @@ def test_synth_is_deterministic():
     np.testing.assert_array_equal(a["weights"]["blocks"][1]["w_down"], b["weights"]["blocks"][1]["w_down"])
     assert a["patches"].shape == (64, 588)
     assert a["weights"]["aligner"].shape == (512, 1024)
+
+
+# ---------------------------------------------------------------- image-embedding merge
+def _merge_fixture():
+    types, expected = None, []
+    for line in open(os.path.join(GOLDEN, "merge_embeddings_small.txt")):
+        if line.startswith("types"):
+            types = np.array([int(v) for v in line.split()[1:]], dtype=np.int32)
+        elif line.startswith("expected"):
+            expected.append([float(v) for v in line.split()[1:]])
+    return types, np.array(expected)
+
+
+def test_merge_embeddings_golden():
+    types, expected = _merge_fixture()
+    q = np.arange(len(types))
+    embeds = np.stack([100.0 + q, -q.astype(float)], axis=1).reshape(2, 9, 2)
+    tokens = np.stack([1000.0 + np.arange(5), 2000.0 + np.arange(5)], axis=1)
+    sentinels = np.array([[7.0, 7.0], [8.0, 8.0], [9.0, 9.0]])
+    got = oracle.merge_image_embeddings(embeds, types.reshape(2, 9), tokens, sentinels)
+    assert got.shape == (2, 9, 2)
+    np.testing.assert_array_equal(got.reshape(-1, 2), expected)
+
+
+def test_merge_embeddings_with_nlayout_places_tokens_in_order():
+    # two images laid out with the newline layout inside a text stream: every IMAGE slot
+    # receives the aligned token its nl_src names (offset by the image's first token)
+    rng = np.random.default_rng(3)
+    L = 6
+    spans, tok_off, src_all = [], 0, []
+    for gh, gw in [(4, 6), (2, 8)]:
+        t, src = oracle.nlayout(gh, gw)
+        spans.append(t)
+        src_all.append(np.where(src >= 0, src + tok_off, -1))
+        tok_off += (gh // 2) * (gw // 2)
+    text = np.full(5, -1, np.int32)
+    types = np.concatenate([text, spans[0], text[:3], spans[1], text[:2]])
+    srcs = np.concatenate([np.full(5, -1), src_all[0], np.full(3, -1), src_all[1], np.full(2, -1)])
+    embeds = rng.standard_normal((len(types), L))
+    tokens = rng.standard_normal((tok_off, L))
+    sentinels = rng.standard_normal((3, L))
+    got = oracle.merge_image_embeddings(embeds, types, tokens, sentinels)
+    for q in range(len(types)):
+        if types[q] == oracle.NL_IMAGE:
+            np.testing.assert_array_equal(got[q], tokens[srcs[q]])
+        elif types[q] == -1:
+            np.testing.assert_array_equal(got[q], embeds[q])
+        else:
+            np.testing.assert_array_equal(got[q], sentinels[[oracle.NL_START, oracle.NL_NEWLINE,
+                                                             oracle.NL_END].index(types[q])])
+    # every token consumed exactly once
+    assert (types == oracle.NL_IMAGE).sum() == tok_off
