@@ -31,7 +31,7 @@ _GEMM_SRC = ("common.h", "gemm_bf16.hip", "gemm_mfma.h", "gemm_mfma.hip")
 KERNEL_SOURCE = {"qkv": _GEMM_SRC, "outproj": _GEMM_SRC, "gateup": _GEMM_SRC, "down": _GEMM_SRC,
                  "embed": _GEMM_SRC, "aligner": _GEMM_SRC, "attn": ("common.h", "attention.hip"),
                  "rmsnorm": ("common.h", "elementwise.hip"), "rope": ("common.h", "elementwise.hip"),
-                 "gather": ("common.h", "elementwise.hip")}
+                 "gather": ("common.h", "elementwise.hip"), "merge": ("common.h", "merge.hip")}
 
 
 def class_flops(cfg):
@@ -74,7 +74,7 @@ def counter_traffic(kernel_class, workload):
 # kernel-name patterns of each class in rocprofv3 output (SwiGLU is the only
 # dual-B GEMM instantiation, i.e. the template argument list ends in "true>")
 KERNEL_NAME_PATTERN = {"gateup": ("gemm_", ", true>("), "attn": ("attn_vt_kernel", ""),
-                       "rmsnorm": ("rmsnorm_kernel", "")}
+                       "rmsnorm": ("rmsnorm_kernel", ""), "merge": ("merge_copy_kernel", "")}
 
 
 def _pmc_rows(d):
@@ -141,12 +141,114 @@ def cpu_baseline(cfg, inp, budget_s=30.0):
                       f"float64 numpy oracle, one pass, {dt:.1f} s)"}
 
 
+def copy_calibration(mb, dev):
+    """A plain device copy of known size, whose counter readings scale FETCH_SIZE /
+    WRITE_SIZE of the measured kernels to bytes."""
+    import torch
+
+    n = mb * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+MERGE_METRIC = "GB/s, image tokens + sentinels merged into the LLM embedding stream (bf16)"
+
+
+def bench_merge(args):
+    """vit_merge_image_embeddings on the throughput batch's aligner output: 16 images
+    of 48x48 patches -> 24x24 merged tokens each, in newline layout (602 positions
+    per image), each image after 256 text positions; LLM width 4096, bf16.  One step
+    is one merge call over the whole stream (group counts, scan, row copies)."""
+    import numpy as np
+    import torch
+
+    from vision_transformer_encoder_image_amd import api
+
+    dev = "cuda:0"
+    n_img, (gh, gw), text, L = 16, (48, 48), 256, 4096
+    _, nl_type, _ = api.aligner_layout(gh, gw, device=dev)
+    span = torch.cat([torch.full((text,), -1, dtype=torch.int32, device=dev), nl_type])
+    types = span.repeat(n_img).contiguous()
+    positions = types.numel()
+    n_tok = n_img * (gh // 2) * (gw // 2)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    tokens = torch.randn((n_tok, L), generator=g).to(dev, torch.bfloat16)
+    sent = torch.randn((3, L), generator=g).to(dev, torch.bfloat16)
+    embeds = torch.randn((positions, L), generator=g).to(dev, torch.bfloat16)
+    ws = torch.empty(api.merge_workspace_bytes(positions), dtype=torch.uint8, device=dev)
+    n_image = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(max(args.warmup, 1)):
+        api.merge_image_embeddings_(embeds, types, tokens, sent, ws=ws, n_image=n_image)
+    torch.cuda.synchronize()
+    assert int(n_image.item()) == n_tok
+    replaced = int((types >= 0).sum().item())  # codes 0..3 are all replaced
+    row_bytes = L * 2
+    alg_bytes = replaced * row_bytes * 2 + positions * 4  # rows read + written, types read
+
+    api.profile_enable("merge", True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        api.merge_image_embeddings_(embeds, types, tokens, sent, ws=ws, n_image=n_image)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms, n = api.profile_read("merge")
+    api.profile_enable("merge", False)
+    copy_s = ms / 1e3 / max(n, 1)
+    achieved = alg_bytes / copy_s / 1e9
+    result = {
+        "metric": MERGE_METRIC,
+        "value": round(alg_bytes * args.steps / elapsed / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "merge_16x48x48_nlayout", "positions": positions,
+                   "replaced_rows": replaced, "image_tokens": n_tok, "hidden": L,
+                   "algorithmic_bytes": alg_bytes},
+        "roofline": {"kernel": "merge_copy", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic("merge", "merge_16x48x48_nlayout"),
+                     "avg_launch_us": round(copy_s * 1e6, 3), "launches": n,
+                     "bytes_per_launch": alg_bytes},
+    }
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb, dev)
+    if not args.no_cpu_baseline:
+        import oracle
+
+        ty, tk, st, em = (types.cpu().numpy(), tokens.float().cpu().numpy(),
+                          sent.float().cpu().numpy(), embeds.float().cpu().numpy())
+        runs, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0:
+            oracle.merge_image_embeddings(em, ty, tk, st)
+            runs += 1
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(alg_bytes * runs / dt / 1e9, 3), "unit": "GB/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": f"the whole stream, {runs} oracle passes in {dt:.1f} s "
+                                            "(float32 rows, one Python thread)"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--stage", choices=("encode", "merge"), default="encode",
+                    help="encode: the encoder step; merge: image tokens into the LLM stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -167,6 +269,10 @@ def main():
               "by image across GPUs with no exchange, so run one process per GPU instead.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.stage == "merge":
+        bench_merge(args)
+        return
 
     import torch
 
@@ -267,13 +373,7 @@ def main():
             bd[k] = e
         result["breakdown"] = bd
     if args.copy_calibration_mb:
-        n = args.copy_calibration_mb * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(args.copy_calibration_mb, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(result), flush=True)

@@ -207,11 +207,35 @@ vit_status vit_gemm(int32_t dtype, int32_t epilogue, const void* A, int64_t lda,
 vit_status vit_aligner_gather(int32_t dtype, const void* x, const int32_t* grid_hw_host,
                               int32_t n_images, int32_t d, void* G, void* stream);
 
+/* Image tokens into the LLM input stream (DeepSeek-V4 model page,
+ * DeepseekV4Model.merge_image_embeddings): for each position p of a text
+ * embedding stream embeds [positions, hidden] (in place, dtype):
+ *   types[p] == 1 (IMAGE)     row p = tokens[t], t = IMAGE positions before p;
+ *   types[p] == 0 / 2 / 3     row p = sentinels[0 / 1 / 2] (image_start,
+ *                             image_newline, image_end);
+ *   any other value (-1 text) row p is left as it is.
+ * types is device int32 [positions] with the codes of vit_aligner_layout's
+ * nl_type, so an image's span is its nl_type array and its tokens are the
+ * aligner output in order; several images simply follow one another.
+ * tokens [n_tokens, hidden] and sentinels [3, hidden] are device, dtype, rows
+ * 16-byte aligned (hidden * sizeof(dtype) % 16 == 0).  IMAGE positions beyond
+ * n_tokens are left unchanged; n_image (device int32, may be NULL) receives the
+ * number of IMAGE positions so the caller can check it against n_tokens.
+ * ws: device scratch of vit_merge_workspace_bytes(positions) bytes (0 is returned
+ * only for positions outside [0, 2^31)).  The rows of
+ * embeds must not overlap tokens or sentinels.  Asynchronous on stream. */
+size_t vit_merge_workspace_bytes(int64_t positions);
+vit_status vit_merge_image_embeddings(int32_t dtype, void* embeds, int64_t positions,
+                                      int32_t hidden, const int32_t* types, const void* tokens,
+                                      int64_t n_tokens, const void* sentinels, int32_t* n_image,
+                                      void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Kernel timing with HIP events (for measurement tools).  When enabled for a
- * kernel class, every launch of that class inside vit_encode(_varlen) is
- * bracketed by events on the call's stream; vit_profile_read synchronises them
- * and returns the summed duration and the launch count, then resets.
+ * kernel class, every launch of that class inside vit_encode(_varlen) and
+ * vit_merge_image_embeddings is bracketed by events on the call's stream;
+ * vit_profile_read synchronises them and returns the summed duration and the
+ * launch count, then resets.
  * ------------------------------------------------------------------------- */
 enum {
   VIT_K_EMBED = 0,
@@ -224,7 +248,8 @@ enum {
   VIT_K_DOWN = 7,
   VIT_K_GATHER = 8,
   VIT_K_ALIGNER = 9,
-  VIT_K_COUNT = 10,
+  VIT_K_MERGE = 10, /* the row copies of vit_merge_image_embeddings */
+  VIT_K_COUNT = 11,
 };
 vit_status vit_profile_enable(int32_t kernel_class, int32_t on);
 vit_status vit_profile_read(int32_t kernel_class, double* total_ms, int64_t* launches);

@@ -93,6 +93,23 @@ def test_host_validation_errors(lib):
     assert lib.vit_gemm(0, 0, 8, 16, 16, None, 16, 16, 8, 1, 1, 16, None) == _lib.VIT_E_ARG  # misaligned
 
 
+def test_merge_host_validation(lib):
+    assert lib.vit_merge_workspace_bytes(-1) == 0
+    assert lib.vit_merge_workspace_bytes(1 << 31) == 0
+    assert lib.vit_merge_workspace_bytes(0) == 256  # never 0, which means an error
+    # one int32 count per 256 positions, rounded up to 256 bytes
+    assert lib.vit_merge_workspace_bytes(256 * 64) == 256
+    assert lib.vit_merge_workspace_bytes(256 * 64 + 1) == 512
+    m = lib.vit_merge_image_embeddings
+    assert m(7, None, 10, 64, None, None, 0, None, None, None, 0, None) == _lib.VIT_E_ARG
+    assert m(0, None, 10, 63, None, None, 0, None, None, None, 0, None) == _lib.VIT_E_SHAPE
+    assert m(1, None, 10, 2, None, None, 0, None, None, None, 0, None) == _lib.VIT_E_SHAPE
+    assert m(0, None, -1, 64, None, None, 0, None, None, None, 0, None) == _lib.VIT_E_SHAPE
+    assert m(0, None, 10, 64, None, None, 0, None, None, None, 0, None) == _lib.VIT_E_ARG
+    assert m(0, 256, 10, 64, 256, None, 3, 256, None, 256, 4096, None) == _lib.VIT_E_ARG
+    assert m(0, 264, 10, 64, 256, 256, 3, 256, None, 256, 4096, None) == _lib.VIT_E_ARG
+
+
 def test_pixel_input_workspace(lib):
     # fp32 pixel input needs a buffer for the cut patches; bf16 reuses the padded one
     tiny = configs.get(0)

@@ -17,7 +17,7 @@ VIT_NO_ALIGNER, VIT_OUT_NLAYOUT, VIT_IN_PIXELS = 1, 2, 4
 VIT_MAX_IMAGES = 128
 VIT_EPI_STORE, VIT_EPI_STORE_F32, VIT_EPI_ADD_F32, VIT_EPI_SWIGLU = 0, 1, 2, 3
 KERNEL_CLASSES = ["embed", "rmsnorm", "qkv", "rope", "attn", "outproj", "gateup", "down",
-                  "gather", "aligner"]
+                  "gather", "aligner", "merge"]
 
 c_i32, c_i64, c_f32, c_vp, c_size = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                      ctypes.c_void_p, ctypes.c_size_t)
@@ -58,6 +58,9 @@ SIGNATURES = {
     "vit_gemm": (c_i32, [c_i32, c_i32, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64,
                          c_i64, c_vp]),
     "vit_aligner_gather": (c_i32, [c_i32, c_vp, P_i32, c_i32, c_i32, c_vp, c_vp]),
+    "vit_merge_workspace_bytes": (c_size, [c_i64]),
+    "vit_merge_image_embeddings": (c_i32, [c_i32, c_vp, c_i64, c_i32, c_vp, c_vp, c_i64, c_vp,
+                                           c_vp, c_vp, c_size, c_vp]),
     "vit_profile_enable": (c_i32, [c_i32, c_i32]),
     "vit_profile_read": (c_i32, [c_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]),
 }

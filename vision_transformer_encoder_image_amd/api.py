@@ -241,6 +241,44 @@ def aligner_gather(x: torch.Tensor, grids, merge: int = 2) -> torch.Tensor:
     return G
 
 
+def merge_workspace_bytes(positions: int) -> int:
+    n = _lib.load().vit_merge_workspace_bytes(int(positions))
+    if n == 0:
+        _lib.check(_lib.VIT_E_SHAPE, "vit_merge_workspace_bytes")
+    return n
+
+
+def merge_image_embeddings_(embeds: torch.Tensor, types: torch.Tensor, tokens: torch.Tensor,
+                            sentinels: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                            n_image: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """vit_merge_image_embeddings, in place on ``embeds`` [..., hidden].
+
+    ``types`` (int32, one code per row of embeds: 0 START, 1 IMAGE, 2 NEWLINE,
+    3 END, other text), ``tokens`` [n_tokens, hidden], ``sentinels`` [3, hidden]
+    (start, newline, end).  ``n_image`` (int32 [1], optional) receives the number
+    of IMAGE positions.
+    """
+    _require_cuda(embeds, types, tokens, sentinels, ws, n_image)
+    if types.dtype != torch.int32 or (n_image is not None and n_image.dtype != torch.int32):
+        raise ValueError("types and n_image must be int32")
+    if not (embeds.dtype == tokens.dtype == sentinels.dtype):
+        raise ValueError("embeds, tokens and sentinels must share one dtype")
+    hidden = embeds.shape[-1]
+    positions = embeds.numel() // hidden if hidden else 0
+    if types.numel() != positions or tokens.shape[-1] != hidden or tuple(sentinels.shape) != (3, hidden):
+        raise ValueError("shape mismatch between embeds, types, tokens and sentinels")
+    code = _lib.VIT_BF16 if embeds.dtype == torch.bfloat16 else _lib.VIT_F32
+    need = merge_workspace_bytes(positions)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=embeds.device)
+    st = _lib.load().vit_merge_image_embeddings(
+        code, embeds.data_ptr(), positions, hidden, types.data_ptr(), tokens.data_ptr(),
+        tokens.shape[0], sentinels.data_ptr(), _ptr(n_image), ws.data_ptr(), ws.numel(),
+        _stream(embeds.device))
+    _lib.check(st, "vit_merge_image_embeddings")
+    return embeds
+
+
 def profile_enable(kernel: str, on: bool = True) -> None:
     _lib.check(_lib.load().vit_profile_enable(_lib.KERNEL_CLASSES.index(kernel), int(on)),
                "vit_profile_enable")

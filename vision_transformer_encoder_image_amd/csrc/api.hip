@@ -613,6 +613,39 @@ vit_status vit_aligner_gather(int32_t dtype, const void* x, const int32_t* grid_
   return hip_check(launch_gather(dtype, x, desc, d, 2, G, (hipStream_t)stream), "gather");
 }
 
+size_t vit_merge_workspace_bytes(int64_t positions) {
+  if (positions < 0 || positions >= (1LL << 31)) {
+    fail(VIT_E_SHAPE, "positions %lld out of range [0, 2^31)", (long long)positions);
+    return 0;
+  }
+  return merge_workspace_bytes(positions);
+}
+
+vit_status vit_merge_image_embeddings(int32_t dtype, void* embeds, int64_t positions,
+                                      int32_t hidden, const int32_t* types, const void* tokens,
+                                      int64_t n_tokens, const void* sentinels, int32_t* n_image,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != VIT_BF16 && dtype != VIT_F32) return fail(VIT_E_ARG, "bad dtype");
+  if (positions < 0 || positions >= (1LL << 31) || n_tokens < 0 || n_tokens >= (1LL << 31))
+    return fail(VIT_E_SHAPE, "positions / n_tokens out of range [0, 2^31)");
+  const int64_t row_bytes = (int64_t)hidden * (int64_t)esize(dtype);
+  if (hidden <= 0 || row_bytes % 16) return fail(VIT_E_SHAPE, "hidden %d: row bytes must be %% 16", hidden);
+  if (positions > 0 && (!embeds || !types || !sentinels))
+    return fail(VIT_E_ARG, "NULL pointer");
+  if (n_tokens > 0 && !tokens) return fail(VIT_E_ARG, "tokens is NULL");
+  if (((uintptr_t)embeds | (uintptr_t)tokens | (uintptr_t)sentinels) & 15)
+    return fail(VIT_E_ARG, "rows must be 16-byte aligned");
+  const size_t need = merge_workspace_bytes(positions);
+  if (!ws || ws_bytes < need)
+    return fail(VIT_E_WORKSPACE, "merge workspace %zu < %zu", ws ? ws_bytes : (size_t)0, need);
+  hipStream_t s = (hipStream_t)stream;
+  VIT_HIP(launch_merge_rank(types, positions, n_image, ws, s), "merge ranks");
+  ProfScope ps(VIT_K_MERGE, s);
+  return hip_check(launch_merge_copy(embeds, positions, row_bytes, types, tokens, n_tokens,
+                                     sentinels, ws, s),
+                   "merge copy");
+}
+
 vit_status vit_profile_enable(int32_t cls, int32_t on) {
   if (cls < 0 || cls >= VIT_K_COUNT) return fail(VIT_E_ARG, "bad kernel class %d", cls);
   Prof& p = prof();

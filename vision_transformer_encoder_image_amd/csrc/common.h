@@ -220,3 +220,12 @@ hipError_t launch_zero_cols(int dtype, void* buf, int64_t rows, int64_t ld, int6
 hipError_t launch_layout(int grid_h, int grid_w, int merge, int32_t* perm, int32_t* nl_type,
                          int32_t* nl_src, hipStream_t s);
 hipError_t launch_nl_rowmap(const VarlenDesc& d, int merge, int32_t* rowmap, hipStream_t s);
+// image tokens and sentinel rows into a text embedding stream (merge.hip)
+size_t merge_workspace_bytes(int64_t positions);
+// group counts of IMAGE positions, scanned in place in ws; total to n_image (optional)
+hipError_t launch_merge_rank(const int32_t* types, int64_t positions, int32_t* n_image, void* ws,
+                             hipStream_t s);
+// the row copies, using the scanned counts left in ws by launch_merge_rank
+hipError_t launch_merge_copy(void* embeds, int64_t positions, int64_t row_bytes,
+                             const int32_t* types, const void* tokens, int64_t n_tokens,
+                             const void* sentinels, const void* ws, hipStream_t s);
