@@ -69,7 +69,8 @@ def test_gemm_full_qkv_shape_sampled_rows():
 BIG_GEMMS = [((2048, 2304, 1024), "store"), ((4096, 3456, 1152), "store"),
              ((9216, 4096, 1024), "store"), ((4096, 4304, 1152), "swiglu"),
              ((4096, 1152, 4352), "add_f32"), ((9216, 1024, 2816), "add_f32"),
-             ((3562, 2816, 1024), "swiglu")]
+             ((3562, 2816, 1024), "swiglu"), ((3562, 1024, 1024), "add_f32"),
+             ((1024, 4096, 4608), "store")]
 
 
 @pytest.mark.gpu

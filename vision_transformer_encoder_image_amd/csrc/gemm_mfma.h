@@ -4,7 +4,7 @@
 #include "common.h"
 
 enum GemmMfmaCfg {
-  GEMM_MFMA_128x128 = 0,     // 4 waves of 64x64, 4 LDS stages of BK 64 (128 KB)
+  GEMM_MFMA_128x128 = 0,     // 8 waves of 32x64, 4 LDS stages of BK 64 (128 KB)
   GEMM_MFMA_256x128_W8 = 1,  // 8 waves of 64x64, 3 stages of BK 64 (144 KB)
   GEMM_MFMA_256x256_W8 = 2,  // 8 waves of 128x64, 4 stages of BK 32 (128 KB)
   GEMM_MFMA_192x256 = 3,     // 4 waves of 96x128 (accumulators in AGPRs), 4 stages of BK 32 (112 KB)

@@ -665,7 +665,7 @@ hipError_t mfma_epi(int epi, const GemmArgs& g, hipStream_t s) {
 
 hipError_t launch_gemm_mfma(int cfg, int epi, const GemmArgs& g, hipStream_t s) {
   switch (cfg) {
-    case GEMM_MFMA_128x128: return mfma_epi<128, 128, 64, 2, 2, 4>(epi, g, s);
+    case GEMM_MFMA_128x128: return mfma_epi<128, 128, 64, 4, 2, 4>(epi, g, s);
     case GEMM_MFMA_256x128_W8: return mfma_epi<256, 128, 64, 4, 2, 3>(epi, g, s);
     case GEMM_MFMA_256x256_W8: return mfma_epi<256, 256, 32, 2, 4, 4>(epi, g, s);
     case GEMM_MFMA_192x256: return mfma_epi<192, 256, 32, 2, 2, 4>(epi, g, s);
