@@ -254,16 +254,17 @@ bool pipe_eligible(const GemmArgs& g) {
 // per flop, relative to a 4-wave 128x128 tile, the 8-wave 128x128 tile is
 // ~1.13x, the 8-wave 256x128 tile ~1.18x, the 4-wave 192x256 tile ~1.26x and
 // the 8-wave 256x256 tile ~1.57x as efficient; with the fp32 read-modify-write
-// epilogue, whose traffic grows with the tile, 1.04x / 1.1x / 1.2x / 1.25x.
-// The 4-wave 128x128 tile is not built: the 8-wave one was never slower.  The
-// folded-RMSNorm producer needs 64-column wave sub-tiles (not 192x256).
+// epilogue, whose traffic grows with the tile, 1.04x / 1.1x / 1.2x, and the
+// 256x256 tile (which spills with it) is not used.  The 4-wave 128x128 tile is
+// not built: the 8-wave one was never slower.  The folded-RMSNorm producer
+// needs 64-column wave sub-tiles (not 192x256).
 int gemm_mfma_choice(int epilogue, bool norm_producer, int64_t M, int64_t N) {
   const bool dual = epilogue == VIT_EPI_SWIGLU;
   const bool rmw = epilogue == VIT_EPI_ADD_F32;
   struct Opt { int cfg, bm, bn; double eff; bool ok; };
   const Opt opts[] = {{GEMM_MFMA_128x128, 128, 128, rmw ? 1.04 : 1.13, true},
                       {GEMM_MFMA_256x128_W8, 256, 128, rmw ? 1.1 : 1.18, true},
-                      {GEMM_MFMA_256x256_W8, 256, 256, rmw ? 1.25 : 1.57, true},
+                      {GEMM_MFMA_256x256_W8, 256, 256, 1.57, !rmw},
                       {GEMM_MFMA_192x256, 192, 256, rmw ? 1.2 : 1.26, !norm_producer}};
   int best = GEMM_MFMA_128x128;
   double best_cost = 1e300;

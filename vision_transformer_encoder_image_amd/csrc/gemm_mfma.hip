@@ -166,6 +166,29 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
 #pragma unroll
     for (int j = 0; j < BJ; ++j) acc[i][j] = f32x16{};
 
+  // fp32 residual add: the rows to add to are loaded into registers right
+  // after the copies of the last K-tile are issued, so their reads overlap the
+  // MFMAs of the last STAGES-1 K-tiles instead of following them.  Those
+  // loads are younger than every copy; the waits of the last K-tiles count
+  // them (kPreLoads).  Needs the last copies issued inside the loop (nk >=
+  // STAGES), no row map, and at most 32 registers of rows per lane (more
+  // would spill with two waves per SIMD).
+  constexpr bool kPre = EPI == VIT_EPI_ADD_F32 && BI * BJ <= 2 && STAGES <= 4;
+  constexpr int kPreLoads = kPre ? BI * BJ * 4 : 0;
+  const bool pre_on = kPre && nk >= STAGES && g.rowmap == nullptr;
+  f32x4 pre[kPre ? BI : 1][kPre ? BJ : 1][4];
+  const int c4 = 4 * (lane >> 5);
+#define W_PRELOAD()                                                                     \
+  do {                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < (kPre ? BI : 0); ++i) {                       \
+      const int m_ = min(m0 + wm * TM + i * 32 + (lane & 31), M - 1);                  \
+      _Pragma("unroll") for (int j = 0; j < BJ; ++j)                                    \
+      _Pragma("unroll") for (int gq = 0; gq < 4; ++gq) pre[i][j][gq] =                  \
+          *reinterpret_cast<const f32x4*>((const float*)g.C + (int64_t)m_ * g.ldc +     \
+                                          min(n0 + wn * TN + j * 32 + 8 * gq + c4, N - 4)); \
+    }                                                                                   \
+  } while (0)
+
   bf16x8 af[2][BI], bfr[2][BJ];
 #define W_LOAD_FRAGS(buf, stage, ks)                                                    \
   do {                                                                                  \
@@ -199,6 +222,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
       }                                                                                 \
       sched_fence();                                                                    \
     }                                                                                   \
+    if (kPre && pre_on && (kt_) == nk - 1) W_PRELOAD();                                 \
+    sched_fence();                                                                      \
   } while (0)
 
   // RMSNorm consumer: thread t < BM reads the partial sums of tile row t before
@@ -250,10 +275,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
     /* barrier also retires every wave's reads of K-tile kt-1, whose buffer */          \
     /* the next copy overwrites */                                                      \
     if ((kt) + 1 < nk) {                                                                \
-      if ((kt) + STAGES - 1 < nk)                                                       \
+      if ((kt) + STAGES - 1 < nk) {                                                     \
         wait_vmcnt<(STAGES - 3) * NI>();                                                \
-      else                                                                              \
+      } else if (pre_on) { /* every copy issued, then the residual loads */             \
+        if (STAGES >= 4 && (kt) + 3 == nk)                                              \
+          wait_vmcnt<(STAGES >= 4 ? NI : 0) + kPreLoads>();                             \
+        else                                                                            \
+          wait_vmcnt<kPreLoads>();                                                      \
+      } else {                                                                          \
         wait_vmcnt<0>();                                                                \
+      }                                                                                 \
     }                                                                                   \
     lds_barrier();                                                                      \
     /* unconditional (after the last K-tile it reads a stale, in-bounds */              \
@@ -286,12 +317,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
 #undef W_LOAD_FRAGS
 #undef W_MFMAS
 #undef W_MFMAS_COPY
+#undef W_PRELOAD
 #undef W_ISSUE
 #undef W_COPY1
 
   // ---- epilogue: acc[i][j] lane holds row (lane & 31) of block i and, for
   // gq = 0..3, columns 8gq + 4*(lane >> 5) .. +3 of block j ----
-  const int c4 = 4 * fh;
   constexpr bool kF32Out = (EPI == VIT_EPI_STORE_F32 || EPI == VIT_EPI_ADD_F32);
   if (!kF32Out && g.ss_in) {
     // RMSNorm consumer: output rows times the rstd computed at kernel start
@@ -321,7 +352,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
     const int n = n0 + wn * TN;
     const bool cols_ok = n < N;
     char* st = (char*)smem + wave * (TM * UROWB);
-    auto produce = [&](auto with_rowmap) __attribute__((always_inline)) {
+    auto produce = [&](auto with_rowmap, auto with_pre) __attribute__((always_inline)) {
       int64_t orow[BI];
 #pragma unroll
       for (int i = 0; i < BI; ++i) {
@@ -349,7 +380,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
               const int i = i0 + ii;
 #pragma unroll
               for (int e = 0; e < 4; ++e) v[ii][j][gq][e] = acc[i][j][4 * gq + e];
-              if constexpr (EPI == VIT_EPI_ADD_F32)
+              if constexpr (EPI == VIT_EPI_ADD_F32 && with_pre)
+                v[ii][j][gq] += pre[kPre ? i : 0][kPre ? j : 0][gq];
+              else if constexpr (EPI == VIT_EPI_ADD_F32)
                 v[ii][j][gq] += *reinterpret_cast<const f32x4*>(
                     (const float*)g.C + orow[i] * g.ldc + min(n + j * 32 + 8 * gq + c4, N - 4));
             }
@@ -384,9 +417,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
       }
     };
     if (has_rowmap)
-      produce(std::true_type{});
+      produce(std::true_type{}, std::false_type{});
+    else if (kPre && pre_on)
+      produce(std::false_type{}, std::bool_constant<kPre>{});
     else
-      produce(std::false_type{});
+      produce(std::false_type{}, std::false_type{});
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staged writes done
     asm volatile("" ::: "memory");
     constexpr int URPI = 64 / UCPR;  // staged rows per read instruction
@@ -527,7 +562,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
 
   // direct stores (fp32 residual add, outputs too wide to stage, the
   // transposed v columns); all loads first, then all stores
-  auto direct = [&](auto with_rowmap) __attribute__((always_inline)) {
+  auto direct = [&](auto with_rowmap, auto with_pre) __attribute__((always_inline)) {
     int64_t orow[BI];
     int vpos_i[BI];
 #pragma unroll
@@ -549,8 +584,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
               const int n = min(n0 + wn * TN + j * 32 + 8 * gq + c4, N - 4);
-              c[ii][j][gq] =
-                  *reinterpret_cast<const f32x4*>((const float*)g.C + orow[i0 + ii] * g.ldc + n);
+              if constexpr (with_pre)
+                c[ii][j][gq] = pre[kPre ? i0 + ii : 0][kPre ? j : 0][gq];
+              else
+                c[ii][j][gq] =
+                    *reinterpret_cast<const f32x4*>((const float*)g.C + orow[i0 + ii] * g.ldc + n);
             }
 #pragma unroll
         for (int ii = 0; ii < GI; ++ii)
@@ -617,9 +655,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
     }
   };
   if (has_rowmap)
-    direct(std::true_type{});
+    direct(std::true_type{}, std::false_type{});
+  else if (kPre && pre_on)
+    direct(std::false_type{}, std::bool_constant<kPre>{});
   else
-    direct(std::false_type{});
+    direct(std::false_type{}, std::false_type{});
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool DUAL>
