@@ -22,6 +22,8 @@
 // softmax in base e.  Used by the single-precision mode.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace {
@@ -247,10 +249,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
 // The k-slot order of P^T is the S^T accumulator order; the V^T key-slot
 // permutation makes the matching 8 keys of a lane one contiguous 16-byte read.
 // Software pipelining: every step reads the K fragments of tile t+1 and the V^T
-// fragments of tile t from LDS, runs the softmax of tile t (whose S^T came from
-// the previous step) while those reads are in flight, then issues the S^T
-// MFMAs of tile t+1 and the O^T MFMAs of tile t as one interleaved run.  The softmax reference max is raised only when some lane's max
-// grows by more than 2^8 (exact after the final 1/sum; p stays <= 256).
+// fragments of tile t from LDS and runs the softmax of one tile and the MFMAs
+// (S^T of tile t+1, O^T of tile t).  The one barrier per tile keeps the waves in
+// step, so the two waves that share a SIMD take opposite orders (softmax first /
+// MFMAs first): while one works on the vector ALU the other feeds the matrix
+// core.  The softmax reference max is raised only when some lane's max grows by
+// more than 2^8 (exact after the final 1/sum; p stays <= 256).
 constexpr int VT_BQ = 256, VT_BKV = 64, VT_STAGES = 4, VT_WAVES = 8;
 constexpr float VT_RESCALE_LOG2 = 8.0f;
 
@@ -335,8 +339,8 @@ __global__ __launch_bounds__(64 * VT_WAVES, 1) void attn_vt_kernel(const bf16* _
   }
 
   f32x16 o[2] = {f32x16{}, f32x16{}};
-  f32x16 sc[2], sn[2];
-  bf16x8 kf[8], vf[8];
+  f32x16 sc[2];
+  bf16x8 kf[8], vf[8], pf[4];
   float mref = -INFINITY, lsum = 0.f;
   const int nkv = (P + VT_BKV - 1) / VT_BKV;
   constexpr int CPS = 16 / VT_WAVES;  // copies per stage per wave
@@ -364,26 +368,9 @@ __global__ __launch_bounds__(64 * VT_WAVES, 1) void attn_vt_kernel(const bf16* _
     for (int kb = 0; kb < 2; ++kb)
       sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * ks + kb], qf[ks], sc[kb], 0, 0, 0);
 
-  for (int t = 0; t < nkv; ++t) {
-    // tile t+1 must have landed; the barrier also retires all reads of tile t-1,
-    // whose buffer the next copy overwrites
-    if (t + 1 < nkv) {
-      if (t + 2 < nkv)
-        wait_vmcnt<CPS>();
-      else
-        wait_vmcnt<0>();
-    }
-    lds_barrier();
-    if (t + 3 < nkv) VIT_ATT_ISSUE(t + 3);
-    // all LDS reads of this step go out first (K of tile t+1 -- after the last
-    // tile a stale, in-bounds buffer whose products are discarded -- and V of
-    // tile t); the softmax below covers their latency, and one wait then
-    // frees a run of 16 MFMAs
-    VIT_ATT_LOADK((t + 1) % VT_STAGES);
-    VIT_ATT_LOADV(t % VT_STAGES);
-    sched_fence();
-
-    const int kv0 = t * VT_BKV;
+  // online softmax of the scores in sc (keys kv0 .. kv0+63) into pf; rescales
+  // o and lsum when the reference max moves
+  auto softmax_tile = [&](int kv0) __attribute__((always_inline)) {
     if (kv0 + VT_BKV > P) {  // ragged last tile of the image
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -406,7 +393,7 @@ __global__ __launch_bounds__(64 * VT_WAVES, 1) void attn_vt_kernel(const bf16* _
       for (int db = 0; db < 2; ++db) o[db] *= alpha;
     }
     const float nmc = -mref * c;
-    bf16x8 pf[4];  // P^T fragment of key slots 32 kb + 16 ks2 + 8 fh .. +7
+    // P^T fragment of key slots 32 kb + 16 ks2 + 8 fh .. +7
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -417,24 +404,70 @@ __global__ __launch_bounds__(64 * VT_WAVES, 1) void attn_vt_kernel(const bf16* _
           lsum += p;
           pf[2 * kb + ks2][j] = f2bf(p);
         }
-    wait_lgkmcnt<0>();
-    sched_fence();
-    // four independent chains (S^T blocks of tile t+1, O^T blocks) interleaved
-    sn[0] = f32x16{};
-    sn[1] = f32x16{};
+  };
+  // S^T of the next tile (K fragments kf) into sc, and O^T += V^T . P^T of
+  // this tile (V fragments vf, P^T fragments pf); the S^T MFMAs go first so
+  // that their results are ready while the O^T ones still run
+  auto mfma_tile = [&]() __attribute__((always_inline)) {
+    f32x16 sn[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * x], qf[x], sn[0], 0, 0, 0);
+      sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * x + 1], qf[x], sn[1], 0, 0, 0);
+    }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int kb = x >> 1, ks2 = x & 1;
-      sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * x], qf[x], sn[0], 0, 0, 0);
-      sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * x + 1], qf[x], sn[1], 0, 0, 0);
       o[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 * kb + 2 * ks2], pf[x], o[0], 0, 0, 0);
       o[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 * kb + 2 * ks2 + 1], pf[x], o[1], 0, 0,
                                                      0);
     }
-    sched_fence();
     sc[0] = sn[0];
     sc[1] = sn[1];
-  }
+  };
+
+  // Two phases, one per half of the workgroup (waves w and w + 4 share a SIMD):
+  // waves 0-3 run the softmax of tile t and then its MFMAs; waves 4-7 run the
+  // MFMAs of tile t first and the softmax of tile t+1 after them.  Both halves
+  // meet at the one barrier per tile, after which one wave of every SIMD works
+  // on the vector ALU while the other keeps the matrix cores busy.
+  auto run = [&](auto mfma_first) __attribute__((always_inline)) {
+    if constexpr (mfma_first) softmax_tile(0);
+    for (int t = 0; t < nkv; ++t) {
+      // tile t+1 must have landed; the barrier also retires all reads of tile
+      // t-1, whose buffer the next copy overwrites
+      if (t + 1 < nkv) {
+        if (t + 2 < nkv)
+          wait_vmcnt<CPS>();
+        else
+          wait_vmcnt<0>();
+      }
+      lds_barrier();
+      if (t + 3 < nkv) VIT_ATT_ISSUE(t + 3);
+      // K of tile t+1 (after the last tile a stale, in-bounds buffer whose
+      // products are discarded) and V of tile t
+      VIT_ATT_LOADK((t + 1) % VT_STAGES);
+      VIT_ATT_LOADV(t % VT_STAGES);
+      sched_fence();
+      if constexpr (mfma_first) {
+        wait_lgkmcnt<0>();
+        sched_fence();
+        mfma_tile();
+        sched_fence();
+        if (t + 1 < nkv) softmax_tile((t + 1) * VT_BKV);
+      } else {
+        softmax_tile(t * VT_BKV);  // covers the latency of the LDS reads
+        wait_lgkmcnt<0>();
+        sched_fence();
+        mfma_tile();
+      }
+      sched_fence();
+    }
+  };
+  if (wave < VT_WAVES / 2)
+    run(std::false_type{});
+  else
+    run(std::true_type{});
 #undef VIT_ATT_ISSUE
 #undef VIT_ATT_LOADK
 #undef VIT_ATT_LOADV
