@@ -31,10 +31,14 @@ from .vit import (  # noqa: F401
     block,
     encode,
     encode_varlen,
+    gelu,
+    layernorm,
     linear,
     mlp,
     nlayout,
     patch_embed,
+    patch_merger,
+    patch_merger_param_count,
     patchify,
     rmsnorm,
     rope_freqs,

@@ -11,6 +11,8 @@ Sources (web pages):
          table with grids and "N-layout" / "Permutation" columns).
   [HF]   summary page of the HF DeepSeek-V4-Flash-Vision-Exp text model (the
          ``rotate_half`` pattern computed in fp32 and cast back).
+  [NVFP4] model page of DeepSeek-V4-Flash-Vision-NVFP4 (the PatchMerger projector:
+         2x2 groups of 1152-dim MoonViT patches -> 4608 -> 4096, 40,119,040 parameters).
 """
 from __future__ import annotations
 
@@ -39,6 +41,12 @@ READINGS = {
                         "order), START/NEWLINE/END take the image_start/image_newline/"
                         "image_end embeddings, -1 (text) and any other type stay as they are; "
                         "image_pad is not used by this layout",
+    "patch_merger": "the 40,119,040 projector parameters decompose exactly as a norm over the "
+                    "1152 patch features with weight and bias (2*1152), Linear(4608, 4608) with "
+                    "bias and Linear(4608, 4096) with bias; so: LayerNorm (mean and variance "
+                    "over the features, eps 1e-6 inside the root) on every patch, the aligner's "
+                    "2x2 gather, the first linear, GELU in its erf form (the activation is not "
+                    "named), the second linear",
 }
 
 NL_START, NL_IMAGE, NL_NEWLINE, NL_END = 0, 1, 2, 3
@@ -248,6 +256,43 @@ def aligner_gather(x, gh, gw, merge=2):
 def aligner(x, gh, gw, w, merge=2, dtype=np.float64):
     """[VIS] DeepseekV4VisionAligner.forward: 2x2 gather, then the linear map to LLM width."""
     return linear(aligner_gather(_f(x, dtype), gh, gw, merge), w, dtype)
+
+
+def layernorm(x, w, b, eps=1e-6, dtype=np.float64):
+    """Norm of the PatchMerger projector ([NVFP4]), reading "patch_merger":
+    y = (x - mean(x)) / sqrt(var(x) + eps) * w + b over the last axis, with the
+    population variance (mean of squared deviations)."""
+    x = _f(x, dtype)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * _f(w, dtype) + _f(b, dtype)
+
+
+def gelu(x, dtype=np.float64):
+    """GELU in its erf form, x * Phi(x) = x/2 * (1 + erf(x / sqrt(2))) (reading
+    "patch_merger": the projector's activation is not named on the pages)."""
+    from scipy.special import erf
+
+    x = _f(x, dtype)
+    return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+def patch_merger(x, gh, gw, p, eps=1e-6, merge=2, dtype=np.float64):
+    """[NVFP4] PatchMerger projector for one image, reading "patch_merger": LayerNorm
+    on every patch of ``x`` ``[gh*gw, d]``, the 2x2 gather of the aligner (same group
+    order), Linear(4d, hidden) + bias, GELU, Linear(hidden, out) + bias.  ``p`` holds
+    ln_w, ln_b [d]; w1 [hidden, 4d], b1 [hidden]; w2 [out, hidden], b2 [out]."""
+    n = layernorm(x, p["ln_w"], p["ln_b"], eps, dtype)
+    g = aligner_gather(n, gh, gw, merge)
+    h = gelu(linear(g, p["w1"], dtype) + _f(p["b1"], dtype), dtype)
+    return linear(h, p["w2"], dtype) + _f(p["b2"], dtype)
+
+
+def patch_merger_param_count(d, hidden, out, merge=2):
+    """Parameters of the projector of ``patch_merger``: norm weight and bias, then
+    the two biased linear maps."""
+    m2 = merge * merge
+    return 2 * d + hidden * m2 * d + hidden + out * hidden + out
 
 
 def nlayout(gh, gw, merge=2):

@@ -553,3 +553,103 @@ def test_merge_embeddings_with_nlayout_places_tokens_in_order():
                                                              oracle.NL_END].index(types[q])])
     # every token consumed exactly once
     assert (types == oracle.NL_IMAGE).sum() == tok_off
+
+
+# ---------------------------------------------------------------- PatchMerger projector
+def _ln_gelu_fixture():
+    ln, ge = [], []
+    for line in open(os.path.join(GOLDEN, "layernorm_gelu_small.txt")):
+        if line.startswith("layernorm"):
+            parts = [list(map(float, p.split())) for p in line[len("layernorm"):].split("|")]
+            ln.append((np.array(parts[0]), np.array(parts[1]), np.array(parts[2]), parts[3][0],
+                       np.array(parts[4])))
+        elif line.startswith("gelu"):
+            x, y = map(float, line.split()[1:])
+            ge.append((x, y))
+    return ln, ge
+
+
+def test_layernorm_golden():
+    ln, _ = _ln_gelu_fixture()
+    assert len(ln) == 3
+    for x, w, b, eps, want in ln:
+        np.testing.assert_allclose(oracle.layernorm(x, w, b, eps), want, rtol=1e-14, atol=1e-14)
+
+
+def test_layernorm_shift_scale_invariance_and_moments():
+    rng = _rng(31)
+    x = rng.standard_normal((5, 16))
+    one, zero = np.ones(16), np.zeros(16)
+    y = oracle.layernorm(x, one, zero, eps=0.0)
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-14)
+    np.testing.assert_allclose((y ** 2).mean(axis=1), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(oracle.layernorm(3.5 * x - 2.0, one, zero, eps=0.0), y, rtol=1e-12,
+                               atol=1e-12)
+    w, b = rng.standard_normal(16), rng.standard_normal(16)
+    np.testing.assert_allclose(oracle.layernorm(x, w, b, eps=0.0), y * w + b, rtol=1e-13, atol=1e-13)
+
+
+def test_gelu_golden_and_odd_identity():
+    _, ge = _ln_gelu_fixture()
+    assert len(ge) == 7
+    for x, want in ge:
+        assert abs(float(oracle.gelu(np.array([x]))[0]) - want) < 1e-14
+    x = np.linspace(-6, 6, 97)
+    # x Phi(x) - (-x) Phi(-x) = x (Phi(x) + Phi(-x)) = x
+    np.testing.assert_allclose(oracle.gelu(x) - oracle.gelu(-x), x, rtol=1e-13, atol=1e-13)
+
+
+def test_patch_merger_param_count_is_the_pages():
+    # the projector of the NVFP4 model page: 2x2 groups of 1152-dim patches, 4608 -> 4096
+    assert oracle.patch_merger_param_count(1152, 4608, 4096) == 40_119_040
+    # the count needs both norm parameters and both biases
+    assert oracle.patch_merger_param_count(1152, 4608, 4096) - 1152 != 40_119_040
+
+
+def test_patch_merger_scalar_loops():
+    """Whole projector by scalar loops on a 2x4 grid: each patch (r, c) goes to merged
+    token (r//2)*(gw//2) + c//2, slot 2*(r%2) + c%2 (placed directly, not through the
+    gather of the oracle)."""
+    rng = _rng(32)
+    gh, gw, d, hid, out = 2, 4, 3, 5, 2
+    x = rng.standard_normal((gh * gw, d))
+    p = {"ln_w": rng.standard_normal(d), "ln_b": rng.standard_normal(d),
+         "w1": rng.standard_normal((hid, 4 * d)), "b1": rng.standard_normal(hid),
+         "w2": rng.standard_normal((out, hid)), "b2": rng.standard_normal(out)}
+    eps = 1e-6
+    T = gh * gw // 4
+    g = [[0.0] * (4 * d) for _ in range(T)]
+    for r in range(gh):
+        for c in range(gw):
+            row = x[r * gw + c]
+            mu = sum(row) / d
+            var = sum((v - mu) ** 2 for v in row) / d
+            t, s = (r // 2) * (gw // 2) + c // 2, 2 * (r % 2) + c % 2
+            for k in range(d):
+                g[t][s * d + k] = (row[k] - mu) / math.sqrt(var + eps) * p["ln_w"][k] + p["ln_b"][k]
+    want = np.zeros((T, out))
+    for t in range(T):
+        h = []
+        for j in range(hid):
+            a = p["b1"][j] + sum(p["w1"][j][k] * g[t][k] for k in range(4 * d))
+            h.append(0.5 * a * (1.0 + math.erf(a / math.sqrt(2.0))))
+        for o in range(out):
+            want[t, o] = p["b2"][o] + sum(p["w2"][o][j] * h[j] for j in range(hid))
+    np.testing.assert_allclose(oracle.patch_merger(x, gh, gw, p, eps), want, rtol=1e-12, atol=1e-12)
+
+
+def test_patch_merger_constant_patches_closed_form():
+    """Constant patches normalise to the norm bias, so every merged token is
+    W2 gelu(W1 [b, b, b, b] + b1) + b2."""
+    rng = _rng(33)
+    d, hid, out = 4, 6, 3
+    p = {"ln_w": rng.standard_normal(d), "ln_b": rng.standard_normal(d),
+         "w1": rng.standard_normal((hid, 4 * d)), "b1": rng.standard_normal(hid),
+         "w2": rng.standard_normal((out, hid)), "b2": rng.standard_normal(out)}
+    x = np.full((4 * 6, d), 2.5)
+    a = p["w1"] @ np.tile(p["ln_b"], 4) + p["b1"]
+    h = np.array([0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0))) for v in a])
+    want = p["w2"] @ h + p["b2"]
+    got = oracle.patch_merger(x, 4, 6, p)
+    assert got.shape == (6, out)
+    np.testing.assert_allclose(got, np.tile(want, (6, 1)), rtol=1e-12, atol=1e-12)
