@@ -31,7 +31,8 @@ _GEMM_SRC = ("common.h", "gemm_bf16.hip", "gemm_mfma.h", "gemm_mfma.hip")
 KERNEL_SOURCE = {"qkv": _GEMM_SRC, "outproj": _GEMM_SRC, "gateup": _GEMM_SRC, "down": _GEMM_SRC,
                  "embed": _GEMM_SRC, "aligner": _GEMM_SRC, "attn": ("common.h", "attention.hip"),
                  "rmsnorm": ("common.h", "elementwise.hip"), "rope": ("common.h", "elementwise.hip"),
-                 "gather": ("common.h", "elementwise.hip"), "merge": ("common.h", "merge.hip")}
+                 "gather": ("common.h", "elementwise.hip"), "merge": ("common.h", "merge.hip"),
+                 "proj1": _GEMM_SRC}
 
 
 def class_flops(cfg):
@@ -74,7 +75,8 @@ def counter_traffic(kernel_class, workload):
 # kernel-name patterns of each class in rocprofv3 output (SwiGLU is the only
 # dual-B GEMM instantiation, i.e. the template argument list ends in "true>")
 KERNEL_NAME_PATTERN = {"gateup": ("gemm_", ", true>("), "attn": ("attn_vt_kernel", ""),
-                       "rmsnorm": ("rmsnorm_kernel", ""), "merge": ("merge_copy_kernel", "")}
+                       "rmsnorm": ("rmsnorm_kernel", ""), "merge": ("merge_copy_kernel", ""),
+                       "proj1": ("gemm_mfma_kernel", ", 5, false>(")}
 
 
 def _pmc_rows(d):
@@ -241,14 +243,109 @@ def bench_merge(args):
     print(json.dumps(result), flush=True)
 
 
+PROJ_METRIC = "TFLOP/s through the PatchMerger projector (bf16)"
+
+
+def bench_projector(args):
+    """vit_patch_merger on the high-res workload's tower output: one 64x64 grid of
+    1152-dim patches (synthetic bf16 stand-in for the encoder output) -> LayerNorm
+    and 2x2 merge -> 1024 x 4608 -> Linear 4608 -> GELU -> Linear 4096 (the
+    projector shape of the NVFP4 model page).  One step is one projector call."""
+    import torch
+
+    from vision_transformer_encoder_image_amd import api, synth
+
+    dev = "cuda:0"
+    gh = gw = 64
+    dim, hidden, out = 1152, 4608, 4096
+    grids = [(gh, gw)]
+    P = gh * gw
+    T = P // 4
+    x_host = synth.random_array((P, dim), 60, bf16=True)
+    w_host = synth.make_merger_weights(dim, hidden, out, seed=61)
+    x = torch.from_numpy(x_host).to(dev, torch.bfloat16)
+    mw = api.MergerWeights(w_host, device=dev)
+    y = torch.empty((T, out), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(api.merger_workspace_bytes(mw, grids), dtype=torch.uint8, device=dev)
+    flops = {"proj1": 2.0 * T * 4 * dim * hidden, "proj2": 2.0 * T * hidden * out}
+    total = sum(flops.values())
+    for _ in range(max(args.warmup, 1)):
+        api.patch_merger(x, grids, mw, out=y, ws=ws)
+    torch.cuda.synchronize()
+    for k in ("lngather", "proj1", "proj2"):
+        api.profile_enable(k, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        api.patch_merger(x, grids, mw, out=y, ws=ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per = {}
+    for k in ("lngather", "proj1", "proj2"):
+        ms, n = api.profile_read(k)
+        api.profile_enable(k, False)
+        per[k] = ms * 1e3 / max(n, 1)
+    avg = per["proj1"] * 1e-6
+    achieved = flops["proj1"] / avg / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    ln_bytes = P * dim * 2 * 2 + 2 * dim * 4  # rows read and written (bf16), weight and bias
+    result = {
+        "metric": PROJ_METRIC,
+        "value": round(total * args.steps / elapsed / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "projector_64x64_1152", "patches": P, "tokens": T, "dim": dim,
+                   "hidden": hidden, "out": out, "flops_per_step": total},
+        "roofline": {"kernel": "proj1", "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": counter_traffic("proj1", "projector_64x64_1152"),
+                     "avg_launch_us": round(per["proj1"], 3), "flops_per_launch": flops["proj1"]},
+        "breakdown": {"lngather": {"avg_us": round(per["lngather"], 2),
+                                   "gbs": round(ln_bytes / (per["lngather"] * 1e-6) / 1e9, 1)},
+                      "proj1": {"avg_us": round(per["proj1"], 2),
+                                "tflops": round(flops["proj1"] / (per["proj1"] * 1e-6) / 1e12, 1)},
+                      "proj2": {"avg_us": round(per["proj2"], 2),
+                                "tflops": round(flops["proj2"] / (per["proj2"] * 1e-6) / 1e12, 1)}},
+    }
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb, dev)
+    if not args.no_cpu_baseline:
+        import threadpoolctl
+
+        import oracle
+
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        rows, runs, t0 = 2, 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0:  # the top two patch rows: 32 merged tokens
+            oracle.patch_merger(x_host[:rows * gw], rows, gw, w_host)
+            runs += 1
+        dt = time.perf_counter() - t0
+        sample_flops = total * (rows * gw) / P
+        result["cpu_baseline"] = {"value": round(sample_flops * runs / dt / 1e12, 4),
+                                  "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+                                  "sample": f"the top {rows} patch rows ({rows * gw // 4} merged "
+                                            f"tokens), {runs} float64 oracle passes in {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--stage", choices=("encode", "merge"), default="encode",
-                    help="encode: the encoder step; merge: image tokens into the LLM stream")
+    ap.add_argument("--stage", choices=("encode", "merge", "projector"), default="encode",
+                    help="encode: the encoder step; merge: image tokens into the LLM stream; "
+                         "projector: the PatchMerger projector")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -272,6 +369,9 @@ def main():
 
     if args.stage == "merge":
         bench_merge(args)
+        return
+    if args.stage == "projector":
+        bench_projector(args)
         return
 
     import torch

@@ -192,6 +192,8 @@ enum {
   VIT_EPI_STORE_F32 = 1, /* C (float32) = A B^T                      */
   VIT_EPI_ADD_F32 = 2,   /* C (float32) += A B^T (residual, in place)  */
   VIT_EPI_SWIGLU = 3,    /* C (dtype)   = silu(A B^T) * (A B2^T)      */
+  VIT_EPI_BIAS = 4,      /* C (bf16)    = A B^T + bias       (vit_gemm_bias) */
+  VIT_EPI_BIAS_GELU = 5, /* C (bf16)    = gelu(A B^T + bias) (vit_gemm_bias) */
 };
 
 /* C[M, N] = epilogue(A[M, K] . B[N, K]^T): the bias-free linear maps of the block
@@ -206,6 +208,53 @@ vit_status vit_gemm(int32_t dtype, int32_t epilogue, const void* A, int64_t lda,
  * with x [sum P, d] and G [sum P/4, 4d] of dtype (DeepseekV4VisionAligner). */
 vit_status vit_aligner_gather(int32_t dtype, const void* x, const int32_t* grid_hw_host,
                               int32_t n_images, int32_t d, void* G, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * PatchMerger projector (DeepSeek-V4-Flash-Vision-NVFP4 model page): an
+ * alternative to the aligner that merges every 2x2 group of encoder patches
+ * and maps the 4*dim features to the LLM width through two biased linear maps.
+ * The page gives the shapes (1152-dim patches, 4608 -> 4096) and the parameter
+ * count, 40,119,040 = norm weight and bias (2*1152) + Linear(4608, 4608) with
+ * bias + Linear(4608, 4096) with bias; the activation between the linear maps
+ * is not named and is taken as GELU (erf form), the norm as LayerNorm.
+ *   out = gelu(G W1^T + b1) W2^T + b2,  G[t] = concat over the 2x2 group of
+ *   merged token t (order TL, TR, BL, BR, as the aligner) of LayerNorm(x[p]).
+ * bf16 only: x [sum P, dim], w1 [hidden, 4*dim], w2 [out_dim, hidden] and out
+ * [sum P/4, out_dim] bf16 (16-byte aligned); ln_w, ln_b [dim], b1 [hidden],
+ * b2 [out_dim] float32 (16-byte aligned).  dim % 16 == 0 and dim <= 4096,
+ * hidden % 64 == 0, out_dim % 8 == 0.  Grids must be even (VIT_E_ODD_GRID).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t dim;     /* encoder width d (1152 on the page)  */
+  int32_t hidden;  /* first linear's width (4608)         */
+  int32_t out_dim; /* LLM width (4096)                    */
+  float eps;       /* LayerNorm eps (1e-6)                */
+  const float* ln_w;
+  const float* ln_b;
+  const void* w1;
+  const float* b1;
+  const void* w2;
+  const float* b2;
+} vit_merger;
+
+/* Workspace of vit_patch_merger: G [sum P/4, 4*dim] and the GELU output
+ * [sum P/4, hidden], bf16.  0 on bad arguments (see vit_last_error). */
+size_t vit_patch_merger_workspace_bytes(const vit_merger* m, const int32_t* grid_hw_host,
+                                        int32_t n_images);
+vit_status vit_patch_merger(const vit_merger* m, const void* x, const int32_t* grid_hw_host,
+                            int32_t n_images, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Step entry points of the projector, for per-step parity tests:
+ * the LayerNorm + 2x2 gather into G [sum P/4, 4*dim] bf16, and the bias GEMMs
+ * C [M, N] bf16 = A . B^T + bias (VIT_EPI_BIAS) or gelu(A . B^T + bias)
+ * (VIT_EPI_BIAS_GELU), A [M, K] and B [N, K] bf16 with K % 64 == 0, bias [N]
+ * float32. */
+vit_status vit_layernorm_gather(const void* x, const int32_t* grid_hw_host, int32_t n_images,
+                                int32_t dim, const float* ln_w, const float* ln_b, float eps,
+                                void* G, void* stream);
+vit_status vit_gemm_bias(int32_t epilogue, const void* A, int64_t lda, const void* B, int64_t ldb,
+                         const float* bias, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                         void* stream);
 
 /* Image tokens into the LLM input stream (DeepSeek-V4 model page,
  * DeepseekV4Model.merge_image_embeddings): for each position p of a text
@@ -232,8 +281,9 @@ vit_status vit_merge_image_embeddings(int32_t dtype, void* embeds, int64_t posit
 
 /* ---------------------------------------------------------------------------
  * Kernel timing with HIP events (for measurement tools).  When enabled for a
- * kernel class, every launch of that class inside vit_encode(_varlen) and
- * vit_merge_image_embeddings is bracketed by events on the call's stream;
+ * kernel class, every launch of that class inside vit_encode(_varlen),
+ * vit_merge_image_embeddings and vit_patch_merger is bracketed by events on the
+ * call's stream;
  * vit_profile_read synchronises them and returns the summed duration and the
  * launch count, then resets.
  * ------------------------------------------------------------------------- */
@@ -248,8 +298,11 @@ enum {
   VIT_K_DOWN = 7,
   VIT_K_GATHER = 8,
   VIT_K_ALIGNER = 9,
-  VIT_K_MERGE = 10, /* the row copies of vit_merge_image_embeddings */
-  VIT_K_COUNT = 11,
+  VIT_K_MERGE = 10,     /* the row copies of vit_merge_image_embeddings */
+  VIT_K_LNGATHER = 11,  /* vit_patch_merger: LayerNorm + 2x2 gather */
+  VIT_K_PROJ1 = 12,     /* vit_patch_merger: first linear (bias, GELU) */
+  VIT_K_PROJ2 = 13,     /* vit_patch_merger: second linear (bias) */
+  VIT_K_COUNT = 14,
 };
 vit_status vit_profile_enable(int32_t kernel_class, int32_t on);
 vit_status vit_profile_read(int32_t kernel_class, double* total_ms, int64_t* launches);

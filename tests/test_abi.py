@@ -110,6 +110,29 @@ def test_merge_host_validation(lib):
     assert m(0, 264, 10, 64, 256, 256, 3, 256, None, 256, 4096, None) == _lib.VIT_E_ARG
 
 
+def test_projector_host_validation(lib):
+    g = _lib.grid_array([(4, 6)])
+    m = _lib.VitMerger(1152, 4608, 4096, 1e-6, None, None, None, None, None, None)
+    T = 4 * 6 // 4
+    want = (T * 4 * 1152 * 2 + 255) // 256 * 256 + (T * 4608 * 2 + 255) // 256 * 256
+    assert lib.vit_patch_merger_workspace_bytes(ctypes.byref(m), g, 1) == want
+    assert lib.vit_patch_merger_workspace_bytes(ctypes.byref(m), _lib.grid_array([(3, 6)]), 1) == 0
+    assert b"not divisible" in lib.vit_last_error()
+    for dim, hidden, out in ((1160, 4608, 4096), (1152, 4600, 4096), (1152, 4608, 4092), (0, 64, 8)):
+        bad = _lib.VitMerger(dim, hidden, out, 1e-6, None, None, None, None, None, None)
+        assert lib.vit_patch_merger_workspace_bytes(ctypes.byref(bad), g, 1) == 0
+    assert lib.vit_patch_merger(None, None, g, 1, None, None, 0, None) == _lib.VIT_E_ARG
+    assert lib.vit_patch_merger(ctypes.byref(m), None, g, 1, None, None, 0, None) == _lib.VIT_E_ARG
+    assert lib.vit_layernorm_gather(None, g, 1, 1152, None, None, 1e-6, None, None) == _lib.VIT_E_ARG
+    assert lib.vit_layernorm_gather(256, g, 1, 1156, 256, 256, 1e-6, 256, None) == _lib.VIT_E_SHAPE
+    assert lib.vit_gemm_bias(0, 256, 64, 256, 64, 256, 256, 64, 8, 8, 64, None) == _lib.VIT_E_ARG
+    assert lib.vit_gemm_bias(_lib.VIT_EPI_BIAS, 256, 64, 256, 64, None, 256, 64, 8, 8, 64,
+                             None) == _lib.VIT_E_ARG
+    # K must be a multiple of 64 for the MFMA path
+    assert lib.vit_gemm_bias(_lib.VIT_EPI_BIAS, 256, 72, 256, 72, 256, 256, 64, 8, 8, 72,
+                             None) == _lib.VIT_E_SHAPE
+
+
 def test_pixel_input_workspace(lib):
     # fp32 pixel input needs a buffer for the cut patches; bf16 reuses the padded one
     tiny = configs.get(0)

@@ -16,8 +16,9 @@ VIT_BF16, VIT_F32 = 0, 1
 VIT_NO_ALIGNER, VIT_OUT_NLAYOUT, VIT_IN_PIXELS = 1, 2, 4
 VIT_MAX_IMAGES = 128
 VIT_EPI_STORE, VIT_EPI_STORE_F32, VIT_EPI_ADD_F32, VIT_EPI_SWIGLU = 0, 1, 2, 3
+VIT_EPI_BIAS, VIT_EPI_BIAS_GELU = 4, 5
 KERNEL_CLASSES = ["embed", "rmsnorm", "qkv", "rope", "attn", "outproj", "gateup", "down",
-                  "gather", "aligner", "merge"]
+                  "gather", "aligner", "merge", "lngather", "proj1", "proj2"]
 
 c_i32, c_i64, c_f32, c_vp, c_size = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                      ctypes.c_void_p, ctypes.c_size_t)
@@ -39,6 +40,12 @@ class VitWeights(ctypes.Structure):
                 ("final_norm", c_vp), ("aligner", c_vp)]
 
 
+class VitMerger(ctypes.Structure):
+    _fields_ = [("dim", c_i32), ("hidden", c_i32), ("out_dim", c_i32), ("eps", c_f32),
+                ("ln_w", c_vp), ("ln_b", c_vp), ("w1", c_vp), ("b1", c_vp), ("w2", c_vp),
+                ("b2", c_vp)]
+
+
 # name -> (restype, argtypes); every function declared in include/vitenc.h
 SIGNATURES = {
     "vit_status_str": (ctypes.c_char_p, [c_i32]),
@@ -58,6 +65,12 @@ SIGNATURES = {
     "vit_gemm": (c_i32, [c_i32, c_i32, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64,
                          c_i64, c_vp]),
     "vit_aligner_gather": (c_i32, [c_i32, c_vp, P_i32, c_i32, c_i32, c_vp, c_vp]),
+    "vit_patch_merger_workspace_bytes": (c_size, [ctypes.POINTER(VitMerger), P_i32, c_i32]),
+    "vit_patch_merger": (c_i32, [ctypes.POINTER(VitMerger), c_vp, P_i32, c_i32, c_vp, c_vp, c_size,
+                                 c_vp]),
+    "vit_layernorm_gather": (c_i32, [c_vp, P_i32, c_i32, c_i32, c_vp, c_vp, c_f32, c_vp, c_vp]),
+    "vit_gemm_bias": (c_i32, [c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_i64, c_i64,
+                              c_i64, c_vp]),
     "vit_merge_workspace_bytes": (c_size, [c_i64]),
     "vit_merge_image_embeddings": (c_i32, [c_i32, c_vp, c_i64, c_i32, c_vp, c_vp, c_i64, c_vp,
                                            c_vp, c_vp, c_size, c_vp]),

@@ -241,6 +241,82 @@ def aligner_gather(x: torch.Tensor, grids, merge: int = 2) -> torch.Tensor:
     return G
 
 
+class MergerWeights:
+    """PatchMerger projector weights on the device: norm weight / bias, two biased
+    linear maps (bf16 matrices ``[out, in]``, float32 vectors)."""
+
+    def __init__(self, host: Dict, eps: float = 1e-6, device="cuda"):
+        def mat(a):
+            return torch.as_tensor(np.asarray(a, dtype=np.float32)).to(device, torch.bfloat16).contiguous()
+
+        def vec(a):
+            return torch.as_tensor(np.asarray(a, dtype=np.float32)).to(device).contiguous()
+
+        self.ln_w, self.ln_b = vec(host["ln_w"]), vec(host["ln_b"])
+        self.w1, self.b1 = mat(host["w1"]), vec(host["b1"])
+        self.w2, self.b2 = mat(host["w2"]), vec(host["b2"])
+        self.dim = self.ln_w.numel()
+        self.hidden, self.out_dim = self.w1.shape[0], self.w2.shape[0]
+        self.c = _lib.VitMerger(self.dim, self.hidden, self.out_dim, eps, self.ln_w.data_ptr(),
+                                self.ln_b.data_ptr(), self.w1.data_ptr(), self.b1.data_ptr(),
+                                self.w2.data_ptr(), self.b2.data_ptr())
+
+
+def merger_workspace_bytes(mw: MergerWeights, grids) -> int:
+    n = _lib.load().vit_patch_merger_workspace_bytes(ctypes.byref(mw.c), _lib.grid_array(grids),
+                                                      len(grids))
+    if n == 0:
+        _lib.check(_lib.VIT_E_SHAPE, "vit_patch_merger_workspace_bytes")
+    return n
+
+
+def patch_merger(x: torch.Tensor, grids, mw: MergerWeights, out: Optional[torch.Tensor] = None,
+                 ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """vit_patch_merger: x [sum P, dim] bf16 (the encoder output) -> [sum P/4, out_dim]."""
+    _require_cuda(x, out, ws)
+    lib = _lib.load()
+    g = _lib.grid_array(grids)
+    need = lib.vit_patch_merger_workspace_bytes(ctypes.byref(mw.c), g, len(grids))
+    if need == 0:
+        _lib.check(_lib.VIT_E_SHAPE, "vit_patch_merger_workspace_bytes")
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    T = sum(h * w for h, w in grids) // 4
+    if out is None:
+        out = torch.empty((T, mw.out_dim), dtype=torch.bfloat16, device=x.device)
+    st = lib.vit_patch_merger(ctypes.byref(mw.c), x.data_ptr(), g, len(grids), out.data_ptr(),
+                              ws.data_ptr(), ws.numel(), _stream(x.device))
+    _lib.check(st, "vit_patch_merger")
+    return out
+
+
+def layernorm_gather(x: torch.Tensor, grids, ln_w: torch.Tensor, ln_b: torch.Tensor,
+                     eps: float = 1e-6) -> torch.Tensor:
+    """vit_layernorm_gather: G [sum P/4, 4*dim] bf16."""
+    _require_cuda(x, ln_w, ln_b)
+    T = sum(h * w for h, w in grids) // 4
+    G = torch.empty((T, 4 * x.shape[1]), dtype=torch.bfloat16, device=x.device)
+    st = _lib.load().vit_layernorm_gather(x.data_ptr(), _lib.grid_array(grids), len(grids),
+                                          x.shape[1], ln_w.data_ptr(), ln_b.data_ptr(), eps,
+                                          G.data_ptr(), _stream(x.device))
+    _lib.check(st, "vit_layernorm_gather")
+    return G
+
+
+def gemm_bias(A: torch.Tensor, B: torch.Tensor, bias: torch.Tensor, gelu: bool = False) -> torch.Tensor:
+    """vit_gemm_bias: C = A . B^T + bias, or gelu of it (bf16 in and out, fp32 bias)."""
+    _require_cuda(A, B, bias)
+    M, K = A.shape
+    N = B.shape[0]
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    epi = _lib.VIT_EPI_BIAS_GELU if gelu else _lib.VIT_EPI_BIAS
+    st = _lib.load().vit_gemm_bias(epi, A.data_ptr(), A.stride(0), B.data_ptr(), B.stride(0),
+                                   bias.data_ptr(), C.data_ptr(), C.stride(0), M, N, K,
+                                   _stream(A.device))
+    _lib.check(st, "vit_gemm_bias")
+    return C
+
+
 def merge_workspace_bytes(positions: int) -> int:
     n = _lib.load().vit_merge_workspace_bytes(int(positions))
     if n == 0:

@@ -464,6 +464,35 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
   return VIT_OK;
 }
 
+// PatchMerger projector: argument checks and workspace layout
+vit_status check_merger(const vit_merger* m) {
+  if (!m) return fail(VIT_E_ARG, "merger is NULL");
+  if (m->dim <= 0 || m->dim % 16 || m->dim > 4096)
+    return fail(VIT_E_SHAPE, "merger dim %d: need a multiple of 16, at most 4096", m->dim);
+  if (m->hidden <= 0 || m->hidden % 64)
+    return fail(VIT_E_SHAPE, "merger hidden %d: need a positive multiple of 64", m->hidden);
+  if (m->out_dim <= 0 || m->out_dim % 8)
+    return fail(VIT_E_SHAPE, "merger out_dim %d: need a positive multiple of 8", m->out_dim);
+  if (!(m->eps >= 0.f)) return fail(VIT_E_ARG, "merger eps must be >= 0");
+  return VIT_OK;
+}
+
+bool misaligned16(const void* p) { return ((uintptr_t)p & 15) != 0; }
+
+struct MergerPlan {
+  int64_t T = 0;
+  size_t G = 0, H = 0, total = 0;
+};
+
+MergerPlan merger_plan(const vit_merger& m, const VarlenDesc& d) {
+  MergerPlan p;
+  p.T = d.total / 4;
+  p.G = 0;
+  p.H = round_up((int64_t)(p.T * 4 * m.dim * 2), 256);
+  p.total = p.H + round_up((int64_t)(p.T * m.hidden * 2), 256);
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -644,6 +673,84 @@ vit_status vit_merge_image_embeddings(int32_t dtype, void* embeds, int64_t posit
   return hip_check(launch_merge_copy(embeds, positions, row_bytes, types, tokens, n_tokens,
                                      sentinels, ws, s),
                    "merge copy");
+}
+
+size_t vit_patch_merger_workspace_bytes(const vit_merger* m, const int32_t* grid_hw_host,
+                                        int32_t n_images) {
+  if (check_merger(m) != VIT_OK) return 0;
+  VarlenDesc d;
+  if (build_desc(grid_hw_host, n_images, 1, true, 2, &d) != VIT_OK) return 0;
+  return merger_plan(*m, d).total;
+}
+
+vit_status vit_patch_merger(const vit_merger* m, const void* x, const int32_t* grid_hw_host,
+                            int32_t n_images, void* out, void* ws, size_t ws_bytes, void* stream) {
+  VIT_TRY(check_merger(m));
+  if (!x || !out || !m->ln_w || !m->ln_b || !m->w1 || !m->b1 || !m->w2 || !m->b2)
+    return fail(VIT_E_ARG, "NULL pointer");
+  if (misaligned16(x) || misaligned16(out) || misaligned16(ws) || misaligned16(m->ln_w) ||
+      misaligned16(m->ln_b) || misaligned16(m->w1) || misaligned16(m->b1) || misaligned16(m->w2) ||
+      misaligned16(m->b2))
+    return fail(VIT_E_ARG, "merger buffers must be 16-byte aligned");
+  VarlenDesc d;
+  VIT_TRY(build_desc(grid_hw_host, n_images, 1, true, 2, &d));
+  const MergerPlan p = merger_plan(*m, d);
+  if (!ws || ws_bytes < p.total)
+    return fail(VIT_E_WORKSPACE, "merger workspace %zu < %zu", ws ? ws_bytes : (size_t)0, p.total);
+  char* base = (char*)ws;
+  void* G = base + p.G;
+  void* H = base + p.H;
+  const int64_t K1 = 4 * (int64_t)m->dim;
+  GemmArgs g1 = gemm_args(G, K1, m->w1, nullptr, K1, H, m->hidden, p.T, m->hidden, K1, nullptr);
+  g1.bias = m->b1;
+  GemmArgs g2 = gemm_args(H, m->hidden, m->w2, nullptr, m->hidden, out, m->out_dim, p.T,
+                          m->out_dim, m->hidden, nullptr);
+  g2.bias = m->b2;
+  if (!gemm_bf16_mfma_eligible(g1) || !gemm_bf16_mfma_eligible(g2))
+    return fail(VIT_E_SHAPE, "merger GEMMs too large for 32-bit operand offsets");
+  hipStream_t s = (hipStream_t)stream;
+  {
+    ProfScope ps(VIT_K_LNGATHER, s);
+    VIT_HIP(launch_ln_gather(x, d, m->dim, m->ln_w, m->ln_b, m->eps, G, s), "merger norm + gather");
+  }
+  {
+    ProfScope ps(VIT_K_PROJ1, s);
+    VIT_HIP(launch_gemm_bf16(VIT_EPI_BIAS_GELU, g1, s), "merger first linear");
+  }
+  ProfScope ps(VIT_K_PROJ2, s);
+  return hip_check(launch_gemm_bf16(VIT_EPI_BIAS, g2, s), "merger second linear");
+}
+
+vit_status vit_layernorm_gather(const void* x, const int32_t* grid_hw_host, int32_t n_images,
+                                int32_t dim, const float* ln_w, const float* ln_b, float eps,
+                                void* G, void* stream) {
+  if (!x || !ln_w || !ln_b || !G) return fail(VIT_E_ARG, "NULL pointer");
+  if (dim <= 0 || dim % 8 || dim > 4096)
+    return fail(VIT_E_SHAPE, "dim %d: need a multiple of 8, at most 4096", dim);
+  if (!(eps >= 0.f)) return fail(VIT_E_ARG, "eps must be >= 0");
+  if (misaligned16(x) || misaligned16(G) || misaligned16(ln_w) || misaligned16(ln_b))
+    return fail(VIT_E_ARG, "buffers must be 16-byte aligned");
+  VarlenDesc d;
+  VIT_TRY(build_desc(grid_hw_host, n_images, 1, true, 2, &d));
+  return hip_check(launch_ln_gather(x, d, dim, ln_w, ln_b, eps, G, (hipStream_t)stream),
+                   "layernorm gather");
+}
+
+vit_status vit_gemm_bias(int32_t epilogue, const void* A, int64_t lda, const void* B, int64_t ldb,
+                         const float* bias, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                         void* stream) {
+  if (epilogue != VIT_EPI_BIAS && epilogue != VIT_EPI_BIAS_GELU)
+    return fail(VIT_E_ARG, "bad bias epilogue %d", epilogue);
+  if (!A || !B || !bias || !C) return fail(VIT_E_ARG, "NULL pointer");
+  if (M < 0 || N <= 0 || K <= 0 || lda < K || ldb < K || ldc < N || M >= (1LL << 31) ||
+      N >= (1LL << 31) || K >= (1LL << 31))
+    return fail(VIT_E_SHAPE, "bad GEMM dims");
+  if (misaligned16(bias)) return fail(VIT_E_ARG, "bias must be 16-byte aligned");
+  GemmArgs g = gemm_args(A, lda, B, nullptr, ldb, C, ldc, M, N, K, nullptr);
+  g.bias = bias;
+  if (!gemm_bf16_mfma_eligible(g))
+    return fail(VIT_E_SHAPE, "bias GEMM needs K %% 64 == 0, N %% 4 == 0, 16-byte aligned rows");
+  return hip_check(launch_gemm_bf16(epilogue, g, (hipStream_t)stream), "bias gemm");
 }
 
 vit_status vit_profile_enable(int32_t cls, int32_t on) {

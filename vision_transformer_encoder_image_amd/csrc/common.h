@@ -155,6 +155,8 @@ struct GemmArgs {
   int32_t ss_groups;
   float rms_eps;
   float rms_inv_dim;
+  // fp32 per-column bias of VIT_EPI_BIAS / VIT_EPI_BIAS_GELU ([N])
+  const float* bias;
 };
 
 // Largest number of 64-column groups (vision_dim / 64) the folded RMSNorm takes.
@@ -162,10 +164,10 @@ constexpr int kMaxNormGroups = 24;
 
 // Internal epilogue: bf16 store with the half-split 2D rotary applied to the
 // q and k columns (head_dim 64 only; each wave owns whole heads).
-constexpr int VIT_EPI_STORE_ROPE = 4;
+constexpr int VIT_EPI_STORE_ROPE = 16;
 // Internal epilogue: as VIT_EPI_STORE_ROPE for the q, k columns (C holds [M, rope_cols])
 // while the v columns are written transposed, one row per (head, dim), into vt.
-constexpr int VIT_EPI_QKV_VT = 5;
+constexpr int VIT_EPI_QKV_VT = 17;
 
 hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_f32(int epilogue, const GemmArgs& g, hipStream_t s);
@@ -220,6 +222,10 @@ hipError_t launch_zero_cols(int dtype, void* buf, int64_t rows, int64_t ld, int6
 hipError_t launch_layout(int grid_h, int grid_w, int merge, int32_t* perm, int32_t* nl_type,
                          int32_t* nl_src, hipStream_t s);
 hipError_t launch_nl_rowmap(const VarlenDesc& d, int merge, int32_t* rowmap, hipStream_t s);
+// PatchMerger projector: LayerNorm of every patch row into its 2x2-merged slot
+// of G [sum P/4, 4*dim] (projector.hip); dim % 8 == 0, dim <= 4096
+hipError_t launch_ln_gather(const void* x, const VarlenDesc& d, int dim, const float* w,
+                            const float* b, float eps, void* G, hipStream_t s);
 // image tokens and sentinel rows into a text embedding stream (merge.hip)
 size_t merge_workspace_bytes(int64_t positions);
 // group counts of IMAGE positions, scanned in place in ws; total to n_image (optional)

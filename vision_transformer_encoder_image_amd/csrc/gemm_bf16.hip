@@ -290,7 +290,9 @@ hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   const bool rope = epilogue == VIT_EPI_STORE_ROPE || epilogue == VIT_EPI_QKV_VT;
   const bool norm = g.norm_w != nullptr || g.ss_in != nullptr;
-  if ((rope || norm) && !pipe_eligible(g)) return hipErrorInvalidValue;
+  const bool bias = epilogue == VIT_EPI_BIAS || epilogue == VIT_EPI_BIAS_GELU;
+  if ((rope || norm || bias) && !pipe_eligible(g)) return hipErrorInvalidValue;
+  if (bias && (!g.bias || norm)) return hipErrorInvalidValue;
   if (g.ss_in && (g.ss_groups < 1 || g.ss_groups > kMaxNormGroups)) return hipErrorInvalidValue;
   if (g.norm_w && (g.N % 64 != 0 || !g.norm_out || !g.ss_out ||
                    (epilogue != VIT_EPI_STORE_F32 && epilogue != VIT_EPI_ADD_F32)))

@@ -28,7 +28,8 @@
 // wave quantisation over the 256 CUs.
 //
 // Epilogues: bf16 store, fp32 store, fp32 residual add, SwiGLU (gate and up rows
-// side by side in the B tile so silu(gate) * up meets in one lane), and the
+// side by side in the B tile so silu(gate) * up meets in one lane), bf16 store
+// with an fp32 column bias (and GELU, erf form, for the projector), and the
 // half-split 2D rotary on the q and k columns (both rotate_half partners,
 // columns c and c+16 of a 32-wide block, sit in one lane), optionally with the
 // v columns written transposed for the attention kernel.  bf16 and fp32-store
@@ -54,6 +55,8 @@ VIT_DEV int chunk_swz(int row) {
 }
 
 VIT_DEV float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+// GELU in its erf form, x * Phi(x)
+VIT_DEV float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool DUAL>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) {
@@ -482,6 +485,34 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
                            TM * ROWB * NW <= STAGES * ROWS * BK * 2;
   const bool v_wave = (EPI == VIT_EPI_QKV_VT) && (n0 + wn * TN >= g.rope_cols);
   const bool staged = kStaged && (g.ldc * OB) % 16 == 0;  // 16-byte aligned output rows
+  constexpr bool kBias = EPI == VIT_EPI_BIAS || EPI == VIT_EPI_BIAS_GELU;
+  // bias of the lane's 4-column groups: loaded once, before any store, when the
+  // wave tile is at most 64 columns wide; wider tiles (whose accumulators fill
+  // the register file) read each group where it is used
+  constexpr bool kBiasHoist = kBias && BJ <= 2;
+  f32x4 bias_v[kBiasHoist ? BJ : 1][4];
+  auto bias_ld = [&](int j, int gq) __attribute__((always_inline)) {
+    return *reinterpret_cast<const f32x4*>(g.bias +
+                                           min(n0 + wn * TN + j * 32 + 8 * gq + c4, N - 4));
+  };
+  if constexpr (kBiasHoist) {
+#pragma unroll
+    for (int j = 0; j < BJ; ++j)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) bias_v[j][gq] = bias_ld(j, gq);
+  }
+  auto bias_group = [&](int j, int gq) __attribute__((always_inline)) {
+    if constexpr (kBiasHoist) return bias_v[j][gq];
+    else if constexpr (kBias) return bias_ld(j, gq);
+    else return f32x4{};
+  };
+  auto bias_act = [&](float v, float bias) __attribute__((always_inline)) {
+    if constexpr (kBias) {
+      v += bias;
+      if constexpr (EPI == VIT_EPI_BIAS_GELU) v = gelu_f(v);
+    }
+    return v;
+  };
   if (staged) {
     lds_barrier();  // every wave is done reading the ring
     if (!v_wave) {
@@ -507,13 +538,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
             } else {
               const int c16 = j * 4 + gq;
               const int hh = fh ^ ((r >> 4) & 1);
+              const f32x4 bq = bias_group(j, gq);
               bf16x4 b;
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 if constexpr (DUAL)
                   b[e] = f2bf(silu_f(acc[i][j][4 * gq + e]) * acc[i][j + BJ / 2][4 * gq + e]);
                 else
-                  b[e] = f2bf(acc[i][j][4 * gq + e]);
+                  b[e] = f2bf(bias_act(acc[i][j][4 * gq + e], bq[e]));
               }
               *reinterpret_cast<bf16x4*>(row + ((c16 ^ sw) << 4) + (hh << 3)) = b;
             }
@@ -532,8 +564,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
           for (int it = 0; it < TM / RPI; ++it)
             dst_row[it] = g.rowmap[min(m0 + wm * TM + it * RPI + lane / CPRW, M - 1)];
         }
-#pragma unroll 4
-        for (int it = 0; it < TM / RPI; ++it) {
+        auto row_out = [&](int it) __attribute__((always_inline)) {
           const int R = it * RPI + lane / CPRW;
           const int m = m0 + wm * TM + R;
           u32x4 d = *reinterpret_cast<const u32x4*>(st + R * ROWB +
@@ -542,7 +573,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
             const uint32_t t0 = d[0], t1 = d[1];
             d[0] = d[2]; d[1] = d[3]; d[2] = t0; d[3] = t1;
           }
-          if (m >= M || n >= N) continue;
+          if (m >= M || n >= N) return;
           int64_t drow = m;
           if constexpr (with_rowmap) drow = dst_row[it];
           char* dst = (char*)g.C + (drow * g.ldc + n) * OB;
@@ -550,6 +581,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
             *reinterpret_cast<u32x4*>(dst) = d;
           else  // N % 8 == 4 tail of a bf16 row: the first 8 bytes
             *reinterpret_cast<uint2*>(dst) = make_uint2(d[0], d[1]);
+        };
+        // fully unrolled with a row map, so that dst_row stays in registers
+        if constexpr (with_rowmap) {
+#pragma unroll
+          for (int it = 0; it < TM / RPI; ++it) row_out(it);
+        } else {
+#pragma unroll 4
+          for (int it = 0; it < TM / RPI; ++it) row_out(it);
         }
       };
       if (has_rowmap)
@@ -644,9 +683,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
             } else if (EPI == VIT_EPI_STORE_F32) {
               *reinterpret_cast<f32x4*>((float*)g.C + orow[i] * g.ldc + n) = v;
             } else {
+              const f32x4 bq = bias_group(j, gq);
               bf16x4 b;
 #pragma unroll
-              for (int r = 0; r < 4; ++r) b[r] = f2bf(v[r]);
+              for (int r = 0; r < 4; ++r) b[r] = f2bf(bias_act(v[r], bq[r]));
               *reinterpret_cast<bf16x4*>((bf16*)g.C + orow[i] * g.ldc + n) = b;
             }
           }
@@ -687,8 +727,14 @@ hipError_t mfma_epi(int epi, const GemmArgs& g, hipStream_t s) {
     case VIT_EPI_STORE_F32:
       return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_STORE_F32, false>(g, s);
     case VIT_EPI_ADD_F32:
-      return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_ADD_F32, false>(g, s);
+      // not built for the 256x256 tile (it spills; the dispatcher never picks it)
+      if constexpr (!(BM == 256 && BN == 256))
+        return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_ADD_F32, false>(g, s);
+      return hipErrorInvalidValue;
     case VIT_EPI_SWIGLU: return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_SWIGLU, true>(g, s);
+    case VIT_EPI_BIAS: return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_BIAS, false>(g, s);
+    case VIT_EPI_BIAS_GELU:
+      return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_BIAS_GELU, false>(g, s);
     case VIT_EPI_STORE_ROPE:
       if constexpr ((BN / WN) % 64 == 0)
         return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_STORE_ROPE, false>(g, s);

@@ -77,5 +77,19 @@ def random_array(shape, seed: int, kind: str = "normal", std: float = 1.0,
     return round_to_bf16(a) if bf16 else a
 
 
+def make_merger_weights(dim: int, hidden: int, out_dim: int, seed: int) -> Dict:
+    """Seeded PatchMerger projector weights: norm weight 1 + N(0, 0.02) and bias
+    N(0, 0.02) (float32), matrices N(0, 0.02) rounded to bf16 ([out, in]), biases
+    N(0, 0.02) (float32)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def normal(*shape):
+        return rng.standard_normal(shape, dtype=np.float32) * np.float32(0.02)
+
+    return {"ln_w": np.float32(1.0) + normal(dim), "ln_b": normal(dim),
+            "w1": round_to_bf16(normal(hidden, 4 * dim)), "b1": normal(hidden),
+            "w2": round_to_bf16(normal(out_dim, hidden)), "b2": normal(out_dim)}
+
+
 def seqlens(grids: List) -> List[int]:
     return [int(gh) * int(gw) for gh, gw in grids]
