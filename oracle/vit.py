@@ -33,7 +33,11 @@ READINGS = {
     "swiglu": "silu(x Wg^T) * (x Wu^T), then Wd; no clamp",
     "aligner": "2x2 groups row-major over (gh/2, gw/2); inside a group TL,TR,BL,BR concatenated "
                "along features; one bias-free linear to the LLM width",
-    "odd_grid": "the aligner needs an even grid; odd grids are rejected",
+    "odd_grid": "the released aligner handles odd grids ([PR] validation: 27x37, 37x27, 112x7 "
+                "exact) by a rule the pages do not give; by default odd grids are rejected, and "
+                "with pad_odd the grid is zero-padded to even (a zero patch row below, a zero "
+                "patch column on the right) before the 2x2 merge, so an image has "
+                "ceil(gh/2)*ceil(gw/2) merged tokens",
     "nlayout": "per image: [START] + per merged row (w' IMAGE, NEWLINE) + [END]; "
                "types START=0 IMAGE=1 NEWLINE=2 END=3; src = merged token index or -1",
     "merge_embeddings": "positions are visited batch-major, sequence-minor; IMAGE positions "
@@ -226,36 +230,48 @@ def tower(patches, gh, gw, weights, n_heads, eps=1e-6, theta=10000.0, dtype=np.f
     return rmsnorm(x, weights["final_norm"], eps, dtype)
 
 
-def aligner_perm(gh, gw, merge=2):
-    """Source patch of every slot of the merged layout, ``[gh*gw]`` int32.
+def _merged_dims(gh, gw, merge, pad_odd):
+    if gh % merge or gw % merge:
+        if not pad_odd:
+            raise ValueError("aligner needs a grid divisible by the merge size")
+        return -(-gh // merge), -(-gw // merge)
+    return gh // merge, gw // merge
+
+
+def aligner_perm(gh, gw, merge=2, pad_odd=False):
+    """Source patch of every slot of the merged layout, ``[4 * tokens]`` int32.
 
     [VIS] DeepseekV4VisionAligner spatially downsamples (downsample_ratio = 2) and
     [PR] reports the permutation as exact; reading "aligner": merged token
-    t = i*(gw/2) + j gathers the 2x2 group at rows 2i..2i+1, cols 2j..2j+1 in
-    row-major order TL, TR, BL, BR.
+    t = i*(w') + j gathers the 2x2 group at rows 2i..2i+1, cols 2j..2j+1 in
+    row-major order TL, TR, BL, BR.  Reading "odd_grid": with ``pad_odd`` a slot
+    outside the grid (row gh or column gw of the padded grid) holds -1.
     """
-    if gh % merge or gw % merge:
-        raise ValueError("aligner needs a grid divisible by the merge size")
+    hq, wq = _merged_dims(gh, gw, merge, pad_odd)
     perm = []
-    for i in range(gh // merge):
-        for j in range(gw // merge):
+    for i in range(hq):
+        for j in range(wq):
             for a in range(merge):
                 for b in range(merge):
-                    perm.append((merge * i + a) * gw + (merge * j + b))
+                    r, c = merge * i + a, merge * j + b
+                    perm.append(r * gw + c if r < gh and c < gw else -1)
     return np.array(perm, dtype=np.int32)
 
 
-def aligner_gather(x, gh, gw, merge=2):
-    """G[t] = concat of x over the group of merged token t: ``[P/4, 4d]``."""
+def aligner_gather(x, gh, gw, merge=2, pad_odd=False):
+    """G[t] = concat of x over the group of merged token t: ``[tokens, 4d]``
+    (zero rows for the padded slots of an odd grid)."""
     x = np.asarray(x)
-    perm = aligner_perm(gh, gw, merge)
+    perm = aligner_perm(gh, gw, merge, pad_odd)
     m2 = merge * merge
-    return x[perm].reshape(len(perm) // m2, m2 * x.shape[1])
+    rows = np.zeros((len(perm), x.shape[1]), dtype=x.dtype)
+    rows[perm >= 0] = x[perm[perm >= 0]]
+    return rows.reshape(len(perm) // m2, m2 * x.shape[1])
 
 
-def aligner(x, gh, gw, w, merge=2, dtype=np.float64):
+def aligner(x, gh, gw, w, merge=2, dtype=np.float64, pad_odd=False):
     """[VIS] DeepseekV4VisionAligner.forward: 2x2 gather, then the linear map to LLM width."""
-    return linear(aligner_gather(_f(x, dtype), gh, gw, merge), w, dtype)
+    return linear(aligner_gather(_f(x, dtype), gh, gw, merge, pad_odd), w, dtype)
 
 
 def layernorm(x, w, b, eps=1e-6, dtype=np.float64):
@@ -295,16 +311,16 @@ def patch_merger_param_count(d, hidden, out, merge=2):
     return 2 * d + hidden * m2 * d + hidden + out * hidden + out
 
 
-def nlayout(gh, gw, merge=2):
+def nlayout(gh, gw, merge=2, pad_odd=False):
     """Newline layout of one image span in the LLM stream: (types, src) int32.
 
     [PR] names the released "N-layout pseudo-token expansion"; [MOD] names the
     sentinels image_start / image_newline / image_end.  Reading "nlayout": the span
     is [START], then for each merged row i its gw/2 IMAGE tokens followed by one
     NEWLINE, then [END].  ``src`` holds the merged token index of IMAGE slots and
-    -1 for sentinels.
+    -1 for sentinels.  With ``pad_odd`` the merged grid is ceil(gh/2) x ceil(gw/2).
     """
-    hh, ww = gh // merge, gw // merge
+    hh, ww = _merged_dims(gh, gw, merge, pad_odd)
     types, src = [NL_START], [-1]
     t = 0
     for _ in range(hh):
@@ -343,22 +359,22 @@ def merge_image_embeddings(embeds, types, tokens, sentinels):
 
 
 def encode(patches, gh, gw, weights, n_heads, eps=1e-6, theta=10000.0, with_aligner=True,
-           dtype=np.float64):
+           dtype=np.float64, pad_odd=False):
     """[MOD] DeepseekV4Model.encode_image: the vision tower, then the aligner."""
     x = tower(patches, gh, gw, weights, n_heads, eps, theta, dtype)
     if not with_aligner:
         return x
-    return aligner(x, gh, gw, weights["aligner"], dtype=dtype)
+    return aligner(x, gh, gw, weights["aligner"], dtype=dtype, pad_odd=pad_odd)
 
 
 def encode_varlen(patches, grids, weights, n_heads, eps=1e-6, theta=10000.0, with_aligner=True,
-                  dtype=np.float64):
+                  dtype=np.float64, pad_odd=False):
     """Concatenated images ([MOD] pixel_values + image_grid_hws): each image alone, in order."""
     outs = []
     off = 0
     for gh, gw in grids:
         P = gh * gw
         outs.append(encode(patches[off:off + P], gh, gw, weights, n_heads, eps, theta,
-                           with_aligner, dtype))
+                           with_aligner, dtype, pad_odd))
         off += P
     return np.concatenate(outs, axis=0)

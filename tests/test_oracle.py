@@ -653,3 +653,35 @@ def test_patch_merger_constant_patches_closed_form():
     got = oracle.patch_merger(x, 4, 6, p)
     assert got.shape == (6, out)
     np.testing.assert_allclose(got, np.tile(want, (6, 1)), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- odd grids (zero padding)
+def test_aligner_pad_odd_golden():
+    vals = {}
+    for line in open(os.path.join(GOLDEN, "aligner_pad_3x3.txt")):
+        if line and not line.startswith("#"):
+            k, *v = line.split()
+            vals[k] = np.array([int(t) for t in v], dtype=np.int32)
+    np.testing.assert_array_equal(oracle.aligner_perm(3, 3, pad_odd=True), vals["perm"])
+    types, src = oracle.nlayout(3, 3, pad_odd=True)
+    np.testing.assert_array_equal(types, vals["types"])
+    np.testing.assert_array_equal(src, vals["src"])
+    with pytest.raises(ValueError):
+        oracle.aligner_perm(3, 3)
+
+
+@pytest.mark.parametrize("grid", [(3, 5), (4, 7), (5, 2), (1, 1), (6, 4)])
+def test_aligner_pad_equals_explicit_zero_padding(grid):
+    """The padded merge of an odd grid equals the plain merge of the grid padded by
+    hand with zero patches (and is the plain merge on even grids)."""
+    gh, gw = grid
+    rng = _rng(34)
+    d = 3
+    x = rng.standard_normal((gh * gw, d))
+    ph, pw = gh + gh % 2, gw + gw % 2
+    xp = np.zeros((ph, pw, d))
+    xp[:gh, :gw] = x.reshape(gh, gw, d)
+    want = oracle.aligner_gather(xp.reshape(ph * pw, d), ph, pw)
+    np.testing.assert_array_equal(oracle.aligner_gather(x, gh, gw, pad_odd=True), want)
+    types, _ = oracle.nlayout(gh, gw, pad_odd=True)
+    assert (types == oracle.NL_IMAGE).sum() == want.shape[0] == (ph // 2) * (pw // 2)
