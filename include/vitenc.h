@@ -57,6 +57,13 @@ enum {
                           patch_dim = 3*ps^2), images back to back; the library cuts
                           them into patches (DeepseekV4VisionTransformer.forward
                           takes [n_h*n_w, 3, ps, ps] patches of the image) */
+  VIT_ALIGN_PAD = 8,   /* odd grids with the aligner: zero-pad to even (a zero patch
+                          row below, a zero patch column on the right) before the
+                          2x2 merge, giving ceil(grid_h/2)*ceil(grid_w/2) merged
+                          tokens and a newline layout over that merged grid.  The
+                          release handles odd grids (PR #3772 validation: 27x37,
+                          37x27, 112x7) by a rule the pages do not give; without
+                          this flag odd grids are rejected (VIT_E_ODD_GRID) */
 };
 
 /* Upper bound on images per varlen call (descriptors travel as kernel args). */
@@ -121,13 +128,14 @@ size_t vit_workspace_bytes(const vit_config* cfg, const int32_t* grid_hw_host, i
  *        flattened in [3, ps, ps] C order (DeepseekV4VisionTransformer.forward);
  *        with VIT_IN_PIXELS the pixel image [3, ps*grid_h, ps*grid_w] instead
  *        (patch_dim must then be 3*ps^2; VIT_E_SHAPE otherwise).
- *   out  aligner on: [(grid_h/merge)*(grid_w/merge), llm_dim], merged tokens
- *        row-major over the merged grid (or newline-layout rows with
- *        VIT_OUT_NLAYOUT: [(h'*(w'+1)+2), llm_dim]);
+ *   out  aligner on: [h'*w', llm_dim] with h' = grid_h/merge, w' = grid_w/merge
+ *        (rounded up with VIT_ALIGN_PAD), merged tokens row-major over the merged
+ *        grid (or newline-layout rows with VIT_OUT_NLAYOUT: [(h'*(w'+1)+2), llm_dim]);
  *        aligner off: [grid_h*grid_w, vision_dim].  dtype = cfg.dtype.
  *   ws   device workspace of ws_bytes >= vit_workspace_bytes(); contents scratch.
  * Errors: VIT_E_ARG (null pointer), VIT_E_SHAPE (dims), VIT_E_ODD_GRID (aligner
- * on an odd grid), VIT_E_WORKSPACE, VIT_E_HIP.  out must not alias in or ws. */
+ * on an odd grid without VIT_ALIGN_PAD), VIT_E_WORKSPACE, VIT_E_HIP.  out must not
+ * alias in or ws. */
 vit_status vit_encode(const vit_config* cfg, const vit_weights* w, const void* in, int32_t grid_h,
                       int32_t grid_w, int32_t flags, void* out, void* ws, size_t ws_bytes,
                       void* stream);

@@ -61,9 +61,13 @@ def test_host_validation_errors(lib):
     assert lib.vit_aligner_layout(27, 37, 2, None, None, None, None) == _lib.VIT_E_ODD_GRID
     assert lib.vit_workspace_bytes(ctypes.byref(cfg), _lib.grid_array([(27, 37)]), 1, 0) == 0
     assert b"not divisible" in lib.vit_last_error()
-    # the same grid is fine without the aligner
+    # the same grid is fine without the aligner, or with the zero-padding rule
     assert lib.vit_workspace_bytes(ctypes.byref(cfg), _lib.grid_array([(27, 37)]), 1,
                                    _lib.VIT_NO_ALIGNER) > 0
+    padded = lib.vit_workspace_bytes(ctypes.byref(cfg), _lib.grid_array([(27, 37)]), 1,
+                                     _lib.VIT_ALIGN_PAD)
+    even = lib.vit_workspace_bytes(ctypes.byref(cfg), _lib.grid_array([(28, 38)]), 1, 0)
+    assert padded > 0 and padded <= even  # 14 x 19 merged tokens either way, fewer patches
     # bad shapes
     bad = api.c_config(configs.get(1))
     bad.head_dim = 60

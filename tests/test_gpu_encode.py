@@ -177,3 +177,51 @@ def test_error_paths_on_device():
                                1, enc.flags, out.data_ptr(), enc.ws.data_ptr(), enc.ws_bytes - 256,
                                torch.cuda.current_stream().cuda_stream)
     assert st == _lib.VIT_E_WORKSPACE
+
+
+def _ragged_aligned_cfg():
+    # the ragged 4-image grids (three of them odd) with a 512-wide aligner, 2 blocks
+    return configs.VitConfig("ragged_aligned", ((27, 37), (37, 27), (10, 78), (112, 7)),
+                             1024, 16, 2816, 2, 512, "bf16")
+
+
+def test_odd_grids_zero_padded_aligner_matches_oracle():
+    cfg = _ragged_aligned_cfg()
+    inp = synth.make_inputs(cfg, seed=97)
+    w = api.DeviceWeights(cfg, inp["weights"])
+    x = torch.from_numpy(inp["patches"]).to("cuda", torch.bfloat16)
+    got = to_np(api.Encoder(cfg, w, cfg.grids, aligner=True, pad_odd=True)(x))
+    ref = oracle.encode_varlen(inp["patches"], inp["grids"], inp["weights"], cfg.n_heads,
+                               cfg.rms_eps, cfg.rope_theta, with_aligner=True, pad_odd=True)
+    assert got.shape == ref.shape == (14 * 19 + 19 * 14 + 5 * 39 + 56 * 4, 512)
+    err = rowwise_rel_err(got, ref)
+    print(f"odd grids, zero-padded aligner: row-wise rel err {err:.3e}")
+    assert err < TOL["bf16"], err
+    # without the flag the odd grids are still refused
+    with pytest.raises(_lib.VitError):
+        api.Encoder(cfg, w, cfg.grids, aligner=True)
+
+
+def test_odd_grids_newline_layout_rows():
+    cfg = _ragged_aligned_cfg()
+    inp = synth.make_inputs(cfg, seed=97)
+    w = api.DeviceWeights(cfg, inp["weights"])
+    x = torch.from_numpy(inp["patches"]).to("cuda", torch.bfloat16)
+    plain = api.Encoder(cfg, w, cfg.grids, aligner=True, pad_odd=True)(x)
+    nl = api.Encoder(cfg, w, cfg.grids, aligner=True, nlayout=True, pad_odd=True)(x)
+    torch.cuda.synchronize()
+    rows, toks = [], []
+    base = tok = 0
+    for gh, gw in cfg.grids:
+        types, src = oracle.nlayout(gh, gw, pad_odd=True)
+        img = np.nonzero(types == oracle.NL_IMAGE)[0]
+        rows.append(base + img)
+        toks.append(tok + src[img])
+        base += len(types)
+        tok += int((types == oracle.NL_IMAGE).sum())
+    rows, toks = np.concatenate(rows), np.concatenate(toks)
+    assert nl.shape[0] == base and plain.shape[0] == tok
+    assert torch.equal(nl[torch.from_numpy(rows).long().cuda()],
+                       plain[torch.from_numpy(toks).long().cuda()])
+    sentinel = np.setdiff1d(np.arange(base), rows)
+    assert (nl[torch.from_numpy(sentinel).long().cuda()] == 0).all()

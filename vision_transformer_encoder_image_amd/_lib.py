@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvitenc.s
 
 VIT_OK, VIT_E_ARG, VIT_E_SHAPE, VIT_E_ODD_GRID, VIT_E_WORKSPACE, VIT_E_HIP = 0, -1, -2, -3, -4, -5
 VIT_BF16, VIT_F32 = 0, 1
-VIT_NO_ALIGNER, VIT_OUT_NLAYOUT, VIT_IN_PIXELS = 1, 2, 4
+VIT_NO_ALIGNER, VIT_OUT_NLAYOUT, VIT_IN_PIXELS, VIT_ALIGN_PAD = 1, 2, 4, 8
 VIT_MAX_IMAGES = 128
 VIT_EPI_STORE, VIT_EPI_STORE_F32, VIT_EPI_ADD_F32, VIT_EPI_SWIGLU = 0, 1, 2, 3
 VIT_EPI_BIAS, VIT_EPI_BIAS_GELU = 4, 5

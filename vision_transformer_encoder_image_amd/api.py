@@ -73,23 +73,30 @@ class DeviceWeights:
             None if self.aligner is None else self.aligner.data_ptr())
 
 
-def output_rows(cfg: VitConfig, grids: Sequence[Tuple[int, int]], aligner: bool, nlayout: bool) -> int:
+def output_rows(cfg: VitConfig, grids: Sequence[Tuple[int, int]], aligner: bool, nlayout: bool,
+                pad_odd: bool = False) -> int:
+    """Rows of the encoder output (merged grids rounded up with pad_odd)."""
     if not aligner:
         return sum(h * w for h, w in grids)
     m = cfg.merge
+
+    def q(v):
+        return -(-v // m) if pad_odd else v // m
+
     if nlayout:
-        return sum((h // m) * (w // m + 1) + 2 for h, w in grids)
-    return sum((h // m) * (w // m) for h, w in grids)
+        return sum(q(h) * (q(w) + 1) + 2 for h, w in grids)
+    return sum(q(h) * q(w) for h, w in grids)
 
 
-def _flags(aligner: bool, nlayout: bool, pixels: bool) -> int:
+def _flags(aligner: bool, nlayout: bool, pixels: bool, pad_odd: bool = False) -> int:
     return ((0 if aligner else _lib.VIT_NO_ALIGNER) | (_lib.VIT_OUT_NLAYOUT if nlayout else 0)
-            | (_lib.VIT_IN_PIXELS if pixels else 0))
+            | (_lib.VIT_IN_PIXELS if pixels else 0) | (_lib.VIT_ALIGN_PAD if pad_odd else 0))
 
 
-def workspace_bytes(cfg: VitConfig, grids, aligner=True, nlayout=False, pixels=False) -> int:
+def workspace_bytes(cfg: VitConfig, grids, aligner=True, nlayout=False, pixels=False,
+                    pad_odd=False) -> int:
     lib = _lib.load()
-    flags = _flags(aligner, nlayout, pixels)
+    flags = _flags(aligner, nlayout, pixels, pad_odd)
     c = c_config(cfg)
     n = lib.vit_workspace_bytes(ctypes.byref(c), _lib.grid_array(grids), len(grids), flags)
     if n == 0:
@@ -101,17 +108,17 @@ class Encoder:
     """Reusable encoder call: keeps the workspace for one set of grids."""
 
     def __init__(self, cfg: VitConfig, weights: DeviceWeights, grids, aligner=True, nlayout=False,
-                 device="cuda", pixels=False):
+                 device="cuda", pixels=False, pad_odd=False):
         self.cfg, self.w = cfg, weights
         self.grids = [tuple(int(v) for v in g) for g in grids]
         self.aligner, self.nlayout = aligner, nlayout
-        self.flags = _flags(aligner, nlayout, pixels)
-        self.ws_bytes = workspace_bytes(cfg, self.grids, aligner, nlayout, pixels)
+        self.flags = _flags(aligner, nlayout, pixels, pad_odd)
+        self.ws_bytes = workspace_bytes(cfg, self.grids, aligner, nlayout, pixels, pad_odd)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         self.c_cfg = c_config(cfg)
         self.c_grids = _lib.grid_array(self.grids)
         cols = cfg.llm_dim if aligner else cfg.vision_dim
-        self.out_shape = (output_rows(cfg, self.grids, aligner, nlayout), cols)
+        self.out_shape = (output_rows(cfg, self.grids, aligner, nlayout, pad_odd), cols)
         self.device = device
 
     def __call__(self, patches: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -130,18 +137,18 @@ class Encoder:
 
 
 def encode(patches: torch.Tensor, grid: Tuple[int, int], weights: DeviceWeights, aligner=True,
-           nlayout=False, pixels=False) -> torch.Tensor:
+           nlayout=False, pixels=False, pad_odd=False) -> torch.Tensor:
     """vit_encode: one image [gh*gw, patch_dim] (or with pixels=True the pixel image
     [3, ps*gh, ps*gw]) -> aligned tokens (or encoded patches)."""
     cfg = weights.cfg
     _require_cuda(patches)
-    ws_bytes = workspace_bytes(cfg, [grid], aligner, nlayout, pixels)
+    ws_bytes = workspace_bytes(cfg, [grid], aligner, nlayout, pixels, pad_odd)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=patches.device)
     cols = cfg.llm_dim if aligner else cfg.vision_dim
-    rows = output_rows(cfg, [grid], aligner, nlayout)
+    rows = output_rows(cfg, [grid], aligner, nlayout, pad_odd)
     out = (torch.zeros if nlayout else torch.empty)((rows, cols), dtype=_TORCH_DTYPE[cfg.dtype],
                                                      device=patches.device)
-    flags = _flags(aligner, nlayout, pixels)
+    flags = _flags(aligner, nlayout, pixels, pad_odd)
     c = c_config(cfg)
     lib = _lib.load()
     st = lib.vit_encode(ctypes.byref(c), ctypes.byref(weights.c), patches.data_ptr(), grid[0],
@@ -152,10 +159,12 @@ def encode(patches: torch.Tensor, grid: Tuple[int, int], weights: DeviceWeights,
 
 
 def encode_varlen(patches: torch.Tensor, grids, weights: DeviceWeights, aligner=True,
-                  nlayout=False, pixels=False) -> torch.Tensor:
+                  nlayout=False, pixels=False, pad_odd=False) -> torch.Tensor:
     """vit_encode_varlen: packed images with block-diagonal attention (patches, or
-    with pixels=True the pixel images back to back)."""
-    return Encoder(weights.cfg, weights, grids, aligner, nlayout, patches.device, pixels)(patches)
+    with pixels=True the pixel images back to back; pad_odd zero-pads odd grids
+    for the 2x2 merge)."""
+    return Encoder(weights.cfg, weights, grids, aligner, nlayout, patches.device, pixels,
+                   pad_odd)(patches)
 
 
 def aligner_layout(grid_h: int, grid_w: int, merge: int = 2, device="cuda"):

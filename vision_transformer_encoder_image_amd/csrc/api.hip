@@ -110,20 +110,22 @@ int patch_size_of(const vit_config& c) {
 }
 
 vit_status build_desc(const int32_t* grid_hw, int32_t n_images, int q_tile, bool need_even,
-                      int merge, VarlenDesc* d) {
+                      int merge, VarlenDesc* d, bool pad_odd = false) {
   if (!grid_hw) return fail(VIT_E_ARG, "grid_hw is NULL");
   if (n_images < 1 || n_images > VIT_MAX_IMAGES)
     return fail(VIT_E_SHAPE, "n_images %d outside [1, %d]", n_images, VIT_MAX_IMAGES);
   std::memset(d, 0, sizeof(*d));
   d->n_images = n_images;
-  int64_t total = 0, tiles = 0, kv = 0;
+  int64_t total = 0, tiles = 0, kv = 0, toks = 0;
   for (int i = 0; i < n_images; ++i) {
     const int gh = grid_hw[2 * i], gw = grid_hw[2 * i + 1];
     if (gh <= 0 || gw <= 0) return fail(VIT_E_SHAPE, "image %d has grid %dx%d", i, gh, gw);
-    if (need_even && (gh % merge || gw % merge))
+    if (need_even && !pad_odd && (gh % merge || gw % merge))
       return fail(VIT_E_ODD_GRID, "image %d grid %dx%d not divisible by merge %d", i, gh, gw,
                   merge);
     d->cu_seqlens[i] = (int32_t)total;
+    d->cu_tokens[i] = (int32_t)toks;
+    toks += (int64_t)((gh + merge - 1) / merge) * ((gw + merge - 1) / merge);
     d->cu_tiles[i] = (int32_t)tiles;
     d->kv_off[i] = (int32_t)kv;
     d->grid_w[i] = gw;
@@ -135,6 +137,7 @@ vit_status build_desc(const int32_t* grid_hw, int32_t n_images, int q_tile, bool
   d->cu_seqlens[n_images] = (int32_t)total;
   d->cu_tiles[n_images] = (int32_t)tiles;
   d->kv_off[n_images] = (int32_t)kv;
+  d->cu_tokens[n_images] = (int32_t)toks;
   d->total = (int32_t)total;
   return VIT_OK;
 }
@@ -156,7 +159,8 @@ Plan make_plan(const vit_config& c, const VarlenDesc& desc, int flags) {
   const bool aligner = !(flags & VIT_NO_ALIGNER);
   const int64_t d = c.vision_dim, h = c.mlp_hidden, m2 = (int64_t)c.merge * c.merge;
   p.P = P;
-  p.tokens = aligner ? P / m2 : 0;
+  p.tokens = aligner ? desc.cu_tokens[desc.n_images] : 0;
+  (void)m2;
   p.Kp = c.dtype == VIT_BF16 ? round_up(c.patch_dim, 64) : c.patch_dim;
   const bool pixels = (flags & VIT_IN_PIXELS) != 0;
   // MLP activations keep a 64-multiple row stride in bf16 so the down GEMM runs
@@ -257,7 +261,7 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
                        void* ws, size_t ws_bytes, hipStream_t s) {
   VIT_TRY(check_config(cfg));
   const vit_config& c = *cfg;
-  if (flags & ~(VIT_NO_ALIGNER | VIT_OUT_NLAYOUT | VIT_IN_PIXELS))
+  if (flags & ~(VIT_NO_ALIGNER | VIT_OUT_NLAYOUT | VIT_IN_PIXELS | VIT_ALIGN_PAD))
     return fail(VIT_E_ARG, "unknown flags %d", flags);
   const int pixel_ps = (flags & VIT_IN_PIXELS) ? patch_size_of(*cfg) : 0;
   if ((flags & VIT_IN_PIXELS) && pixel_ps == 0)
@@ -270,7 +274,7 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
   VIT_TRY(check_weights(c, w, aligner));
   VarlenDesc desc;
   VIT_TRY(build_desc(grid_hw, n_images, attention_q_tile(c.dtype, c.head_dim), aligner, c.merge,
-                     &desc));
+                     &desc, (flags & VIT_ALIGN_PAD) != 0));
   const Plan p = make_plan(c, desc, flags);
   if (!ws || ws_bytes < p.total)
     return fail(VIT_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0,
@@ -514,7 +518,7 @@ const char* vit_last_error(void) { return g_last_error.c_str(); }
 size_t vit_workspace_bytes(const vit_config* cfg, const int32_t* grid_hw_host, int32_t n_images,
                            int32_t flags) {
   if (check_config(cfg) != VIT_OK) return 0;
-  if (flags & ~(VIT_NO_ALIGNER | VIT_OUT_NLAYOUT | VIT_IN_PIXELS)) {
+  if (flags & ~(VIT_NO_ALIGNER | VIT_OUT_NLAYOUT | VIT_IN_PIXELS | VIT_ALIGN_PAD)) {
     fail(VIT_E_ARG, "unknown flags %d", flags);
     return 0;
   }
@@ -525,7 +529,7 @@ size_t vit_workspace_bytes(const vit_config* cfg, const int32_t* grid_hw_host, i
   VarlenDesc d;
   const bool aligner = !(flags & VIT_NO_ALIGNER);
   if (build_desc(grid_hw_host, n_images, attention_q_tile(cfg->dtype, cfg->head_dim), aligner,
-                 cfg->merge, &d) != VIT_OK)
+                 cfg->merge, &d, (flags & VIT_ALIGN_PAD) != 0) != VIT_OK)
     return 0;
   return make_plan(*cfg, d, flags).total;
 }

@@ -108,6 +108,9 @@ struct VarlenDesc {
   int32_t grid_w[VIT_MAX_IMAGES];
   int32_t cu_tiles[VIT_MAX_IMAGES + 1];  // prefix sum of q-tiles per image (attention)
   int32_t kv_off[VIT_MAX_IMAGES + 1];    // image starts in the transposed-V layout (64-aligned)
+  // merged-token starts of the 2x2 merge: ceil(gh/2) * ceil(gw/2) tokens per image
+  // (gh*gw/4 on even grids; odd grids only with VIT_ALIGN_PAD)
+  int32_t cu_tokens[VIT_MAX_IMAGES + 1];
 };
 
 // Keys of one image start at a multiple of this in the transposed-V layout.

@@ -103,22 +103,25 @@ __global__ void gather_kernel(const T* __restrict__ x, VarlenDesc d, int dim, in
   constexpr int V = 16 / sizeof(T);
   const int m2 = merge * merge;
   const int64_t row_chunks = (int64_t)m2 * dim / V;
-  const int64_t tokens = d.total / m2;
+  const int64_t tokens = d.cu_tokens[d.n_images];
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= tokens * row_chunks) return;
   const int64_t t = idx / row_chunks;
   const int col = (int)(idx % row_chunks) * V;
   const int s = col / dim;
   const int e = col % dim;
-  // image of merged token t: token offsets are cu_seqlens / m2
+  // image of merged token t
   int img = 0;
-  while (img + 1 < d.n_images && t >= d.cu_seqlens[img + 1] / m2) ++img;
-  const int tl = (int)(t - d.cu_seqlens[img] / m2);
+  while (img + 1 < d.n_images && t >= d.cu_tokens[img + 1]) ++img;
+  const int tl = (int)(t - d.cu_tokens[img]);
   const int gw = d.grid_w[img];
-  const int wq = gw / merge;
+  const int gh = (d.cu_seqlens[img + 1] - d.cu_seqlens[img]) / gw;
+  const int wq = (gw + merge - 1) / merge;  // merged columns (odd grids zero-padded)
   const int gi = tl / wq, gj = tl % wq;
-  const int src = d.cu_seqlens[img] + (merge * gi + s / merge) * gw + merge * gj + s % merge;
-  st16(G + t * (int64_t)m2 * dim + col, ld16(x + (int64_t)src * dim + e));
+  const int r = merge * gi + s / merge, c = merge * gj + s % merge;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (r < gh && c < gw) v = ld16(x + ((int64_t)d.cu_seqlens[img] + r * gw + c) * dim + e);
+  st16(G + t * (int64_t)m2 * dim + col, v);
 }
 
 // Copy rows [rows, cols] into [rows, ld_dst] zero-padding columns cols..ld_dst-1.
@@ -296,18 +299,17 @@ __global__ void layout_kernel(int gh, int gw, int merge, int32_t* perm, int32_t*
 
 // Output row of every merged token when the aligner writes newline-layout spans.
 __global__ void nl_rowmap_kernel(VarlenDesc d, int merge, int32_t* rowmap) {
-  const int m2 = merge * merge;
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= d.total / m2) return;
+  if (t >= d.cu_tokens[d.n_images]) return;
   int img = 0, base = 0;
-  while (img + 1 < d.n_images && t >= d.cu_seqlens[img + 1] / m2) {
-    const int P = d.cu_seqlens[img + 1] - d.cu_seqlens[img];
-    const int wq = d.grid_w[img] / merge, hq = P / d.grid_w[img] / merge;
+  while (img + 1 < d.n_images && t >= d.cu_tokens[img + 1]) {
+    const int wq = (d.grid_w[img] + merge - 1) / merge;
+    const int hq = (d.cu_tokens[img + 1] - d.cu_tokens[img]) / wq;
     base += hq * (wq + 1) + 2;
     ++img;
   }
-  const int tl = t - d.cu_seqlens[img] / m2;
-  const int wq = d.grid_w[img] / merge;
+  const int tl = t - d.cu_tokens[img];
+  const int wq = (d.grid_w[img] + merge - 1) / merge;
   rowmap[t] = base + 1 + (tl / wq) * (wq + 1) + tl % wq;
 }
 
@@ -351,7 +353,7 @@ hipError_t launch_rope(int dtype, void* qkv, const void* table, int64_t P, int n
 hipError_t launch_gather(int dtype, const void* x, const VarlenDesc& d, int dim, int merge,
                          void* G, hipStream_t s) {
   const int esz = dtype == VIT_BF16 ? 2 : 4;
-  const int64_t n = (int64_t)d.total * dim * esz / 16;
+  const int64_t n = (int64_t)d.cu_tokens[d.n_images] * merge * merge * dim * esz / 16;
   if (n == 0) return hipSuccess;
   if (dtype == VIT_BF16)
     gather_kernel<bf16><<<blocks_for(n), kThreads, 0, s>>>((const bf16*)x, d, dim, merge,
@@ -446,7 +448,7 @@ hipError_t launch_layout(int grid_h, int grid_w, int merge, int32_t* perm, int32
 }
 
 hipError_t launch_nl_rowmap(const VarlenDesc& d, int merge, int32_t* rowmap, hipStream_t s) {
-  const int n = d.total / (merge * merge);
+  const int n = d.cu_tokens[d.n_images];
   if (n == 0) return hipSuccess;
   nl_rowmap_kernel<<<blocks_for(n), kThreads, 0, s>>>(d, merge, rowmap);
   return hipGetLastError();
