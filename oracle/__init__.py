@@ -35,6 +35,7 @@ from .vit import (  # noqa: F401
     layernorm,
     linear,
     mlp,
+    mlp_half_backward,
     nlayout,
     patch_embed,
     patch_merger,

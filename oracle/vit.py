@@ -197,6 +197,39 @@ def mlp(x, w_gate, w_up, w_down, dtype=np.float64):
     return linear((g / (1.0 + np.exp(-g))) * u, w_down, dtype)
 
 
+def mlp_half_backward(x, norm_w, w_gate, w_up, w_down, dy, eps=1e-6, dtype=np.float64):
+    """Gradients of the MLP half of a block ([VIS] DeepseekV4VisionBlock's second
+    residual branch, y = x + mlp(norm2(x)); [PR] lists backward over ragged grids
+    among the tested paths): given dy = dL/dy, returns dL/d(x, norm_w, w_gate,
+    w_up, w_down) by the chain rule through the steps of ``rmsnorm`` and ``mlp``.
+
+    With r = (mean(x^2) + eps)^-1/2, n = norm_w * x * r, g = n Wg^T, u = n Wu^T,
+    s = sigmoid(g), a = g s u:
+      da = dy Wd,  dWd = dy^T a,
+      dg = da u (s + g s (1 - s)),  du = da g s,
+      dn = dg Wg + du Wu,  dWg = dg^T n,  dWu = du^T n,
+      d norm_w = sum over rows of dn x r,
+      dx = dy + r (norm_w dn) - x r^3 mean(norm_w dn x).
+    """
+    x, dy = _f(x, dtype), _f(dy, dtype)
+    w, wg, wu, wd = (_f(a, dtype) for a in (norm_w, w_gate, w_up, w_down))
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    n = w * x * r
+    g, u = n @ wg.T, n @ wu.T
+    sg = 1.0 / (1.0 + np.exp(-g))
+    a = g * sg * u
+    da = dy @ wd
+    d_wd = dy.T @ a
+    dg = da * u * (sg + g * sg * (1.0 - sg))
+    du = da * g * sg
+    dn = dg @ wg + du @ wu
+    d_wg, d_wu = dg.T @ n, du.T @ n
+    d_w = np.sum(dn * x * r, axis=0)
+    wdn = w * dn
+    dx = dy + r * wdn - x * r ** 3 * np.mean(wdn * x, axis=-1, keepdims=True)
+    return dx, d_w, d_wg, d_wu, d_wd
+
+
 def block(x, blk, cos, sin, n_heads, eps=1e-6, dtype=np.float64):
     """[VIS] DeepseekV4VisionBlock: x += attn(norm1(x)); x += mlp(norm2(x)).
 

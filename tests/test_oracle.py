@@ -685,3 +685,52 @@ def test_aligner_pad_equals_explicit_zero_padding(grid):
     np.testing.assert_array_equal(oracle.aligner_gather(x, gh, gw, pad_odd=True), want)
     types, _ = oracle.nlayout(gh, gw, pad_odd=True)
     assert (types == oracle.NL_IMAGE).sum() == want.shape[0] == (ph // 2) * (pw // 2)
+
+
+# ---------------------------------------------------------------- MLP half backward
+def test_mlp_half_backward_matches_finite_differences():
+    """Central differences of L = sum(dy * (x + mlp(rmsnorm(x, w)))) built from the
+    pinned forward steps, for every input of the MLP half."""
+    rng = _rng(35)
+    P, d, h = 3, 4, 5
+    x = rng.standard_normal((P, d))
+    w = 1.0 + 0.3 * rng.standard_normal(d)
+    wg, wu = rng.standard_normal((h, d)), rng.standard_normal((h, d))
+    wd = rng.standard_normal((d, h))
+    dy = rng.standard_normal((P, d))
+    eps = 1e-3
+
+    def loss(x_, w_, wg_, wu_, wd_):
+        y = x_ + oracle.mlp(oracle.rmsnorm(x_, w_, eps), wg_, wu_, wd_)
+        return float(np.sum(dy * y))
+
+    grads = oracle.mlp_half_backward(x, w, wg, wu, wd, dy, eps)
+    args = [x, w, wg, wu, wd]
+    step = 1e-6
+    for k, (arg, grad) in enumerate(zip(args, grads)):
+        assert grad.shape == arg.shape
+        fd = np.zeros_like(arg)
+        for idx in np.ndindex(arg.shape):
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[k][idx] += step
+            minus[k][idx] -= step
+            fd[idx] = (loss(*plus) - loss(*minus)) / (2 * step)
+        np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-7, err_msg=f"input {k}")
+
+
+def test_mlp_half_backward_zero_branch_passes_dy():
+    """With W_down = 0 the branch is constant zero: dx = dy, and only dW_down is non-zero
+    (it equals dy^T a)."""
+    rng = _rng(36)
+    P, d, h = 5, 8, 6
+    x = rng.standard_normal((P, d))
+    w = np.ones(d)
+    wg, wu = rng.standard_normal((h, d)), rng.standard_normal((h, d))
+    dy = rng.standard_normal((P, d))
+    dx, dw, dwg, dwu, dwd = oracle.mlp_half_backward(x, w, wg, wu, np.zeros((d, h)), dy)
+    np.testing.assert_array_equal(dx, dy)
+    assert not dw.any() and not dwg.any() and not dwu.any()
+    n = oracle.rmsnorm(x, w)
+    g, u = n @ wg.T, n @ wu.T
+    np.testing.assert_allclose(dwd, dy.T @ (g / (1 + np.exp(-g)) * u), rtol=1e-13, atol=1e-13)
