@@ -337,15 +337,107 @@ def bench_projector(args):
     print(json.dumps(result), flush=True)
 
 
+BWD_METRIC = "TFLOP/s through the backward of a block's MLP half (bf16 GEMMs)"
+
+
+def bench_mlp_backward(args):
+    """vit_mlp_backward at the ragged 4-image batch's shape: 3,562 rows, vision_dim
+    1024, MLP hidden 2816 (synthetic fp32 x / dy, bf16 weights).  One step is one
+    backward call: the SwiGLU pre-activations recomputed, da, dn and the three
+    weight gradients (GEMMs), plus norm, cast, transpose and SwiGLU-gradient passes."""
+    import numpy as np
+    import torch
+
+    from vision_transformer_encoder_image_amd import api, synth
+
+    dev = "cuda:0"
+    P, d, h = 3562, 1024, 2816
+    Pp = (P + 63) // 64 * 64
+    host = [synth.random_array((P, d), 100), np.float32(1.0) + synth.random_array((d,), 101, std=0.02),
+            synth.random_array((h, d), 102, std=0.02, bf16=True),
+            synth.random_array((h, d), 103, std=0.02, bf16=True),
+            synth.random_array((d, h), 104, std=0.02, bf16=True), synth.random_array((P, d), 105)]
+    f = lambda a: torch.from_numpy(a).to(dev)
+    b = lambda a: torch.from_numpy(a).to(dev, torch.bfloat16)
+    x, w, wg, wu, wd, dy = f(host[0]), f(host[1]), b(host[2]), b(host[3]), b(host[4]), f(host[5])
+    ws = torch.empty(api._lib.load().vit_mlp_backward_workspace_bytes(P, d, h), dtype=torch.uint8,
+                     device=dev)
+    flops = {"recompute": 4.0 * P * h * d, "da": 2.0 * P * d * h, "dn": 4.0 * P * h * d,
+             "wgrad": 6.0 * d * h * Pp}
+    total = sum(flops.values())
+    for _ in range(max(args.warmup, 1)):
+        api.mlp_backward(x, w, wg, wu, wd, dy, ws=ws)
+    torch.cuda.synchronize()
+    for k in ("bwd_gemm", "bwd_dn", "bwd_pass"):
+        api.profile_enable(k, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        api.mlp_backward(x, w, wg, wu, wd, dy, ws=ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per = {}
+    for k in ("bwd_gemm", "bwd_dn", "bwd_pass"):
+        ms, n = api.profile_read(k)
+        api.profile_enable(k, False)
+        per[k] = (ms, n)
+    dn_us = per["bwd_dn"][0] * 1e3 / max(per["bwd_dn"][1], 1)
+    peak = PEAK_TFLOPS["bf16"]
+    achieved = flops["dn"] / (dn_us * 1e-6) / 1e12
+    result = {
+        "metric": BWD_METRIC,
+        "value": round(total * args.steps / elapsed / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mlp_backward_ragged_varlen_4img", "rows": P, "dim": d, "hidden": h,
+                   "flops_per_step": total},
+        "roofline": {"kernel": "bwd_dn", "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None, "avg_launch_us": round(dn_us, 3),
+                     "flops_per_launch": flops["dn"]},
+        "breakdown": {"gemms_us_per_step": round(per["bwd_gemm"][0] * 1e3 / args.steps, 1),
+                      "gemm_tflops": round(total / (per["bwd_gemm"][0] * 1e-3 / args.steps) / 1e12, 1),
+                      "passes_us_per_step": round(per["bwd_pass"][0] * 1e3 / args.steps, 1)},
+    }
+    if not args.no_cpu_baseline:
+        import threadpoolctl
+
+        import oracle
+
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        rows, runs, t0 = 512, 0, time.perf_counter()
+        sample = [host[0][:rows], host[1], host[2], host[3], host[4], host[5][:rows]]
+        while time.perf_counter() - t0 < 10.0:
+            oracle.mlp_half_backward(*sample)
+            runs += 1
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(total * rows / P * runs / dt / 1e12, 4),
+                                  "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+                                  "sample": f"{rows} of {P} rows, {runs} float64 oracle passes "
+                                            f"in {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--stage", choices=("encode", "merge", "projector"), default="encode",
+    ap.add_argument("--stage", choices=("encode", "merge", "projector", "mlp_backward"),
+                    default="encode",
                     help="encode: the encoder step; merge: image tokens into the LLM stream; "
-                         "projector: the PatchMerger projector")
+                         "projector: the PatchMerger projector; mlp_backward: the backward "
+                         "of a block's MLP half")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -372,6 +464,9 @@ def main():
         return
     if args.stage == "projector":
         bench_projector(args)
+        return
+    if args.stage == "mlp_backward":
+        bench_mlp_backward(args)
         return
 
     import torch

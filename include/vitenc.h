@@ -264,6 +264,39 @@ vit_status vit_gemm_bias(int32_t epilogue, const void* A, int64_t lda, const voi
                          const float* bias, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                          void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Backward of the MLP half of an encoder block (DeepseekV4VisionBlock on the
+ * vision page: y = x + mlp(norm2(x)), mlp the bias-free SwiGLU; PR #3772 lists
+ * backward over ragged grids among its tested paths).  Given dy = dL/dy,
+ * computes dL/dx, dL/dnorm_w, dL/dW_gate, dL/dW_up and dL/dW_down, the exact
+ * chain rule of the forward (the SwiGLU pre-activations are recomputed from x).
+ * Rows are independent (patches of any images).  bf16 GEMM operands (x's
+ * normalised rows, dy, the activations and their gradients are rounded to
+ * bf16), fp32 accumulation and fp32 outputs.  dim and hidden multiples of 64,
+ * dim <= 2048.  Every pointer 16-byte aligned, all device memory.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int64_t rows;        /* sum of patches                                  */
+  int32_t dim;         /* vision_dim d                                    */
+  int32_t hidden;      /* MLP hidden h                                    */
+  float eps;           /* RMSNorm eps                                     */
+  const float* x;      /* [rows, dim] fp32: input of the MLP half         */
+  const float* norm_w; /* [dim] fp32: norm2 scale                         */
+  const void* w_gate;  /* [hidden, dim] bf16                              */
+  const void* w_up;    /* [hidden, dim] bf16                              */
+  const void* w_down;  /* [dim, hidden] bf16                              */
+  const float* dy;     /* [rows, dim] fp32: gradient of y                 */
+  float* dx;           /* [rows, dim] fp32 out: gradient of x (dy + ...)  */
+  float* d_norm_w;     /* [dim] fp32 out                                  */
+  float* d_w_gate;     /* [hidden, dim] fp32 out                          */
+  float* d_w_up;       /* [hidden, dim] fp32 out                          */
+  float* d_w_down;     /* [dim, hidden] fp32 out                          */
+} vit_mlp_grad;
+
+/* Workspace bytes of vit_mlp_backward (0 on bad sizes). */
+size_t vit_mlp_backward_workspace_bytes(int64_t rows, int32_t dim, int32_t hidden);
+vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, void* stream);
+
 /* Image tokens into the LLM input stream (DeepSeek-V4 model page,
  * DeepseekV4Model.merge_image_embeddings): for each position p of a text
  * embedding stream embeds [positions, hidden] (in place, dtype):
@@ -290,8 +323,8 @@ vit_status vit_merge_image_embeddings(int32_t dtype, void* embeds, int64_t posit
 /* ---------------------------------------------------------------------------
  * Kernel timing with HIP events (for measurement tools).  When enabled for a
  * kernel class, every launch of that class inside vit_encode(_varlen),
- * vit_merge_image_embeddings and vit_patch_merger is bracketed by events on the
- * call's stream;
+ * vit_merge_image_embeddings, vit_patch_merger and vit_mlp_backward is bracketed
+ * by events on the call's stream;
  * vit_profile_read synchronises them and returns the summed duration and the
  * launch count, then resets.
  * ------------------------------------------------------------------------- */
@@ -310,7 +343,10 @@ enum {
   VIT_K_LNGATHER = 11,  /* vit_patch_merger: LayerNorm + 2x2 gather */
   VIT_K_PROJ1 = 12,     /* vit_patch_merger: first linear (bias, GELU) */
   VIT_K_PROJ2 = 13,     /* vit_patch_merger: second linear (bias) */
-  VIT_K_COUNT = 14,
+  VIT_K_BWD_GEMM = 14,  /* vit_mlp_backward: every GEMM */
+  VIT_K_BWD_DN = 15,    /* vit_mlp_backward: the GEMM of the normed rows' gradient */
+  VIT_K_BWD_PASS = 16,  /* vit_mlp_backward: norm, casts, transposes, SwiGLU gradient */
+  VIT_K_COUNT = 17,
 };
 vit_status vit_profile_enable(int32_t kernel_class, int32_t on);
 vit_status vit_profile_read(int32_t kernel_class, double* total_ms, int64_t* launches);

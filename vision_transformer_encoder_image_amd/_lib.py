@@ -18,7 +18,8 @@ VIT_MAX_IMAGES = 128
 VIT_EPI_STORE, VIT_EPI_STORE_F32, VIT_EPI_ADD_F32, VIT_EPI_SWIGLU = 0, 1, 2, 3
 VIT_EPI_BIAS, VIT_EPI_BIAS_GELU = 4, 5
 KERNEL_CLASSES = ["embed", "rmsnorm", "qkv", "rope", "attn", "outproj", "gateup", "down",
-                  "gather", "aligner", "merge", "lngather", "proj1", "proj2"]
+                  "gather", "aligner", "merge", "lngather", "proj1", "proj2", "bwd_gemm",
+                  "bwd_dn", "bwd_pass"]
 
 c_i32, c_i64, c_f32, c_vp, c_size = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                      ctypes.c_void_p, ctypes.c_size_t)
@@ -46,6 +47,13 @@ class VitMerger(ctypes.Structure):
                 ("b2", c_vp)]
 
 
+class VitMlpGrad(ctypes.Structure):
+    _fields_ = [("rows", c_i64), ("dim", c_i32), ("hidden", c_i32), ("eps", c_f32),
+                ("x", c_vp), ("norm_w", c_vp), ("w_gate", c_vp), ("w_up", c_vp), ("w_down", c_vp),
+                ("dy", c_vp), ("dx", c_vp), ("d_norm_w", c_vp), ("d_w_gate", c_vp),
+                ("d_w_up", c_vp), ("d_w_down", c_vp)]
+
+
 # name -> (restype, argtypes); every function declared in include/vitenc.h
 SIGNATURES = {
     "vit_status_str": (ctypes.c_char_p, [c_i32]),
@@ -71,6 +79,8 @@ SIGNATURES = {
     "vit_layernorm_gather": (c_i32, [c_vp, P_i32, c_i32, c_i32, c_vp, c_vp, c_f32, c_vp, c_vp]),
     "vit_gemm_bias": (c_i32, [c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_i64, c_i64,
                               c_i64, c_vp]),
+    "vit_mlp_backward_workspace_bytes": (c_size, [c_i64, c_i32, c_i32]),
+    "vit_mlp_backward": (c_i32, [ctypes.POINTER(VitMlpGrad), c_vp, c_size, c_vp]),
     "vit_merge_workspace_bytes": (c_size, [c_i64]),
     "vit_merge_image_embeddings": (c_i32, [c_i32, c_vp, c_i64, c_i32, c_vp, c_vp, c_i64, c_vp,
                                            c_vp, c_vp, c_size, c_vp]),

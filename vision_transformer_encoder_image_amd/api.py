@@ -326,6 +326,31 @@ def gemm_bias(A: torch.Tensor, B: torch.Tensor, bias: torch.Tensor, gelu: bool =
     return C
 
 
+def mlp_backward(x: torch.Tensor, norm_w: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
+                 w_down: torch.Tensor, dy: torch.Tensor, eps: float = 1e-6,
+                 ws: Optional[torch.Tensor] = None):
+    """vit_mlp_backward: gradients of y = x + mlp(norm2(x)) for dy; returns
+    (dx, d_norm_w, d_w_gate, d_w_up, d_w_down), all float32."""
+    _require_cuda(x, norm_w, w_gate, w_up, w_down, dy, ws)
+    P, d = x.shape
+    h = w_gate.shape[0]
+    lib = _lib.load()
+    need = lib.vit_mlp_backward_workspace_bytes(P, d, h)
+    if need == 0:
+        _lib.check(_lib.VIT_E_SHAPE, "vit_mlp_backward_workspace_bytes")
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    f32 = dict(dtype=torch.float32, device=x.device)
+    dx, dnw = torch.empty((P, d), **f32), torch.empty(d, **f32)
+    dwg, dwu, dwd = torch.empty((h, d), **f32), torch.empty((h, d), **f32), torch.empty((d, h), **f32)
+    args = _lib.VitMlpGrad(P, d, h, eps, x.data_ptr(), norm_w.data_ptr(), w_gate.data_ptr(),
+                           w_up.data_ptr(), w_down.data_ptr(), dy.data_ptr(), dx.data_ptr(),
+                           dnw.data_ptr(), dwg.data_ptr(), dwu.data_ptr(), dwd.data_ptr())
+    st = lib.vit_mlp_backward(ctypes.byref(args), ws.data_ptr(), ws.numel(), _stream(x.device))
+    _lib.check(st, "vit_mlp_backward")
+    return dx, dnw, dwg, dwu, dwd
+
+
 def merge_workspace_bytes(positions: int) -> int:
     n = _lib.load().vit_merge_workspace_bytes(int(positions))
     if n == 0:

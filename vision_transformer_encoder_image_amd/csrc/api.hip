@@ -58,7 +58,7 @@ struct ProfScope {
   ProfScope(int c, hipStream_t st) : cls(c), s(st) {
     Prof& p = prof();
     std::lock_guard<std::mutex> lk(p.mu);
-    if (!p.on[cls]) return;
+    if (cls < 0 || cls >= VIT_K_COUNT || !p.on[cls]) return;  // -1: not timed
     if (p.used[cls] == p.ev[cls].size()) {
       hipEvent_t a, b;
       if (hipEventCreate(&a) != hipSuccess) return;
@@ -468,6 +468,48 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
   return VIT_OK;
 }
 
+// Backward of the MLP half: workspace layout
+struct MlpGradPlan {
+  int64_t Pp = 0;  // rows rounded up to 64 (K of the weight-gradient GEMMs)
+  size_t n = 0, dy16 = 0, gu = 0, da = 0, a = 0, dgdu = 0, dn = 0, wdT = 0, wguT = 0;
+  size_t dyT = 0, aT = 0, dgduT = 0, nT = 0, partial = 0, total = 0;
+};
+
+MlpGradPlan mlp_grad_plan(int64_t P, int64_t d, int64_t h) {
+  MlpGradPlan p;
+  p.Pp = round_up(P, 64);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (size_t)round_up((int64_t)bytes, 256);
+    return o;
+  };
+  p.n = take(P * d * 2);
+  p.dy16 = take(P * d * 2);
+  p.gu = take(P * 2 * h * 4);
+  p.da = take(P * h * 4);
+  p.a = take(P * h * 2);
+  p.dgdu = take(P * 2 * h * 2);
+  p.dn = take(P * d * 4);
+  p.wdT = take(h * d * 2);
+  p.wguT = take(d * 2 * h * 2);
+  p.dyT = take(d * p.Pp * 2);
+  p.aT = take(h * p.Pp * 2);
+  p.dgduT = take(2 * h * p.Pp * 2);
+  p.nT = take(d * p.Pp * 2);
+  p.partial = take((size_t)rmsnorm_bwd_blocks(P) * d * 4);
+  p.total = off;
+  return p;
+}
+
+vit_status check_mlp_grad_sizes(int64_t rows, int32_t dim, int32_t hidden) {
+  if (rows < 1 || rows > (1 << 24)) return fail(VIT_E_SHAPE, "rows %lld out of range", (long long)rows);
+  if (dim <= 0 || dim % 64 || dim > 2048)
+    return fail(VIT_E_SHAPE, "dim %d: need a multiple of 64, at most 2048", dim);
+  if (hidden <= 0 || hidden % 64) return fail(VIT_E_SHAPE, "hidden %d: need a multiple of 64", hidden);
+  return VIT_OK;
+}
+
 // PatchMerger projector: argument checks and workspace layout
 vit_status check_merger(const vit_merger* m) {
   if (!m) return fail(VIT_E_ARG, "merger is NULL");
@@ -755,6 +797,113 @@ vit_status vit_gemm_bias(int32_t epilogue, const void* A, int64_t lda, const voi
   if (!gemm_bf16_mfma_eligible(g))
     return fail(VIT_E_SHAPE, "bias GEMM needs K %% 64 == 0, N %% 4 == 0, 16-byte aligned rows");
   return hip_check(launch_gemm_bf16(epilogue, g, (hipStream_t)stream), "bias gemm");
+}
+
+size_t vit_mlp_backward_workspace_bytes(int64_t rows, int32_t dim, int32_t hidden) {
+  if (check_mlp_grad_sizes(rows, dim, hidden) != VIT_OK) return 0;
+  return mlp_grad_plan(rows, dim, hidden).total;
+}
+
+vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, void* stream) {
+  if (!a) return fail(VIT_E_ARG, "arguments are NULL");
+  VIT_TRY(check_mlp_grad_sizes(a->rows, a->dim, a->hidden));
+  if (!(a->eps >= 0.f)) return fail(VIT_E_ARG, "eps must be >= 0");
+  const void* ptrs[] = {a->x, a->norm_w, a->w_gate, a->w_up, a->w_down, a->dy, a->dx,
+                        a->d_norm_w, a->d_w_gate, a->d_w_up, a->d_w_down};
+  for (const void* q : ptrs) {
+    if (!q) return fail(VIT_E_ARG, "NULL pointer");
+    if (misaligned16(q)) return fail(VIT_E_ARG, "buffers must be 16-byte aligned");
+  }
+  const int64_t P = a->rows, d = a->dim, h = a->hidden;
+  const MlpGradPlan p = mlp_grad_plan(P, d, h);
+  if (!ws || ws_bytes < p.total || misaligned16(ws))
+    return fail(VIT_E_WORKSPACE, "workspace %zu < %zu (or misaligned)", ws ? ws_bytes : (size_t)0,
+                p.total);
+  char* base = (char*)ws;
+  bf16* n = (bf16*)(base + p.n);
+  bf16* dy16 = (bf16*)(base + p.dy16);
+  float* gu = (float*)(base + p.gu);
+  float* da = (float*)(base + p.da);
+  bf16* act = (bf16*)(base + p.a);
+  bf16* dgdu = (bf16*)(base + p.dgdu);
+  float* dn = (float*)(base + p.dn);
+  bf16* wdT = (bf16*)(base + p.wdT);
+  bf16* wguT = (bf16*)(base + p.wguT);
+  bf16* dyT = (bf16*)(base + p.dyT);
+  bf16* aT = (bf16*)(base + p.aT);
+  bf16* dgduT = (bf16*)(base + p.dgduT);
+  bf16* nT = (bf16*)(base + p.nT);
+  float* partial = (float*)(base + p.partial);
+  hipStream_t s = (hipStream_t)stream;
+  auto mm = [&](const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                int64_t M, int64_t N, int64_t K, bool dn_gemm = false) -> vit_status {
+    GemmArgs g = gemm_args(A, lda, B, nullptr, ldb, C, ldc, M, N, K, nullptr);
+    if (!gemm_bf16_mfma_eligible(g)) return fail(VIT_E_SHAPE, "backward GEMM %lldx%lldx%lld too large",
+                                                 (long long)M, (long long)N, (long long)K);
+    ProfScope all(VIT_K_BWD_GEMM, s);
+    ProfScope one(dn_gemm ? VIT_K_BWD_DN : -1, s);
+    return hip_check(launch_gemm_bf16(VIT_EPI_STORE_F32, g, s), "backward gemm");
+  };
+  // the memory-bound passes below are each timed as VIT_K_BWD_PASS
+  // forward recomputation: n = bf16(norm2(x)), g and u (fp32, side by side)
+  {
+    ProfScope ps(VIT_K_BWD_PASS, s);
+    VIT_HIP(launch_rmsnorm(a->x, a->norm_w, a->eps, P, (int)d, VIT_BF16, n, s), "norm");
+  }
+  VIT_TRY(mm(n, d, a->w_gate, d, gu, 2 * h, P, h, d));
+  VIT_TRY(mm(n, d, a->w_up, d, gu + h, 2 * h, P, h, d));
+  // da = dy . W_down
+  {
+    ProfScope ps(VIT_K_BWD_PASS, s);
+    VIT_HIP(launch_cast_bf16(a->dy, P * d, dy16, s), "cast dy");
+  }
+  {
+    ProfScope ps(VIT_K_BWD_PASS, s);
+    VIT_HIP(launch_transpose_bf16(a->w_down, d, h, h, wdT, d, d, s), "transpose W_down");
+  }
+  VIT_TRY(mm(dy16, d, wdT, d, da, h, P, h, d));
+  // SwiGLU gradient (and the activation for dW_down)
+  {
+    ProfScope ps(VIT_K_BWD_PASS, s);
+    VIT_HIP(launch_swiglu_bwd(gu, da, P, (int)h, act, dgdu, s), "swiglu backward");
+  }
+  // dn = dg . W_gate + du . W_up
+  {
+    ProfScope ps(VIT_K_BWD_PASS, s);
+    VIT_HIP(launch_transpose_bf16(a->w_gate, h, d, d, wguT, h, 2 * h, s), "transpose W_gate");
+  }
+  {
+    ProfScope ps(VIT_K_BWD_PASS, s);
+    VIT_HIP(launch_transpose_bf16(a->w_up, h, d, d, wguT + h, h, 2 * h, s), "transpose W_up");
+  }
+  VIT_TRY(mm(dgdu, 2 * h, wguT, 2 * h, dn, d, P, d, 2 * h, true));
+  // RMSNorm gradient + residual, and the norm scale gradient
+  {
+    ProfScope ps(VIT_K_BWD_PASS, s);
+    VIT_HIP(launch_rmsnorm_bwd(a->x, a->norm_w, dn, a->dy, P, (int)d, a->eps, a->dx, partial,
+                               a->d_norm_w, s),
+            "norm backward");
+  }
+  // weight gradients: contractions over the rows (zero-padded to Pp)
+  {
+    ProfScope ps(VIT_K_BWD_PASS, s);
+    VIT_HIP(launch_transpose_bf16(dy16, P, d, d, dyT, p.Pp, p.Pp, s), "transpose dy");
+  }
+  {
+    ProfScope ps(VIT_K_BWD_PASS, s);
+    VIT_HIP(launch_transpose_bf16(act, P, h, h, aT, p.Pp, p.Pp, s), "transpose a");
+  }
+  {
+    ProfScope ps(VIT_K_BWD_PASS, s);
+    VIT_HIP(launch_transpose_bf16(dgdu, P, 2 * h, 2 * h, dgduT, p.Pp, p.Pp, s), "transpose dg, du");
+  }
+  {
+    ProfScope ps(VIT_K_BWD_PASS, s);
+    VIT_HIP(launch_transpose_bf16(n, P, d, d, nT, p.Pp, p.Pp, s), "transpose n");
+  }
+  VIT_TRY(mm(dyT, p.Pp, aT, p.Pp, a->d_w_down, h, d, h, p.Pp));
+  VIT_TRY(mm(dgduT, p.Pp, nT, p.Pp, a->d_w_gate, d, h, d, p.Pp));
+  return mm(dgduT + h * p.Pp, p.Pp, nT, p.Pp, a->d_w_up, d, h, d, p.Pp);
 }
 
 vit_status vit_profile_enable(int32_t cls, int32_t on) {

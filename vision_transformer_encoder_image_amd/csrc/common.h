@@ -229,6 +229,17 @@ hipError_t launch_nl_rowmap(const VarlenDesc& d, int merge, int32_t* rowmap, hip
 // of G [sum P/4, 4*dim] (projector.hip); dim % 8 == 0, dim <= 4096
 hipError_t launch_ln_gather(const void* x, const VarlenDesc& d, int dim, const float* w,
                             const float* b, float eps, void* G, hipStream_t s);
+// backward of the MLP half of a block (backward.hip)
+hipError_t launch_cast_bf16(const float* src, int64_t n, void* dst, hipStream_t s);
+// dst [C, ld_dst] = src [R, C]^T, columns R .. cols_out-1 zero (bf16, ld % 8 == 0)
+hipError_t launch_transpose_bf16(const void* src, int64_t R, int64_t C, int64_t ld_src, void* dst,
+                                 int64_t cols_out, int64_t ld_dst, hipStream_t s);
+hipError_t launch_swiglu_bwd(const float* gu, const float* da, int64_t rows, int h, void* a,
+                             void* dgdu, hipStream_t s);
+int rmsnorm_bwd_blocks(int64_t rows);
+hipError_t launch_rmsnorm_bwd(const float* x, const float* w, const float* dn, const float* dy,
+                              int64_t rows, int d, float eps, float* dx, float* partial,
+                              float* dw, hipStream_t s);
 // image tokens and sentinel rows into a text embedding stream (merge.hip)
 size_t merge_workspace_bytes(int64_t positions);
 // group counts of IMAGE positions, scanned in place in ws; total to n_image (optional)
