@@ -28,6 +28,7 @@ from .vit import (  # noqa: F401
     apply_rope,
     attention,
     attention_probs,
+    attn_half_backward,
     block,
     encode,
     encode_varlen,

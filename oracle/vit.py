@@ -230,6 +230,51 @@ def mlp_half_backward(x, norm_w, w_gate, w_up, w_down, dy, eps=1e-6, dtype=np.fl
     return dx, d_w, d_wg, d_wu, d_wd
 
 
+def attn_half_backward(x, norm_w, wqkv, wo, cos, sin, n_heads, dy, eps=1e-6, dtype=np.float64):
+    """Gradients of the attention half of a block for one image ([VIS]
+    DeepseekV4VisionBlock's first residual branch, y = x + attn(norm1(x)) with the
+    steps of ``block``; reading "backward"): given dy, returns dL/d(x, norm_w,
+    wqkv, wo) by the chain rule.
+
+    With n = norm1(x), [q|k|v] = n Wqkv^T, q', k' the rotated q, k, per head
+    P = softmax(q' k'^T / sqrt(D)) and o = P v:
+      do = dy Wo,  dWo = dy^T o,
+      dv = P^T do,  dP = do v^T,  dS = P (dP - rowsum(dP P)),
+      dq' = dS k' / sqrt(D),  dk' = dS^T q' / sqrt(D),
+      dq, dk = the rotary applied with the opposite angles (its transpose),
+      dn = [dq|dk|dv] Wqkv,  dWqkv = [dq|dk|dv]^T n,
+      then the RMSNorm gradient as in ``mlp_half_backward``, plus dy.
+    """
+    x, dy = _f(x, dtype), _f(dy, dtype)
+    w, wqkv, wo = _f(norm_w, dtype), _f(wqkv, dtype), _f(wo, dtype)
+    P, d = x.shape
+    D = d // n_heads
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    n = w * x * r
+    qkv = n @ wqkv.T
+    q = apply_rope(qkv[:, 0:d].reshape(P, n_heads, D), cos, sin, dtype)
+    k = apply_rope(qkv[:, d:2 * d].reshape(P, n_heads, D), cos, sin, dtype)
+    v = qkv[:, 2 * d:].reshape(P, n_heads, D)
+    probs = attention_probs(q, k, dtype)                    # [H, P, P]
+    o = np.einsum("hqk,khd->qhd", probs, v).reshape(P, d)
+    do = (dy @ wo).reshape(P, n_heads, D)
+    d_wo = dy.T @ o
+    dv = np.einsum("hqk,qhd->khd", probs, do)
+    dp = np.einsum("qhd,khd->hqk", do, v)
+    ds = probs * (dp - np.sum(dp * probs, axis=-1, keepdims=True))
+    dq = np.einsum("hqk,khd->qhd", ds, k) / np.sqrt(D)
+    dk = np.einsum("hqk,qhd->khd", ds, q) / np.sqrt(D)
+    dq = apply_rope(dq, cos, -np.asarray(sin), dtype)
+    dk = apply_rope(dk, cos, -np.asarray(sin), dtype)
+    dqkv = np.concatenate([dq.reshape(P, d), dk.reshape(P, d), dv.reshape(P, d)], axis=1)
+    d_wqkv = dqkv.T @ n
+    dn = dqkv @ wqkv
+    d_w = np.sum(dn * x * r, axis=0)
+    wdn = w * dn
+    dx = dy + r * wdn - x * r ** 3 * np.mean(wdn * x, axis=-1, keepdims=True)
+    return dx, d_w, d_wqkv, d_wo
+
+
 def block(x, blk, cos, sin, n_heads, eps=1e-6, dtype=np.float64):
     """[VIS] DeepseekV4VisionBlock: x += attn(norm1(x)); x += mlp(norm2(x)).
 

@@ -734,3 +734,41 @@ def test_mlp_half_backward_zero_branch_passes_dy():
     n = oracle.rmsnorm(x, w)
     g, u = n @ wg.T, n @ wu.T
     np.testing.assert_allclose(dwd, dy.T @ (g / (1 + np.exp(-g)) * u), rtol=1e-13, atol=1e-13)
+
+
+def test_attn_half_backward_matches_finite_differences():
+    """Central differences of L = sum(dy * (x + attn(norm1(x)))) built from the pinned
+    forward steps (rmsnorm, linear, apply_rope, attention) on a 2x3 grid, 2 heads."""
+    rng = _rng(37)
+    gh, gw, H, D = 2, 3, 2, 4
+    P, d = gh * gw, H * D
+    x = rng.standard_normal((P, d))
+    w = 1.0 + 0.3 * rng.standard_normal(d)
+    wqkv = 0.5 * rng.standard_normal((3 * d, d))
+    wo = rng.standard_normal((d, d))
+    dy = rng.standard_normal((P, d))
+    cos, sin = oracle.rope_table(gh, gw, D, 10000.0)
+    eps = 1e-3
+
+    def loss(x_, w_, wqkv_, wo_):
+        n = oracle.rmsnorm(x_, w_, eps)
+        qkv = oracle.linear(n, wqkv_)
+        q = oracle.apply_rope(qkv[:, :d].reshape(P, H, D), cos, sin)
+        k = oracle.apply_rope(qkv[:, d:2 * d].reshape(P, H, D), cos, sin)
+        v = qkv[:, 2 * d:].reshape(P, H, D)
+        o = oracle.attention(q, k, v).reshape(P, d)
+        return float(np.sum(dy * (x_ + oracle.linear(o, wo_))))
+
+    grads = oracle.attn_half_backward(x, w, wqkv, wo, cos, sin, H, dy, eps)
+    args = [x, w, wqkv, wo]
+    step = 1e-6
+    for k_, (arg, grad) in enumerate(zip(args, grads)):
+        assert grad.shape == arg.shape
+        fd = np.zeros_like(arg)
+        for idx in np.ndindex(arg.shape):
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[k_][idx] += step
+            minus[k_][idx] -= step
+            fd[idx] = (loss(*plus) - loss(*minus)) / (2 * step)
+        np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-7, err_msg=f"input {k_}")
