@@ -297,6 +297,35 @@ typedef struct {
 size_t vit_mlp_backward_workspace_bytes(int64_t rows, int32_t dim, int32_t hidden);
 vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, void* stream);
 
+/* Backward of the attention half of an encoder block (DeepseekV4VisionBlock:
+ * y = x + attn(norm1(x)), attn = wqkv, half-split 2D rotary on q and k, full
+ * bidirectional attention per image and head, out-projection wo).  Given dy,
+ * computes dL/dx, dL/dnorm_w, dL/dwqkv and dL/dwo by the chain rule; q, k, v
+ * and each query's softmax log-sum-exp are recomputed by a forward pass.  bf16
+ * GEMM and attention operands, fp32 accumulation and outputs; head_dim 64
+ * (dim = 64 * n_heads), dim <= 2048.  Images as in vit_encode_varlen (rows of
+ * x / dy concatenated in image order).  Every pointer 16-byte aligned, device. */
+typedef struct {
+  int32_t dim;         /* vision_dim d = 64 * n_heads                     */
+  int32_t n_heads;
+  float rope_theta;
+  float eps;           /* RMSNorm eps                                     */
+  const float* x;      /* [sum P, dim] fp32: input of the attention half  */
+  const float* norm_w; /* [dim] fp32: norm1 scale                         */
+  const void* wqkv;    /* [3*dim, dim] bf16, rows [q; k; v]               */
+  const void* wo;      /* [dim, dim] bf16                                 */
+  const float* dy;     /* [sum P, dim] fp32: gradient of y                */
+  float* dx;           /* [sum P, dim] fp32 out                           */
+  float* d_norm_w;     /* [dim] fp32 out                                  */
+  float* d_wqkv;       /* [3*dim, dim] fp32 out                           */
+  float* d_wo;         /* [dim, dim] fp32 out                             */
+} vit_attn_grad;
+
+size_t vit_attn_backward_workspace_bytes(const vit_attn_grad* a, const int32_t* grid_hw_host,
+                                         int32_t n_images);
+vit_status vit_attn_backward(const vit_attn_grad* a, const int32_t* grid_hw_host,
+                             int32_t n_images, void* ws, size_t ws_bytes, void* stream);
+
 /* Image tokens into the LLM input stream (DeepSeek-V4 model page,
  * DeepseekV4Model.merge_image_embeddings): for each position p of a text
  * embedding stream embeds [positions, hidden] (in place, dtype):

@@ -256,14 +256,17 @@ def attn_half_backward(x, norm_w, wqkv, wo, cos, sin, n_heads, dy, eps=1e-6, dty
     k = apply_rope(qkv[:, d:2 * d].reshape(P, n_heads, D), cos, sin, dtype)
     v = qkv[:, 2 * d:].reshape(P, n_heads, D)
     probs = attention_probs(q, k, dtype)                    # [H, P, P]
-    o = np.einsum("hqk,khd->qhd", probs, v).reshape(P, d)
+    o = np.stack([probs[h] @ v[:, h] for h in range(n_heads)], axis=1).reshape(P, d)
     do = (dy @ wo).reshape(P, n_heads, D)
     d_wo = dy.T @ o
-    dv = np.einsum("hqk,qhd->khd", probs, do)
-    dp = np.einsum("qhd,khd->hqk", do, v)
-    ds = probs * (dp - np.sum(dp * probs, axis=-1, keepdims=True))
-    dq = np.einsum("hqk,khd->qhd", ds, k) / np.sqrt(D)
-    dk = np.einsum("hqk,qhd->khd", ds, q) / np.sqrt(D)
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    for h in range(n_heads):
+        p_h = probs[h]                                      # [queries, keys]
+        dv[:, h] = p_h.T @ do[:, h]
+        dp = do[:, h] @ v[:, h].T
+        ds = p_h * (dp - np.sum(dp * p_h, axis=-1, keepdims=True))
+        dq[:, h] = ds @ k[:, h] / np.sqrt(D)
+        dk[:, h] = ds.T @ q[:, h] / np.sqrt(D)
     dq = apply_rope(dq, cos, -np.asarray(sin), dtype)
     dk = apply_rope(dk, cos, -np.asarray(sin), dtype)
     dqkv = np.concatenate([dq.reshape(P, d), dk.reshape(P, d), dv.reshape(P, d)], axis=1)

@@ -54,6 +54,12 @@ class VitMlpGrad(ctypes.Structure):
                 ("d_w_up", c_vp), ("d_w_down", c_vp)]
 
 
+class VitAttnGrad(ctypes.Structure):
+    _fields_ = [("dim", c_i32), ("n_heads", c_i32), ("rope_theta", c_f32), ("eps", c_f32),
+                ("x", c_vp), ("norm_w", c_vp), ("wqkv", c_vp), ("wo", c_vp), ("dy", c_vp),
+                ("dx", c_vp), ("d_norm_w", c_vp), ("d_wqkv", c_vp), ("d_wo", c_vp)]
+
+
 # name -> (restype, argtypes); every function declared in include/vitenc.h
 SIGNATURES = {
     "vit_status_str": (ctypes.c_char_p, [c_i32]),
@@ -79,6 +85,8 @@ SIGNATURES = {
     "vit_layernorm_gather": (c_i32, [c_vp, P_i32, c_i32, c_i32, c_vp, c_vp, c_f32, c_vp, c_vp]),
     "vit_gemm_bias": (c_i32, [c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_i64, c_i64,
                               c_i64, c_vp]),
+    "vit_attn_backward_workspace_bytes": (c_size, [ctypes.POINTER(VitAttnGrad), P_i32, c_i32]),
+    "vit_attn_backward": (c_i32, [ctypes.POINTER(VitAttnGrad), P_i32, c_i32, c_vp, c_size, c_vp]),
     "vit_mlp_backward_workspace_bytes": (c_size, [c_i64, c_i32, c_i32]),
     "vit_mlp_backward": (c_i32, [ctypes.POINTER(VitMlpGrad), c_vp, c_size, c_vp]),
     "vit_merge_workspace_bytes": (c_size, [c_i64]),

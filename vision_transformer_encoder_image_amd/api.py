@@ -351,6 +351,32 @@ def mlp_backward(x: torch.Tensor, norm_w: torch.Tensor, w_gate: torch.Tensor, w_
     return dx, dnw, dwg, dwu, dwd
 
 
+def attn_backward(x: torch.Tensor, norm_w: torch.Tensor, wqkv: torch.Tensor, wo: torch.Tensor,
+                  dy: torch.Tensor, grids, n_heads: int, theta: float = 10000.0,
+                  eps: float = 1e-6, ws: Optional[torch.Tensor] = None):
+    """vit_attn_backward: gradients of y = x + attn(norm1(x)) for dy over packed
+    images; returns (dx, d_norm_w, d_wqkv, d_wo), all float32."""
+    _require_cuda(x, norm_w, wqkv, wo, dy, ws)
+    P, d = x.shape
+    f32 = dict(dtype=torch.float32, device=x.device)
+    dx, dnw = torch.empty((P, d), **f32), torch.empty(d, **f32)
+    dwqkv, dwo = torch.empty((3 * d, d), **f32), torch.empty((d, d), **f32)
+    args = _lib.VitAttnGrad(d, n_heads, theta, eps, x.data_ptr(), norm_w.data_ptr(),
+                            wqkv.data_ptr(), wo.data_ptr(), dy.data_ptr(), dx.data_ptr(),
+                            dnw.data_ptr(), dwqkv.data_ptr(), dwo.data_ptr())
+    lib = _lib.load()
+    g = _lib.grid_array(grids)
+    need = lib.vit_attn_backward_workspace_bytes(ctypes.byref(args), g, len(grids))
+    if need == 0:
+        _lib.check(_lib.VIT_E_SHAPE, "vit_attn_backward_workspace_bytes")
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    st = lib.vit_attn_backward(ctypes.byref(args), g, len(grids), ws.data_ptr(), ws.numel(),
+                               _stream(x.device))
+    _lib.check(st, "vit_attn_backward")
+    return dx, dnw, dwqkv, dwo
+
+
 def merge_workspace_bytes(positions: int) -> int:
     n = _lib.load().vit_merge_workspace_bytes(int(positions))
     if n == 0:

@@ -510,6 +510,60 @@ vit_status check_mlp_grad_sizes(int64_t rows, int32_t dim, int32_t hidden) {
   return VIT_OK;
 }
 
+// Backward of the attention half: workspace layout
+struct AttnGradPlan {
+  int64_t P = 0, Pp = 0, kv = 0;
+  size_t n = 0, qkv = 0, table = 0, vt = 0, o = 0, lse = 0, dy16 = 0, dO = 0, Dq = 0, qt = 0,
+         kt = 0, dot = 0, dqkv = 0, woT = 0, wqkvT = 0, dn = 0, dyT = 0, oT = 0, dqkvT = 0,
+         nT = 0, partial = 0, total = 0;
+};
+
+AttnGradPlan attn_grad_plan(const VarlenDesc& desc, int64_t d, int64_t H) {
+  AttnGradPlan p;
+  p.P = desc.total;
+  p.Pp = round_up(p.P, 64);
+  p.kv = desc.kv_off[desc.n_images];
+  const int64_t P = p.P;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (size_t)round_up((int64_t)bytes, 256);
+    return o;
+  };
+  p.n = take(P * d * 2);
+  p.qkv = take(P * 3 * d * 2);
+  p.table = take(P * 32 * 8);
+  p.vt = take(d * p.kv * 2);
+  p.o = take(P * d * 2);
+  p.lse = take(H * P * 4);
+  p.dy16 = take(P * d * 2);
+  p.dO = take(P * d * 2);
+  p.Dq = take(H * P * 4);
+  p.qt = take(d * p.kv * 2);
+  p.kt = take(d * p.kv * 2);
+  p.dot = take(d * p.kv * 2);
+  p.dqkv = take(P * 3 * d * 2);
+  p.woT = take(d * d * 2);
+  p.wqkvT = take(d * 3 * d * 2);
+  p.dn = take(P * d * 4);
+  p.dyT = take(d * p.Pp * 2);
+  p.oT = take(d * p.Pp * 2);
+  p.dqkvT = take(3 * d * p.Pp * 2);
+  p.nT = take(d * p.Pp * 2);
+  p.partial = take((size_t)rmsnorm_bwd_blocks(P) * d * 4);
+  p.total = off;
+  return p;
+}
+
+vit_status check_attn_grad(const vit_attn_grad* a) {
+  if (!a) return fail(VIT_E_ARG, "arguments are NULL");
+  if (a->n_heads <= 0 || a->dim != 64 * a->n_heads || a->dim > 2048)
+    return fail(VIT_E_SHAPE, "dim %d, n_heads %d: need head_dim 64 and dim <= 2048", a->dim,
+                a->n_heads);
+  if (!(a->eps >= 0.f) || !(a->rope_theta > 0.f)) return fail(VIT_E_ARG, "bad eps / theta");
+  return VIT_OK;
+}
+
 // PatchMerger projector: argument checks and workspace layout
 vit_status check_merger(const vit_merger* m) {
   if (!m) return fail(VIT_E_ARG, "merger is NULL");
@@ -904,6 +958,102 @@ vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, vo
   VIT_TRY(mm(dyT, p.Pp, aT, p.Pp, a->d_w_down, h, d, h, p.Pp));
   VIT_TRY(mm(dgduT, p.Pp, nT, p.Pp, a->d_w_gate, d, h, d, p.Pp));
   return mm(dgduT + h * p.Pp, p.Pp, nT, p.Pp, a->d_w_up, d, h, d, p.Pp);
+}
+
+size_t vit_attn_backward_workspace_bytes(const vit_attn_grad* a, const int32_t* grid_hw_host,
+                                         int32_t n_images) {
+  if (check_attn_grad(a) != VIT_OK) return 0;
+  VarlenDesc d;
+  if (build_desc(grid_hw_host, n_images, attention_bwd_tile(), false, 2, &d) != VIT_OK) return 0;
+  return attn_grad_plan(d, a->dim, a->n_heads).total;
+}
+
+vit_status vit_attn_backward(const vit_attn_grad* a, const int32_t* grid_hw_host,
+                             int32_t n_images, void* ws, size_t ws_bytes, void* stream) {
+  VIT_TRY(check_attn_grad(a));
+  const void* ptrs[] = {a->x, a->norm_w, a->wqkv, a->wo, a->dy, a->dx, a->d_norm_w, a->d_wqkv,
+                        a->d_wo};
+  for (const void* q : ptrs) {
+    if (!q) return fail(VIT_E_ARG, "NULL pointer");
+    if (misaligned16(q)) return fail(VIT_E_ARG, "buffers must be 16-byte aligned");
+  }
+  VarlenDesc fwd, bwd;  // q-tiles of the forward attention and of the backward kernels
+  VIT_TRY(build_desc(grid_hw_host, n_images, attention_q_tile(VIT_BF16, 64), false, 2, &fwd));
+  VIT_TRY(build_desc(grid_hw_host, n_images, attention_bwd_tile(), false, 2, &bwd));
+  const int64_t d = a->dim, H = a->n_heads;
+  const AttnGradPlan p = attn_grad_plan(bwd, d, H);
+  const int64_t P = p.P;
+  if (!ws || ws_bytes < p.total || misaligned16(ws))
+    return fail(VIT_E_WORKSPACE, "workspace %zu < %zu (or misaligned)", ws ? ws_bytes : (size_t)0,
+                p.total);
+  char* base = (char*)ws;
+  bf16* n = (bf16*)(base + p.n);
+  bf16* qkv = (bf16*)(base + p.qkv);
+  void* table = base + p.table;
+  bf16* vt = (bf16*)(base + p.vt);
+  bf16* o = (bf16*)(base + p.o);
+  float* lse = (float*)(base + p.lse);
+  bf16* dy16 = (bf16*)(base + p.dy16);
+  bf16* dO = (bf16*)(base + p.dO);
+  float* Dq = (float*)(base + p.Dq);
+  bf16* qt = (bf16*)(base + p.qt);
+  bf16* kt = (bf16*)(base + p.kt);
+  bf16* dot = (bf16*)(base + p.dot);
+  bf16* dqkv = (bf16*)(base + p.dqkv);
+  bf16* woT = (bf16*)(base + p.woT);
+  bf16* wqkvT = (bf16*)(base + p.wqkvT);
+  float* dn = (float*)(base + p.dn);
+  bf16* dyT = (bf16*)(base + p.dyT);
+  bf16* oT = (bf16*)(base + p.oT);
+  bf16* dqkvT = (bf16*)(base + p.dqkvT);
+  bf16* nT = (bf16*)(base + p.nT);
+  float* partial = (float*)(base + p.partial);
+  hipStream_t s = (hipStream_t)stream;
+  auto mm = [&](int epi, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                int64_t ldc, int64_t M, int64_t N, int64_t K) -> vit_status {
+    GemmArgs g = gemm_args(A, lda, B, nullptr, ldb, C, ldc, M, N, K, nullptr);
+    if (!gemm_bf16_mfma_eligible(g)) return fail(VIT_E_SHAPE, "backward GEMM %lldx%lldx%lld too large",
+                                                 (long long)M, (long long)N, (long long)K);
+    ProfScope all(VIT_K_BWD_GEMM, s);
+    return hip_check(launch_gemm_bf16(epi, g, s), "backward gemm");
+  };
+  // forward recomputation: n, rotated q, k and v, attention output and lse
+  VIT_HIP(launch_rmsnorm(a->x, a->norm_w, a->eps, P, (int)d, VIT_BF16, n, s), "norm");
+  VIT_TRY(mm(VIT_EPI_STORE, n, d, a->wqkv, d, qkv, 3 * d, P, 3 * d, d));
+  VIT_HIP(launch_rope_table(fwd, 64, a->rope_theta, table, s), "rope table");
+  VIT_HIP(launch_rope(VIT_BF16, qkv, table, P, (int)H, 64, s), "rope");
+  VIT_HIP(launch_vt_pack(qkv, fwd, (int)H, 64, vt, p.kv, s), "pack V");
+  {
+    ProfScope ps(VIT_K_ATTN, s);
+    VIT_HIP(launch_attention_vt(qkv, 3 * d, vt, p.kv, fwd, (int)H, o, s, lse), "attention");
+  }
+  // dO = dy . Wo, Dq = rowsum(dO o), transposed operands of the attention gradient
+  VIT_HIP(launch_cast_bf16(a->dy, P * d, dy16, s), "cast dy");
+  VIT_HIP(launch_transpose_bf16(a->wo, d, d, d, woT, d, d, s), "transpose wo");
+  VIT_TRY(mm(VIT_EPI_STORE, dy16, d, woT, d, dO, d, P, d, d));
+  VIT_HIP(launch_rowdot(dO, o, P, (int)H, Dq, s), "rowsum(dO o)");
+  VIT_HIP(launch_tpack(qkv, 3 * d, 0, fwd, (int)H, qt, p.kv, s), "pack Q^T");
+  VIT_HIP(launch_tpack(qkv, 3 * d, d, fwd, (int)H, kt, p.kv, s), "pack K^T");
+  VIT_HIP(launch_tpack(dO, d, 0, fwd, (int)H, dot, p.kv, s), "pack dO^T");
+  {
+    ProfScope ps(VIT_K_BWD_DN, s);
+    VIT_HIP(launch_attention_bwd(qkv, 3 * d, dO, qt, kt, dot, p.kv, lse, Dq, table, bwd, (int)H,
+                                 dqkv, 3 * d, s),
+            "attention backward");
+  }
+  // dn = dqkv . Wqkv, then the norm gradient and the residual
+  VIT_HIP(launch_transpose_bf16(a->wqkv, 3 * d, d, d, wqkvT, 3 * d, 3 * d, s), "transpose wqkv");
+  VIT_TRY(mm(VIT_EPI_STORE_F32, dqkv, 3 * d, wqkvT, 3 * d, dn, d, P, d, 3 * d));
+  VIT_HIP(launch_rmsnorm_bwd(a->x, a->norm_w, dn, a->dy, P, (int)d, a->eps, a->dx, partial,
+                             a->d_norm_w, s),
+          "norm backward");
+  // weight gradients: contractions over the rows (zero-padded to Pp)
+  VIT_HIP(launch_transpose_bf16(dy16, P, d, d, dyT, p.Pp, p.Pp, s), "transpose dy");
+  VIT_HIP(launch_transpose_bf16(o, P, d, d, oT, p.Pp, p.Pp, s), "transpose o");
+  VIT_HIP(launch_transpose_bf16(dqkv, P, 3 * d, 3 * d, dqkvT, p.Pp, p.Pp, s), "transpose dqkv");
+  VIT_HIP(launch_transpose_bf16(n, P, d, d, nT, p.Pp, p.Pp, s), "transpose n");
+  VIT_TRY(mm(VIT_EPI_STORE_F32, dyT, p.Pp, oT, p.Pp, a->d_wo, d, d, d, p.Pp));
+  return mm(VIT_EPI_STORE_F32, dqkvT, p.Pp, nT, p.Pp, a->d_wqkv, d, 3 * d, d, p.Pp);
 }
 
 vit_status vit_profile_enable(int32_t cls, int32_t on) {

@@ -263,7 +263,8 @@ VIT_DEV int vt_swz(int row) { return (row >> 1) & 7; }
 __global__ __launch_bounds__(64 * VT_WAVES, 1) void attn_vt_kernel(const bf16* __restrict__ qk, int64_t ldq,
                                                          const bf16* __restrict__ vt,
                                                          int64_t vt_ld, VarlenDesc desc, int H,
-                                                         bf16* __restrict__ out, float c) {
+                                                         bf16* __restrict__ out, float c,
+                                                         float* __restrict__ lse2) {
   __shared__ __attribute__((aligned(16))) bf16 sm[VT_STAGES][2][VT_BKV * 64];
   // 1D grid over (head, q-tile); workgroup ids are dealt round-robin to the 8
   // XCDs, so give every XCD a contiguous range of work items: the q-tiles of one
@@ -476,6 +477,8 @@ __global__ __launch_bounds__(64 * VT_WAVES, 1) void attn_vt_kernel(const bf16* _
   const float inv = 1.0f / l;
   const int qi = q0 + wave * 32 + fr;
   if (qi < P) {
+    // base-2 log-sum-exp of the scaled scores, log2(sum 2^(s c)), for the backward
+    if (lse2 && fh == 0) lse2[(int64_t)h * desc.total + seq0 + qi] = mref * c + __log2f(l);
     bf16* orow = out + (int64_t)(seq0 + qi) * dm + h * 64;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -547,13 +550,14 @@ __global__ __launch_bounds__(FQ) void attn_f32_kernel(const float* __restrict__ 
 int attention_q_tile(int dtype, int /*head_dim*/) { return dtype == VIT_BF16 ? BQ_DESC : FQ; }
 
 hipError_t launch_attention_vt(const void* qk, int64_t ld_qk, const void* vt, int64_t vt_ld,
-                               const VarlenDesc& d, int n_heads, void* out, hipStream_t s) {
+                               const VarlenDesc& d, int n_heads, void* out, hipStream_t s,
+                               float* lse2) {
   static_assert(VT_BQ == BQ_DESC && 2 * BQ == BQ_DESC, "both bf16 kernels share the q-tile descriptor");
   const int tiles = d.cu_tiles[d.n_images];
   if (tiles == 0) return hipSuccess;
   const float c = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
   attn_vt_kernel<<<dim3((unsigned)(tiles * n_heads)), 64 * VT_WAVES, 0, s>>>(
-      (const bf16*)qk, ld_qk, (const bf16*)vt, vt_ld, d, n_heads, (bf16*)out, c);
+      (const bf16*)qk, ld_qk, (const bf16*)vt, vt_ld, d, n_heads, (bf16*)out, c, lse2);
   return hipGetLastError();
 }
 

@@ -1,0 +1,414 @@
+// Backward of the full bidirectional patch attention (NeMo Automodel vision
+// page, DeepseekV4VisionAttention: per image and head, O = softmax(Q K^T /
+// sqrt(D)) V), bf16 with head_dim 64, varlen (block-diagonal).  With each
+// query's log-sum-exp saved by the forward (base 2, lse2), P is recomputed
+// tile by tile; with Dq = rowsum(dO * O):
+//   dS = P (dO V^T - Dq),  dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D),  dV = P^T dO.
+// Two kernels, no atomics (deterministic):
+//   attn_dq_kernel   32 queries per wave; per 64-key tile: S^T = K Q^T,
+//                    dP^T = V dO^T (Q, dO fragments in registers), then
+//                    dQ^T += K^T dS^T with dS^T straight from the accumulators;
+//   attn_dkv_kernel  32 keys per wave; per 64-query tile: S = Q K^T, dP = dO V^T
+//                    (K, V fragments in registers), then dV^T += dO^T P and
+//                    dK^T += Q^T dS.
+// The transposed operands (K^T, Q^T, dO^T) use the layout of the forward's V^T:
+// [H*64, sum of 64-aligned image spans], the 16-key groups permuted as
+// vt_key_slot, so a lane's 8 contraction slots match the 8 accumulator rows it
+// holds.  Tiles are copied into LDS with global_load_lds_dwordx4 (16-byte chunks
+// XOR-swizzled per 128-byte row), double-buffered, one barrier per tile.
+#include <type_traits>
+
+#include "common.h"
+
+namespace {
+
+constexpr int AB_WAVES = 4;              // waves per workgroup
+constexpr int AB_ROWS = 32 * AB_WAVES;   // queries (dQ) or keys (dK, dV) per workgroup
+constexpr int AB_T = 64;                 // inner tile: keys (dQ) or queries (dK, dV)
+constexpr int kThreads = 256;
+
+VIT_DEV int ab_swz(int row) { return (row >> 1) & 7; }
+
+// dst[h*64 + e][kv_off[img] + slot] = src[cu[img] + vt_key_slot(slot)][col0 + h*64 + e]
+// (zero past the image), for every 64-aligned image span
+__global__ __launch_bounds__(kThreads) void tpack_kernel(const bf16* __restrict__ src,
+                                                         int64_t ld_src, int64_t col0,
+                                                         VarlenDesc d, bf16* __restrict__ dst,
+                                                         int64_t ld) {
+  const int64_t row = blockIdx.y;  // h*64 + e
+  const int col = blockIdx.x * kThreads + threadIdx.x;
+  if (col >= d.kv_off[d.n_images]) return;
+  int img = 0;
+  while (img + 1 < d.n_images && col >= d.kv_off[img + 1]) ++img;
+  const int key = vt_key_slot(col - d.kv_off[img]);
+  const int P = d.cu_seqlens[img + 1] - d.cu_seqlens[img];
+  bf16 v = f2bf(0.f);
+  if (key < P) v = src[(int64_t)(d.cu_seqlens[img] + key) * ld_src + col0 + row];
+  dst[row * ld + col] = v;
+}
+
+// Dq[h * total + p] = sum over e < 64 of dO[p, h*64 + e] * O[p, h*64 + e]
+__global__ __launch_bounds__(kThreads) void rowdot_kernel(const bf16* __restrict__ dO,
+                                                          const bf16* __restrict__ O, int64_t P,
+                                                          int H, float* __restrict__ Dq) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= P * H) return;
+  const int64_t p = i / H;
+  const int h = (int)(i % H);
+  const int64_t base = p * (int64_t)H * 64 + h * 64;
+  float t = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(dO + base + 8 * c));
+    const bf16x8 b = __builtin_bit_cast(bf16x8, ld16(O + base + 8 * c));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t += bf2f(a[e]) * bf2f(b[e]);
+  }
+  Dq[(int64_t)h * P + p] = t;
+}
+
+// work item -> (head, tile), every XCD a contiguous range (as the forward)
+struct Item {
+  int h, img, seq0, P, r0;
+};
+VIT_DEV Item ab_item(const VarlenDesc& desc, int H) {
+  const int ntiles = desc.cu_tiles[desc.n_images];
+  const int nitems = ntiles * H;
+  const int per = nitems / 8, rem = nitems % 8;
+  const int xcd = blockIdx.x % 8;
+  const int item = xcd * per + min(xcd, rem) + (int)blockIdx.x / 8;
+  Item it;
+  it.h = item / ntiles;
+  const int tile = item % ntiles;
+  int img = 0;
+  while (img + 1 < desc.n_images && tile >= desc.cu_tiles[img + 1]) ++img;
+  it.img = img;
+  it.seq0 = desc.cu_seqlens[img];
+  it.P = desc.cu_seqlens[img + 1] - it.seq0;
+  it.r0 = (tile - desc.cu_tiles[img]) * AB_ROWS;
+  return it;
+}
+
+// one 1 KB copy (8 rows of 128 bytes) of a row-major [rows][64] tile whose rows
+// r = 8*q .. 8*q+7 are taken from row_ptr(r); chunk position lane % 8 of row
+// lane / 8 holds the row's chunk (lane % 8) ^ ab_swz(row)
+template <typename RowPtr>
+VIT_DEV void ab_copy(RowPtr row_ptr, int q, int lane, bf16* lds_tile) {
+  const int r = 8 * q + (lane >> 3);
+  const int kc = (lane & 7) ^ ab_swz(r);
+  copy16_to_lds(row_ptr(r) + kc * 8, lds_tile + q * 512);
+}
+
+// fragment of row r (16-byte chunk ch) of a swizzled [64][64] tile
+VIT_DEV bf16x8 ab_frag(const bf16* tile, int r, int ch) {
+  return *reinterpret_cast<const bf16x8*>(tile + r * 64 + ((ch ^ ab_swz(r)) << 3));
+}
+
+// The rotary's gradient on a lane's accumulator column: dims 32 db + 8 g + 4 fh + r
+// (acc[db][4 g + r]) of the row at position p; dims i and i + 16 of each
+// 32-dim half (g and g + 2) are rotation partners and sit in the same lane.
+// Rotation by the opposite angles, times `scale`, rounded to bf16 once.
+VIT_DEV void rope_inv_store(const f32x16 (&acc)[2], const float2* __restrict__ table, int64_t p,
+                            int fh, float scale, bf16* row) {
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      bf16x4 lo, hi;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float2 cs = table[p * 32 + db * 16 + 8 * g + 4 * fh + r];
+        const float a1 = acc[db][4 * g + r] * scale, a2 = acc[db][4 * (g + 2) + r] * scale;
+        lo[r] = f2bf(a1 * cs.x + a2 * cs.y);
+        hi[r] = f2bf(a2 * cs.x - a1 * cs.y);
+      }
+      *reinterpret_cast<bf16x4*>(row + db * 32 + g * 8 + fh * 4) = lo;
+      *reinterpret_cast<bf16x4*>(row + db * 32 + (g + 2) * 8 + fh * 4) = hi;
+    }
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64 * AB_WAVES, 1) void attn_dq_kernel(
+    const bf16* __restrict__ qkv, int64_t ldq, const bf16* __restrict__ dO,
+    const bf16* __restrict__ kt, int64_t t_ld, const float* __restrict__ lse2,
+    const float* __restrict__ Dq, VarlenDesc desc, int H, float c,
+    const float2* __restrict__ table, bf16* __restrict__ dq_out, int64_t ld_out) {
+  __shared__ __attribute__((aligned(16))) bf16 sm[2][3][AB_T * 64];  // K, V, K^T
+  const Item it = ab_item(desc, H);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int fr = lane & 31, fh = lane >> 5;
+  const int64_t dm = (int64_t)H * 64;
+  const int h = it.h, P = it.P, seq0 = it.seq0;
+  const int kvo = desc.kv_off[it.img];
+
+  // this lane's query (column of S^T): Q and dO fragments, lse, Dq
+  const int qi = min(it.r0 + wave * 32 + fr, P - 1);
+  bf16x8 qf[4], df[4];
+  {
+    const bf16* qrow = qkv + (int64_t)(seq0 + qi) * ldq + h * 64 + fh * 8;
+    const bf16* drow = dO + (int64_t)(seq0 + qi) * dm + h * 64 + fh * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      qf[ks] = __builtin_bit_cast(bf16x8, ld16(qrow + ks * 16));
+      df[ks] = __builtin_bit_cast(bf16x8, ld16(drow + ks * 16));
+    }
+  }
+  const float lse = lse2[(int64_t)h * desc.total + seq0 + qi];
+  const float dq_ref = Dq[(int64_t)h * desc.total + seq0 + qi];
+
+  auto issue = [&](int t, int st) __attribute__((always_inline)) {
+    const int kv0 = t * AB_T;
+    // 24 copies: 8 of K rows, 8 of V rows, 8 of K^T rows; wave w takes w, w+4, ...
+#pragma unroll
+    for (int i = 0; i < 24 / AB_WAVES; ++i) {
+      const int q = wave + AB_WAVES * i;
+      const int sub = q >> 3;
+      if (sub == 0)
+        ab_copy([&](int r) { return qkv + (int64_t)(seq0 + min(kv0 + r, P - 1)) * ldq + dm + h * 64; },
+                q & 7, lane, sm[st][0]);
+      else if (sub == 1)
+        ab_copy([&](int r) { return qkv + (int64_t)(seq0 + min(kv0 + r, P - 1)) * ldq + 2 * dm + h * 64; },
+                q & 7, lane, sm[st][1]);
+      else
+        ab_copy([&](int r) { return kt + (int64_t)(h * 64 + r) * t_ld + kvo + kv0; }, q & 7, lane,
+                sm[st][2]);
+    }
+  };
+
+  f32x16 acc[2] = {f32x16{}, f32x16{}};  // dQ^T: dims 32*db .. +31 x this wave's queries
+  const int nkv = (P + AB_T - 1) / AB_T;
+  asm volatile("" : "+s"(c));
+  issue(0, 0);
+  for (int t = 0; t < nkv; ++t) {
+    const int st = t & 1;
+    wait_vmcnt<0>();
+    __syncthreads();  // tile t landed; every wave is done with the other buffer
+    if (t + 1 < nkv) issue(t + 1, st ^ 1);
+    // S^T = K Q^T and dP^T = V dO^T: rows = keys (2 blocks of 32), columns = queries
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = ab_frag(sm[st][0], kb * 32 + fr, 2 * ks + fh);
+        const bf16x8 vf = ab_frag(sm[st][1], kb * 32 + fr, 2 * ks + fh);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[ks], dp[kb], 0, 0, 0);
+      }
+    // dS^T = P^T (dP^T - Dq), P^T = 2^(S^T c - lse); keys past the image give 0
+    const int kv0 = t * AB_T;
+    bf16x8 dsf[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = 8 * ks2 + j;
+          const int key = kv0 + kb * 32 + (i >> 2) * 8 + fh * 4 + (i & 3);
+          const float p = key < P ? __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -lse)) : 0.f;
+          dsf[2 * kb + ks2][j] = f2bf(p * (dp[kb][i] - dq_ref));
+        }
+    // dQ^T += K^T dS^T: K^T rows = dims, key slots 32 kb + 16 ks2 + 8 fh .. +7
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int kb = x >> 1, ks2 = x & 1;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const bf16x8 tf = ab_frag(sm[st][2], db * 32 + fr, kb * 4 + ks2 * 2 + fh);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf, dsf[x], acc[db], 0, 0, 0);
+      }
+    }
+  }
+  // dq (rotated space) x 1/sqrt(64), rotated back to the space of wqkv's output
+  const int q = it.r0 + wave * 32 + fr;
+  if (q < P)
+    rope_inv_store(acc, table, seq0 + q, fh, 0.125f, dq_out + (int64_t)(seq0 + q) * ld_out + h * 64);
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64 * AB_WAVES, 1) void attn_dkv_kernel(
+    const bf16* __restrict__ qkv, int64_t ldq, const bf16* __restrict__ dO,
+    const bf16* __restrict__ qt, const bf16* __restrict__ dot, int64_t t_ld,
+    const float* __restrict__ lse2, const float* __restrict__ Dq, VarlenDesc desc, int H, float c,
+    const float2* __restrict__ table, bf16* __restrict__ dkv_out, int64_t ld_out) {
+  // dynamic LDS (65 KB, above the static limit): Q, dO, Q^T, dO^T tiles of two
+  // stages, then the lse and Dq of the tile
+  extern __shared__ __attribute__((aligned(16))) char dkv_smem[];
+  auto sm = reinterpret_cast<bf16 (*)[4][AB_T * 64]>(dkv_smem);
+  auto sl = reinterpret_cast<float (*)[2][AB_T]>(dkv_smem + 2 * 4 * AB_T * 64 * sizeof(bf16));
+  const Item it = ab_item(desc, H);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int fr = lane & 31, fh = lane >> 5;
+  const int64_t dm = (int64_t)H * 64;
+  const int h = it.h, P = it.P, seq0 = it.seq0;
+  const int kvo = desc.kv_off[it.img];
+
+  // this lane's key (column of S): K and V fragments
+  const int ki = min(it.r0 + wave * 32 + fr, P - 1);
+  bf16x8 kf[4], vf[4];
+  {
+    const bf16* krow = qkv + (int64_t)(seq0 + ki) * ldq + dm + h * 64 + fh * 8;
+    const bf16* vrow = qkv + (int64_t)(seq0 + ki) * ldq + 2 * dm + h * 64 + fh * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      kf[ks] = __builtin_bit_cast(bf16x8, ld16(krow + ks * 16));
+      vf[ks] = __builtin_bit_cast(bf16x8, ld16(vrow + ks * 16));
+    }
+  }
+
+  auto issue = [&](int t, int st) __attribute__((always_inline)) {
+    const int q0 = t * AB_T;
+    // 32 copies: Q rows, dO rows, Q^T rows, dO^T rows (8 each); wave w takes w, w+4, ...
+#pragma unroll
+    for (int i = 0; i < 32 / AB_WAVES; ++i) {
+      const int q = wave + AB_WAVES * i;
+      const int sub = q >> 3;
+      if (sub == 0)
+        ab_copy([&](int r) { return qkv + (int64_t)(seq0 + min(q0 + r, P - 1)) * ldq + h * 64; },
+                q & 7, lane, sm[st][0]);
+      else if (sub == 1)
+        ab_copy([&](int r) { return dO + (int64_t)(seq0 + min(q0 + r, P - 1)) * dm + h * 64; },
+                q & 7, lane, sm[st][1]);
+      else if (sub == 2)
+        ab_copy([&](int r) { return qt + (int64_t)(h * 64 + r) * t_ld + kvo + q0; }, q & 7, lane,
+                sm[st][2]);
+      else
+        ab_copy([&](int r) { return dot + (int64_t)(h * 64 + r) * t_ld + kvo + q0; }, q & 7, lane,
+                sm[st][3]);
+    }
+  };
+  // lse and Dq of tile t, one value per thread of the first 128, into registers
+  auto load_stats = [&](int t) __attribute__((always_inline)) {
+    float v = 0.f;
+    if (threadIdx.x < 2 * AB_T) {
+      const int qq = min(t * AB_T + (int)(threadIdx.x & (AB_T - 1)), P - 1);
+      const float* src = threadIdx.x < AB_T ? lse2 : Dq;
+      v = src[(int64_t)h * desc.total + seq0 + qq];
+    }
+    return v;
+  };
+
+  f32x16 dv[2] = {f32x16{}, f32x16{}}, dk[2] = {f32x16{}, f32x16{}};  // dims x keys
+  const int nq = (P + AB_T - 1) / AB_T;
+  asm volatile("" : "+s"(c));
+  issue(0, 0);
+  float stat = load_stats(0);
+  for (int t = 0; t < nq; ++t) {
+    const int st = t & 1;
+    wait_vmcnt<0>();
+    if (threadIdx.x < 2 * AB_T) sl[st][threadIdx.x >> 6][threadIdx.x & (AB_T - 1)] = stat;
+    __syncthreads();  // tile t (and its lse, Dq) landed; every wave is done with the other buffer
+    if (t + 1 < nq) {
+      issue(t + 1, st ^ 1);
+      stat = load_stats(t + 1);
+    }
+    // S = Q K^T and dP = dO V^T: rows = queries (2 blocks of 32), columns = keys
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const bf16x8 qf = ab_frag(sm[st][0], qb * 32 + fr, 2 * ks + fh);
+        const bf16x8 of = ab_frag(sm[st][1], qb * 32 + fr, 2 * ks + fh);
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[ks], s[qb], 0, 0, 0);
+        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, vf[ks], dp[qb], 0, 0, 0);
+      }
+    // P = 2^(S c - lse[q]) (0 for queries past the image), dS = P (dP - Dq[q])
+    const int q0 = t * AB_T;
+    bf16x8 pf[4], dsf[4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row = qb * 32 + g * 8 + fh * 4;  // this lane's rows row .. row+3
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sl[st][0][row]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sl[st][1][row]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * g + r;
+          const float p =
+              q0 + row + r < P ? __builtin_amdgcn_exp2f(fmaf(s[qb][i], c, -l4[r])) : 0.f;
+          pf[2 * qb + (i >> 3)][i & 7] = f2bf(p);
+          dsf[2 * qb + (i >> 3)][i & 7] = f2bf(p * (dp[qb][i] - d4[r]));
+        }
+      }
+    // dV^T += dO^T P, dK^T += Q^T dS: rows = dims, query slots 32 qb + 16 ks2 + 8 fh .. +7
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int qb = x >> 1, ks2 = x & 1;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const bf16x8 of = ab_frag(sm[st][3], db * 32 + fr, qb * 4 + ks2 * 2 + fh);
+        const bf16x8 qtf = ab_frag(sm[st][2], db * 32 + fr, qb * 4 + ks2 * 2 + fh);
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, pf[x], dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtf, dsf[x], dk[db], 0, 0, 0);
+      }
+    }
+  }
+  // dk x 1/sqrt(64) rotated back like dq; dv as is
+  const int k = it.r0 + wave * 32 + fr;
+  if (k < P) {
+    bf16* krow = dkv_out + (int64_t)(seq0 + k) * ld_out + h * 64;
+    bf16* vrow = krow + dm;
+    rope_inv_store(dk, table, seq0 + k, fh, 0.125f, krow);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 b;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) b[r] = f2bf(dv[db][4 * g + r]);
+        *reinterpret_cast<bf16x4*>(vrow + db * 32 + g * 8 + fh * 4) = b;
+      }
+  }
+}
+
+unsigned blocks_of(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+
+}  // namespace
+
+int attention_bwd_tile() { return AB_ROWS; }
+
+hipError_t launch_tpack(const void* src, int64_t ld_src, int64_t col0, const VarlenDesc& d,
+                        int n_heads, void* dst, int64_t ld, hipStream_t s) {
+  const int cols = d.kv_off[d.n_images];
+  if (cols == 0) return hipSuccess;
+  tpack_kernel<<<dim3(blocks_of(cols), (unsigned)(n_heads * 64)), kThreads, 0, s>>>(
+      (const bf16*)src, ld_src, col0, d, (bf16*)dst, ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowdot(const void* dO, const void* O, int64_t P, int n_heads, float* Dq,
+                         hipStream_t s) {
+  if (P == 0) return hipSuccess;
+  rowdot_kernel<<<blocks_of(P * n_heads), kThreads, 0, s>>>((const bf16*)dO, (const bf16*)O, P,
+                                                            n_heads, Dq);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_bwd(const void* qkv, int64_t ldq, const void* dO, const void* qt,
+                                const void* kt, const void* dot, int64_t t_ld, const float* lse2,
+                                const float* Dq, const void* table, const VarlenDesc& d,
+                                int n_heads, void* dqkv, int64_t ld_out, hipStream_t s) {
+  const int tiles = d.cu_tiles[d.n_images];
+  if (tiles == 0) return hipSuccess;
+  const float c = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
+  const dim3 grid((unsigned)(tiles * n_heads));
+  attn_dq_kernel<<<grid, 64 * AB_WAVES, 0, s>>>((const bf16*)qkv, ldq, (const bf16*)dO,
+                                                (const bf16*)kt, t_ld, lse2, Dq, d, n_heads, c,
+                                                (const float2*)table, (bf16*)dqkv, ld_out);
+  constexpr size_t dkv_lds = 2 * 4 * AB_T * 64 * sizeof(bf16) + 2 * 2 * AB_T * sizeof(float);
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute((const void*)attn_dkv_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)dkv_lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  attn_dkv_kernel<<<grid, 64 * AB_WAVES, dkv_lds, s>>>(
+      (const bf16*)qkv, ldq, (const bf16*)dO, (const bf16*)qt, (const bf16*)dot, t_ld, lse2, Dq, d,
+      n_heads, c, (const float2*)table, (bf16*)dqkv + (int64_t)n_heads * 64, ld_out);
+  return hipGetLastError();
+}

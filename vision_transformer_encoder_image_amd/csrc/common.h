@@ -186,8 +186,11 @@ hipError_t launch_rope(int dtype, void* qkv, const void* table, int64_t P, int n
 hipError_t launch_attention(int dtype, const void* qkv, const VarlenDesc& d, int n_heads,
                             int head_dim, void* out, hipStream_t s);
 int attention_q_tile(int dtype, int head_dim);
+// lse2 (optional, [n_heads, total] fp32): each query's log2(sum over keys of 2^(s c)),
+// s the raw q.k score and c = log2(e)/sqrt(64)
 hipError_t launch_attention_vt(const void* qk, int64_t ld_qk, const void* vt, int64_t vt_ld,
-                               const VarlenDesc& d, int n_heads, void* out, hipStream_t s);
+                               const VarlenDesc& d, int n_heads, void* out, hipStream_t s,
+                               float* lse2 = nullptr);
 // Per-call preparation of an encode (bf16): zero-padded patches and patch
 // weight (K padded to Kp), rotary table, transposed-V positions and padding.
 // A null destination skips its part; b[] is filled in by the launcher.
@@ -240,6 +243,21 @@ int rmsnorm_bwd_blocks(int64_t rows);
 hipError_t launch_rmsnorm_bwd(const float* x, const float* w, const float* dn, const float* dy,
                               int64_t rows, int d, float eps, float* dx, float* partial,
                               float* dw, hipStream_t s);
+// backward of the attention (attention_bwd.hip), bf16, head_dim 64
+int attention_bwd_tile();  // queries / keys per workgroup: the q-tile of its descriptor
+// dst [H*64, ld] = columns col0 .. col0+H*64 of src, transposed into the forward's
+// V^T layout (64-aligned image spans, keys permuted by vt_key_slot, zero padding)
+hipError_t launch_tpack(const void* src, int64_t ld_src, int64_t col0, const VarlenDesc& d,
+                        int n_heads, void* dst, int64_t ld, hipStream_t s);
+hipError_t launch_rowdot(const void* dO, const void* O, int64_t P, int n_heads, float* Dq,
+                         hipStream_t s);
+// dq -> columns [0, H*64) of dqkv, dk, dv -> [H*64, 3*H*64), dq and dk rotated back
+// with the rotary table (the gradients before the rotary); q, k, v read from qkv
+// ([P, ldq], rotated q, k); qt, kt, dot in the tpack layout
+hipError_t launch_attention_bwd(const void* qkv, int64_t ldq, const void* dO, const void* qt,
+                                const void* kt, const void* dot, int64_t t_ld, const float* lse2,
+                                const float* Dq, const void* table, const VarlenDesc& d,
+                                int n_heads, void* dqkv, int64_t ld_out, hipStream_t s);
 // image tokens and sentinel rows into a text embedding stream (merge.hip)
 size_t merge_workspace_bytes(int64_t positions);
 // group counts of IMAGE positions, scanned in place in ws; total to n_image (optional)
