@@ -427,13 +427,111 @@ def bench_mlp_backward(args):
     print(json.dumps(result), flush=True)
 
 
+ATTN_BWD_METRIC = "TFLOP/s through the backward of a block's attention half (bf16)"
+
+
+def bench_attn_backward(args):
+    """vit_attn_backward on the ragged 4-image batch (27x37, 37x27, 10x78, 112x7;
+    vision_dim 1024, 16 heads x 64; synthetic fp32 x / dy, bf16 weights).  One step
+    is one backward call: the forward recomputation (norm, wqkv, rotary, attention
+    with log-sum-exp), dO, the attention gradient, the wqkv / out-projection
+    gradients and the norm gradient."""
+    import numpy as np
+    import torch
+
+    from vision_transformer_encoder_image_amd import api, configs, synth
+
+    dev = "cuda:0"
+    cfg = configs.get("ragged_varlen_4img")
+    grids = list(cfg.grids)
+    P, d, H = cfg.total_patches, cfg.vision_dim, cfg.n_heads
+    Pp = (P + 63) // 64 * 64
+    sq = sum((h * w) ** 2 for h, w in grids)
+    host = [synth.random_array((P, d), 140), np.float32(1.0) + synth.random_array((d,), 141, std=0.02),
+            synth.random_array((3 * d, d), 142, std=0.02, bf16=True),
+            synth.random_array((d, d), 143, std=0.02, bf16=True), synth.random_array((P, d), 144)]
+    f = lambda a: torch.from_numpy(a).to(dev)
+    b = lambda a: torch.from_numpy(a).to(dev, torch.bfloat16)
+    x, w, wqkv, wo, dy = f(host[0]), f(host[1]), b(host[2]), b(host[3]), f(host[4])
+    flops = {"recompute": 6.0 * P * d * d + 4.0 * d * sq, "do": 2.0 * P * d * d,
+             "attn": 10.0 * d * sq, "dn": 6.0 * P * d * d, "wgrad": 8.0 * d * d * Pp}
+    total = sum(flops.values())
+    for _ in range(max(args.warmup, 1)):
+        api.attn_backward(x, w, wqkv, wo, dy, grids, H)
+    torch.cuda.synchronize()
+    for k in ("bwd_attn", "bwd_gemm"):
+        api.profile_enable(k, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        api.attn_backward(x, w, wqkv, wo, dy, grids, H)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per = {}
+    for k in ("bwd_attn", "bwd_gemm"):
+        ms, n = api.profile_read(k)
+        api.profile_enable(k, False)
+        per[k] = (ms, n)
+    attn_us = per["bwd_attn"][0] * 1e3 / max(per["bwd_attn"][1], 1)
+    peak = PEAK_TFLOPS["bf16"]
+    achieved = flops["attn"] / (attn_us * 1e-6) / 1e12
+    result = {
+        "metric": ATTN_BWD_METRIC,
+        "value": round(total * args.steps / elapsed / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "attn_backward_ragged_varlen_4img", "grids": [list(g) for g in grids],
+                   "patches": P, "dim": d, "heads": H, "head_dim": 64, "flops_per_step": total},
+        "roofline": {"kernel": "bwd_attn", "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None, "avg_launch_us": round(attn_us, 3),
+                     "flops_per_launch": flops["attn"],
+                     "note": "the dQ and dK/dV kernels together; algorithmic FLOPs 10 d sum(P_i^2) "
+                             "(S recomputed once); the kernels execute 14 d sum(P_i^2)"},
+        "breakdown": {"gemms_us_per_step": round(per["bwd_gemm"][0] * 1e3 / args.steps, 1)},
+    }
+    if not args.no_cpu_baseline:
+        import threadpoolctl
+
+        import oracle
+
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        gh, gw = grids[2]  # the 10x78 image: 780 patches
+        off = grids[0][0] * grids[0][1] + grids[1][0] * grids[1][1]
+        cos, sin = oracle.rope_table(gh, gw, 64, 10000.0)
+        Pi = gh * gw
+        runs, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0:
+            oracle.attn_half_backward(host[0][off:off + Pi], host[1], host[2], host[3], cos, sin, H,
+                                      host[4][off:off + Pi])
+            runs += 1
+        dt = time.perf_counter() - t0
+        sample = 6.0 * Pi * d * d + 4.0 * d * Pi * Pi + 2.0 * Pi * d * d + 10.0 * d * Pi * Pi + \
+            6.0 * Pi * d * d + 8.0 * d * d * Pi
+        result["cpu_baseline"] = {"value": round(sample * runs / dt / 1e12, 4), "unit": "TFLOP/s",
+                                  "cores": int(cores), "kind": "oracle",
+                                  "sample": f"the 10x78 image ({Pi} patches), {runs} float64 "
+                                            f"oracle passes in {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--stage", choices=("encode", "merge", "projector", "mlp_backward"),
+    ap.add_argument("--stage", choices=("encode", "merge", "projector", "mlp_backward",
+                                        "attn_backward"),
                     default="encode",
                     help="encode: the encoder step; merge: image tokens into the LLM stream; "
                          "projector: the PatchMerger projector; mlp_backward: the backward "
@@ -467,6 +565,9 @@ def main():
         return
     if args.stage == "mlp_backward":
         bench_mlp_backward(args)
+        return
+    if args.stage == "attn_backward":
+        bench_attn_backward(args)
         return
 
     import torch

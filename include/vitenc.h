@@ -352,8 +352,8 @@ vit_status vit_merge_image_embeddings(int32_t dtype, void* embeds, int64_t posit
 /* ---------------------------------------------------------------------------
  * Kernel timing with HIP events (for measurement tools).  When enabled for a
  * kernel class, every launch of that class inside vit_encode(_varlen),
- * vit_merge_image_embeddings, vit_patch_merger and vit_mlp_backward is bracketed
- * by events on the call's stream;
+ * vit_merge_image_embeddings, vit_patch_merger, vit_mlp_backward and
+ * vit_attn_backward is bracketed by events on the call's stream;
  * vit_profile_read synchronises them and returns the summed duration and the
  * launch count, then resets.
  * ------------------------------------------------------------------------- */
@@ -375,7 +375,8 @@ enum {
   VIT_K_BWD_GEMM = 14,  /* vit_mlp_backward: every GEMM */
   VIT_K_BWD_DN = 15,    /* vit_mlp_backward: the GEMM of the normed rows' gradient */
   VIT_K_BWD_PASS = 16,  /* vit_mlp_backward: norm, casts, transposes, SwiGLU gradient */
-  VIT_K_COUNT = 17,
+  VIT_K_BWD_ATTN = 17,  /* vit_attn_backward: the dQ and dK/dV kernels */
+  VIT_K_COUNT = 18,
 };
 vit_status vit_profile_enable(int32_t kernel_class, int32_t on);
 vit_status vit_profile_read(int32_t kernel_class, double* total_ms, int64_t* launches);

@@ -116,10 +116,15 @@ def _attn_run(x, w, wqkv, wo, dy, grids, H):
 ATTN_GRAD_TOL = 3e-2
 
 
-def _attn_check(got, ref, tag):
+def _attn_check(got, ref, tag, whole_matrix_weights=False):
+    """Row-wise relative error; with very few rows (whole_matrix_weights) each
+    weight-gradient row is a sum of a handful of products that can nearly cancel,
+    so the weight gradients are measured against the whole matrix instead."""
     for name, g, r in zip(["dx", "d_norm_w", "d_wqkv", "d_wo"], got, ref):
         assert g.shape == r.shape, name
         g2, r2 = (g[None], r[None]) if g.ndim == 1 else (g, r)
+        if whole_matrix_weights and name in ("d_wqkv", "d_wo"):
+            g2, r2 = g2.reshape(1, -1), r2.reshape(1, -1)
         err = rowwise_rel_err(g2, r2)
         print(f"{tag} {name}: row-wise rel err {err:.3e}")
         assert err < ATTN_GRAD_TOL, (name, err)
@@ -129,7 +134,9 @@ def _attn_check(got, ref, tag):
 def test_attn_backward_small_grids_match_oracle(grids):
     H, d = 2, 128
     args = _attn_case(grids, d, seed=110 + len(grids))
-    _attn_check(_attn_run(*args, grids, H), _attn_oracle(*args, grids, H), f"{grids}")
+    rows = sum(h * w for h, w in grids)
+    _attn_check(_attn_run(*args, grids, H), _attn_oracle(*args, grids, H), f"{grids}",
+                whole_matrix_weights=rows < 64)
 
 
 def test_attn_backward_ragged_batch_matches_oracle():

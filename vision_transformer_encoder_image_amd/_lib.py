@@ -19,7 +19,7 @@ VIT_EPI_STORE, VIT_EPI_STORE_F32, VIT_EPI_ADD_F32, VIT_EPI_SWIGLU = 0, 1, 2, 3
 VIT_EPI_BIAS, VIT_EPI_BIAS_GELU = 4, 5
 KERNEL_CLASSES = ["embed", "rmsnorm", "qkv", "rope", "attn", "outproj", "gateup", "down",
                   "gather", "aligner", "merge", "lngather", "proj1", "proj2", "bwd_gemm",
-                  "bwd_dn", "bwd_pass"]
+                  "bwd_dn", "bwd_pass", "bwd_attn"]
 
 c_i32, c_i64, c_f32, c_vp, c_size = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                      ctypes.c_void_p, ctypes.c_size_t)

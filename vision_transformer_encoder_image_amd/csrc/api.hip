@@ -1019,9 +1019,16 @@ vit_status vit_attn_backward(const vit_attn_grad* a, const int32_t* grid_hw_host
   };
   // forward recomputation: n, rotated q, k and v, attention output and lse
   VIT_HIP(launch_rmsnorm(a->x, a->norm_w, a->eps, P, (int)d, VIT_BF16, n, s), "norm");
-  VIT_TRY(mm(VIT_EPI_STORE, n, d, a->wqkv, d, qkv, 3 * d, P, 3 * d, d));
   VIT_HIP(launch_rope_table(fwd, 64, a->rope_theta, table, s), "rope table");
-  VIT_HIP(launch_rope(VIT_BF16, qkv, table, P, (int)H, 64, s), "rope");
+  {
+    // qkv = n . Wqkv^T with the rotary applied to the q and k columns in the epilogue
+    GemmArgs g = gemm_args(n, d, a->wqkv, nullptr, d, qkv, 3 * d, P, 3 * d, d, nullptr);
+    g.rope_table = table;
+    g.rope_cols = 2 * d;
+    if (!gemm_bf16_can_fuse_rope(g)) return fail(VIT_E_SHAPE, "wqkv GEMM too large");
+    ProfScope all(VIT_K_BWD_GEMM, s);
+    VIT_HIP(launch_gemm_bf16(VIT_EPI_STORE_ROPE, g, s), "qkv + rotary gemm");
+  }
   VIT_HIP(launch_vt_pack(qkv, fwd, (int)H, 64, vt, p.kv, s), "pack V");
   {
     ProfScope ps(VIT_K_ATTN, s);
@@ -1036,7 +1043,7 @@ vit_status vit_attn_backward(const vit_attn_grad* a, const int32_t* grid_hw_host
   VIT_HIP(launch_tpack(qkv, 3 * d, d, fwd, (int)H, kt, p.kv, s), "pack K^T");
   VIT_HIP(launch_tpack(dO, d, 0, fwd, (int)H, dot, p.kv, s), "pack dO^T");
   {
-    ProfScope ps(VIT_K_BWD_DN, s);
+    ProfScope ps(VIT_K_BWD_ATTN, s);
     VIT_HIP(launch_attention_bwd(qkv, 3 * d, dO, qt, kt, dot, p.kv, lse, Dq, table, bwd, (int)H,
                                  dqkv, 3 * d, s),
             "attention backward");

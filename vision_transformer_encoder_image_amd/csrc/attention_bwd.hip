@@ -29,24 +29,6 @@ constexpr int kThreads = 256;
 
 VIT_DEV int ab_swz(int row) { return (row >> 1) & 7; }
 
-// dst[h*64 + e][kv_off[img] + slot] = src[cu[img] + vt_key_slot(slot)][col0 + h*64 + e]
-// (zero past the image), for every 64-aligned image span
-__global__ __launch_bounds__(kThreads) void tpack_kernel(const bf16* __restrict__ src,
-                                                         int64_t ld_src, int64_t col0,
-                                                         VarlenDesc d, bf16* __restrict__ dst,
-                                                         int64_t ld) {
-  const int64_t row = blockIdx.y;  // h*64 + e
-  const int col = blockIdx.x * kThreads + threadIdx.x;
-  if (col >= d.kv_off[d.n_images]) return;
-  int img = 0;
-  while (img + 1 < d.n_images && col >= d.kv_off[img + 1]) ++img;
-  const int key = vt_key_slot(col - d.kv_off[img]);
-  const int P = d.cu_seqlens[img + 1] - d.cu_seqlens[img];
-  bf16 v = f2bf(0.f);
-  if (key < P) v = src[(int64_t)(d.cu_seqlens[img] + key) * ld_src + col0 + row];
-  dst[row * ld + col] = v;
-}
-
 // Dq[h * total + p] = sum over e < 64 of dO[p, h*64 + e] * O[p, h*64 + e]
 __global__ __launch_bounds__(kThreads) void rowdot_kernel(const bf16* __restrict__ dO,
                                                           const bf16* __restrict__ O, int64_t P,
@@ -369,15 +351,6 @@ unsigned blocks_of(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads)
 }  // namespace
 
 int attention_bwd_tile() { return AB_ROWS; }
-
-hipError_t launch_tpack(const void* src, int64_t ld_src, int64_t col0, const VarlenDesc& d,
-                        int n_heads, void* dst, int64_t ld, hipStream_t s) {
-  const int cols = d.kv_off[d.n_images];
-  if (cols == 0) return hipSuccess;
-  tpack_kernel<<<dim3(blocks_of(cols), (unsigned)(n_heads * 64)), kThreads, 0, s>>>(
-      (const bf16*)src, ld_src, col0, d, (bf16*)dst, ld);
-  return hipGetLastError();
-}
 
 hipError_t launch_rowdot(const void* dO, const void* O, int64_t P, int n_heads, float* Dq,
                          hipStream_t s) {

@@ -246,18 +246,45 @@ __global__ __launch_bounds__(kThreads) void encode_prep_kernel(PrepArgs a) {
 
 // V part of a packed qkv buffer [P, 3*H*D] -> vt [H*D, ld] (images 64-aligned,
 // padding zeroed).  One thread per element of vt.
-__global__ void vt_pack_kernel(const bf16* __restrict__ qkv, VarlenDesc d, int H, int D,
-                               bf16* __restrict__ vt, int64_t ld) {
-  const int64_t row = blockIdx.y;  // h*D + e
-  const int col = blockIdx.x * blockDim.x + threadIdx.x;
-  if (col >= d.kv_off[d.n_images]) return;
+// Columns col0 .. col0 + H*64 of src [P, ld_src] transposed into the V^T layout:
+// dst[h*64 + e][kv_off[img] + slot] = src[cu[img] + vt_key_slot(slot)][col0 + h*64 + e],
+// zero past the image.  One block per (64-key tile of an image span, head):
+// 64 source rows of 128 bytes into LDS, then 64 destination rows of 64 slots.
+__global__ __launch_bounds__(256) void tpack_kernel(const bf16* __restrict__ src, int64_t ld_src,
+                                                    int64_t col0, VarlenDesc d,
+                                                    bf16* __restrict__ dst, int64_t ld) {
+  __shared__ bf16 tile[64][64 + 2];
+  const int col = blockIdx.x * 64;  // first destination column (a 64-aligned span start + 64 j)
+  const int h = blockIdx.y;
   int img = 0;
   while (img + 1 < d.n_images && col >= d.kv_off[img + 1]) ++img;
-  const int key = vt_key_slot(col - d.kv_off[img]);
+  const int k0 = col - d.kv_off[img];  // first key of the tile
   const int P = d.cu_seqlens[img + 1] - d.cu_seqlens[img];
-  bf16 v = f2bf(0.f);
-  if (key < P) v = qkv[(int64_t)(d.cu_seqlens[img] + key) * 3 * H * D + 2 * H * D + row];
-  vt[row * ld + col] = v;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = threadIdx.x + 256 * k;
+    const int r = q >> 3, ch = q & 7;  // key row, 8-element chunk
+    bf16x8 v;
+    if (k0 + r < P) {
+      v = __builtin_bit_cast(bf16x8, ld16(src + (int64_t)(d.cu_seqlens[img] + k0 + r) * ld_src +
+                                          col0 + h * 64 + ch * 8));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = f2bf(0.f);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[r][ch * 8 + e] = v[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = threadIdx.x + 256 * k;
+    const int e = q >> 3, ch = q & 7;  // destination row (dim), chunk of 8 slots
+    bf16x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = tile[vt_key_slot(ch * 8 + j)][e];
+    st16(dst + (int64_t)(h * 64 + e) * ld + col + ch * 8, __builtin_bit_cast(u32x4, v));
+  }
 }
 
 // Zero columns [c0, c1) of every row of a [rows, ld] buffer.
@@ -431,13 +458,21 @@ hipError_t launch_vt_zero_pads(const VarlenDesc& d, int64_t rows, void* vt, int6
   return hipGetLastError();
 }
 
-hipError_t launch_vt_pack(const void* qkv, const VarlenDesc& d, int n_heads, int head_dim,
-                          void* vt, int64_t vt_ld, hipStream_t s) {
+hipError_t launch_tpack(const void* src, int64_t ld_src, int64_t col0, const VarlenDesc& d,
+                        int n_heads, void* dst, int64_t ld, hipStream_t s) {
   const int cols = d.kv_off[d.n_images];
   if (cols == 0) return hipSuccess;
-  vt_pack_kernel<<<dim3(blocks_for(cols), (unsigned)(n_heads * head_dim)), kThreads, 0, s>>>(
-      (const bf16*)qkv, d, n_heads, head_dim, (bf16*)vt, vt_ld);
+  if (ld_src % 8 || col0 % 8 || ld % 8) return hipErrorInvalidValue;
+  tpack_kernel<<<dim3((unsigned)(cols / 64), (unsigned)n_heads), 256, 0, s>>>(
+      (const bf16*)src, ld_src, col0, d, (bf16*)dst, ld);
   return hipGetLastError();
+}
+
+hipError_t launch_vt_pack(const void* qkv, const VarlenDesc& d, int n_heads, int head_dim,
+                          void* vt, int64_t vt_ld, hipStream_t s) {
+  if (head_dim != 64) return hipErrorInvalidValue;
+  const int64_t dm = (int64_t)n_heads * 64;
+  return launch_tpack(qkv, 3 * dm, 2 * dm, d, n_heads, vt, vt_ld, s);
 }
 
 hipError_t launch_layout(int grid_h, int grid_w, int merge, int32_t* perm, int32_t* nl_type,
