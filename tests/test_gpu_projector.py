@@ -51,7 +51,10 @@ def test_layernorm_gather_matches_oracle(dim):
 
 
 @pytest.mark.parametrize("gelu", [False, True])
-@pytest.mark.parametrize("shape", [(130, 200, 128), (257, 4096, 256), (64, 4608, 4608)])
+# (3000, 5632, 256) takes a column split: 256x256 tiles over 5376 columns, the
+# rest (bias offset by the split) in a second launch of 128x128 tiles
+@pytest.mark.parametrize("shape", [(130, 200, 128), (257, 4096, 256), (64, 4608, 4608),
+                                   (3000, 5632, 256)])
 def test_gemm_bias_matches_oracle(shape, gelu):
     M, N, K = shape
     A = synth.random_array((M, K), 42, bf16=True)

@@ -63,14 +63,17 @@ def test_gemm_full_qkv_shape_sampled_rows():
     assert rowwise_rel_err(got[rows], oracle.linear(A[rows], B)) < 8e-3
 
 
-# Larger shapes, rows sampled: chosen so that the tile cost model takes each of
-# its tile configurations (8-wave 256x128, 8-wave 256x256, 4-wave 192x256 with
+# Larger shapes, rows sampled (every column checked): chosen so that the tile
+# cost model takes each of its tile configurations and column splits (8-wave 256x128, 8-wave 256x256, 4-wave 192x256 with
 # the bf16 store, SwiGLU and fp32 residual-add epilogues), with partial tiles.
 BIG_GEMMS = [((2048, 2304, 1024), "store"), ((4096, 3456, 1152), "store"),
              ((9216, 4096, 1024), "store"), ((4096, 4304, 1152), "swiglu"),
              ((4096, 1152, 4352), "add_f32"), ((9216, 1024, 2816), "add_f32"),
              ((3562, 2816, 1024), "swiglu"), ((3562, 1024, 1024), "add_f32"),
-             ((1024, 4096, 4608), "store")]
+             ((1024, 4096, 4608), "store"),
+             # column-split plans: one round of large tiles, the rest in a second launch
+             ((3562, 4736, 1024), "store"), ((2500, 4736, 1024), "add_f32"),
+             ((3000, 5632, 512), "store_f32"), ((1500, 5632, 640), "swiglu")]
 
 
 @pytest.mark.gpu
@@ -82,7 +85,7 @@ def test_gemm_tile_configs_sampled_rows(shape, epi):
     B2 = synth.random_array((N, K), 13, std=0.03, bf16=True)
     C0 = synth.random_array((M, N), 14)
     code = {"store": _lib.VIT_EPI_STORE, "swiglu": _lib.VIT_EPI_SWIGLU,
-            "add_f32": _lib.VIT_EPI_ADD_F32}[epi]
+            "add_f32": _lib.VIT_EPI_ADD_F32, "store_f32": _lib.VIT_EPI_STORE_F32}[epi]
     C = _dev(C0) if epi == "add_f32" else None
     got = to_np(api.gemm(_dev(A, "bf16"), _dev(B, "bf16"), code,
                          B2=_dev(B2, "bf16") if epi == "swiglu" else None, C=C))
@@ -93,7 +96,7 @@ def test_gemm_tile_configs_sampled_rows(shape, epi):
         ref = oracle.linear(A[rows], B)
     if epi == "add_f32":
         ref = ref + C0[rows]
-    tol = 1e-4 if epi == "add_f32" else 8e-3
+    tol = 1e-4 if epi in ("add_f32", "store_f32") else 8e-3
     assert rowwise_rel_err(got[rows], ref) < tol
 
 

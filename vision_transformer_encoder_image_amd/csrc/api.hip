@@ -725,7 +725,7 @@ vit_status vit_gemm(int32_t dtype, int32_t epilogue, const void* A, int64_t lda,
   if (M >= (1LL << 31) || N >= (1LL << 31) || K >= (1LL << 31))
     return fail(VIT_E_SHAPE, "GEMM dims must stay below 2^31");
   if (dtype == VIT_BF16) {
-    if (K % 8 || lda % 8 || ldb % 8) return fail(VIT_E_SHAPE, "bf16 GEMM needs K, lda, ldb % 8 == 0");
+    if (K % 8 || lda % 8 || ldb % 8) return fail(VIT_E_SHAPE, "bf16 GEMM needs K, lda, ldb multiples of 8");
     if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)(B2 ? B2 : B)) & 15)
       return fail(VIT_E_ARG, "bf16 GEMM operands must be 16-byte aligned");
   }
@@ -736,7 +736,7 @@ vit_status vit_aligner_gather(int32_t dtype, const void* x, const int32_t* grid_
                               int32_t n_images, int32_t d, void* G, void* stream) {
   if (!x || !G) return fail(VIT_E_ARG, "NULL pointer");
   if (dtype != VIT_BF16 && dtype != VIT_F32) return fail(VIT_E_ARG, "bad dtype");
-  if (d <= 0 || (d * (int)esize(dtype)) % 16) return fail(VIT_E_SHAPE, "row bytes must be % 16");
+  if (d <= 0 || (d * (int)esize(dtype)) % 16) return fail(VIT_E_SHAPE, "row bytes must be a multiple of 16");
   VarlenDesc desc;
   VIT_TRY(build_desc(grid_hw_host, n_images, 1, true, 2, &desc));
   return hip_check(launch_gather(dtype, x, desc, d, 2, G, (hipStream_t)stream), "gather");

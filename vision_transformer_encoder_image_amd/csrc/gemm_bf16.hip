@@ -258,25 +258,98 @@ bool pipe_eligible(const GemmArgs& g) {
 // 256x256 tile (which spills with it) is not used.  The 4-wave 128x128 tile is
 // not built: the 8-wave one was never slower.  The folded-RMSNorm producer
 // needs 64-column wave sub-tiles (not 192x256).
-int gemm_mfma_choice(int epilogue, bool norm_producer, int64_t M, int64_t N) {
-  const bool dual = epilogue == VIT_EPI_SWIGLU;
+namespace {
+
+struct TileOpt {
+  int cfg, bm, bn;
+  double eff;
+  bool ok;
+};
+
+constexpr int kCUs = 256;
+
+int tile_opts(int epilogue, bool norm_producer, TileOpt* o) {
   const bool rmw = epilogue == VIT_EPI_ADD_F32;
-  struct Opt { int cfg, bm, bn; double eff; bool ok; };
-  const Opt opts[] = {{GEMM_MFMA_128x128, 128, 128, rmw ? 1.04 : 1.13, true},
-                      {GEMM_MFMA_256x128_W8, 256, 128, rmw ? 1.1 : 1.18, true},
-                      {GEMM_MFMA_256x256_W8, 256, 256, 1.57, !rmw},
-                      {GEMM_MFMA_192x256, 192, 256, rmw ? 1.2 : 1.26, !norm_producer}};
+  o[0] = {GEMM_MFMA_128x128, 128, 128, rmw ? 1.04 : 1.13, true};
+  o[1] = {GEMM_MFMA_256x128_W8, 256, 128, rmw ? 1.1 : 1.18, true};
+  o[2] = {GEMM_MFMA_256x256_W8, 256, 256, 1.57, !rmw};
+  o[3] = {GEMM_MFMA_192x256, 192, 256, rmw ? 1.2 : 1.26, !norm_producer};
+  return 4;
+}
+
+// output columns of one tile (the SwiGLU tile holds gate and up halves)
+int64_t tile_cols(const TileOpt& o, int epilogue) {
+  return epilogue == VIT_EPI_SWIGLU ? o.bn / 2 : o.bn;
+}
+
+double tile_cost(const TileOpt& o, int epilogue, int64_t M, int64_t N) {
+  const int64_t bno = tile_cols(o, epilogue);
+  const int64_t tiles = ((M + o.bm - 1) / o.bm) * ((N + bno - 1) / bno);
+  return (double)((tiles + kCUs - 1) / kCUs) * o.bm * o.bn / o.eff;
+}
+
+int best_tile(int epilogue, bool norm_producer, int64_t M, int64_t N, double* cost) {
+  TileOpt opts[4];
+  const int n = tile_opts(epilogue, norm_producer, opts);
   int best = GEMM_MFMA_128x128;
   double best_cost = 1e300;
-  for (const Opt& o : opts) {
+  for (int i = 0; i < n; ++i) {
+    if (!opts[i].ok) continue;
+    const double c = tile_cost(opts[i], epilogue, M, N);
+    if (c < best_cost) {
+      best_cost = c;
+      best = opts[i].cfg;
+    }
+  }
+  if (cost) *cost = best_cost;
+  return best;
+}
+
+// A split adds a launch whose own ramp-up and drain are not hidden by the
+// first one's; in the model's units (a 128x128 round ~ 14.5e3 ~ 11 us) ~1 us.
+constexpr double kSplitPenalty = 1.3e3;
+
+}  // namespace
+
+int gemm_mfma_choice(int epilogue, bool norm_producer, int64_t M, int64_t N) {
+  return best_tile(epilogue, norm_producer, M, N, nullptr);
+}
+
+// Column split: when a wide GEMM's best single tile leaves a ragged last round
+// (e.g. SwiGLU gate/up at M = 3,562: five rounds of 128x128 tiles, or a
+// second 256x256 round holding 52 of 308 tiles), one launch of large tiles
+// covers the columns that fill exactly one round and a second launch of
+// smaller tiles covers the rest.  Only epilogues whose arithmetic does not
+// depend on the absolute column take it (not the rotary, transposed-V or
+// folded-norm producer forms).
+GemmSplit gemm_mfma_split(int epilogue, bool norm_producer, int64_t M, int64_t N) {
+  GemmSplit best{};
+  double best_cost;
+  best.cfg_main = best_tile(epilogue, norm_producer, M, N, &best_cost);
+  best.n_main = N;
+  best.cfg_tail = -1;
+  const bool col_free = epilogue == VIT_EPI_STORE || epilogue == VIT_EPI_STORE_F32 ||
+                        epilogue == VIT_EPI_ADD_F32 || epilogue == VIT_EPI_SWIGLU ||
+                        epilogue == VIT_EPI_BIAS || epilogue == VIT_EPI_BIAS_GELU;
+  if (!col_free || norm_producer) return best;
+  TileOpt opts[4];
+  tile_opts(epilogue, norm_producer, opts);
+  // largest tiles first: at equal cost the large-tile launch is the main one
+  for (const int i : {2, 3, 1, 0}) {
+    const TileOpt& o = opts[i];
     if (!o.ok) continue;
-    const int64_t bno = dual ? o.bn / 2 : o.bn;
-    const int64_t tiles = ((M + o.bm - 1) / o.bm) * ((N + bno - 1) / bno);
-    const double rounds = (double)((tiles + 255) / 256);
-    const double cost = rounds * o.bm * o.bn / o.eff;
-    if (cost < best_cost) {
-      best_cost = cost;
-      best = o.cfg;
+    const int64_t bno = tile_cols(o, epilogue);
+    const int64_t row_tiles = (M + o.bm - 1) / o.bm;
+    const int64_t n_main = (kCUs / row_tiles) * bno;
+    if (n_main <= 0 || n_main >= N) continue;
+    double tail_cost;
+    const int tail = best_tile(epilogue, norm_producer, M, N - n_main, &tail_cost);
+    const double c = o.bm * o.bn / o.eff + tail_cost + kSplitPenalty;
+    if (c < best_cost) {
+      best_cost = c;
+      best.cfg_main = o.cfg;
+      best.n_main = n_main;
+      best.cfg_tail = tail;
     }
   }
   return best;
@@ -298,8 +371,24 @@ hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s) {
                    (epilogue != VIT_EPI_STORE_F32 && epilogue != VIT_EPI_ADD_F32)))
     return hipErrorInvalidValue;
   if (pipe_eligible(g)) {
-    const int cfg = gemm_mfma_choice(rope ? VIT_EPI_STORE : epilogue, g.norm_w != nullptr, g.M, g.N);
-    return launch_gemm_mfma(cfg, epilogue, g, s);
+    if (rope) {
+      const int cfg = gemm_mfma_choice(VIT_EPI_STORE, g.norm_w != nullptr, g.M, g.N);
+      return launch_gemm_mfma(cfg, epilogue, g, s);
+    }
+    const GemmSplit sp = gemm_mfma_split(epilogue, g.norm_w != nullptr, g.M, g.N);
+    if (sp.n_main == g.N) return launch_gemm_mfma(sp.cfg_main, epilogue, g, s);
+    GemmArgs a = g, b = g;
+    a.N = sp.n_main;
+    b.N = g.N - sp.n_main;
+    const int64_t out_bytes =
+        epilogue == VIT_EPI_STORE_F32 || epilogue == VIT_EPI_ADD_F32 ? 4 : 2;
+    b.B = (const bf16*)g.B + sp.n_main * g.ldb;
+    if (g.B2) b.B2 = (const bf16*)g.B2 + sp.n_main * g.ldb;
+    b.C = (char*)g.C + sp.n_main * out_bytes;
+    if (g.bias) b.bias = g.bias + sp.n_main;
+    const hipError_t e = launch_gemm_mfma(sp.cfg_main, epilogue, a, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm_mfma(sp.cfg_tail, epilogue, b, s);
   }
   return launch_simple(epilogue, g, s);
 }

@@ -12,3 +12,11 @@ enum GemmMfmaCfg {
 };
 
 hipError_t launch_gemm_mfma(int cfg, int epi, const GemmArgs& g, hipStream_t s);
+
+// Launch plan of one GEMM: cfg_main over columns [0, n_main), and when
+// n_main < N a second launch of cfg_tail over [n_main, N).
+struct GemmSplit {
+  int cfg_main;
+  int64_t n_main;
+  int cfg_tail;
+};
