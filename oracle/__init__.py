@@ -43,7 +43,9 @@ from .vit import (  # noqa: F401
     patch_merger_param_count,
     patchify,
     rmsnorm,
+    rmsnorm_backward,
     rope_freqs,
     rope_table,
     tower,
+    tower_backward,
 )

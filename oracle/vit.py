@@ -278,6 +278,76 @@ def attn_half_backward(x, norm_w, wqkv, wo, cos, sin, n_heads, dy, eps=1e-6, dty
     return dx, d_w, d_wqkv, d_wo
 
 
+def rmsnorm_backward(x, norm_w, dy, eps=1e-6, dtype=np.float64):
+    """Gradients of y = rmsnorm(x, norm_w) ([VIS] DeepseekV4VisionRMSNorm) for dy:
+    with r = (mean(x^2) + eps)^-1/2 and g = norm_w dy,
+      dx = r g - x r^3 mean(g x),  d norm_w = sum over rows of dy x r."""
+    x, dy, w = _f(x, dtype), _f(dy, dtype), _f(norm_w, dtype)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    g = w * dy
+    dx = r * g - x * r ** 3 * np.mean(g * x, axis=-1, keepdims=True)
+    return dx, np.sum(dy * x * r, axis=0)
+
+
+def _attn_branch(x, blk, cos, sin, n_heads, eps, dtype):
+    """x + attn(norm1(x)) for one image: the first residual branch of ``block``."""
+    P, d = x.shape
+    D = d // n_heads
+    n = rmsnorm(x, blk["norm1"], eps, dtype)
+    qkv = linear(n, blk["wqkv"], dtype)
+    q = apply_rope(qkv[:, 0:d].reshape(P, n_heads, D), cos, sin, dtype)
+    k = apply_rope(qkv[:, d:2 * d].reshape(P, n_heads, D), cos, sin, dtype)
+    v = qkv[:, 2 * d:3 * d].reshape(P, n_heads, D)
+    return x + linear(attention(q, k, v, dtype).reshape(P, d), blk["wo"], dtype)
+
+
+def tower_backward(patches, grids, weights, n_heads, dy, eps=1e-6, theta=10000.0,
+                   dtype=np.float64):
+    """Gradients of the tower ([VIS] DeepseekV4VisionTransformer.forward: patch
+    embedding, blocks, final norm) over concatenated images, for dy = dL/d(output)
+    ([PR] lists backward over ragged grids among the tested paths).
+
+    The forward is run once with the residual stream kept at the input of every
+    residual branch; then, in reverse, the final norm's gradient, each block's MLP
+    half (``mlp_half_backward``) and attention half (``attn_half_backward``, one
+    image at a time, weight gradients summed over the images), and last the patch
+    embedding's weight gradient dWpe = dx0^T patches.  Returns a dict with
+    ``patch_embed``, ``final_norm`` and ``blocks`` (per block ``norm1``, ``wqkv``,
+    ``wo``, ``norm2``, ``w_gate``, ``w_up``, ``w_down``)."""
+    patches, dy = _f(patches, dtype), _f(dy, dtype)
+    x = patch_embed(patches, weights["patch_embed"], dtype)
+    d = x.shape[1]
+    spans, tables, off = [], [], 0
+    for gh, gw in grids:
+        spans.append(slice(off, off + gh * gw))
+        tables.append(rope_table(gh, gw, d // n_heads, theta))
+        off += gh * gw
+    saved = []
+    for blk in weights["blocks"]:
+        xm = np.empty_like(x)
+        for sl, (cos, sin) in zip(spans, tables):
+            xm[sl] = _attn_branch(x[sl], blk, cos, sin, n_heads, eps, dtype)
+        saved.append((x, xm))
+        x = xm + mlp(rmsnorm(xm, blk["norm2"], eps, dtype), blk["w_gate"], blk["w_up"],
+                     blk["w_down"], dtype)
+    dx, d_final = rmsnorm_backward(x, weights["final_norm"], dy, eps, dtype)
+    grads = []
+    for blk, (xa, xm) in zip(reversed(weights["blocks"]), reversed(saved)):
+        dx, d_n2, d_wg, d_wu, d_wd = mlp_half_backward(xm, blk["norm2"], blk["w_gate"],
+                                                       blk["w_up"], blk["w_down"], dx, eps, dtype)
+        dxa = np.empty_like(dx)
+        d_n1, d_wqkv, d_wo = 0.0, 0.0, 0.0
+        for sl, (cos, sin) in zip(spans, tables):
+            r = attn_half_backward(xa[sl], blk["norm1"], blk["wqkv"], blk["wo"], cos, sin,
+                                   n_heads, dx[sl], eps, dtype)
+            dxa[sl] = r[0]
+            d_n1, d_wqkv, d_wo = d_n1 + r[1], d_wqkv + r[2], d_wo + r[3]
+        dx = dxa
+        grads.append({"norm1": d_n1, "wqkv": d_wqkv, "wo": d_wo, "norm2": d_n2,
+                      "w_gate": d_wg, "w_up": d_wu, "w_down": d_wd})
+    return {"patch_embed": dx.T @ patches, "final_norm": d_final, "blocks": grads[::-1]}
+
+
 def block(x, blk, cos, sin, n_heads, eps=1e-6, dtype=np.float64):
     """[VIS] DeepseekV4VisionBlock: x += attn(norm1(x)); x += mlp(norm2(x)).
 

@@ -772,3 +772,73 @@ def test_attn_half_backward_matches_finite_differences():
             minus[k_][idx] -= step
             fd[idx] = (loss(*plus) - loss(*minus)) / (2 * step)
         np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-7, err_msg=f"input {k_}")
+
+
+def _fd_check(loss, args, grads, rng=None, max_entries=None, rtol=1e-6, atol=1e-7, tag=""):
+    """Central differences of loss(*args) against the analytic grads (all entries,
+    or max_entries random ones per argument)."""
+    step = 1e-6
+    for k_, (arg, grad) in enumerate(zip(args, grads)):
+        assert grad.shape == arg.shape, (tag, k_)
+        idxs = list(np.ndindex(arg.shape))
+        if max_entries is not None and len(idxs) > max_entries:
+            idxs = [idxs[i] for i in rng.choice(len(idxs), max_entries, replace=False)]
+        for idx in idxs:
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[k_][idx] += step
+            minus[k_][idx] -= step
+            fd = (loss(*plus) - loss(*minus)) / (2 * step)
+            np.testing.assert_allclose(grad[idx], fd, rtol=rtol, atol=atol,
+                                       err_msg=f"{tag} argument {k_} entry {idx}")
+
+
+def test_rmsnorm_backward_matches_finite_differences():
+    """Central differences of L = sum(G * rmsnorm(x, w)) built from the pinned rmsnorm."""
+    rng = _rng(41)
+    x = rng.standard_normal((4, 8))
+    w = 1.0 + 0.3 * rng.standard_normal(8)
+    G = rng.standard_normal((4, 8))
+    eps = 1e-3
+    loss = lambda x_, w_: float(np.sum(G * oracle.rmsnorm(x_, w_, eps)))
+    _fd_check(loss, [x, w], oracle.rmsnorm_backward(x, w, G, eps), tag="rmsnorm")
+
+
+@pytest.mark.parametrize("n_blocks", [0, 2])
+def test_tower_backward_matches_finite_differences(n_blocks):
+    """Central differences of L = sum(G * tower outputs) with the pinned forward
+    (encode_varlen without the aligner: patch embedding, blocks, final norm, one
+    image at a time) on two ragged grids (2x3, 3x2), 2 heads of 4, every weight
+    tensor (up to 12 random entries of each larger one)."""
+    rng = _rng(42 + n_blocks)
+    grids = [(2, 3), (3, 2)]
+    H, D, hdn, pd = 2, 4, 12, 6
+    d = H * D
+    P = sum(a * b for a, b in grids)
+    patches = rng.standard_normal((P, pd))
+    G = rng.standard_normal((P, d))
+    eps = 1e-3
+    weights = {"patch_embed": 0.5 * rng.standard_normal((d, pd)),
+               "final_norm": 1.0 + 0.3 * rng.standard_normal(d), "blocks": []}
+    names = ["norm1", "wqkv", "wo", "norm2", "w_gate", "w_up", "w_down"]
+    shapes = [(d,), (3 * d, d), (d, d), (d,), (hdn, d), (hdn, d), (d, hdn)]
+    for _ in range(n_blocks):
+        blk = {}
+        for nm, sh in zip(names, shapes):
+            blk[nm] = (1.0 + 0.3 * rng.standard_normal(sh)) if nm.startswith("norm") else \
+                0.5 * rng.standard_normal(sh)
+        weights["blocks"].append(blk)
+    got = oracle.tower_backward(patches, grids, weights, H, G, eps)
+
+    flat = [weights["patch_embed"], weights["final_norm"]] + \
+        [blk[nm] for blk in weights["blocks"] for nm in names]
+    grads = [got["patch_embed"], got["final_norm"]] + \
+        [gb[nm] for gb in got["blocks"] for nm in names]
+
+    def loss(*ws):
+        w = {"patch_embed": ws[0], "final_norm": ws[1],
+             "blocks": [dict(zip(names, ws[2 + 7 * b:9 + 7 * b])) for b in range(n_blocks)]}
+        out = oracle.encode_varlen(patches, grids, w, H, eps, with_aligner=False)
+        return float(np.sum(G * out))
+
+    _fd_check(loss, flat, grads, rng=rng, max_entries=12, rtol=1e-5, atol=1e-7, tag="tower")
