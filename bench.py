@@ -524,6 +524,114 @@ def bench_attn_backward(args):
     print(json.dumps(result), flush=True)
 
 
+TOWER_BWD_METRIC = "TFLOP/s through the backward of the whole tower (bf16)"
+
+
+def tower_backward_flops(cfg, grids):
+    """Algorithmic FLOPs of one tower backward: the forward once (patch embedding,
+    blocks), every block GEMM's data and weight gradients (2x its forward FLOPs),
+    the attention gradient 8 d sum(P_i^2) per block (dV, dP, dQ, dK; no recomputed
+    S) and the patch embedding's weight gradient."""
+    P, d, h = sum(a * b for a, b in grids), cfg.vision_dim, cfg.mlp_hidden
+    sq = sum((a * b) ** 2 for a, b in grids)
+    gemm = 8.0 * P * d * d + 6.0 * P * d * h
+    fwd = cfg.n_blocks * (gemm + 4.0 * d * sq) + 2.0 * P * cfg.patch_dim * d
+    return fwd + cfg.n_blocks * (2.0 * gemm + 8.0 * d * sq) + 2.0 * P * cfg.patch_dim * d
+
+
+def bench_tower_backward(args):
+    """vit_tower_backward on the ragged 4-image batch (27x37, 37x27, 10x78, 112x7;
+    vision_dim 1024, 16 heads x 64, hidden 2816, 4 blocks; synthetic bf16 patches and
+    weights, fp32 dy).  One step is one call: the forward with residual checkpoints,
+    the final norm's gradient, the four blocks' halves in reverse and the patch
+    embedding's gradient."""
+    import torch
+
+    from vision_transformer_encoder_image_amd import api, configs, synth
+
+    dev = "cuda:0"
+    cfg = configs.get("ragged_varlen_4img")
+    grids = list(cfg.grids)
+    P, d, h, L = cfg.total_patches, cfg.vision_dim, cfg.mlp_hidden, cfg.n_blocks
+    Pp = (P + 63) // 64 * 64
+    inp = synth.make_inputs(cfg, seed=2)
+    w = api.DeviceWeights(cfg, inp["weights"], device=dev)
+    x = torch.from_numpy(inp["patches"]).to(dev, torch.bfloat16)
+    dy = torch.from_numpy(synth.random_array((P, d), 180)).to(dev)
+    ws = torch.empty(api.tower_backward_workspace_bytes(cfg, grids), dtype=torch.uint8, device=dev)
+    total = tower_backward_flops(cfg, grids)
+    # FLOPs the backward GEMM class executes per call (with the halves' recomputed
+    # forward GEMMs and the weight gradients' row padding)
+    gemm_exec = L * (6.0 * P * d * d + 2.0 * P * d * d + 6.0 * P * d * d + 8.0 * d * d * Pp +
+                     4.0 * P * d * h + 2.0 * P * d * h + 4.0 * P * d * h + 6.0 * d * h * Pp)
+    for _ in range(max(args.warmup, 1)):
+        api.tower_backward(x, grids, w, dy, ws=ws)
+    torch.cuda.synchronize()
+    classes = ("bwd_gemm", "bwd_attn", "bwd_pass")
+    for k in classes:
+        api.profile_enable(k, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        api.tower_backward(x, grids, w, dy, ws=ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per = {}
+    for k in classes:
+        per[k] = api.profile_read(k)
+        api.profile_enable(k, False)
+    gemm_us = per["bwd_gemm"][0] * 1e3 / args.steps
+    peak = PEAK_TFLOPS["bf16"]
+    achieved = gemm_exec / (gemm_us * 1e-6) / 1e12
+    result = {
+        "metric": TOWER_BWD_METRIC,
+        "value": round(total * args.steps / elapsed / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "tower_backward_ragged_varlen_4img", "grids": [list(g) for g in grids],
+                   "patches": P, "dim": d, "heads": cfg.n_heads, "mlp_hidden": h, "blocks": L,
+                   "flops_per_step": total},
+        "roofline": {"kernel": "bwd_gemm", "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None, "avg_launch_us": round(gemm_us, 3),
+                     "flops_per_launch": gemm_exec,
+                     "note": "every GEMM of the blocks' backward halves per call (the halves' "
+                             "recomputed forward GEMMs included), timed as one class"},
+        "breakdown": {k + "_us_per_step": round(per[k][0] * 1e3 / args.steps, 1) for k in classes},
+    }
+    if not args.no_cpu_baseline:
+        import threadpoolctl
+
+        import oracle
+
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        sub = [grids[2]]  # the 10x78 image: 780 patches, all four blocks
+        off = grids[0][0] * grids[0][1] + grids[1][0] * grids[1][1]
+        Pi = sub[0][0] * sub[0][1]
+        pt = inp["patches"][off:off + Pi]
+        dyh = synth.random_array((P, d), 180)[off:off + Pi]
+        runs, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0:
+            oracle.tower_backward(pt, sub, inp["weights"], cfg.n_heads, dyh, cfg.rms_eps,
+                                  cfg.rope_theta)
+            runs += 1
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(tower_backward_flops(cfg, sub) * runs / dt / 1e12, 4),
+                                  "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+                                  "sample": f"the 10x78 image ({Pi} patches, 4 blocks), {runs} "
+                                            f"float64 oracle passes in {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -531,11 +639,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--stage", choices=("encode", "merge", "projector", "mlp_backward",
-                                        "attn_backward"),
+                                        "attn_backward", "tower_backward"),
                     default="encode",
                     help="encode: the encoder step; merge: image tokens into the LLM stream; "
-                         "projector: the PatchMerger projector; mlp_backward: the backward "
-                         "of a block's MLP half")
+                         "projector: the PatchMerger projector; mlp_backward / attn_backward: "
+                         "the backward of a block's MLP / attention half; tower_backward: the "
+                         "backward of the whole tower")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -568,6 +677,9 @@ def main():
         return
     if args.stage == "attn_backward":
         bench_attn_backward(args)
+        return
+    if args.stage == "tower_backward":
+        bench_tower_backward(args)
         return
 
     import torch

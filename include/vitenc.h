@@ -326,6 +326,40 @@ size_t vit_attn_backward_workspace_bytes(const vit_attn_grad* a, const int32_t* 
 vit_status vit_attn_backward(const vit_attn_grad* a, const int32_t* grid_hw_host,
                              int32_t n_images, void* ws, size_t ws_bytes, void* stream);
 
+/* Backward of the whole tower (DeepseekV4VisionTransformer.forward on the vision
+ * page: patch embedding, blocks, final norm; PR #3772 lists backward over ragged
+ * grids among its tested paths).  Given dy = dL/d(out) for the tower's output
+ * (the final norm's, as vit_encode_varlen with VIT_NO_ALIGNER returns it),
+ * computes the gradient of every weight: the forward is run once, keeping the
+ * fp32 residual stream at the input of each residual branch; then the final
+ * norm's gradient, the blocks in reverse (each as vit_mlp_backward then
+ * vit_attn_backward) and the patch embedding's weight gradient dx0^T . patches.
+ * bf16 weights and patches, fp32 gradients; head_dim 64, vision_dim <= 2048 and
+ * mlp_hidden multiples of 64, patch_dim a multiple of 4.  Images as in
+ * vit_encode_varlen (patches [sum P, patch_dim], rows of dy in the same order).
+ * The per-block arrays are HOST arrays of n_blocks device pointers (as in
+ * vit_weights).  Every device pointer 16-byte aligned; the workspace must not
+ * alias any argument.  Errors as vit_encode_varlen, VIT_E_ARG for a NULL
+ * gradient pointer. */
+typedef struct {
+  float* d_patch_embed;       /* [d, patch_dim] */
+  float* const* d_wqkv;       /* [3d, d] per block */
+  float* const* d_wo;         /* [d, d] */
+  float* const* d_w_gate;     /* [h, d] */
+  float* const* d_w_up;       /* [h, d] */
+  float* const* d_w_down;     /* [d, h] */
+  float* const* d_norm1;      /* [d] */
+  float* const* d_norm2;      /* [d] */
+  float* d_final_norm;        /* [d] */
+} vit_tower_grads;
+
+size_t vit_tower_backward_workspace_bytes(const vit_config* cfg, const int32_t* grid_hw_host,
+                                          int32_t n_images);
+vit_status vit_tower_backward(const vit_config* cfg, const vit_weights* w, const void* patches,
+                              const int32_t* grid_hw_host, int32_t n_images, const float* dy,
+                              const vit_tower_grads* grads, void* ws, size_t ws_bytes,
+                              void* stream);
+
 /* Image tokens into the LLM input stream (DeepSeek-V4 model page,
  * DeepseekV4Model.merge_image_embeddings): for each position p of a text
  * embedding stream embeds [positions, hidden] (in place, dtype):

@@ -157,6 +157,25 @@ def test_workspace_grows_with_patches(lib):
     assert big >= P * c.vision_dim * 4 + P * 3 * c.vision_dim * 2
 
 
+def test_tower_backward_workspace_host_checks(lib):
+    """Host-side sizing of vit_tower_backward: bf16 with head_dim 64 only; the
+    workspace holds at least the forward's plus 2 n_blocks + 1 fp32 residual
+    checkpoints."""
+    c = configs.get(2)
+    grids = list(c.grids)
+    need = api.tower_backward_workspace_bytes(c, grids)
+    P, d = c.total_patches, c.vision_dim
+    assert need >= api.workspace_bytes(c, grids, aligner=False) + (2 * c.n_blocks + 1) * P * d * 4
+    g = _lib.grid_array(grids)
+    for bad in (configs.VitConfig("f", c.grids, 1024, 16, 2816, 4, 0, "f32"),
+                configs.VitConfig("h", c.grids, 1024, 8, 2816, 4, 0, "bf16"),
+                configs.VitConfig("m", c.grids, 1024, 16, 2800, 4, 0, "bf16")):
+        assert lib.vit_tower_backward_workspace_bytes(ctypes.byref(api.c_config(bad)), g, 4) == 0
+    one = api.tower_backward_workspace_bytes(
+        configs.VitConfig("b1", c.grids, 1024, 16, 2816, 1, 0, "bf16"), grids)
+    assert need - one >= 6 * P * d * 4
+
+
 def test_configs_flops_match_hand_count():
     c = configs.get(2)
     assert c.total_patches == 3562  # 999 + 999 + 780 + 784

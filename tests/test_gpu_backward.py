@@ -157,3 +157,92 @@ def test_attn_backward_deterministic_and_errors():
     bad = _lib.VitAttnGrad(96, 2, 1e4, 1e-6, *([None] * 9))  # head_dim 48
     assert lib.vit_attn_backward_workspace_bytes(bad, _lib.grid_array(grids), 2) == 0
     assert lib.vit_attn_backward(bad, _lib.grid_array(grids), 2, None, 0, None) == _lib.VIT_E_SHAPE
+
+
+# ------------------------------------------------------------- whole tower
+# Bar of the whole-tower gradients: one half's bar (ATTN_GRAD_TOL, 3e-2) plus the
+# forward's own bar (2e-2): each half's input is the residual stream of the bf16
+# forward, not the exact one, and each half's incoming gradient already carries
+# the later halves' error.  Measured: 2e-4 - 7e-3 for the norms, the patch
+# embedding and the MLP weights; 1.5e-2 - 4.2e-2 for wqkv and wo, whose rows are
+# sums over the patches of products with near-cancelling attention outputs.
+TOWER_GRAD_TOL = 5e-2
+
+
+def _tower_case(grids, d, H, h, n_blocks, seed, patch_size=4):
+    from vision_transformer_encoder_image_amd import configs
+    cfg = configs.VitConfig("tower", tuple(grids), d, H, h, n_blocks, 0, "bf16",
+                            patch_size=patch_size)
+    inp = synth.make_inputs(cfg, seed)
+    P = cfg.total_patches
+    dy = synth.random_array((P, d), seed + 1, std=1.0)
+    return cfg, inp["patches"], inp["weights"], dy
+
+
+def _tower_run(cfg, patches, weights, dy):
+    w = api.DeviceWeights(cfg, weights)
+    x = torch.from_numpy(patches).to("cuda", torch.bfloat16)
+    out = api.tower_backward(x, list(cfg.grids), w, torch.from_numpy(dy).cuda())
+    torch.cuda.synchronize()
+    return out
+
+
+def _tower_check(cfg, got, patches, weights, dy, tag):
+    ref = oracle.tower_backward(patches, list(cfg.grids), weights, cfg.n_heads, dy,
+                                cfg.rms_eps, cfg.rope_theta)
+    pairs = [("patch_embed", got["patch_embed"], ref["patch_embed"]),
+             ("final_norm", got["final_norm"], ref["final_norm"])]
+    for b, (gb, rb) in enumerate(zip(got["blocks"], ref["blocks"])):
+        pairs += [(f"block{b}.{k}", gb[k], rb[k]) for k in api.TOWER_GRAD_KEYS]
+    for name, g, r in pairs:
+        g = to_np(g)
+        assert g.shape == r.shape, name
+        g2, r2 = (g[None], r[None]) if g.ndim == 1 else (g, r)
+        err = rowwise_rel_err(g2, r2)
+        print(f"{tag} {name}: row-wise rel err {err:.3e}")
+        assert err < TOWER_GRAD_TOL, (name, err)
+
+
+@pytest.mark.parametrize("grids,n_blocks", [([(4, 6), (3, 5), (8, 8)], 2),
+                                            ([(9, 7), (2, 40)], 1), ([(5, 13)], 0)])
+def test_tower_backward_small_matches_oracle(grids, n_blocks):
+    """Ragged grids (one 64-row tile and a ragged tail), 2 heads of 64, hidden 192,
+    14x14 -> 4x4 patches (patch_dim 48); zero blocks leaves the final norm and the
+    patch embedding."""
+    cfg, patches, weights, dy = _tower_case(grids, 128, 2, 192, n_blocks, seed=150 + n_blocks)
+    got = _tower_run(cfg, patches, weights, dy)
+    _tower_check(cfg, got, patches, weights, dy, f"{grids} x{n_blocks}")
+
+
+def test_tower_backward_encoder_width_matches_oracle():
+    """Encoder widths (1024, 16 heads of 64, hidden 2816, 14x14 patches: patch_dim 588)
+    on two of the ragged batch's images (27x37, 10x78), two blocks."""
+    cfg, patches, weights, dy = _tower_case([(27, 37), (10, 78)], 1024, 16, 2816, 2, seed=160,
+                                            patch_size=14)
+    got = _tower_run(cfg, patches, weights, dy)
+    _tower_check(cfg, got, patches, weights, dy, "27x37+10x78 x2")
+
+
+def test_tower_backward_deterministic_and_errors():
+    cfg, patches, weights, dy = _tower_case([(6, 10), (5, 5)], 128, 2, 192, 1, seed=170)
+    a, b = _tower_run(cfg, patches, weights, dy), _tower_run(cfg, patches, weights, dy)
+    assert torch.equal(a["patch_embed"], b["patch_embed"])
+    for ga, gb in zip(a["blocks"], b["blocks"]):
+        for k in api.TOWER_GRAD_KEYS:
+            assert torch.equal(ga[k], gb[k]), k
+    lib = _lib.load()
+    grids = _lib.grid_array(list(cfg.grids))
+    from vision_transformer_encoder_image_amd import configs
+    for bad, st in [(configs.VitConfig("f", cfg.grids, 128, 2, 192, 1, 0, "f32", patch_size=4),
+                     _lib.VIT_E_ARG),
+                    (configs.VitConfig("h", cfg.grids, 192, 2, 192, 1, 0, "bf16", patch_size=4),
+                     _lib.VIT_E_SHAPE)]:
+        c = api.c_config(bad)
+        assert lib.vit_tower_backward_workspace_bytes(c, grids, 2) == 0
+        w = api.DeviceWeights(cfg, weights)
+        assert lib.vit_tower_backward(c, w.c, None, grids, 2, None, None, None, 0, None) == st
+    w = api.DeviceWeights(cfg, weights)
+    x = torch.from_numpy(patches).to("cuda", torch.bfloat16)
+    small = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(RuntimeError):
+        api.tower_backward(x, list(cfg.grids), w, torch.from_numpy(dy).cuda(), ws=small)

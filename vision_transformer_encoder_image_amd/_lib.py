@@ -54,6 +54,14 @@ class VitMlpGrad(ctypes.Structure):
                 ("d_w_up", c_vp), ("d_w_down", c_vp)]
 
 
+class VitTowerGrads(ctypes.Structure):
+    _fields_ = [("d_patch_embed", c_vp), ("d_wqkv", ctypes.POINTER(c_vp)),
+                ("d_wo", ctypes.POINTER(c_vp)), ("d_w_gate", ctypes.POINTER(c_vp)),
+                ("d_w_up", ctypes.POINTER(c_vp)), ("d_w_down", ctypes.POINTER(c_vp)),
+                ("d_norm1", ctypes.POINTER(c_vp)), ("d_norm2", ctypes.POINTER(c_vp)),
+                ("d_final_norm", c_vp)]
+
+
 class VitAttnGrad(ctypes.Structure):
     _fields_ = [("dim", c_i32), ("n_heads", c_i32), ("rope_theta", c_f32), ("eps", c_f32),
                 ("x", c_vp), ("norm_w", c_vp), ("wqkv", c_vp), ("wo", c_vp), ("dy", c_vp),
@@ -87,6 +95,10 @@ SIGNATURES = {
                               c_i64, c_vp]),
     "vit_attn_backward_workspace_bytes": (c_size, [ctypes.POINTER(VitAttnGrad), P_i32, c_i32]),
     "vit_attn_backward": (c_i32, [ctypes.POINTER(VitAttnGrad), P_i32, c_i32, c_vp, c_size, c_vp]),
+    "vit_tower_backward_workspace_bytes": (c_size, [ctypes.POINTER(VitConfig), P_i32, c_i32]),
+    "vit_tower_backward": (c_i32, [ctypes.POINTER(VitConfig), ctypes.POINTER(VitWeights), c_vp,
+                                   P_i32, c_i32, c_vp, ctypes.POINTER(VitTowerGrads), c_vp,
+                                   c_size, c_vp]),
     "vit_mlp_backward_workspace_bytes": (c_size, [c_i64, c_i32, c_i32]),
     "vit_mlp_backward": (c_i32, [ctypes.POINTER(VitMlpGrad), c_vp, c_size, c_vp]),
     "vit_merge_workspace_bytes": (c_size, [c_i64]),

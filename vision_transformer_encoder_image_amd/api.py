@@ -377,6 +377,55 @@ def attn_backward(x: torch.Tensor, norm_w: torch.Tensor, wqkv: torch.Tensor, wo:
     return dx, dnw, dwqkv, dwo
 
 
+TOWER_GRAD_KEYS = ("norm1", "wqkv", "wo", "norm2", "w_gate", "w_up", "w_down")
+
+
+def tower_backward_workspace_bytes(cfg: VitConfig, grids) -> int:
+    c = c_config(cfg)
+    n = _lib.load().vit_tower_backward_workspace_bytes(ctypes.byref(c), _lib.grid_array(grids),
+                                                        len(grids))
+    if n == 0:
+        _lib.check(_lib.VIT_E_SHAPE, "vit_tower_backward_workspace_bytes")
+    return n
+
+
+def tower_backward(patches: torch.Tensor, grids, w: "DeviceWeights", dy: torch.Tensor,
+                   ws: Optional[torch.Tensor] = None) -> Dict:
+    """vit_tower_backward: gradients of every tower weight for dy = dL/d(output of
+    the final norm) over packed images (patches [sum P, patch_dim] bf16, dy float32
+    [sum P, vision_dim]).  Returns float32 tensors in a dict shaped like the
+    weights: ``patch_embed``, ``final_norm`` and ``blocks`` (one dict per block)."""
+    _require_cuda(patches, dy, ws)
+    cfg = w.cfg
+    d, h, pd = cfg.vision_dim, cfg.mlp_hidden, cfg.patch_dim
+    f32 = dict(dtype=torch.float32, device=patches.device)
+    shapes = {"norm1": (d,), "wqkv": (3 * d, d), "wo": (d, d), "norm2": (d,), "w_gate": (h, d),
+              "w_up": (h, d), "w_down": (d, h)}
+    out = {"patch_embed": torch.empty((d, pd), **f32), "final_norm": torch.empty(d, **f32),
+           "blocks": [{k: torch.empty(shapes[k], **f32) for k in TOWER_GRAD_KEYS}
+                      for _ in range(cfg.n_blocks)]}
+    n = cfg.n_blocks
+
+    def arr(key):
+        return (ctypes.c_void_p * max(n, 1))(*[b[key].data_ptr() for b in out["blocks"]])
+
+    arrays = {k: arr(k) for k in TOWER_GRAD_KEYS}
+    grads = _lib.VitTowerGrads(out["patch_embed"].data_ptr(), arrays["wqkv"], arrays["wo"],
+                               arrays["w_gate"], arrays["w_up"], arrays["w_down"], arrays["norm1"],
+                               arrays["norm2"], out["final_norm"].data_ptr())
+    c = c_config(cfg)
+    lib = _lib.load()
+    g = _lib.grid_array(grids)
+    if ws is None:
+        ws = torch.empty(tower_backward_workspace_bytes(cfg, grids), dtype=torch.uint8,
+                         device=patches.device)
+    st = lib.vit_tower_backward(ctypes.byref(c), ctypes.byref(w.c), patches.data_ptr(), g,
+                                len(grids), dy.data_ptr(), ctypes.byref(grads), ws.data_ptr(),
+                                ws.numel(), _stream(patches.device))
+    _lib.check(st, "vit_tower_backward")
+    return out
+
+
 def merge_workspace_bytes(positions: int) -> int:
     n = _lib.load().vit_merge_workspace_bytes(int(positions))
     if n == 0:

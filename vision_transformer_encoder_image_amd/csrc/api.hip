@@ -256,9 +256,12 @@ vit_status check_weights(const vit_config& c, const vit_weights* w, bool aligner
   return VIT_OK;
 }
 
+// ckpt (optional, fp32 [2 n_blocks + 1][P][d]): the residual stream at the input
+// of every residual branch and after the last block, copied out as it is formed
+// (used by the backward of the tower)
 vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* in,
                        const int32_t* grid_hw, int32_t n_images, int32_t flags, void* out,
-                       void* ws, size_t ws_bytes, hipStream_t s) {
+                       void* ws, size_t ws_bytes, hipStream_t s, float* ckpt = nullptr) {
   VIT_TRY(check_config(cfg));
   const vit_config& c = *cfg;
   if (flags & ~(VIT_NO_ALIGNER | VIT_OUT_NLAYOUT | VIT_IN_PIXELS | VIT_ALIGN_PAD))
@@ -362,6 +365,13 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
       VIT_HIP(launch_rope_table(desc, c.head_dim, c.rope_theta, table, s), "rope table");
     }
   }
+  auto save = [&](int k) -> vit_status {
+    if (!ckpt) return VIT_OK;
+    return hip_check(hipMemcpyAsync(ckpt + (int64_t)k * P * d, x, (size_t)P * d * sizeof(float),
+                                    hipMemcpyDeviceToDevice, s),
+                     "residual checkpoint");
+  };
+  VIT_TRY(save(0));
   if (p.hp > h)
     VIT_HIP(launch_zero_cols(dt, act, P, p.hp, h, p.hp, s), "zero MLP pad columns");
   void* a_in = fuse ? u : n;  // A operand of the GEMMs after a norm
@@ -417,6 +427,7 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
         VIT_TRY(gemm(dt, VIT_EPI_ADD_F32, n, d, w->wo[b], nullptr, d, x, d, P, d, d, nullptr, s));
       }
     }
+    VIT_TRY(save(2 * b + 1));
     if (!fuse) {
       ProfScope ps(VIT_K_RMSNORM, s);
       VIT_HIP(launch_rmsnorm(x, w->norm2[b], c.rms_eps, P, (int)d, dt, n, s), "norm2");
@@ -441,6 +452,7 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
                              : launch_gemm_f32(VIT_EPI_ADD_F32, gd, s),
               "down gemm");
     }
+    VIT_TRY(save(2 * b + 2));
   }
   {
     ProfScope ps(VIT_K_RMSNORM, s);
@@ -561,6 +573,64 @@ vit_status check_attn_grad(const vit_attn_grad* a) {
     return fail(VIT_E_SHAPE, "dim %d, n_heads %d: need head_dim 64 and dim <= 2048", a->dim,
                 a->n_heads);
   if (!(a->eps >= 0.f) || !(a->rope_theta > 0.f)) return fail(VIT_E_ARG, "bad eps / theta");
+  return VIT_OK;
+}
+
+// Backward of the whole tower: workspace layout.  The forward's own workspace
+// comes first (its zero-padded patches are the B operand of the patch
+// embedding's gradient), then the residual checkpoints, two gradient buffers,
+// and one region that each half's backward reuses in turn (afterwards the
+// operands of the patch embedding's gradient).
+struct TowerGradPlan {
+  Plan fwd;
+  int64_t P = 0, Pp = 0;
+  size_t out = 0, ckpt = 0, dxa = 0, dxb = 0, partial = 0, half = 0, half_bytes = 0, total = 0;
+  size_t dx16 = 0, dxT = 0, xT = 0;  // offsets inside the half region
+};
+
+vit_status tower_setup(const vit_config* cfg, const int32_t* grid_hw, int32_t n_images,
+                       TowerGradPlan* t) {
+  VIT_TRY(check_config(cfg));
+  const vit_config& c = *cfg;
+  if (c.dtype != VIT_BF16) return fail(VIT_E_ARG, "tower backward: bf16 only");
+  if (c.head_dim != 64 || c.vision_dim % 64 || c.vision_dim > 2048)
+    return fail(VIT_E_SHAPE, "tower backward: head_dim 64 and vision_dim <= 2048 (got %d, %d)",
+                c.head_dim, c.vision_dim);
+  if (c.mlp_hidden % 64)
+    return fail(VIT_E_SHAPE, "tower backward: mlp_hidden %d not a multiple of 64", c.mlp_hidden);
+  if (c.patch_dim % 4)
+    return fail(VIT_E_SHAPE, "tower backward: patch_dim %d not a multiple of 4", c.patch_dim);
+  VarlenDesc fdesc, bdesc;
+  VIT_TRY(build_desc(grid_hw, n_images, attention_q_tile(c.dtype, c.head_dim), false, c.merge,
+                     &fdesc));
+  VIT_TRY(build_desc(grid_hw, n_images, attention_bwd_tile(), false, 2, &bdesc));
+  const int64_t P = fdesc.total, d = c.vision_dim;
+  t->fwd = make_plan(c, fdesc, VIT_NO_ALIGNER);
+  t->P = P;
+  t->Pp = round_up(P, 64);
+  size_t off = t->fwd.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (size_t)round_up((int64_t)bytes, 256);
+    return o;
+  };
+  t->out = take(P * d * 2);
+  t->ckpt = take((2 * (int64_t)c.n_blocks + 1) * P * d * 4);
+  t->dxa = take(P * d * 4);
+  t->dxb = take(P * d * 4);
+  t->partial = take((size_t)rmsnorm_bwd_blocks(P) * d * 4);
+  size_t half = 0;
+  if (c.n_blocks > 0) {
+    half = std::max(mlp_grad_plan(P, d, c.mlp_hidden).total,
+                    attn_grad_plan(bdesc, d, c.n_heads).total);
+  }
+  t->dx16 = 0;
+  t->dxT = (size_t)round_up(P * d * 2, 256);
+  t->xT = t->dxT + (size_t)round_up(d * t->Pp * 2, 256);
+  const size_t pe = t->xT + (size_t)round_up(t->fwd.Kp * t->Pp * 2, 256);
+  t->half_bytes = std::max(half, pe);
+  t->half = take(t->half_bytes);
+  t->total = off;
   return VIT_OK;
 }
 
@@ -1061,6 +1131,100 @@ vit_status vit_attn_backward(const vit_attn_grad* a, const int32_t* grid_hw_host
   VIT_HIP(launch_transpose_bf16(n, P, d, d, nT, p.Pp, p.Pp, s), "transpose n");
   VIT_TRY(mm(VIT_EPI_STORE_F32, dyT, p.Pp, oT, p.Pp, a->d_wo, d, d, d, p.Pp));
   return mm(VIT_EPI_STORE_F32, dqkvT, p.Pp, nT, p.Pp, a->d_wqkv, d, 3 * d, d, p.Pp);
+}
+
+size_t vit_tower_backward_workspace_bytes(const vit_config* cfg, const int32_t* grid_hw_host,
+                                          int32_t n_images) {
+  TowerGradPlan t;
+  if (tower_setup(cfg, grid_hw_host, n_images, &t) != VIT_OK) return 0;
+  return t.total;
+}
+
+vit_status vit_tower_backward(const vit_config* cfg, const vit_weights* w, const void* patches,
+                              const int32_t* grid_hw_host, int32_t n_images, const float* dy,
+                              const vit_tower_grads* gr, void* ws, size_t ws_bytes, void* stream) {
+  TowerGradPlan t;
+  VIT_TRY(tower_setup(cfg, grid_hw_host, n_images, &t));
+  const vit_config& c = *cfg;
+  VIT_TRY(check_weights(c, w, false));
+  if (!patches || !dy || !gr) return fail(VIT_E_ARG, "NULL pointer");
+  const int L = c.n_blocks;
+  if (L > 0 && (!gr->d_wqkv || !gr->d_wo || !gr->d_w_gate || !gr->d_w_up || !gr->d_w_down ||
+                !gr->d_norm1 || !gr->d_norm2))
+    return fail(VIT_E_ARG, "per-block gradient array NULL");
+  {
+    const void* ptrs[] = {dy, gr->d_patch_embed, gr->d_final_norm};
+    for (const void* q : ptrs) {
+      if (!q) return fail(VIT_E_ARG, "NULL pointer");
+      if (misaligned16(q)) return fail(VIT_E_ARG, "buffers must be 16-byte aligned");
+    }
+  }
+  if (!ws || ws_bytes < t.total || misaligned16(ws))
+    return fail(VIT_E_WORKSPACE, "workspace %zu < %zu (or misaligned)", ws ? ws_bytes : (size_t)0,
+                t.total);
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  const int64_t P = t.P, d = c.vision_dim;
+  float* ckpt = (float*)(base + t.ckpt);
+  float* cur = (float*)(base + t.dxa);
+  float* other = (float*)(base + t.dxb);
+  char* half = base + t.half;
+  // forward with the residual stream kept at the input of every residual branch
+  VIT_TRY(encode_impl(cfg, w, patches, grid_hw_host, n_images, VIT_NO_ALIGNER, base + t.out, base,
+                      t.fwd.total, s, ckpt));
+  // final norm (no residual around it)
+  VIT_HIP(launch_rmsnorm_bwd(ckpt + 2 * (int64_t)L * P * d, w->final_norm, dy, nullptr, P, (int)d,
+                             c.rms_eps, cur, (float*)(base + t.partial), gr->d_final_norm, s),
+          "final norm backward");
+  // blocks in reverse: the MLP half, then the attention half
+  for (int b = L - 1; b >= 0; --b) {
+    vit_mlp_grad m{};
+    m.rows = P;
+    m.dim = (int32_t)d;
+    m.hidden = c.mlp_hidden;
+    m.eps = c.rms_eps;
+    m.x = ckpt + (2 * (int64_t)b + 1) * P * d;
+    m.norm_w = w->norm2[b];
+    m.w_gate = w->w_gate[b];
+    m.w_up = w->w_up[b];
+    m.w_down = w->w_down[b];
+    m.dy = cur;
+    m.dx = other;
+    m.d_norm_w = gr->d_norm2[b];
+    m.d_w_gate = gr->d_w_gate[b];
+    m.d_w_up = gr->d_w_up[b];
+    m.d_w_down = gr->d_w_down[b];
+    VIT_TRY(vit_mlp_backward(&m, half, t.half_bytes, stream));
+    vit_attn_grad a{};
+    a.dim = (int32_t)d;
+    a.n_heads = c.n_heads;
+    a.rope_theta = c.rope_theta;
+    a.eps = c.rms_eps;
+    a.x = ckpt + 2 * (int64_t)b * P * d;
+    a.norm_w = w->norm1[b];
+    a.wqkv = w->wqkv[b];
+    a.wo = w->wo[b];
+    a.dy = other;
+    a.dx = cur;
+    a.d_norm_w = gr->d_norm1[b];
+    a.d_wqkv = gr->d_wqkv[b];
+    a.d_wo = gr->d_wo[b];
+    VIT_TRY(vit_attn_backward(&a, grid_hw_host, n_images, half, t.half_bytes, stream));
+  }
+  // patch embedding: dWpe [d, patch_dim] = dx0^T . patches, a contraction over
+  // the rows (zero-padded to Pp) of the transposed gradient and of the forward's
+  // zero-padded patches
+  bf16* dx16 = (bf16*)(half + t.dx16);
+  bf16* dxT = (bf16*)(half + t.dxT);
+  bf16* xT = (bf16*)(half + t.xT);
+  VIT_HIP(launch_cast_bf16(cur, P * d, dx16, s), "cast dx0");
+  VIT_HIP(launch_transpose_bf16(dx16, P, d, d, dxT, t.Pp, t.Pp, s), "transpose dx0");
+  VIT_HIP(launch_transpose_bf16(base + t.fwd.xpad, P, t.fwd.Kp, t.fwd.Kp, xT, t.Pp, t.Pp, s),
+          "transpose patches");
+  GemmArgs g = gemm_args(dxT, t.Pp, xT, nullptr, t.Pp, gr->d_patch_embed, c.patch_dim, d,
+                         c.patch_dim, t.Pp, nullptr);
+  if (!gemm_bf16_mfma_eligible(g)) return fail(VIT_E_SHAPE, "patch embedding gradient GEMM");
+  return hip_check(launch_gemm_bf16(VIT_EPI_STORE_F32, g, s), "patch embedding gradient");
 }
 
 vit_status vit_profile_enable(int32_t cls, int32_t on) {

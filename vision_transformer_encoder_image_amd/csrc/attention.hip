@@ -402,9 +402,20 @@ __global__ __launch_bounds__(64 * VT_WAVES, 1) void attn_vt_kernel(const bf16* _
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * ks2 + j], c, nmc));
-          lsum += p;
           pf[2 * kb + ks2][j] = f2bf(p);
         }
+    // the running sum adds the bf16 probabilities that the P.V MFMAs use, two
+    // per v_dot2c_f32_bf16 (half the vector-ALU adds), in two chains
+    const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[x], pf[x], 0, 1), one2, s0, false);
+      s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[x], pf[x], 2, 3), one2, s1, false);
+      s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[x], pf[x], 4, 5), one2, s0, false);
+      s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[x], pf[x], 6, 7), one2, s1, false);
+    }
+    lsum += s0 + s1;
   };
   // S^T of the next tile (K fragments kf) into sc, and O^T += V^T . P^T of
   // this tile (V fragments vf, P^T fragments pf); the S^T MFMAs go first so

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(64 * kNbWaves) void rmsnorm_bwd_kernel(
     for (int k = 0; k < kNbMaxChunks; ++k) {
       const int ch = lane + 64 * k;
       if (ch < nch) {
-        const f32x4 yv = *reinterpret_cast<const f32x4*>(dy + r * d + 4 * ch);
+        const f32x4 yv = dy ? *reinterpret_cast<const f32x4*>(dy + r * d + 4 * ch) : f32x4{};
         const f32x4 nv = *reinterpret_cast<const f32x4*>(dn + r * d + 4 * ch);
         f32x4 o;
 #pragma unroll
