@@ -97,18 +97,24 @@ def pmc_summary(fetch_dir, write_dir, kernel, workload, copy_mb, out_path=None):
     out = {"kernel": kernel, "workload": workload, "source_sha256": source_sha(kernel)}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _pmc_rows(d) if r["Counter_Name"] == counter]
-        sel = [float(r["Counter_Value"]) for r in rows
-               if pat in r["Kernel_Name"] and tail in r["Kernel_Name"]]
+        # one call of a class may launch several kernels (a column-split GEMM: a
+        # large-tile launch and a tail launch): per call, the sum over the distinct
+        # matching kernels of each one's median
+        by_name = {}
+        for r in rows:
+            if pat in r["Kernel_Name"] and tail in r["Kernel_Name"]:
+                by_name.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]
                 or "copy_kernel" in r["Kernel_Name"] or "elementwise" in r["Kernel_Name"]]
         known_kib = copy_mb * 1024.0
         scale = known_kib / max(copy) if copy else 1.0
-        kib = statistics.median(sel) if sel else float("nan")
+        kib = sum(statistics.median(v) for v in by_name.values()) if by_name else float("nan")
         out[counter.lower() + "_kib_raw"] = kib
         out[counter.lower() + "_copy_kib_raw"] = max(copy) if copy else None
         out[counter.lower() + "_scale"] = scale
         out[counter.lower() + "_bytes_per_launch"] = kib * scale * 1024.0
-        out[counter.lower() + "_launches"] = len(sel)
+        out[counter.lower() + "_launches"] = sum(len(v) for v in by_name.values())
+        out[counter.lower() + "_kernels_per_call"] = len(by_name)
     out["hbm_bytes_per_launch"] = out["fetch_size_bytes_per_launch"] + out["write_size_bytes_per_launch"]
     path = out_path or os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     with open(path, "w") as f:

@@ -173,7 +173,8 @@ vit_status vit_rmsnorm(const float* x, const float* w, float eps, int64_t rows, 
 
 /* Rotary table for a batch of grids (get_vision_cos_sin on the vision page):
  * table [sum P, head_dim/2] of float2 (cos, sin); entries k < head_dim/4 use the
- * patch row angle row * theta^(-k/(head_dim/4)), the rest the column angle. */
+ * patch row angle row * theta^(-k/(head_dim/4)), the rest the column angle.
+ * head_dim a multiple of 4, at most 128 (VIT_E_SHAPE otherwise). */
 vit_status vit_rope_table(const int32_t* grid_hw_host, int32_t n_images, int32_t head_dim,
                           float theta, void* table, void* stream);
 

@@ -345,7 +345,7 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
       pa.Kp = p.Kp;
       pa.table = table;
       pa.head_dim = c.head_dim;
-      pa.theta = (double)c.rope_theta;
+      pa.freqs = rope_freqs(c.head_dim, (double)c.rope_theta);
       pa.vpos = vpos;
       pa.vt = vt;
       pa.vt_rows = p.use_vt ? d : 0;
@@ -738,7 +738,9 @@ vit_status vit_rmsnorm(const float* x, const float* w, float eps, int64_t rows, 
 vit_status vit_rope_table(const int32_t* grid_hw_host, int32_t n_images, int32_t head_dim,
                           float theta, void* table, void* stream) {
   if (!table) return fail(VIT_E_ARG, "table is NULL");
-  if (head_dim <= 0 || head_dim % 4) return fail(VIT_E_SHAPE, "bad head_dim");
+  if (head_dim <= 0 || head_dim % 4 || head_dim / 4 > kRopeMaxFreqs)
+    return fail(VIT_E_SHAPE, "head_dim %d: need a multiple of 4, at most %d", head_dim,
+                4 * kRopeMaxFreqs);
   VarlenDesc d;
   VIT_TRY(build_desc(grid_hw_host, n_images, 1, false, 2, &d));
   return hip_check(launch_rope_table(d, head_dim, theta, table, (hipStream_t)stream), "rope table");

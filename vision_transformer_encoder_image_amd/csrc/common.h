@@ -195,6 +195,14 @@ hipError_t launch_attention_vt(const void* qk, int64_t ld_qk, const void* vt, in
 // Per-call preparation of an encode (bf16): zero-padded patches and patch
 // weight (K padded to Kp), rotary table, transposed-V positions and padding.
 // A null destination skips its part; b[] is filled in by the launcher.
+// Rotary frequencies theta^(-k / (head_dim/4)), k < head_dim/4 (computed on the
+// host in double, passed by value to the table kernels).
+constexpr int kRopeMaxFreqs = 32;
+struct RopeFreqs {
+  double f[kRopeMaxFreqs];
+};
+RopeFreqs rope_freqs(int head_dim, double theta);
+
 struct PrepArgs {
   VarlenDesc desc;
   const void* patches;  // [P, patch_dim] -> xpad [P, Kp]; pixel images if pixel_ps > 0
@@ -205,7 +213,7 @@ struct PrepArgs {
   int64_t P, d, patch_dim, Kp;
   void* table;          // float2 [P, head_dim / 2]
   int32_t head_dim;
-  double theta;
+  RopeFreqs freqs;
   int32_t* vpos;        // [P]
   void* vt;             // [vt_rows, vt_ld]
   int64_t vt_rows, vt_ld;

@@ -2,6 +2,8 @@
 // rotary application, 2x2 aligner gather, row padding, layout index arrays.
 #include <math.h>
 
+#include <cmath>
+
 #include "common.h"
 
 namespace {
@@ -46,8 +48,8 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const float* __restri
 // (cos, sin) of row * theta^(-k/(D/4)) for k < D/4 and of
 // col * theta^(-(k-D/4)/(D/4)) otherwise; row/col restart at every image.
 // Built in double precision, stored as float2.
-VIT_DEV void rope_table_elem(const VarlenDesc& d, int head_dim, double theta, float2* table,
-                             int64_t idx) {
+VIT_DEV void rope_table_elem(const VarlenDesc& d, int head_dim, const RopeFreqs& fr,
+                             float2* table, int64_t idx) {
   const int half = head_dim / 2, q4 = head_dim / 4;
   if (idx >= (int64_t)d.total * half) return;
   const int p = (int)(idx / half);
@@ -57,14 +59,13 @@ VIT_DEV void rope_table_elem(const VarlenDesc& d, int head_dim, double theta, fl
   const int gw = d.grid_w[img];
   const int pos = (k < q4) ? local / gw : local % gw;
   const int kk = (k < q4) ? k : k - q4;
-  const double f = pow(theta, -(double)kk / (double)q4);
   double s, c;
-  sincos((double)pos * f, &s, &c);
+  sincos((double)pos * fr.f[kk], &s, &c);
   table[idx] = make_float2((float)c, (float)s);
 }
 
-__global__ void rope_table_kernel(VarlenDesc d, int head_dim, double theta, float2* table) {
-  rope_table_elem(d, head_dim, theta, table, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+__global__ void rope_table_kernel(VarlenDesc d, int head_dim, RopeFreqs fr, float2* table) {
+  rope_table_elem(d, head_dim, fr, table, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -133,14 +134,19 @@ VIT_DEV void pad_rows_elem(const T* __restrict__ src, int64_t rows, int64_t cols
   if (idx >= rows * q) return;
   const int64_t r = idx / q;
   const int64_t c = (idx % q) * 4;
-  T v[4];
-  if (c < cols) {
-    const T* s = src + r * cols + c;
-    for (int k = 0; k < 4; ++k) v[k] = s[k];
-  } else {
-    for (int k = 0; k < 4; ++k) v[k] = from_f32<T>(0.f);
-  }
   T* o = dst + r * ld_dst + c;
+  if constexpr (sizeof(T) == 2) {
+    // bf16 with 4-element aligned rows: one 8-byte load and store per thread
+    if (cols % 4 == 0 && ((uintptr_t)src & 7) == 0 && ((uintptr_t)dst & 7) == 0 &&
+        ld_dst % 4 == 0) {
+      uint2 v = make_uint2(0u, 0u);
+      if (c < cols) v = *reinterpret_cast<const uint2*>(src + r * cols + c);
+      *reinterpret_cast<uint2*>(o) = v;
+      return;
+    }
+  }
+  T v[4];
+  for (int k = 0; k < 4; ++k) v[k] = c + k < cols ? src[r * cols + c + k] : from_f32<T>(0.f);
   for (int k = 0; k < 4; ++k) o[k] = v[k];
 }
 
@@ -234,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void encode_prep_kernel(PrepArgs a) {
     pad_rows_elem((const bf16*)a.w_pe, a.d, a.patch_dim, a.Kp, (bf16*)a.wpe,
                   (b - a.b[0]) * kThreads + t);
   } else if (b < a.b[2]) {
-    rope_table_elem(a.desc, a.head_dim, a.theta, (float2*)a.table, (b - a.b[1]) * kThreads + t);
+    rope_table_elem(a.desc, a.head_dim, a.freqs, (float2*)a.table, (b - a.b[1]) * kThreads + t);
   } else if (b < a.b[3]) {
     vpos_elem(a.desc, a.vpos, (b - a.b[2]) * kThreads + t);
   } else if (b < a.b[4]) {
@@ -355,11 +361,19 @@ hipError_t launch_rmsnorm(const float* x, const float* w, float eps, int64_t row
   return hipGetLastError();
 }
 
+RopeFreqs rope_freqs(int head_dim, double theta) {
+  RopeFreqs fr{};
+  const int q4 = head_dim / 4;
+  for (int k = 0; k < q4 && k < kRopeMaxFreqs; ++k) fr.f[k] = std::pow(theta, -(double)k / q4);
+  return fr;
+}
+
 hipError_t launch_rope_table(const VarlenDesc& d, int head_dim, float theta, void* table,
                              hipStream_t s) {
   const int64_t n = (int64_t)d.total * (head_dim / 2);
   if (n == 0) return hipSuccess;
-  rope_table_kernel<<<blocks_for(n), kThreads, 0, s>>>(d, head_dim, (double)theta,
+  if (head_dim / 4 > kRopeMaxFreqs) return hipErrorInvalidValue;
+  rope_table_kernel<<<blocks_for(n), kThreads, 0, s>>>(d, head_dim, rope_freqs(head_dim, theta),
                                                         (float2*)table);
   return hipGetLastError();
 }
@@ -416,6 +430,7 @@ hipError_t launch_zero_cols(int dtype, void* buf, int64_t rows, int64_t ld, int6
 }
 
 hipError_t launch_encode_prep(PrepArgs a, hipStream_t s) {
+  if (a.table && a.head_dim / 4 > kRopeMaxFreqs) return hipErrorInvalidValue;
   const int64_t n[5] = {a.patches ? a.P * (a.pixel_ps > 0 ? a.Kp : a.Kp / 4) : 0,
                         a.w_pe ? a.d * (a.Kp / 4) : 0,
                         a.table ? (int64_t)a.desc.total * (a.head_dim / 2) : 0,
