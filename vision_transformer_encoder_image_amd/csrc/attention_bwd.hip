@@ -110,7 +110,7 @@ VIT_DEV void rope_inv_store(const f32x16 (&acc)[2], const float2* __restrict__ t
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64 * AB_WAVES, 1) void attn_dq_kernel(
+__global__ __launch_bounds__(64 * AB_WAVES, 2) void attn_dq_kernel(
     const bf16* __restrict__ qkv, int64_t ldq, const bf16* __restrict__ dO,
     const bf16* __restrict__ kt, int64_t t_ld, const float* __restrict__ lse2,
     const float* __restrict__ Dq, VarlenDesc desc, int H, float c,
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(64 * AB_WAVES, 1) void attn_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64 * AB_WAVES, 1) void attn_dkv_kernel(
+__global__ __launch_bounds__(64 * AB_WAVES, 2) void attn_dkv_kernel(
     const bf16* __restrict__ qkv, int64_t ldq, const bf16* __restrict__ dO,
     const bf16* __restrict__ qt, const bf16* __restrict__ dot, int64_t t_ld,
     const float* __restrict__ lse2, const float* __restrict__ Dq, VarlenDesc desc, int H, float c,
