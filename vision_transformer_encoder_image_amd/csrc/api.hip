@@ -981,7 +981,7 @@ vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, vo
   // da = dy . W_down
   {
     ProfScope ps(VIT_K_BWD_PASS, s);
-    VIT_HIP(launch_cast_bf16(a->dy, P * d, dy16, s), "cast dy");
+    VIT_HIP(launch_cast_transpose(a->dy, P, d, dy16, dyT, p.Pp, p.Pp, s), "cast + transpose dy");
   }
   {
     ProfScope ps(VIT_K_BWD_PASS, s);
@@ -1011,10 +1011,6 @@ vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, vo
             "norm backward");
   }
   // weight gradients: contractions over the rows (zero-padded to Pp)
-  {
-    ProfScope ps(VIT_K_BWD_PASS, s);
-    VIT_HIP(launch_transpose_bf16(dy16, P, d, d, dyT, p.Pp, p.Pp, s), "transpose dy");
-  }
   {
     ProfScope ps(VIT_K_BWD_PASS, s);
     VIT_HIP(launch_transpose_bf16(act, P, h, h, aT, p.Pp, p.Pp, s), "transpose a");
@@ -1107,7 +1103,7 @@ vit_status vit_attn_backward(const vit_attn_grad* a, const int32_t* grid_hw_host
     VIT_HIP(launch_attention_vt(qkv, 3 * d, vt, p.kv, fwd, (int)H, o, s, lse), "attention");
   }
   // dO = dy . Wo, Dq = rowsum(dO o), transposed operands of the attention gradient
-  VIT_HIP(launch_cast_bf16(a->dy, P * d, dy16, s), "cast dy");
+  VIT_HIP(launch_cast_transpose(a->dy, P, d, dy16, dyT, p.Pp, p.Pp, s), "cast + transpose dy");
   VIT_HIP(launch_transpose_bf16(a->wo, d, d, d, woT, d, d, s), "transpose wo");
   VIT_TRY(mm(VIT_EPI_STORE, dy16, d, woT, d, dO, d, P, d, d));
   VIT_HIP(launch_rowdot(dO, o, P, (int)H, Dq, s), "rowsum(dO o)");
@@ -1127,12 +1123,17 @@ vit_status vit_attn_backward(const vit_attn_grad* a, const int32_t* grid_hw_host
                              a->d_norm_w, s),
           "norm backward");
   // weight gradients: contractions over the rows (zero-padded to Pp)
-  VIT_HIP(launch_transpose_bf16(dy16, P, d, d, dyT, p.Pp, p.Pp, s), "transpose dy");
   VIT_HIP(launch_transpose_bf16(o, P, d, d, oT, p.Pp, p.Pp, s), "transpose o");
   VIT_HIP(launch_transpose_bf16(dqkv, P, 3 * d, 3 * d, dqkvT, p.Pp, p.Pp, s), "transpose dqkv");
   VIT_HIP(launch_transpose_bf16(n, P, d, d, nT, p.Pp, p.Pp, s), "transpose n");
-  VIT_TRY(mm(VIT_EPI_STORE_F32, dyT, p.Pp, oT, p.Pp, a->d_wo, d, d, d, p.Pp));
-  return mm(VIT_EPI_STORE_F32, dqkvT, p.Pp, nT, p.Pp, a->d_wqkv, d, 3 * d, d, p.Pp);
+  // dWqkv (3d x d) and dWo (d x d) in one grouped launch: 192 + 64 tiles of 128x128
+  // fill the 256 CUs once where the two alone would take two launches
+  GemmArgs gq = gemm_args(dqkvT, p.Pp, nT, nullptr, p.Pp, a->d_wqkv, d, 3 * d, d, p.Pp, nullptr);
+  GemmArgs go = gemm_args(dyT, p.Pp, oT, nullptr, p.Pp, a->d_wo, d, d, d, p.Pp, nullptr);
+  if (!gemm_bf16_mfma_eligible(gq) || !gemm_bf16_mfma_eligible(go))
+    return fail(VIT_E_SHAPE, "weight-gradient GEMMs too large");
+  ProfScope all(VIT_K_BWD_GEMM, s);
+  return hip_check(launch_gemm_bf16_pair(VIT_EPI_STORE_F32, gq, go, s), "weight gradients");
 }
 
 size_t vit_tower_backward_workspace_bytes(const vit_config* cfg, const int32_t* grid_hw_host,
@@ -1219,8 +1220,7 @@ vit_status vit_tower_backward(const vit_config* cfg, const vit_weights* w, const
   bf16* dx16 = (bf16*)(half + t.dx16);
   bf16* dxT = (bf16*)(half + t.dxT);
   bf16* xT = (bf16*)(half + t.xT);
-  VIT_HIP(launch_cast_bf16(cur, P * d, dx16, s), "cast dx0");
-  VIT_HIP(launch_transpose_bf16(dx16, P, d, d, dxT, t.Pp, t.Pp, s), "transpose dx0");
+  VIT_HIP(launch_cast_transpose(cur, P, d, dx16, dxT, t.Pp, t.Pp, s), "cast + transpose dx0");
   VIT_HIP(launch_transpose_bf16(base + t.fwd.xpad, P, t.fwd.Kp, t.fwd.Kp, xT, t.Pp, t.Pp, s),
           "transpose patches");
   GemmArgs g = gemm_args(dxT, t.Pp, xT, nullptr, t.Pp, gr->d_patch_embed, c.patch_dim, d,

@@ -25,10 +25,13 @@ __global__ __launch_bounds__(kThreads) void cast_bf16_kernel(const float* __rest
 // dst[c][j] = src[j][c] for j < R, 0 for R <= j < cols_out; c < C.  src rows
 // have ld_src elements, dst rows ld_dst.  One 64x64 tile per block through LDS
 // (rows padded by 8 elements against bank conflicts of the scattered writes).
+// An fp32 source is rounded to bf16 on the way, and then also written row-major
+// to copy [R, C] (the cast and the transpose of one operand in one pass).
 constexpr int kTT = 64;
+template <typename TS>
 __global__ __launch_bounds__(kThreads) void transpose_bf16_kernel(
-    const bf16* __restrict__ src, int64_t R, int64_t C, int64_t ld_src, bf16* __restrict__ dst,
-    int64_t cols_out, int64_t ld_dst) {
+    const TS* __restrict__ src, int64_t R, int64_t C, int64_t ld_src, bf16* __restrict__ dst,
+    int64_t cols_out, int64_t ld_dst, bf16* __restrict__ copy) {
   __shared__ bf16 tile[kTT][kTT + 8];
   const int64_t j0 = (int64_t)blockIdx.x * kTT;  // source row block = dst column block
   const int64_t c0 = (int64_t)blockIdx.y * kTT;  // source column block = dst row block
@@ -40,11 +43,28 @@ __global__ __launch_bounds__(kThreads) void transpose_bf16_kernel(
     const int64_t j = j0 + r, c = c0 + ch * 8;
     bf16x8 v;
     if (j < R && c + 8 <= C) {
-      v = __builtin_bit_cast(bf16x8, ld16(src + j * ld_src + c));
+      if constexpr (sizeof(TS) == 2) {
+        v = __builtin_bit_cast(bf16x8, ld16(src + j * ld_src + c));
+      } else {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(src + j * ld_src + c);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(src + j * ld_src + c + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = f2bf(lo[e]);
+          v[e + 4] = f2bf(hi[e]);
+        }
+        st16(copy + j * C + c, __builtin_bit_cast(u32x4, v));
+      }
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        v[e] = (j < R && c + e < C) ? src[j * ld_src + c + e] : f2bf(0.f);
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (sizeof(TS) == 2) {
+          v[e] = (j < R && c + e < C) ? src[j * ld_src + c + e] : f2bf(0.f);
+        } else {
+          v[e] = (j < R && c + e < C) ? f2bf(src[j * ld_src + c + e]) : f2bf(0.f);
+          if (j < R && c + e < C) copy[j * C + c + e] = v[e];
+        }
+      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) tile[ch * 8 + e][r] = v[e];
@@ -105,6 +125,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(const float* __res
 constexpr int kNbRows = 16;       // rows per block (enough blocks to fill the CUs)
 constexpr int kNbWaves = 8;
 constexpr int kNbMaxChunks = 8;   // 4-column chunks per lane: d <= 64 * 4 * 8 = 2048
+template <int NCH>  // 4-column chunks per lane (d <= 256 * NCH)
 __global__ __launch_bounds__(64 * kNbWaves) void rmsnorm_bwd_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ dn,
     const float* __restrict__ dy, int64_t rows, int d, float eps, float* __restrict__ dx,
@@ -112,25 +133,35 @@ __global__ __launch_bounds__(64 * kNbWaves) void rmsnorm_bwd_kernel(
   __shared__ float s_part[kNbWaves / 2][2048];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nch = d / 4;
-  f32x4 acc[kNbMaxChunks];
+  f32x4 acc[NCH];
 #pragma unroll
-  for (int k = 0; k < kNbMaxChunks; ++k) acc[k] = f32x4{};
+  for (int k = 0; k < NCH; ++k) acc[k] = f32x4{};
   const int64_t r0 = (int64_t)blockIdx.x * kNbRows;
   for (int rr = wave; rr < kNbRows; rr += kNbWaves) {
     const int64_t r = r0 + rr;
     if (r >= rows) break;
-    f32x4 xv[kNbMaxChunks], gv[kNbMaxChunks];
-    float ss = 0.f, sd = 0.f;
+    // every load of the row first (x, dn, the residual dy, w), then the two
+    // row sums, then the stores
+    f32x4 xv[NCH], nv[NCH], yv[NCH], gv[NCH];
 #pragma unroll
-    for (int k = 0; k < kNbMaxChunks; ++k) {
+    for (int k = 0; k < NCH; ++k) {
       const int ch = lane + 64 * k;
+      xv[k] = nv[k] = yv[k] = f32x4{};
       if (ch < nch) {
         xv[k] = *reinterpret_cast<const f32x4*>(x + r * d + 4 * ch);
+        nv[k] = *reinterpret_cast<const f32x4*>(dn + r * d + 4 * ch);
+        if (dy) yv[k] = *reinterpret_cast<const f32x4*>(dy + r * d + 4 * ch);
+      }
+    }
+    float ss = 0.f, sd = 0.f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int ch = lane + 64 * k;
+      if (ch < nch) {
         const f32x4 wv = *reinterpret_cast<const f32x4*>(w + 4 * ch);
-        const f32x4 nv = *reinterpret_cast<const f32x4*>(dn + r * d + 4 * ch);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          gv[k][e] = wv[e] * nv[e];
+          gv[k][e] = wv[e] * nv[k][e];
           ss += xv[k][e] * xv[k][e];
           sd += gv[k][e] * xv[k][e];
         }
@@ -139,16 +170,14 @@ __global__ __launch_bounds__(64 * kNbWaves) void rmsnorm_bwd_kernel(
     const float rs = 1.0f / sqrtf(wave_sum(ss) / (float)d + eps);
     const float coef = rs * rs * rs * wave_sum(sd) / (float)d;
 #pragma unroll
-    for (int k = 0; k < kNbMaxChunks; ++k) {
+    for (int k = 0; k < NCH; ++k) {
       const int ch = lane + 64 * k;
       if (ch < nch) {
-        const f32x4 yv = dy ? *reinterpret_cast<const f32x4*>(dy + r * d + 4 * ch) : f32x4{};
-        const f32x4 nv = *reinterpret_cast<const f32x4*>(dn + r * d + 4 * ch);
         f32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          o[e] = yv[e] + rs * gv[k][e] - xv[k][e] * coef;
-          acc[k][e] += nv[e] * xv[k][e] * rs;
+          o[e] = yv[k][e] + rs * gv[k][e] - xv[k][e] * coef;
+          acc[k][e] += nv[k][e] * xv[k][e] * rs;
         }
         *reinterpret_cast<f32x4*>(dx + r * d + 4 * ch) = o;
       }
@@ -158,7 +187,7 @@ __global__ __launch_bounds__(64 * kNbWaves) void rmsnorm_bwd_kernel(
   // (through LDS), then the four pairs
   if (wave >= kNbWaves / 2) {
 #pragma unroll
-    for (int k = 0; k < kNbMaxChunks; ++k) {
+    for (int k = 0; k < NCH; ++k) {
       const int ch = lane + 64 * k;
       if (ch < nch) *reinterpret_cast<f32x4*>(&s_part[wave - kNbWaves / 2][4 * ch]) = acc[k];
     }
@@ -166,7 +195,7 @@ __global__ __launch_bounds__(64 * kNbWaves) void rmsnorm_bwd_kernel(
   __syncthreads();
   if (wave < kNbWaves / 2) {
 #pragma unroll
-    for (int k = 0; k < kNbMaxChunks; ++k) {
+    for (int k = 0; k < NCH; ++k) {
       const int ch = lane + 64 * k;
       if (ch < nch) {
         f32x4 t = *reinterpret_cast<const f32x4*>(&s_part[wave][4 * ch]);
@@ -223,8 +252,18 @@ hipError_t launch_transpose_bf16(const void* src, int64_t R, int64_t C, int64_t 
   if (R <= 0 || C <= 0 || cols_out <= 0) return hipSuccess;
   if (cols_out > ld_dst || ld_src < C || ld_src % 8 || ld_dst % 8) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((cols_out + kTT - 1) / kTT), (unsigned)((C + kTT - 1) / kTT));
-  transpose_bf16_kernel<<<grid, kThreads, 0, s>>>((const bf16*)src, R, C, ld_src, (bf16*)dst,
-                                                  cols_out, ld_dst);
+  transpose_bf16_kernel<bf16><<<grid, kThreads, 0, s>>>((const bf16*)src, R, C, ld_src,
+                                                        (bf16*)dst, cols_out, ld_dst, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_transpose(const float* src, int64_t R, int64_t C, void* copy, void* dst,
+                                 int64_t cols_out, int64_t ld_dst, hipStream_t s) {
+  if (R <= 0 || C <= 0 || cols_out <= 0) return hipSuccess;
+  if (cols_out > ld_dst || C % 8 || ld_dst % 8) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((cols_out + kTT - 1) / kTT), (unsigned)((C + kTT - 1) / kTT));
+  transpose_bf16_kernel<float><<<grid, kThreads, 0, s>>>(src, R, C, C, (bf16*)dst, cols_out,
+                                                         ld_dst, (bf16*)copy);
   return hipGetLastError();
 }
 
@@ -245,7 +284,11 @@ hipError_t launch_rmsnorm_bwd(const float* x, const float* w, const float* dn, c
   if (d % 4 || d > 64 * 4 * kNbMaxChunks) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
   const int nb = rmsnorm_bwd_blocks(rows);
-  rmsnorm_bwd_kernel<<<nb, 64 * kNbWaves, 0, s>>>(x, w, dn, dy, rows, d, eps, dx, partial);
+  if (d <= 256 * 4)
+    rmsnorm_bwd_kernel<4><<<nb, 64 * kNbWaves, 0, s>>>(x, w, dn, dy, rows, d, eps, dx, partial);
+  else
+    rmsnorm_bwd_kernel<kNbMaxChunks><<<nb, 64 * kNbWaves, 0, s>>>(x, w, dn, dy, rows, d, eps, dx,
+                                                                  partial);
   colsum_kernel<<<(unsigned)((d + 63) / 64), 64 * kCsGroups, 0, s>>>(partial, nb, d, dw);
   return hipGetLastError();
 }

@@ -174,6 +174,9 @@ constexpr int VIT_EPI_STORE_ROPE = 16;
 constexpr int VIT_EPI_QKV_VT = 17;
 
 hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s);
+// two independent GEMMs with one epilogue, in one launch when both take the MFMA path
+hipError_t launch_gemm_bf16_pair(int epilogue, const GemmArgs& g0, const GemmArgs& g1,
+                                 hipStream_t s);
 hipError_t launch_gemm_f32(int epilogue, const GemmArgs& g, hipStream_t s);
 bool gemm_bf16_can_fuse_rope(const GemmArgs& g);
 // the MFMA GEMM path (rotary, transposed-V and RMSNorm epilogues) takes these arguments
@@ -245,6 +248,10 @@ hipError_t launch_ln_gather(const void* x, const VarlenDesc& d, int dim, const f
 hipError_t launch_cast_bf16(const float* src, int64_t n, void* dst, hipStream_t s);
 // dst [C, ld_dst] = src [R, C]^T, columns R .. cols_out-1 zero (bf16, ld % 8 == 0)
 hipError_t launch_transpose_bf16(const void* src, int64_t R, int64_t C, int64_t ld_src, void* dst,
+                                 int64_t cols_out, int64_t ld_dst, hipStream_t s);
+// fp32 src [R, C] -> bf16 copy [R, C] and its transpose dst [C, ld_dst] (columns
+// R .. cols_out-1 zero) in one pass; C % 8 == 0
+hipError_t launch_cast_transpose(const float* src, int64_t R, int64_t C, void* copy, void* dst,
                                  int64_t cols_out, int64_t ld_dst, hipStream_t s);
 hipError_t launch_swiglu_bwd(const float* gu, const float* da, int64_t rows, int h, void* a,
                              void* dgdu, hipStream_t s);

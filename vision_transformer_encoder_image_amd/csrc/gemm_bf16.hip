@@ -355,6 +355,40 @@ GemmSplit gemm_mfma_split(int epilogue, bool norm_producer, int64_t M, int64_t N
   return best;
 }
 
+// Two independent GEMMs of one epilogue in one launch (e.g. weight gradients
+// whose tiles together fill the CUs once): the tile configuration is chosen by
+// the same cost model over the combined tile count.  Plain epilogues only (no
+// folded norm, rotary or row map); otherwise, or when either GEMM cannot take
+// the MFMA path, two ordinary launches.
+hipError_t launch_gemm_bf16_pair(int epilogue, const GemmArgs& g0, const GemmArgs& g1,
+                                 hipStream_t s) {
+  const bool plain = epilogue == VIT_EPI_STORE || epilogue == VIT_EPI_STORE_F32;
+  const bool simple = !g0.norm_w && !g0.ss_in && !g1.norm_w && !g1.ss_in && !g0.rowmap &&
+                      !g1.rowmap;
+  if (!plain || !simple || !pipe_eligible(g0) || !pipe_eligible(g1) || g0.M == 0 || g0.N == 0 ||
+      g1.M == 0 || g1.N == 0) {
+    const hipError_t e = launch_gemm_bf16(epilogue, g0, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm_bf16(epilogue, g1, s);
+  }
+  TileOpt opts[4];
+  tile_opts(epilogue, false, opts);
+  int best = GEMM_MFMA_128x128;
+  double best_cost = 1e300;
+  for (const TileOpt& o : opts) {
+    if (!o.ok) continue;
+    const int64_t bno = tile_cols(o, epilogue);
+    const int64_t tiles = ((g0.M + o.bm - 1) / o.bm) * ((g0.N + bno - 1) / bno) +
+                          ((g1.M + o.bm - 1) / o.bm) * ((g1.N + bno - 1) / bno);
+    const double c = (double)((tiles + kCUs - 1) / kCUs) * o.bm * o.bn / o.eff;
+    if (c < best_cost) {
+      best_cost = c;
+      best = o.cfg;
+    }
+  }
+  return launch_gemm_mfma(best, epilogue, g0, s, &g1);
+}
+
 bool gemm_bf16_can_fuse_rope(const GemmArgs& g) { return pipe_eligible(g); }
 
 bool gemm_bf16_mfma_eligible(const GemmArgs& g) { return pipe_eligible(g); }

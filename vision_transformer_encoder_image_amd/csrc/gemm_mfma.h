@@ -11,7 +11,10 @@ enum GemmMfmaCfg {
   GEMM_MFMA_NCFG = 4,
 };
 
-hipError_t launch_gemm_mfma(int cfg, int epi, const GemmArgs& g, hipStream_t s);
+// g1 (optional): a second GEMM of the same configuration and epilogue in the
+// same launch (its workgroups follow g's)
+hipError_t launch_gemm_mfma(int cfg, int epi, const GemmArgs& g, hipStream_t s,
+                            const GemmArgs* g1 = nullptr);
 
 // Launch plan of one GEMM: cfg_main over columns [0, n_main), and when
 // n_main < N a second launch of cfg_tail over [n_main, N).

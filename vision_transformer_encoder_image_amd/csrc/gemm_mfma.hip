@@ -58,8 +58,14 @@ VIT_DEV float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 // GELU in its erf form, x * Phi(x)
 VIT_DEV float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
+// One launch computes one GEMM, or two independent GEMMs of the same tile
+// configuration and epilogue (a grouped launch: workgroups below tiles0 take
+// g0, the rest g1), which fills the CUs when each alone would leave many idle.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool DUAL>
-__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) {
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0, GemmArgs g1,
+                                                                    int tiles0) {
+  const bool second = (int)blockIdx.x >= tiles0;
+  const GemmArgs& g = second ? g1 : g0;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;  // wave sub-tile
   constexpr int BI = TM / 32, BJ = TN / 32;  // 32x32 blocks per wave
@@ -87,7 +93,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
   // Workgroup ids go round-robin over the 8 XCDs; give each XCD a contiguous
   // run of the grouped tile order (kGroupM tile rows share a column band), so
   // the A rows and B columns one XCD touches stay in its own L2.
-  int L = blockIdx.x;
+  int L = second ? (int)blockIdx.x - tiles0 : (int)blockIdx.x;
   {
     const int per = ntiles / kXcds, rem = ntiles % kXcds;
     const int xcd = L % kXcds, idx = L / kXcds;
@@ -703,7 +709,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g) 
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool DUAL>
-hipError_t mfma_cfg(const GemmArgs& g, hipStream_t s) {
+hipError_t mfma_cfg(const GemmArgs& g, hipStream_t s, const GemmArgs* g1 = nullptr) {
   constexpr int BNO = DUAL ? BN / 2 : BN;
   // the ring, then BM floats of per-row RMSNorm scale
   constexpr size_t lds = (size_t)STAGES * (BM + BN) * BK * sizeof(bf16) + BM * sizeof(float);
@@ -716,32 +722,34 @@ hipError_t mfma_cfg(const GemmArgs& g, hipStream_t s) {
     attr = true;
   }
   const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BNO - 1) / BNO);
-  kern<<<dim3((unsigned)tiles), dim3(WM * WN * 64), lds, s>>>(g);
+  const int64_t tiles1 = g1 ? ((g1->M + BM - 1) / BM) * ((g1->N + BNO - 1) / BNO) : 0;
+  kern<<<dim3((unsigned)(tiles + tiles1)), dim3(WM * WN * 64), lds, s>>>(g, g1 ? *g1 : g,
+                                                                          (int)tiles);
   return hipGetLastError();
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES>
-hipError_t mfma_epi(int epi, const GemmArgs& g, hipStream_t s) {
+hipError_t mfma_epi(int epi, const GemmArgs& g, hipStream_t s, const GemmArgs* g1 = nullptr) {
   switch (epi) {
-    case VIT_EPI_STORE: return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_STORE, false>(g, s);
+    case VIT_EPI_STORE: return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_STORE, false>(g, s, g1);
     case VIT_EPI_STORE_F32:
-      return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_STORE_F32, false>(g, s);
+      return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_STORE_F32, false>(g, s, g1);
     case VIT_EPI_ADD_F32:
       // not built for the 256x256 tile (it spills; the dispatcher never picks it)
       if constexpr (!(BM == 256 && BN == 256))
-        return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_ADD_F32, false>(g, s);
+        return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_ADD_F32, false>(g, s, g1);
       return hipErrorInvalidValue;
-    case VIT_EPI_SWIGLU: return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_SWIGLU, true>(g, s);
-    case VIT_EPI_BIAS: return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_BIAS, false>(g, s);
+    case VIT_EPI_SWIGLU: return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_SWIGLU, true>(g, s, g1);
+    case VIT_EPI_BIAS: return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_BIAS, false>(g, s, g1);
     case VIT_EPI_BIAS_GELU:
-      return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_BIAS_GELU, false>(g, s);
+      return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_BIAS_GELU, false>(g, s, g1);
     case VIT_EPI_STORE_ROPE:
       if constexpr ((BN / WN) % 64 == 0)
-        return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_STORE_ROPE, false>(g, s);
+        return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_STORE_ROPE, false>(g, s, g1);
       return hipErrorInvalidValue;
     case VIT_EPI_QKV_VT:
       if constexpr ((BN / WN) % 64 == 0)
-        return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_QKV_VT, false>(g, s);
+        return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_QKV_VT, false>(g, s, g1);
       return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
@@ -749,12 +757,13 @@ hipError_t mfma_epi(int epi, const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gemm_mfma(int cfg, int epi, const GemmArgs& g, hipStream_t s) {
+hipError_t launch_gemm_mfma(int cfg, int epi, const GemmArgs& g, hipStream_t s,
+                            const GemmArgs* g1) {
   switch (cfg) {
-    case GEMM_MFMA_128x128: return mfma_epi<128, 128, 64, 4, 2, 4>(epi, g, s);
-    case GEMM_MFMA_256x128_W8: return mfma_epi<256, 128, 64, 4, 2, 3>(epi, g, s);
-    case GEMM_MFMA_256x256_W8: return mfma_epi<256, 256, 32, 2, 4, 4>(epi, g, s);
-    case GEMM_MFMA_192x256: return mfma_epi<192, 256, 32, 2, 2, 4>(epi, g, s);
+    case GEMM_MFMA_128x128: return mfma_epi<128, 128, 64, 4, 2, 4>(epi, g, s, g1);
+    case GEMM_MFMA_256x128_W8: return mfma_epi<256, 128, 64, 4, 2, 3>(epi, g, s, g1);
+    case GEMM_MFMA_256x256_W8: return mfma_epi<256, 256, 32, 2, 4, 4>(epi, g, s, g1);
+    case GEMM_MFMA_192x256: return mfma_epi<192, 256, 32, 2, 2, 4>(epi, g, s, g1);
   }
   return hipErrorInvalidValue;
 }
