@@ -651,6 +651,8 @@ def main():
                          "projector: the PatchMerger projector; mlp_backward / attn_backward: "
                          "the backward of a block's MLP / attention half; tower_backward: the "
                          "backward of the whole tower")
+    ap.add_argument("--pixels", action="store_true",
+                    help="encode stage: pixel images in (the library cuts the patches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -697,8 +699,12 @@ def main():
     inp = synth.make_inputs(cfg, seed=idx)
     dev = "cuda:0"
     w = api.DeviceWeights(cfg, inp["weights"], device=dev)
+    # with --pixels the same synthetic values are read as the images' pixels
+    # ([3, 14 gh, 14 gw] each, back to back) and the library cuts the patches
     x = torch.from_numpy(inp["patches"]).to(dev, torch.bfloat16 if cfg.dtype == "bf16" else torch.float32)
-    enc = api.Encoder(cfg, w, cfg.grids, aligner=cfg.aligner, device=dev)
+    if args.pixels:
+        x = x.reshape(-1)
+    enc = api.Encoder(cfg, w, cfg.grids, aligner=cfg.aligner, device=dev, pixels=args.pixels)
     out = torch.empty(enc.out_shape, dtype=x.dtype, device=dev)
 
     flops = class_flops(cfg)
@@ -752,7 +758,8 @@ def main():
         "config": {"workload": cfg.name, "grids": [list(g) for g in cfg.grids], "patches": P,
                    "vision_dim": cfg.vision_dim, "heads": cfg.n_heads, "head_dim": cfg.head_dim,
                    "mlp_hidden": cfg.mlp_hidden, "blocks": cfg.n_blocks,
-                   "aligner": cfg.llm_dim if cfg.aligner else None},
+                   "aligner": cfg.llm_dim if cfg.aligner else None,
+                   "input": "pixels" if args.pixels else "patches"},
         "mfma_frac_step": round(cfg.total_flops() / (ms_per_step / 1e3) / (peak * 1e12), 4),
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),

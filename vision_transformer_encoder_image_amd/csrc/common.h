@@ -210,6 +210,7 @@ struct PrepArgs {
   VarlenDesc desc;
   const void* patches;  // [P, patch_dim] -> xpad [P, Kp]; pixel images if pixel_ps > 0
   int32_t pixel_ps;     // patch size of pixel input (0: `patches` holds patches)
+  int32_t pix_rows;     // set by the launcher: pixel rows copied as 32-bit words
   void* xpad;
   const void* w_pe;     // [d, patch_dim] -> wpe [d, Kp]
   void* wpe;

@@ -216,6 +216,34 @@ VIT_DEV void patchify_elem(const T* __restrict__ pix, const VarlenDesc& d, int p
   dst[idx] = v;
 }
 
+// bf16 pixels with an even patch size and 4-byte aligned rows: one thread per
+// (patch, channel, pixel row of the patch) copies the ps contiguous pixels of
+// that row as ps/2 32-bit words into the patch row; unit 3*ps of a patch zeroes
+// the padding columns pd .. ld_dst-1.  Same result as patchify_elem.
+VIT_DEV void patchify_rows_elem(const bf16* __restrict__ pix, const VarlenDesc& d, int ps,
+                                int64_t ld_dst, bf16* __restrict__ dst, int64_t idx) {
+  const int units = 3 * ps + 1;
+  if (idx >= (int64_t)d.total * units) return;
+  const int p = (int)(idx / units);
+  const int u = (int)(idx % units);
+  const int pd = 3 * ps * ps;
+  uint32_t* o = reinterpret_cast<uint32_t*>(dst + (int64_t)p * ld_dst);
+  if (u == 3 * ps) {
+    for (int k = pd / 2; k < ld_dst / 2; ++k) o[k] = 0u;
+    return;
+  }
+  const int img = find_image(d, p);
+  const int start = d.cu_seqlens[img], gw = d.grid_w[img];
+  const int gh = (d.cu_seqlens[img + 1] - start) / gw;
+  const int local = p - start, r = local / gw, c = local % gw;
+  const int ch = u / ps, y = u % ps;
+  const int64_t W = (int64_t)gw * ps, Hh = (int64_t)gh * ps;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(
+      pix + (int64_t)pd * start + (ch * Hh + (int64_t)r * ps + y) * W + (int64_t)c * ps);
+  uint32_t* out = o + (ch * ps * ps + y * ps) / 2;
+  for (int k = 0; k < ps / 2; ++k) out[k] = src[k];
+}
+
 template <typename T>
 __global__ void patchify_kernel(const T* __restrict__ pix, VarlenDesc d, int ps, int64_t ld_dst,
                                 T* __restrict__ dst) {
@@ -230,7 +258,10 @@ __global__ __launch_bounds__(kThreads) void encode_prep_kernel(PrepArgs a) {
   const int64_t b = blockIdx.x;
   const int t = threadIdx.x;
   if (b < a.b[0]) {
-    if (a.pixel_ps > 0)
+    if (a.pixel_ps > 0 && a.pix_rows)
+      patchify_rows_elem((const bf16*)a.patches, a.desc, a.pixel_ps, a.Kp, (bf16*)a.xpad,
+                         b * kThreads + t);
+    else if (a.pixel_ps > 0)
       patchify_elem((const bf16*)a.patches, a.desc, a.pixel_ps, a.Kp, (bf16*)a.xpad,
                     b * kThreads + t);
     else
@@ -431,7 +462,10 @@ hipError_t launch_zero_cols(int dtype, void* buf, int64_t rows, int64_t ld, int6
 
 hipError_t launch_encode_prep(PrepArgs a, hipStream_t s) {
   if (a.table && a.head_dim / 4 > kRopeMaxFreqs) return hipErrorInvalidValue;
-  const int64_t n[5] = {a.patches ? a.P * (a.pixel_ps > 0 ? a.Kp : a.Kp / 4) : 0,
+  a.pix_rows = a.pixel_ps > 0 && a.pixel_ps % 2 == 0 && a.Kp % 2 == 0 &&
+               ((uintptr_t)a.patches & 3) == 0 && ((uintptr_t)a.xpad & 3) == 0;
+  const int64_t n[5] = {a.patches ? a.P * (a.pix_rows ? 3 * a.pixel_ps + 1
+                                           : a.pixel_ps > 0 ? a.Kp : a.Kp / 4) : 0,
                         a.w_pe ? a.d * (a.Kp / 4) : 0,
                         a.table ? (int64_t)a.desc.total * (a.head_dim / 2) : 0,
                         a.vpos ? (int64_t)a.desc.total : 0,
