@@ -483,7 +483,7 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
 // Backward of the MLP half: workspace layout
 struct MlpGradPlan {
   int64_t Pp = 0;  // rows rounded up to 64 (K of the weight-gradient GEMMs)
-  size_t n = 0, dy16 = 0, gu = 0, da = 0, a = 0, dgdu = 0, dn = 0, wdT = 0, wguT = 0;
+  size_t n = 0, dy16 = 0, gu = 0, da = 0, dgdu = 0, dn = 0, wdT = 0, wguT = 0;
   size_t dyT = 0, aT = 0, dgduT = 0, nT = 0, partial = 0, total = 0;
 };
 
@@ -500,7 +500,6 @@ MlpGradPlan mlp_grad_plan(int64_t P, int64_t d, int64_t h) {
   p.dy16 = take(P * d * 2);
   p.gu = take(P * 2 * h * 4);
   p.da = take(P * h * 4);
-  p.a = take(P * h * 2);
   p.dgdu = take(P * 2 * h * 2);
   p.dn = take(P * d * 4);
   p.wdT = take(h * d * 2);
@@ -950,7 +949,6 @@ vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, vo
   bf16* dy16 = (bf16*)(base + p.dy16);
   float* gu = (float*)(base + p.gu);
   float* da = (float*)(base + p.da);
-  bf16* act = (bf16*)(base + p.a);
   bf16* dgdu = (bf16*)(base + p.dgdu);
   float* dn = (float*)(base + p.dn);
   bf16* wdT = (bf16*)(base + p.wdT);
@@ -988,10 +986,11 @@ vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, vo
     VIT_HIP(launch_transpose_bf16(a->w_down, d, h, h, wdT, d, d, s), "transpose W_down");
   }
   VIT_TRY(mm(dy16, d, wdT, d, da, h, P, h, d));
-  // SwiGLU gradient (and the activation for dW_down)
+  // SwiGLU gradient: dg, du row-major, and a, dg, du transposed for the
+  // weight gradients (zero past row P)
   {
     ProfScope ps(VIT_K_BWD_PASS, s);
-    VIT_HIP(launch_swiglu_bwd(gu, da, P, (int)h, act, dgdu, s), "swiglu backward");
+    VIT_HIP(launch_swiglu_bwd_t(gu, da, P, (int)h, p.Pp, dgdu, aT, dgduT, s), "swiglu backward");
   }
   // dn = dg . W_gate + du . W_up
   {
@@ -1011,14 +1010,6 @@ vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, vo
             "norm backward");
   }
   // weight gradients: contractions over the rows (zero-padded to Pp)
-  {
-    ProfScope ps(VIT_K_BWD_PASS, s);
-    VIT_HIP(launch_transpose_bf16(act, P, h, h, aT, p.Pp, p.Pp, s), "transpose a");
-  }
-  {
-    ProfScope ps(VIT_K_BWD_PASS, s);
-    VIT_HIP(launch_transpose_bf16(dgdu, P, 2 * h, 2 * h, dgduT, p.Pp, p.Pp, s), "transpose dg, du");
-  }
   {
     ProfScope ps(VIT_K_BWD_PASS, s);
     VIT_HIP(launch_transpose_bf16(n, P, d, d, nT, p.Pp, p.Pp, s), "transpose n");
