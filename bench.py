@@ -144,9 +144,35 @@ def cpu_baseline(cfg, inp, budget_s=30.0):
     oracle.encode_varlen(inp["patches"][:P], take, inp["weights"], cfg.n_heads, cfg.rms_eps,
                          cfg.rope_theta, with_aligner=cfg.aligner)
     dt = time.perf_counter() - t0
+    # one BLAS thread, on the smallest image of the sample
+    small = min(take, key=lambda g: g[0] * g[1])
+    off = 0
+    for g in take:
+        if g == small:
+            break
+        off += g[0] * g[1]
+    Ps = small[0] * small[1]
+    with threadpoolctl.threadpool_limits(limits=1, user_api="blas"):
+        t1 = time.perf_counter()
+        oracle.encode_varlen(inp["patches"][off:off + Ps], [small], inp["weights"], cfg.n_heads,
+                             cfg.rms_eps, cfg.rope_theta, with_aligner=cfg.aligner)
+        dt1 = time.perf_counter() - t1
+    blas = sorted({i.get("internal_api", "?") for i in info if i.get("user_api") == "blas"})
+    cpu_model = "?"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": P / dt, "unit": "patches/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{len(take)} of {len(grids)} images ({P} patches, {cfg.n_blocks} blocks, "
-                      f"float64 numpy oracle, one pass, {dt:.1f} s)"}
+                      f"float64 numpy oracle, one pass, {dt:.1f} s)",
+            "value_1_thread": Ps / dt1,
+            "sample_1_thread": f"the {small[0]}x{small[1]} image, one BLAS thread, {dt1:.1f} s",
+            "cpu_model": cpu_model, "cpu_count": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)), "blas": blas}
 
 
 def copy_calibration(mb, dev):
@@ -714,14 +740,17 @@ def main():
 
     # which kernel dominates: one profiled step per class (not part of the timing)
     per_class = {}
-    for k in flops:
+    for k in list(flops) + ["rmsnorm"]:
         api.profile_enable(k, True)
     enc(x, out)
     torch.cuda.synchronize()
-    for k in flops:
+    for k in list(flops) + ["rmsnorm"]:
         ms, n = api.profile_read(k)
         api.profile_enable(k, False)
         per_class[k] = ms
+    outside_ms = per_class.pop("embed", 0.0) + per_class.pop("rmsnorm", 0.0)
+    if cfg.aligner:
+        outside_ms += per_class.pop("aligner", 0.0)
     dominant = max(per_class, key=per_class.get)
 
     # timed region: K steps, HIP events around every launch of the dominant kernel
@@ -761,11 +790,24 @@ def main():
                    "aligner": cfg.llm_dim if cfg.aligner else None,
                    "input": "pixels" if args.pixels else "patches"},
         "mfma_frac_step": round(cfg.total_flops() / (ms_per_step / 1e3) / (peak * 1e12), 4),
+        # the block stack alone (norm1 .. down + residual of every block): the step's
+        # time less the patch embedding, the final norm and the aligner, timed with
+        # HIP events in one profiled step before the timed region
+        "mfma_frac_blocks": round(cfg.n_blocks * cfg.block_flops() /
+                                  ((ms_per_step - outside_ms) / 1e3) / (peak * 1e12), 4),
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "avg_launch_us": round(avg_launch_s * 1e6, 3),
                      "launches": dom_n, "flops_per_launch": flops[dominant]},
     }
+    # the dense-MFMA probe: what the chip sustains, beside the published peak
+    measured = api.mfma_peak_tflops(device=dev)
+    result["mfma_peak_measured"] = {
+        "tflops": round(measured, 1), "kernel": "mfma_peak_kernel",
+        "roofline_frac_of_measured": round(achieved / measured, 4),
+        "blocks_frac_of_measured": round(result["mfma_frac_blocks"] * peak / measured, 4),
+        "note": "back-to-back v_mfma_f32_32x32x16_bf16 on register operands, one 8-wave "
+                "workgroup per CU, no memory traffic; best of 5 calls"}
     if args.breakdown:
         bd = {}
         for k in list(flops) + ["rmsnorm", "rope", "gather"]:

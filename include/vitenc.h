@@ -361,6 +361,18 @@ vit_status vit_tower_backward(const vit_config* cfg, const vit_weights* w, const
                               const vit_tower_grads* grads, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* Measured dense bf16 MFMA peak (a measurement aid beside the encoder, used to
+ * report its kernels against the throughput the chip sustains as well as against
+ * the published 2.5 PFLOP/s): one 8-wave workgroup per CU issues `iters` rounds
+ * of 8 back-to-back v_mfma_f32_32x32x16_bf16 on register operands, no memory
+ * traffic in the loop.  *flops (host) receives the call's FLOP count; time the
+ * call with events on `stream`.  out: device float buffer of
+ * vit_mfma_peak_out_floats() elements (receives the accumulator sums, so the
+ * work is not optimised away).  VIT_E_ARG for NULL pointers or iters outside
+ * [1, 2^24]. */
+int64_t vit_mfma_peak_out_floats(void);
+vit_status vit_mfma_peak(int32_t iters, float* out, double* flops, void* stream);
+
 /* Image tokens into the LLM input stream (DeepSeek-V4 model page,
  * DeepseekV4Model.merge_image_embeddings): for each position p of a text
  * embedding stream embeds [positions, hidden] (in place, dtype):

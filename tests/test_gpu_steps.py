@@ -1,5 +1,7 @@
 """GPU tier, per step: every kernel of the path against the oracle on the same
 seeded inputs, through the C ABI.  Sizes span several tiles and ragged tails."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -246,3 +248,16 @@ def test_aligner_gather_bitwise(dtype):
         ref.append(oracle.aligner_gather(x[off:off + gh * gw], gh, gw))
         off += gh * gw
     np.testing.assert_array_equal(got, np.concatenate(ref))
+
+
+@pytest.mark.gpu
+def test_mfma_peak_probe():
+    """The dense-MFMA probe runs and reports a rate below the published bf16 peak
+    (2.5 PFLOP/s at 2.4 GHz) and above a tenth of it; the error paths reject bad
+    arguments before any launch."""
+    tf = api.mfma_peak_tflops(iters=2000, reps=2)
+    print(f"measured dense bf16 MFMA rate {tf:.1f} TFLOP/s")
+    assert 250.0 < tf < 2600.0
+    lib = _lib.load()
+    flops = ctypes.c_double()
+    assert lib.vit_mfma_peak(0, None, ctypes.byref(flops), None) == _lib.VIT_E_ARG

@@ -101,6 +101,8 @@ SIGNATURES = {
                                    c_size, c_vp]),
     "vit_mlp_backward_workspace_bytes": (c_size, [c_i64, c_i32, c_i32]),
     "vit_mlp_backward": (c_i32, [ctypes.POINTER(VitMlpGrad), c_vp, c_size, c_vp]),
+    "vit_mfma_peak_out_floats": (c_i64, []),
+    "vit_mfma_peak": (c_i32, [c_i32, c_vp, ctypes.POINTER(ctypes.c_double), c_vp]),
     "vit_merge_workspace_bytes": (c_size, [c_i64]),
     "vit_merge_image_embeddings": (c_i32, [c_i32, c_vp, c_i64, c_i32, c_vp, c_vp, c_i64, c_vp,
                                            c_vp, c_vp, c_size, c_vp]),

@@ -426,6 +426,27 @@ def tower_backward(patches: torch.Tensor, grids, w: "DeviceWeights", dy: torch.T
     return out
 
 
+def mfma_peak_tflops(iters: int = 20000, reps: int = 5, device="cuda") -> float:
+    """vit_mfma_peak: the best of `reps` timed calls of the dense-MFMA probe, in
+    TFLOP/s (bf16)."""
+    lib = _lib.load()
+    out = torch.empty(lib.vit_mfma_peak_out_floats(), dtype=torch.float32, device=device)
+    flops = ctypes.c_double()
+    st = _stream(out.device)
+    _lib.check(lib.vit_mfma_peak(iters, out.data_ptr(), ctypes.byref(flops), st), "vit_mfma_peak")
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _lib.check(lib.vit_mfma_peak(iters, out.data_ptr(), ctypes.byref(flops), st),
+                   "vit_mfma_peak")
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, flops.value / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return best
+
+
 def merge_workspace_bytes(positions: int) -> int:
     n = _lib.load().vit_merge_workspace_bytes(int(positions))
     if n == 0:

@@ -1220,6 +1220,15 @@ vit_status vit_tower_backward(const vit_config* cfg, const vit_weights* w, const
   return hip_check(launch_gemm_bf16(VIT_EPI_STORE_F32, g, s), "patch embedding gradient");
 }
 
+int64_t vit_mfma_peak_out_floats(void) { return mfma_peak_out_floats(); }
+
+vit_status vit_mfma_peak(int32_t iters, float* out, double* flops, void* stream) {
+  if (!out || !flops) return fail(VIT_E_ARG, "NULL pointer");
+  if (iters <= 0 || iters > (1 << 24)) return fail(VIT_E_ARG, "iters %d out of range", iters);
+  *flops = mfma_peak_flops(iters);
+  return hip_check(launch_mfma_peak(iters, out, (hipStream_t)stream), "mfma peak probe");
+}
+
 vit_status vit_profile_enable(int32_t cls, int32_t on) {
   if (cls < 0 || cls >= VIT_K_COUNT) return fail(VIT_E_ARG, "bad kernel class %d", cls);
   Prof& p = prof();
