@@ -122,6 +122,33 @@ def pmc_summary(fetch_dir, write_dir, kernel, workload, copy_mb, out_path=None):
     print(json.dumps(out))
 
 
+def mfma_util_summary(pmc_dir, out_path):
+    """Per kernel, the median over its dispatches of MFMA busy cycles over the SIMD
+    cycles of the dispatch (SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE
+    / 8 XCDs)), from one rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE."""
+    import statistics
+
+    per = {}
+    for r in _pmc_rows(pmc_dir):
+        key = (r["Kernel_Name"], r.get("Dispatch_Id", ""))
+        per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    util = {}
+    for (name, _), c in per.items():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in c or not c.get("GRBM_GUI_ACTIVE"):
+            continue
+        u = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024.0 * c["GRBM_GUI_ACTIVE"] / 8.0)
+        util.setdefault(name, []).append(u)
+    rows = sorted(util.items(), key=lambda kv: -statistics.median(kv[1]))
+    lines = ["| Kernel | Dispatches | MFMA busy / SIMD cycles (median) |", "|---|---|---|"]
+    for name, v in rows:
+        n = name.replace("void (anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+        lines.append(f"| `{n[:95]}` | {len(v)} | {statistics.median(v):.3f} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(cfg, inp, budget_s=30.0):
     """Time the oracle (as is) on a bounded sample of the workload on host cores."""
     import numpy as np  # noqa: F401
@@ -680,6 +707,8 @@ def main():
     ap.add_argument("--pixels", action="store_true",
                     help="encode stage: pixel images in (the library cuts the patches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the dense-MFMA probe (e.g. under a counter run)")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after the timed steps, run a plain device copy of this many MiB "
@@ -688,8 +717,14 @@ def main():
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script into profiles/traffic_<kernel>_<workload>.json and exit")
     ap.add_argument("--kernel", default="gateup", help="kernel class for --pmc-summary")
+    ap.add_argument("--mfma-summary", nargs=2, metavar=("PMC_DIR", "OUT"),
+                    help="summarise a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE run "
+                         "of this script into a per-kernel MFMA-utilisation table and exit")
     ap.add_argument("--pmc-out", default=None, help="output path for --pmc-summary")
     args = ap.parse_args()
+    if args.mfma_summary:
+        mfma_util_summary(args.mfma_summary[0], args.mfma_summary[1])
+        return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.kernel, args.workload,
                     args.copy_calibration_mb, args.pmc_out)
@@ -801,13 +836,14 @@ def main():
                      "launches": dom_n, "flops_per_launch": flops[dominant]},
     }
     # the dense-MFMA probe: what the chip sustains, beside the published peak
-    measured = api.mfma_peak_tflops(device=dev)
-    result["mfma_peak_measured"] = {
-        "tflops": round(measured, 1), "kernel": "mfma_peak_kernel",
-        "roofline_frac_of_measured": round(achieved / measured, 4),
-        "blocks_frac_of_measured": round(result["mfma_frac_blocks"] * peak / measured, 4),
-        "note": "back-to-back v_mfma_f32_32x32x16_bf16 on register operands, one 8-wave "
-                "workgroup per CU, no memory traffic; best of 5 calls"}
+    measured = None if args.no_mfma_probe else api.mfma_peak_tflops(device=dev)
+    if measured:
+        result["mfma_peak_measured"] = {
+            "tflops": round(measured, 1), "kernel": "mfma_peak_kernel",
+            "roofline_frac_of_measured": round(achieved / measured, 4),
+            "blocks_frac_of_measured": round(result["mfma_frac_blocks"] * peak / measured, 4),
+            "note": "back-to-back v_mfma_f32_32x32x16_bf16 on register operands, one 8-wave "
+                    "workgroup per CU, no memory traffic; best of 5 calls"}
     if args.breakdown:
         bd = {}
         for k in list(flops) + ["rmsnorm", "rope", "gather"]:
