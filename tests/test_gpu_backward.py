@@ -252,8 +252,20 @@ def test_tower_backward_deterministic_and_errors():
         assert lib.vit_tower_backward_workspace_bytes(c, grids, 2) == 0
         w = api.DeviceWeights(cfg, weights)
         assert lib.vit_tower_backward(c, w.c, None, grids, 2, None, None, None, 0, None) == st
+    # a NULL gradient pointer of one block is rejected before any work is enqueued
+    import ctypes
     w = api.DeviceWeights(cfg, weights)
     x = torch.from_numpy(patches).to("cuda", torch.bfloat16)
+    buf = torch.zeros(1 << 22, dtype=torch.float32, device="cuda")
+    ok = (ctypes.c_void_p * 1)(buf.data_ptr())
+    bad = (ctypes.c_void_p * 1)(None)
+    grads = _lib.VitTowerGrads(buf.data_ptr(), ok, bad, ok, ok, ok, ok, ok, buf.data_ptr())
+    ws = torch.empty(api.tower_backward_workspace_bytes(cfg, list(cfg.grids)), dtype=torch.uint8,
+                     device="cuda")
+    dyd = torch.from_numpy(dy).cuda()
+    st = lib.vit_tower_backward(api.c_config(cfg), w.c, x.data_ptr(), grids, 2, dyd.data_ptr(),
+                                grads, ws.data_ptr(), ws.numel(), None)
+    assert st == _lib.VIT_E_ARG
     small = torch.empty(1024, dtype=torch.uint8, device="cuda")
     with pytest.raises(RuntimeError):
         api.tower_backward(x, list(cfg.grids), w, torch.from_numpy(dy).cuda(), ws=small)

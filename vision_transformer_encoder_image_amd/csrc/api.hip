@@ -1152,6 +1152,15 @@ vit_status vit_tower_backward(const vit_config* cfg, const vit_weights* w, const
       if (!q) return fail(VIT_E_ARG, "NULL pointer");
       if (misaligned16(q)) return fail(VIT_E_ARG, "buffers must be 16-byte aligned");
     }
+    // every block's gradient buffers before any work is enqueued
+    for (int b = 0; b < L; ++b) {
+      const void* blk[] = {gr->d_wqkv[b], gr->d_wo[b], gr->d_w_gate[b], gr->d_w_up[b],
+                           gr->d_w_down[b], gr->d_norm1[b], gr->d_norm2[b]};
+      for (const void* q : blk) {
+        if (!q) return fail(VIT_E_ARG, "block %d has a NULL gradient pointer", b);
+        if (misaligned16(q)) return fail(VIT_E_ARG, "block %d: gradients must be 16-byte aligned", b);
+      }
+    }
   }
   if (!ws || ws_bytes < t.total || misaligned16(ws))
     return fail(VIT_E_WORKSPACE, "workspace %zu < %zu (or misaligned)", ws ? ws_bytes : (size_t)0,
