@@ -358,9 +358,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
     constexpr int UROWB = TN * 2;            // bytes per staged u row
     constexpr int UCPR = UROWB / 16, URPL = 256 / UROWB;
     static_assert(TM * UROWB * NW <= STAGES * ROWS * BK * 2, "u staging fits the ring");
+    // x_new is staged too (after every wave's u rows) where the ring has room, so
+    // its fp32 rows also leave as row-contiguous 16-byte stores; otherwise (and
+    // with a row map) it is stored straight from the MFMA layout
+    constexpr int XROWB = TN * 4, XCPR = XROWB / 16;
+    constexpr bool kStageX = TM * (UROWB + XROWB) * NW <= STAGES * ROWS * BK * 2;
     const int n = n0 + wn * TN;
     const bool cols_ok = n < N;
     char* st = (char*)smem + wave * (TM * UROWB);
+    char* xs = (char*)smem + NW * TM * UROWB + wave * (TM * XROWB);
     auto produce = [&](auto with_rowmap, auto with_pre) __attribute__((always_inline)) {
       int64_t orow[BI];
 #pragma unroll
@@ -407,9 +413,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
           for (int j = 0; j < BJ; ++j)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-              if (ok)
+              if constexpr (kStageX && !with_rowmap) {
+                // chunk j*8 + 2*gq + fh of the row's 16, XOR-swizzled by the row
+                const int c16x = j * 8 + 2 * gq + fh;
+                *reinterpret_cast<f32x4*>(xs + r * XROWB + ((c16x ^ (r & 15)) << 4)) = v[ii][j][gq];
+              } else if (ok) {
                 *reinterpret_cast<f32x4*>((float*)g.C + orow[i] * g.ldc + n + j * 32 + 8 * gq + c4) =
                     v[ii][j][gq];
+              }
               bf16x4 u;
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
@@ -433,6 +444,19 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
       produce(std::false_type{}, std::false_type{});
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staged writes done
     asm volatile("" ::: "memory");
+    if (kStageX && !has_rowmap) {
+      constexpr int XRPI = 64 / XCPR;  // staged x rows per read instruction
+      const int xcl = lane % XCPR;
+#pragma unroll 4
+      for (int it = 0; it < TM / XRPI; ++it) {
+        const int R = it * XRPI + lane / XCPR;
+        const int m = m0 + wm * TM + R;
+        const f32x4 xv =
+            *reinterpret_cast<const f32x4*>(xs + R * XROWB + ((xcl ^ (R & 15)) << 4));
+        if (!cols_ok || m >= M) continue;
+        *reinterpret_cast<f32x4*>((float*)g.C + (int64_t)m * g.ldc + n + xcl * 4) = xv;
+      }
+    }
     constexpr int URPI = 64 / UCPR;  // staged rows per read instruction
     const int cl = lane % UCPR;
 #pragma unroll 4
