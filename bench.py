@@ -149,6 +149,36 @@ def mfma_util_summary(pmc_dir, out_path):
     print("\n".join(lines))
 
 
+def timed_then_profiled(fn, steps, roofline_class, classes):
+    """K timed calls with the library's HIP events around the roofline class's
+    launches only (few events: each record costs the GPU a few microseconds), then
+    K more with events on every class of the breakdown; returns (elapsed seconds
+    of the timed calls, {class: (ms, launches)}), the roofline class's figures
+    from the timed calls."""
+    from vision_transformer_encoder_image_amd import api
+    import torch
+
+    api.profile_enable(roofline_class, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per = {roofline_class: api.profile_read(roofline_class)}
+    api.profile_enable(roofline_class, False)
+    others = [k for k in classes if k != roofline_class]
+    for k in others:
+        api.profile_enable(k, True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    for k in others:
+        per[k] = api.profile_read(k)
+        api.profile_enable(k, False)
+    return elapsed, per
+
+
 def cpu_baseline(cfg, inp, budget_s=30.0):
     """Time the oracle (as is) on a bounded sample of the workload on host cores."""
     import numpy as np  # noqa: F401
@@ -427,19 +457,8 @@ def bench_mlp_backward(args):
     for _ in range(max(args.warmup, 1)):
         api.mlp_backward(x, w, wg, wu, wd, dy, ws=ws)
     torch.cuda.synchronize()
-    for k in ("bwd_gemm", "bwd_dn", "bwd_pass"):
-        api.profile_enable(k, True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        api.mlp_backward(x, w, wg, wu, wd, dy, ws=ws)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    per = {}
-    for k in ("bwd_gemm", "bwd_dn", "bwd_pass"):
-        ms, n = api.profile_read(k)
-        api.profile_enable(k, False)
-        per[k] = (ms, n)
+    elapsed, per = timed_then_profiled(lambda: api.mlp_backward(x, w, wg, wu, wd, dy, ws=ws),
+                                       args.steps, "bwd_dn", ("bwd_gemm", "bwd_dn", "bwd_pass"))
     dn_us = per["bwd_dn"][0] * 1e3 / max(per["bwd_dn"][1], 1)
     peak = PEAK_TFLOPS["bf16"]
     achieved = flops["dn"] / (dn_us * 1e-6) / 1e12
@@ -518,19 +537,8 @@ def bench_attn_backward(args):
     for _ in range(max(args.warmup, 1)):
         api.attn_backward(x, w, wqkv, wo, dy, grids, H)
     torch.cuda.synchronize()
-    for k in ("bwd_attn", "bwd_gemm"):
-        api.profile_enable(k, True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        api.attn_backward(x, w, wqkv, wo, dy, grids, H)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    per = {}
-    for k in ("bwd_attn", "bwd_gemm"):
-        ms, n = api.profile_read(k)
-        api.profile_enable(k, False)
-        per[k] = (ms, n)
+    elapsed, per = timed_then_profiled(lambda: api.attn_backward(x, w, wqkv, wo, dy, grids, H),
+                                       args.steps, "bwd_attn", ("bwd_attn", "bwd_gemm"))
     attn_us = per["bwd_attn"][0] * 1e3 / max(per["bwd_attn"][1], 1)
     peak = PEAK_TFLOPS["bf16"]
     achieved = flops["attn"] / (attn_us * 1e-6) / 1e12
@@ -627,18 +635,8 @@ def bench_tower_backward(args):
         api.tower_backward(x, grids, w, dy, ws=ws)
     torch.cuda.synchronize()
     classes = ("bwd_gemm", "bwd_attn", "bwd_pass")
-    for k in classes:
-        api.profile_enable(k, True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        api.tower_backward(x, grids, w, dy, ws=ws)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    per = {}
-    for k in classes:
-        per[k] = api.profile_read(k)
-        api.profile_enable(k, False)
+    elapsed, per = timed_then_profiled(lambda: api.tower_backward(x, grids, w, dy, ws=ws),
+                                       args.steps, "bwd_gemm", classes)
     gemm_us = per["bwd_gemm"][0] * 1e3 / args.steps
     peak = PEAK_TFLOPS["bf16"]
     achieved = gemm_exec / (gemm_us * 1e-6) / 1e12

@@ -60,9 +60,12 @@ struct ProfScope {
     std::lock_guard<std::mutex> lk(p.mu);
     if (cls < 0 || cls >= VIT_K_COUNT || !p.on[cls]) return;  // -1: not timed
     if (p.used[cls] == p.ev[cls].size()) {
+      // timing events without the system-scope release/acquire fence an
+      // ordinary event adds around its timestamp (which writes back the caches
+      // at every record and would slow the timed work down)
       hipEvent_t a, b;
-      if (hipEventCreate(&a) != hipSuccess) return;
-      if (hipEventCreate(&b) != hipSuccess) {
+      if (hipEventCreateWithFlags(&a, hipEventDisableSystemFence) != hipSuccess) return;
+      if (hipEventCreateWithFlags(&b, hipEventDisableSystemFence) != hipSuccess) {
         (void)hipEventDestroy(a);
         return;
       }
@@ -483,7 +486,7 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
 // Backward of the MLP half: workspace layout
 struct MlpGradPlan {
   int64_t Pp = 0;  // rows rounded up to 64 (K of the weight-gradient GEMMs)
-  size_t n = 0, dy16 = 0, gu = 0, da = 0, dgdu = 0, dn = 0, wdT = 0, wguT = 0;
+  size_t n = 0, dy16 = 0, gu = 0, da = 0, a = 0, dgdu = 0, dn = 0, wdT = 0, wguT = 0;
   size_t dyT = 0, aT = 0, dgduT = 0, nT = 0, partial = 0, total = 0;
 };
 
@@ -500,6 +503,7 @@ MlpGradPlan mlp_grad_plan(int64_t P, int64_t d, int64_t h) {
   p.dy16 = take(P * d * 2);
   p.gu = take(P * 2 * h * 4);
   p.da = take(P * h * 4);
+  p.a = take(P * h * 2);
   p.dgdu = take(P * 2 * h * 2);
   p.dn = take(P * d * 4);
   p.wdT = take(h * d * 2);
@@ -949,6 +953,7 @@ vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, vo
   bf16* dy16 = (bf16*)(base + p.dy16);
   float* gu = (float*)(base + p.gu);
   float* da = (float*)(base + p.da);
+  bf16* act = (bf16*)(base + p.a);
   bf16* dgdu = (bf16*)(base + p.dgdu);
   float* dn = (float*)(base + p.dn);
   bf16* wdT = (bf16*)(base + p.wdT);
@@ -986,11 +991,10 @@ vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, vo
     VIT_HIP(launch_transpose_bf16(a->w_down, d, h, h, wdT, d, d, s), "transpose W_down");
   }
   VIT_TRY(mm(dy16, d, wdT, d, da, h, P, h, d));
-  // SwiGLU gradient: dg, du row-major, and a, dg, du transposed for the
-  // weight gradients (zero past row P)
+  // SwiGLU gradient (and the activation for dW_down)
   {
     ProfScope ps(VIT_K_BWD_PASS, s);
-    VIT_HIP(launch_swiglu_bwd_t(gu, da, P, (int)h, p.Pp, dgdu, aT, dgduT, s), "swiglu backward");
+    VIT_HIP(launch_swiglu_bwd(gu, da, P, (int)h, act, dgdu, s), "swiglu backward");
   }
   // dn = dg . W_gate + du . W_up
   {
@@ -1010,6 +1014,14 @@ vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, vo
             "norm backward");
   }
   // weight gradients: contractions over the rows (zero-padded to Pp)
+  {
+    ProfScope ps(VIT_K_BWD_PASS, s);
+    VIT_HIP(launch_transpose_bf16(act, P, h, h, aT, p.Pp, p.Pp, s), "transpose a");
+  }
+  {
+    ProfScope ps(VIT_K_BWD_PASS, s);
+    VIT_HIP(launch_transpose_bf16(dgdu, P, 2 * h, 2 * h, dgduT, p.Pp, p.Pp, s), "transpose dg, du");
+  }
   {
     ProfScope ps(VIT_K_BWD_PASS, s);
     VIT_HIP(launch_transpose_bf16(n, P, d, d, nT, p.Pp, p.Pp, s), "transpose n");

@@ -91,58 +91,32 @@ __global__ __launch_bounds__(kThreads) void transpose_bf16_kernel(
 }
 
 // SwiGLU gradient: g, u = gu[:, :h], gu[:, h:] (fp32), da (fp32, [rows, h]) ->
-// a = silu(g) u, dg = da u (s + g s (1 - s)), du = da g s (bf16), s = sigmoid(g),
-// over 64-row x 64-column tiles, writing dg, du
-// row-major (the A operand of dn = [dg|du] [Wg;Wu]) and a, dg, du transposed
-// through LDS (the operands of the weight gradients, rows zero-padded to
-// ld_t): aT [h, ld_t], dgduT [2h, ld_t] (dg^T rows then du^T rows).  This
-// replaces the row-major a and two transpose passes.
-__global__ __launch_bounds__(kThreads) void swiglu_bwd_t_kernel(
-    const float* __restrict__ gu, const float* __restrict__ da, int64_t rows, int h,
-    int64_t ld_t, bf16* __restrict__ dgdu, bf16* __restrict__ aT, bf16* __restrict__ dgduT) {
-  __shared__ bf16 t[3][64][64 + 8];  // a, dg, du: [column][row]
-  const int64_t r0 = (int64_t)blockIdx.y * 64;
-  const int c0 = blockIdx.x * 64;
+// a = silu(g) u (bf16, [rows, h]), dg = da u (s + g s (1 - s)), du = da g s
+// (bf16, side by side in dgdu [rows, 2h]); s = sigmoid(g)
+__global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(const float* __restrict__ gu,
+                                                              const float* __restrict__ da,
+                                                              int64_t rows, int h,
+                                                              bf16* __restrict__ a,
+                                                              bf16* __restrict__ dgdu) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // group of 4 columns
+  const int h4 = h / 4;
+  if (i >= rows * h4) return;
+  const int64_t r = i / h4;
+  const int c = (int)(i % h4) * 4;
+  const f32x4 g = *reinterpret_cast<const f32x4*>(gu + r * 2 * h + c);
+  const f32x4 u = *reinterpret_cast<const f32x4*>(gu + r * 2 * h + h + c);
+  const f32x4 d = *reinterpret_cast<const f32x4*>(da + r * h + c);
+  bf16x4 av, dgv, duv;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int q = it * kThreads + threadIdx.x;
-    const int rr = q >> 4, cc = (q & 15) * 4;  // row in the tile, first of 4 columns
-    const int64_t r = r0 + rr;
-    f32x4 g = f32x4{}, u = f32x4{}, d = f32x4{};
-    if (r < rows) {
-      g = *reinterpret_cast<const f32x4*>(gu + r * 2 * h + c0 + cc);
-      u = *reinterpret_cast<const f32x4*>(gu + r * 2 * h + h + c0 + cc);
-      d = *reinterpret_cast<const f32x4*>(da + r * h + c0 + cc);
-    }
-    bf16x4 dgv, duv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float sg = 1.0f / (1.0f + __expf(-g[e]));
-      const bf16 av = f2bf(g[e] * sg * u[e]);
-      dgv[e] = f2bf(d[e] * u[e] * (sg + g[e] * sg * (1.0f - sg)));
-      duv[e] = f2bf(d[e] * g[e] * sg);
-      t[0][cc + e][rr] = av;
-      t[1][cc + e][rr] = dgv[e];
-      t[2][cc + e][rr] = duv[e];
-    }
-    if (r < rows) {
-      *reinterpret_cast<bf16x4*>(dgdu + r * 2 * h + c0 + cc) = dgv;
-      *reinterpret_cast<bf16x4*>(dgdu + r * 2 * h + h + c0 + cc) = duv;
-    }
+  for (int e = 0; e < 4; ++e) {
+    const float s = 1.0f / (1.0f + __expf(-g[e]));
+    av[e] = f2bf(g[e] * s * u[e]);
+    dgv[e] = f2bf(d[e] * u[e] * (s + g[e] * s * (1.0f - s)));
+    duv[e] = f2bf(d[e] * g[e] * s);
   }
-  __syncthreads();
-  // 3 outputs x 64 columns x 8 chunks of 8 rows: 6 chunks per thread
-#pragma unroll
-  for (int it = 0; it < 6; ++it) {
-    const int q = it * kThreads + threadIdx.x;
-    const int o = q >> 9, cc = (q >> 3) & 63, ch = q & 7;
-    bf16x8 v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = t[o][cc][ch * 8 + e];
-    bf16* dst = o == 0 ? aT + (int64_t)(c0 + cc) * ld_t
-                       : dgduT + ((int64_t)(o - 1) * h + c0 + cc) * ld_t;
-    st16(dst + r0 + ch * 8, __builtin_bit_cast(u32x4, v));
-  }
+  *reinterpret_cast<bf16x4*>(a + r * h + c) = av;
+  *reinterpret_cast<bf16x4*>(dgdu + r * 2 * h + c) = dgv;
+  *reinterpret_cast<bf16x4*>(dgdu + r * 2 * h + h + c) = duv;
 }
 
 // RMSNorm gradient plus the residual: per row, r = (mean(x^2) + eps)^-1/2,
@@ -293,14 +267,12 @@ hipError_t launch_cast_transpose(const float* src, int64_t R, int64_t C, void* c
   return hipGetLastError();
 }
 
-
-hipError_t launch_swiglu_bwd_t(const float* gu, const float* da, int64_t rows, int h, int64_t ld_t,
-                               void* dgdu, void* aT, void* dgduT, hipStream_t s) {
-  if (h % 64 || ld_t % 64 || ld_t < rows) return hipErrorInvalidValue;
+hipError_t launch_swiglu_bwd(const float* gu, const float* da, int64_t rows, int h, void* a,
+                             void* dgdu, hipStream_t s) {
+  if (h % 4) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)(h / 64), (unsigned)(ld_t / 64));
-  swiglu_bwd_t_kernel<<<grid, kThreads, 0, s>>>(gu, da, rows, h, ld_t, (bf16*)dgdu, (bf16*)aT,
-                                                (bf16*)dgduT);
+  swiglu_bwd_kernel<<<blocks_of(rows * (h / 4)), kThreads, 0, s>>>(gu, da, rows, h, (bf16*)a,
+                                                                   (bf16*)dgdu);
   return hipGetLastError();
 }
 

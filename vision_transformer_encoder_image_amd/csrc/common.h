@@ -254,15 +254,12 @@ hipError_t launch_transpose_bf16(const void* src, int64_t R, int64_t C, int64_t 
 // R .. cols_out-1 zero) in one pass; C % 8 == 0
 hipError_t launch_cast_transpose(const float* src, int64_t R, int64_t C, void* copy, void* dst,
                                  int64_t cols_out, int64_t ld_dst, hipStream_t s);
-// SwiGLU gradient over 64x64 tiles: dgdu row-major plus a^T [h, ld_t] and
-// [dg|du]^T [2h, ld_t] (rows past `rows` zero); h and ld_t multiples of 64
 // measured dense-MFMA peak (microbench.hip)
 int64_t mfma_peak_out_floats();
 double mfma_peak_flops(int iters);
 hipError_t launch_mfma_peak(int iters, float* out, hipStream_t s);
-hipError_t launch_swiglu_bwd_t(const float* gu, const float* da, int64_t rows, int h, int64_t ld_t,
-                               void* dgdu, void* aT, void* dgduT, hipStream_t s);
-
+hipError_t launch_swiglu_bwd(const float* gu, const float* da, int64_t rows, int h, void* a,
+                             void* dgdu, hipStream_t s);
 int rmsnorm_bwd_blocks(int64_t rows);
 hipError_t launch_rmsnorm_bwd(const float* x, const float* w, const float* dn, const float* dy,
                               int64_t rows, int d, float eps, float* dx, float* partial,
