@@ -176,6 +176,16 @@ def test_tower_backward_workspace_host_checks(lib):
     assert need - one >= 6 * P * d * 4
 
 
+def test_mfma_probe_host_checks(lib):
+    """vit_mfma_peak rejects NULL pointers and bad iteration counts on the host,
+    before any launch; its output buffer size is a fixed, positive count."""
+    flops = ctypes.c_double()
+    assert lib.vit_mfma_peak(100, None, ctypes.byref(flops), None) == _lib.VIT_E_ARG
+    assert lib.vit_mfma_peak(0, ctypes.c_void_p(16), ctypes.byref(flops), None) == _lib.VIT_E_ARG
+    assert lib.vit_mfma_peak(1 << 25, ctypes.c_void_p(16), ctypes.byref(flops), None) == _lib.VIT_E_ARG
+    assert lib.vit_mfma_peak_out_floats() == 256 * 512
+
+
 def test_configs_flops_match_hand_count():
     c = configs.get(2)
     assert c.total_patches == 3562  # 999 + 999 + 780 + 784
