@@ -204,11 +204,12 @@ def _tower_check(cfg, got, patches, weights, dy, tag):
 
 
 @pytest.mark.parametrize("grids,n_blocks", [([(4, 6), (3, 5), (8, 8)], 2),
-                                            ([(9, 7), (2, 40)], 1), ([(5, 13)], 0)])
+                                            ([(9, 7), (2, 40)], 1), ([(5, 13)], 0),
+                                            ([(1, 1), (2, 3), (1, 70)], 1)])
 def test_tower_backward_small_matches_oracle(grids, n_blocks):
-    """Ragged grids (one 64-row tile and a ragged tail), 2 heads of 64, hidden 192,
-    14x14 -> 4x4 patches (patch_dim 48); zero blocks leaves the final norm and the
-    patch embedding."""
+    """Ragged grids (one 64-row tile and a ragged tail; a single-patch image; a 1x70
+    strip), 2 heads of 64, hidden 192, 14x14 -> 4x4 patches (patch_dim 48); zero
+    blocks leaves the final norm and the patch embedding."""
     cfg, patches, weights, dy = _tower_case(grids, 128, 2, 192, n_blocks, seed=150 + n_blocks)
     got = _tower_run(cfg, patches, weights, dy)
     _tower_check(cfg, got, patches, weights, dy, f"{grids} x{n_blocks}")
