@@ -149,49 +149,67 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
           s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ds], s[kb][qb], 0, 0, 0);
       }
 
+    // online softmax in base 2 with the scale folded into one FMA per score;
+    // keys past the image only in the image's last tile; the reference max
+    // (mrow, scaled) is raised only when some lane's max grows by more than 2^8,
+    // so most tiles skip the rescale of o and of the sum (p then stays <= 2^8)
+    if (kv0 + BKV > seq1) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kv0 + kb * 16 + fk * 4 + i >= seq1) s[kb][qb][i] = -INFINITY;
+    }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kv0 + kb * 16 + fk * 4 + i;
-          const float v = key < seq1 ? s[kb][qb][i] * scale_log2 : -INFINITY;
-          s[kb][qb][i] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrow[qb], mx);
-      const float alpha = exp2f(mrow[qb] - mnew);
-      mrow[qb] = mnew;
-      float ls = lsum[qb] * alpha;
+      const float mxs = mx * scale_log2;
+      if (__any(mxs - mrow[qb] > 8.0f)) {
+        const float mnew = fmaxf(mrow[qb], mxs);
+        const float alpha = __builtin_amdgcn_exp2f(mrow[qb] - mnew);
+        mrow[qb] = mnew;
+        lsum[qb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[db][qb][i] *= alpha;
+          for (int i = 0; i < 4; ++i) o[db][qb][i] *= alpha;
+      }
+      const float nm = -mrow[qb];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(s[kb][qb][i] - mnew);
-          ls += p;
-          s[kb][qb][i] = p;
-        }
-      lsum[qb] = ls;
+        for (int i = 0; i < 4; ++i)
+          s[kb][qb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][i], scale_log2, nm));
     }
 
 #pragma unroll
     for (int ks = 0; ks < BKV / 32; ++ks) {
       bf16x8 pf[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           pf[qb][i] = f2bf(s[2 * ks][qb][i]);
           pf[qb][4 + i] = f2bf(s[2 * ks + 1][qb][i]);
         }
+        // the sum adds the bf16 probabilities the P.V MFMAs use, two per dot2
+        const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+        const bf16x8 q8 = pf[qb];
+        float t = lsum[qb];
+        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q8, q8, 0, 1), one2, t, false);
+        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q8, q8, 2, 3), one2, t, false);
+        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q8, q8, 4, 5), one2, t, false);
+        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q8, q8, 6, 7), one2, t, false);
+        lsum[qb] = t;
+      }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const bf16* vr = &sVt[(db * 16 + fr) * VS + ks * 32 + fk * 4];
