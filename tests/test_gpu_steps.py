@@ -163,6 +163,32 @@ def test_rope_apply(grids, dtype, D):
         off += gh * gw
 
 
+@pytest.mark.parametrize("D,offset", [(68, 0), (64, 1), (72, 1)])
+def test_rope_apply_narrow_vectors(D, offset):
+    # D/4 odd (68) or a buffer that starts one bf16 element past an aligned address:
+    # the rotary then moves its operands 1 element at a time instead of 2 or 4.
+    grids, H = [(27, 37), (10, 78)], 3
+    d = H * D
+    P = sum(a * b for a, b in grids)
+    qkv = synth.random_array((P, 3 * d), 12, bf16=True)
+    buf = torch.zeros(P * 3 * d + 8, dtype=torch.bfloat16, device="cuda")
+    view = buf[offset:offset + P * 3 * d].view(P, 3 * d)
+    view.copy_(_dev(qkv, "bf16"))
+    got = to_np(api.rope_(view, api.rope_table(grids, D), H, D))
+    off = 0
+    for gh, gw in grids:
+        cos, sin = oracle.rope_table(gh, gw, D)
+        sl = slice(off, off + gh * gw)
+        for part in range(2):
+            x = qkv[sl, part * d:(part + 1) * d].reshape(-1, H, D)
+            ref = oracle.apply_rope(x, cos, sin).reshape(-1, d)
+            assert rowwise_rel_err(got[sl, part * d:(part + 1) * d], ref) < 8e-3, part
+        np.testing.assert_array_equal(got[sl, 2 * d:], qkv[sl, 2 * d:])
+        off += gh * gw
+    # nothing outside the view was written
+    assert not buf[:offset].any() and not buf[offset + P * 3 * d:].any()
+
+
 def test_rope_preserves_pair_norms_on_gpu():
     grids, D, H = [(40, 30)], 64, 2
     d = H * D

@@ -70,28 +70,43 @@ __global__ void rope_table_kernel(VarlenDesc d, int head_dim, RopeFreqs fr, floa
 
 // ---------------------------------------------------------------------------
 // Half-split 2D rotary (vision page, apply_vision_rotary) on the q and k parts of
-// a packed [P, 3*H*D] qkv buffer, in place, fp32 math.  One thread per rotated
-// pair (i, i + D/4) inside one half of one head.
-template <typename T>
+// a packed [P, 3*H*D] qkv buffer, in place, fp32 math.  One thread per V
+// consecutive rotated pairs (i, i + D/4) inside one half of one head, so the
+// two operands and the V table entries move as V-wide vectors (the host picks
+// the widest V that divides D/4 and the pointers' alignment).
+template <typename T, int V>
+struct alignas(sizeof(T) * V) RopeVec {
+  T v[V];
+};
+
+template <typename T, int V>
 __global__ void rope_kernel(T* qkv, const float2* __restrict__ table, int64_t P, int H, int D) {
-  const int q4 = D / 4;
-  const int d = H * D;
+  const int q4 = D / 4, qv = q4 / V;
+  const int per_row = 4 * H * qv;  // 2 parts * H heads * 2 halves * D/(4V)
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= P * d) return;  // d pairs per row: 2 parts * H heads * 2 halves * D/4
-  const int64_t p = idx / d;
-  int j = (int)(idx % d);
-  const int kk = j % q4;
-  j /= q4;
+  if (idx >= P * per_row) return;
+  const int64_t p = idx / per_row;
+  int j = (int)(idx % per_row);
+  const int kk = (j % qv) * V;
+  j /= qv;
   const int half = j & 1;
   j >>= 1;
   const int h = j % H;
   const int part = j / H;  // 0 = q, 1 = k
+  const int d = H * D;
   T* row = qkv + p * (3 * (int64_t)d) + part * d + h * D + half * (D / 2);
-  const float2 cs = table[p * (D / 2) + half * q4 + kk];
-  const float a1 = to_f32(row[kk]);
-  const float a2 = to_f32(row[kk + q4]);
-  row[kk] = from_f32<T>(a1 * cs.x - a2 * cs.y);
-  row[kk + q4] = from_f32<T>(a2 * cs.x + a1 * cs.y);
+  const float2* cs = table + p * (D / 2) + half * q4 + kk;
+  RopeVec<T, V> x1 = *reinterpret_cast<const RopeVec<T, V>*>(row + kk);
+  RopeVec<T, V> x2 = *reinterpret_cast<const RopeVec<T, V>*>(row + kk + q4);
+  RopeVec<float2, V> c = *reinterpret_cast<const RopeVec<float2, V>*>(cs);
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    const float a1 = to_f32(x1.v[e]), a2 = to_f32(x2.v[e]);
+    x1.v[e] = from_f32<T>(a1 * c.v[e].x - a2 * c.v[e].y);
+    x2.v[e] = from_f32<T>(a2 * c.v[e].x + a1 * c.v[e].y);
+  }
+  *reinterpret_cast<RopeVec<T, V>*>(row + kk) = x1;
+  *reinterpret_cast<RopeVec<T, V>*>(row + kk + q4) = x2;
 }
 
 // ---------------------------------------------------------------------------
@@ -409,17 +424,29 @@ hipError_t launch_rope_table(const VarlenDesc& d, int head_dim, float theta, voi
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_rope_t(T* qkv, const float2* table, int64_t P, int H, int D, hipStream_t s) {
+  const int q4 = D / 4;
+  auto fits = [&](int v) {
+    return q4 % v == 0 && (uintptr_t)qkv % (v * sizeof(T)) == 0 &&
+           (uintptr_t)table % (v * sizeof(float2)) == 0;
+  };
+  const int64_t pairs = P * H * D;  // 2 parts * 2 halves * D/4 pairs per head
+  if (fits(4))
+    rope_kernel<T, 4><<<blocks_for(pairs / 4), kThreads, 0, s>>>(qkv, table, P, H, D);
+  else if (fits(2))
+    rope_kernel<T, 2><<<blocks_for(pairs / 2), kThreads, 0, s>>>(qkv, table, P, H, D);
+  else
+    rope_kernel<T, 1><<<blocks_for(pairs), kThreads, 0, s>>>(qkv, table, P, H, D);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope(int dtype, void* qkv, const void* table, int64_t P, int n_heads,
                        int head_dim, hipStream_t s) {
-  const int64_t n = P * n_heads * head_dim;
-  if (n == 0) return hipSuccess;
+  if (P * n_heads * head_dim == 0) return hipSuccess;
   if (dtype == VIT_BF16)
-    rope_kernel<bf16><<<blocks_for(n), kThreads, 0, s>>>((bf16*)qkv, (const float2*)table, P,
-                                                         n_heads, head_dim);
-  else
-    rope_kernel<float><<<blocks_for(n), kThreads, 0, s>>>((float*)qkv, (const float2*)table, P,
-                                                          n_heads, head_dim);
-  return hipGetLastError();
+    return launch_rope_t((bf16*)qkv, (const float2*)table, P, n_heads, head_dim, s);
+  return launch_rope_t((float*)qkv, (const float2*)table, P, n_heads, head_dim, s);
 }
 
 hipError_t launch_gather(int dtype, const void* x, const VarlenDesc& d, int dim, int merge,
