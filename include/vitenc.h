@@ -187,8 +187,8 @@ vit_status vit_rope(int32_t dtype, void* qkv, const void* table, int64_t P, int3
 /* Full bidirectional attention per image and head (DeepseekV4VisionAttention):
  * out[p, h*D:(h+1)*D] = softmax(q k^T / sqrt(D)) v over the patches of p's image.
  * qkv [P, 3*n_heads*D] (rows [q|k|v], rotary already applied), out [P, n_heads*D].
- * bf16 with head_dim 64 first packs V transposed per head into ws (size from
- * vit_attention_workspace_bytes; other cases need none and accept NULL). */
+ * bf16 first packs V transposed per head into ws (size from
+ * vit_attention_workspace_bytes); fp32 needs none and accepts NULL. */
 size_t vit_attention_workspace_bytes(int32_t dtype, const int32_t* grid_hw_host,
                                      int32_t n_images, int32_t n_heads, int32_t head_dim);
 vit_status vit_attention_varlen(int32_t dtype, const void* qkv, const int32_t* grid_hw_host,

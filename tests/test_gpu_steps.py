@@ -235,16 +235,18 @@ def test_attention_varlen(grids, dtype, D):
     assert err < (1e-5 if dtype == "f32" else 1e-2), err
 
 
-def test_attention_single_patch_returns_v():
-    H, D = 2, 64
+@pytest.mark.parametrize("D", [64, 72])
+def test_attention_single_patch_returns_v(D):
+    H = 2
     qkv = synth.random_array((1, 3 * H * D), 13, bf16=True)
     got = to_np(api.attention_varlen(_dev(qkv, "bf16"), [(1, 1)], H, D))
     np.testing.assert_array_equal(got[0], qkv[0, 2 * H * D:])
 
 
-def test_attention_large_logits_stay_finite():
+@pytest.mark.parametrize("D", [64, 72])
+def test_attention_large_logits_stay_finite(D):
     """Scaled-up q/k (logits ~ +-100) exercise the running max of the online softmax."""
-    H, D, grids = 2, 64, [(20, 20)]
+    H, grids = 2, [(20, 20)]
     qkv = synth.random_array((400, 3 * H * D), 14, std=4.0, bf16=True)
     got = to_np(api.attention_varlen(_dev(qkv, "bf16"), grids, H, D))
     assert np.isfinite(got).all()

@@ -151,6 +151,7 @@ struct Plan {
   size_t vt = 0, vpos = 0, u = 0, ss = 0;
   int64_t kv_total = 0;
   bool use_vt = false;  // bf16, head_dim 64: V written transposed by the wqkv GEMM
+  bool pack_vt = false;  // bf16, head_dim 72: V transposed by a pack pass after the rotary
   bool fuse_norm = false;  // bf16, vision_dim % 64 == 0: RMSNorm folded into the GEMMs
   size_t total = 0;
 };
@@ -187,11 +188,12 @@ Plan make_plan(const vit_config& c, const VarlenDesc& desc, int flags) {
   p.qkv = take((size_t)P * 3 * d * es);
   p.act = take((size_t)P * p.hp * es);
   p.use_vt = c.dtype == VIT_BF16 && c.head_dim == 64;
-  if (p.use_vt) {
+  p.pack_vt = c.dtype == VIT_BF16 && c.head_dim == 72;
+  if (p.use_vt || p.pack_vt) {
     p.kv_total = desc.kv_off[desc.n_images];
     p.vt = take((size_t)d * p.kv_total * es);
-    p.vpos = take((size_t)P * sizeof(int32_t));
   }
+  if (p.use_vt) p.vpos = take((size_t)P * sizeof(int32_t));
   p.fuse_norm = c.dtype == VIT_BF16 && d % 64 == 0 && d / 64 <= kMaxNormGroups && c.n_blocks > 0;
   if (p.fuse_norm) {
     p.u = take((size_t)P * d * es);                     // bf16(x * norm weight)
@@ -324,7 +326,7 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
     for (const GemmArgs& g : chk) fuse = fuse && gemm_bf16_mfma_eligible(g);
   }
 
-  void* vt = p.use_vt ? base + p.vt : nullptr;
+  void* vt = (p.use_vt || p.pack_vt) ? base + p.vt : nullptr;
   int32_t* vpos = p.use_vt ? (int32_t*)(base + p.vpos) : nullptr;
   // patch embedding: x (fp32 residual stream) = patches . Wpe^T
   {
@@ -411,14 +413,18 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
     if (!fuse_rope) {
       ProfScope ps(VIT_K_ROPE, s);
       VIT_HIP(launch_rope(dt, qkv, table, P, c.n_heads, c.head_dim, s), "rope");
+      if (vt)
+        VIT_HIP(launch_vt_pack(qkv, desc, c.n_heads, c.head_dim, vt, p.kv_total, s), "pack V");
     }
     {
       ProfScope ps(VIT_K_ATTN, s);
-      if (fuse_rope)
-        VIT_HIP(launch_attention_vt(qkv, 2 * d, vt, p.kv_total, desc, c.n_heads, n, s),
+      if (p.use_vt)  // q, k rows of stride 2d after the fused epilogue, else 3d
+        VIT_HIP(launch_attention_vt(qkv, fuse_rope ? 2 * d : 3 * d, vt, p.kv_total, desc,
+                                    c.n_heads, n, s),
                 "attention");
       else
-        VIT_HIP(launch_attention(dt, qkv, desc, c.n_heads, c.head_dim, n, s), "attention");
+        VIT_HIP(launch_attention(dt, qkv, vt, p.kv_total, desc, c.n_heads, c.head_dim, n, s),
+                "attention");
     }
     {
       ProfScope ps(VIT_K_OUTPROJ, s);
@@ -760,7 +766,7 @@ vit_status vit_rope(int32_t dtype, void* qkv, const void* table, int64_t P, int3
 
 size_t vit_attention_workspace_bytes(int32_t dtype, const int32_t* grid_hw_host,
                                      int32_t n_images, int32_t n_heads, int32_t head_dim) {
-  if (dtype != VIT_BF16 || head_dim != 64) return 0;
+  if (dtype != VIT_BF16 || (head_dim != 64 && head_dim != 72)) return 0;
   VarlenDesc d;
   if (build_desc(grid_hw_host, n_images, attention_q_tile(dtype, head_dim), false, 2, &d) != VIT_OK)
     return 0;
@@ -777,16 +783,21 @@ vit_status vit_attention_varlen(int32_t dtype, const void* qkv, const int32_t* g
   VarlenDesc d;
   VIT_TRY(build_desc(grid_hw_host, n_images, attention_q_tile(dtype, head_dim), false, 2, &d));
   hipStream_t s = (hipStream_t)stream;
-  if (dtype == VIT_BF16 && head_dim == 64) {
+  if (dtype == VIT_BF16) {
     const size_t need = (size_t)n_heads * head_dim * d.kv_off[n_images] * 2;
     if (!ws || ws_bytes < need)
       return fail(VIT_E_WORKSPACE, "attention workspace %zu < %zu", ws ? ws_bytes : (size_t)0, need);
     VIT_HIP(launch_vt_pack(qkv, d, n_heads, head_dim, ws, d.kv_off[n_images], s), "pack V");
-    return hip_check(launch_attention_vt(qkv, 3 * (int64_t)n_heads * head_dim, ws,
-                                         d.kv_off[n_images], d, n_heads, out, s),
+    if (head_dim == 64)
+      return hip_check(launch_attention_vt(qkv, 3 * (int64_t)n_heads * head_dim, ws,
+                                           d.kv_off[n_images], d, n_heads, out, s),
+                       "attention");
+    return hip_check(launch_attention(dtype, qkv, ws, d.kv_off[n_images], d, n_heads, head_dim,
+                                      out, s),
                      "attention");
   }
-  return hip_check(launch_attention(dtype, qkv, d, n_heads, head_dim, out, s), "attention");
+  return hip_check(launch_attention(dtype, qkv, nullptr, 0, d, n_heads, head_dim, out, s),
+                   "attention");
 }
 
 vit_status vit_gemm(int32_t dtype, int32_t epilogue, const void* A, int64_t lda, const void* B,

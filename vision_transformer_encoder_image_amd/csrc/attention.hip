@@ -4,8 +4,11 @@
 // batch is block-diagonal).  Flash-style single pass with an online softmax, so
 // the P_i x P_i score matrix never leaves registers.
 //
-// bf16 kernel (gfx950 MFMA).  One workgroup = 128 queries of one (image, head),
-// 4 waves x 32 queries.  Per 64-key tile:
+// head_dim 72 bf16 kernel (gfx950 MFMA; head_dim 64 takes attn_vt_kernel below).
+// One workgroup = 128 queries of one (image, head), 4 waves x 32 queries.  V
+// comes transposed per head, [H*72, kv_total] with images at 64-aligned
+// columns, keys ordered inside each 64-key tile by vt16_slot_key and zero past
+// the image (a pack pass before the kernel).  Per 64-key tile:
 //   S^T = K . Q^T  on v_mfma_f32_16x16x32_bf16 with K from LDS (A operand, rows =
 //        keys) and Q held in registers for the whole kernel (B operand, columns =
 //        queries).  Transposing S puts one query per lane column, so the row max
@@ -14,7 +17,8 @@
 //        end.
 //   O^T += V^T . P^T  with P^T taken straight from the S^T accumulators (the
 //        MFMA k-slots are permuted identically in both operands, so no shuffle
-//        is needed) and V^T read from an LDS tile stored key-contiguous.
+//        is needed) and V^T read from its LDS tile, one 16-byte read per
+//        fragment.
 // Softmax in base 2 with the 1/sqrt(D) scale folded into log2(e); fp32 state.
 // The next K/V tile is prefetched into registers during the current one.
 //
@@ -36,8 +40,9 @@ constexpr int kThreads = 256;
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __restrict__ qkv,
-                                                                VarlenDesc desc, int H,
-                                                                bf16* __restrict__ out,
+                                                                const bf16* __restrict__ vt,
+                                                                int64_t vt_ld, VarlenDesc desc,
+                                                                int H, bf16* __restrict__ out,
                                                                 float scale_log2) {
   constexpr int DP = (D + 31) / 32 * 32;  // QK contraction length padded to the MFMA k
   constexpr int DO = (D + 15) / 16 * 16;  // output rows padded to the MFMA block
@@ -46,9 +51,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
   constexpr int KS = DP + 8;    // LDS row stride of K (elements), skews banks
   constexpr int VS = BKV + 8;   // LDS row stride of V^T
   constexpr int KCH = DP / 8;   // 16-byte chunks per K row (zero beyond D)
-  constexpr int VCH = D / 8;    // 16-byte chunks per V row
+  constexpr int VN = D * (BKV / 8);  // 16-byte chunks of a V^T tile (D rows of 64 keys)
   constexpr int KLD = (BKV * KCH + kThreads - 1) / kThreads;
-  constexpr int VLD = (BKV * VCH + kThreads - 1) / kThreads;
+  constexpr int VLD = (VN + kThreads - 1) / kThreads;
   __shared__ __attribute__((aligned(16))) bf16 sK[BKV * KS];
   __shared__ __attribute__((aligned(16))) bf16 sVt[DO * VS];
 
@@ -60,7 +65,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
   const int64_t ld = 3 * (int64_t)H * D;
   const bf16* Qb = qkv + h * D;
   const bf16* Kb = qkv + (int64_t)H * D + h * D;
-  const bf16* Vb = qkv + 2 * (int64_t)H * D + h * D;
+  const bf16* Vb = vt + (int64_t)h * D * vt_ld + desc.kv_off[img] - seq0;  // key kidx at Vb[kidx]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, fk = lane >> 4;
@@ -93,12 +98,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
     }                                                                            \
     _Pragma("unroll") for (int i = 0; i < VLD; ++i) {                            \
       const int c = tid + kThreads * i;                                          \
-      const int key = c / VCH, vc = c % VCH;                                     \
-      const int kidx = (kv0) + key;                                              \
-      if (c < BKV * VCH && kidx < seq1)                                          \
-        rv[i] = ld16(Vb + kidx * ld + vc * 8);                                   \
-      else                                                                       \
-        rv[i] = u32x4{0, 0, 0, 0};                                               \
+      if (c < VN) rv[i] = ld16(Vb + (c >> 3) * vt_ld + (kv0) + (c & 7) * 8);     \
     }                                                                            \
   } while (0)
 #define VIT_LSTORE()                                                             \
@@ -109,11 +109,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
     }                                                                            \
     _Pragma("unroll") for (int i = 0; i < VLD; ++i) {                            \
       const int c = tid + kThreads * i;                                          \
-      if (c < BKV * VCH) {                                                       \
-        const int key = c / VCH, vc = c % VCH;                                   \
-        const bf16x8 v = __builtin_bit_cast(bf16x8, rv[i]);                      \
-        _Pragma("unroll") for (int j = 0; j < 8; ++j) sVt[(vc * 8 + j) * VS + key] = v[j]; \
-      }                                                                          \
+      if (c < VN) st16(&sVt[(c >> 3) * VS + (c & 7) * 8], rv[i]);                \
     }                                                                            \
   } while (0)
 
@@ -212,10 +208,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
       }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const bf16* vr = &sVt[(db * 16 + fr) * VS + ks * 32 + fk * 4];
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
-        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        // V^T slots 8 fk .. 8 fk + 7 of this 32-key half hold keys 4 fk .. 4 fk + 3
+        // and 16 + 4 fk .. 16 + 4 fk + 3, the k-slots of pf (vt16_slot_key)
+        const bf16x8 vf =
+            *reinterpret_cast<const bf16x8*>(&sVt[(db * 16 + fr) * VS + ks * 32 + fk * 8]);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], o[db][qb], 0, 0, 0);
@@ -590,20 +586,19 @@ hipError_t launch_attention_vt(const void* qk, int64_t ld_qk, const void* vt, in
   return hipGetLastError();
 }
 
-hipError_t launch_attention(int dtype, const void* qkv, const VarlenDesc& d, int n_heads,
-                            int head_dim, void* out, hipStream_t s) {
+hipError_t launch_attention(int dtype, const void* qkv, const void* vt, int64_t vt_ld,
+                            const VarlenDesc& d, int n_heads, int head_dim, void* out,
+                            hipStream_t s) {
   const int tiles = d.cu_tiles[d.n_images];
   if (tiles == 0) return hipSuccess;
   // bf16: two 128-query workgroups per 256-query descriptor tile
   const dim3 grid((unsigned)(dtype == VIT_BF16 ? 2 * tiles : tiles), (unsigned)n_heads);
   if (dtype == VIT_BF16) {
     const float sl2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
-    if (head_dim == 64)
-      attn_bf16_kernel<64><<<grid, kThreads, 0, s>>>((const bf16*)qkv, d, n_heads, (bf16*)out, sl2);
-    else if (head_dim == 72)
-      attn_bf16_kernel<72><<<grid, kThreads, 0, s>>>((const bf16*)qkv, d, n_heads, (bf16*)out, sl2);
-    else
+    if (head_dim != 72 || !vt || vt_ld < d.kv_off[d.n_images] || vt_ld % 8)
       return hipErrorInvalidValue;
+    attn_bf16_kernel<72><<<grid, kThreads, 0, s>>>((const bf16*)qkv, (const bf16*)vt, vt_ld, d,
+                                                   n_heads, (bf16*)out, sl2);
   } else {
     const float sc = (float)(1.0 / sqrt((double)head_dim));
     if (head_dim == 64)

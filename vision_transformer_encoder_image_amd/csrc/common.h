@@ -123,6 +123,12 @@ constexpr int VT_ALIGN = 64;
 // map is its own inverse.
 VIT_DEV int vt_key_slot(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
 
+// The same for the 16x16x32 MFMA layout of the head_dim-72 attention kernel:
+// inside each 32-slot group, lane group g (0..3) reads slots 8g .. 8g+7, which
+// hold keys 4g .. 4g+3 and 16+4g .. 16+4g+3 (the k-slots of its P^T operand).
+// Returns the key (inside the 64-key tile) stored in slot s.
+VIT_DEV int vt16_slot_key(int s) { return (s & 35) | ((s >> 1) & 12) | ((s & 4) << 2); }
+
 VIT_DEV int find_image(const VarlenDesc& d, int p) {
   int i = 0;
   while (i + 1 < d.n_images && p >= d.cu_seqlens[i + 1]) ++i;
@@ -187,8 +193,10 @@ hipError_t launch_rope_table(const VarlenDesc& d, int head_dim, float theta, voi
                              hipStream_t s);
 hipError_t launch_rope(int dtype, void* qkv, const void* table, int64_t P, int n_heads,
                        int head_dim, hipStream_t s);
-hipError_t launch_attention(int dtype, const void* qkv, const VarlenDesc& d, int n_heads,
-                            int head_dim, void* out, hipStream_t s);
+// fp32: vt unused.  bf16: head_dim 72 only, with vt from launch_vt_pack.
+hipError_t launch_attention(int dtype, const void* qkv, const void* vt, int64_t vt_ld,
+                            const VarlenDesc& d, int n_heads, int head_dim, void* out,
+                            hipStream_t s);
 int attention_q_tile(int dtype, int head_dim);
 // lse2 (optional, [n_heads, total] fp32): each query's log2(sum over keys of 2^(s c)),
 // s the raw q.k score and c = log2(e)/sqrt(64)

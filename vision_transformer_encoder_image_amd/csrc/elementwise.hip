@@ -296,16 +296,20 @@ __global__ __launch_bounds__(kThreads) void encode_prep_kernel(PrepArgs a) {
   }
 }
 
-// V part of a packed qkv buffer [P, 3*H*D] -> vt [H*D, ld] (images 64-aligned,
-// padding zeroed).  One thread per element of vt.
-// Columns col0 .. col0 + H*64 of src [P, ld_src] transposed into the V^T layout:
-// dst[h*64 + e][kv_off[img] + slot] = src[cu[img] + vt_key_slot(slot)][col0 + h*64 + e],
-// zero past the image.  One block per (64-key tile of an image span, head):
-// 64 source rows of 128 bytes into LDS, then 64 destination rows of 64 slots.
+// Columns col0 .. col0 + H*D of src [P, ld_src] transposed into a V^T layout:
+// dst[h*D + e][kv_off[img] + slot] = src[cu[img] + key(slot)][col0 + h*D + e],
+// zero past the image, where key() orders the keys of a 64-key tile for the
+// MFMA that reads them (vt_key_slot for the 32x32x16 layout of head_dim 64,
+// vt16_slot_key for the 16x16x32 layout of head_dim 72).  One block per
+// (64-key tile of an image span, head): 64 source rows of D elements into
+// LDS, then D destination rows of 64 slots.
+template <int D, bool K16>
 __global__ __launch_bounds__(256) void tpack_kernel(const bf16* __restrict__ src, int64_t ld_src,
                                                     int64_t col0, VarlenDesc d,
                                                     bf16* __restrict__ dst, int64_t ld) {
-  __shared__ bf16 tile[64][64 + 2];
+  constexpr int CH = D / 8;  // 16-byte chunks per source row
+  constexpr int N = 64 * CH;  // chunks per tile, both ways
+  __shared__ bf16 tile[64][D + 2];
   const int col = blockIdx.x * 64;  // first destination column (a 64-aligned span start + 64 j)
   const int h = blockIdx.y;
   int img = 0;
@@ -313,13 +317,14 @@ __global__ __launch_bounds__(256) void tpack_kernel(const bf16* __restrict__ src
   const int k0 = col - d.kv_off[img];  // first key of the tile
   const int P = d.cu_seqlens[img + 1] - d.cu_seqlens[img];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < (N + 255) / 256; ++k) {
     const int q = threadIdx.x + 256 * k;
-    const int r = q >> 3, ch = q & 7;  // key row, 8-element chunk
+    if (q >= N) break;
+    const int r = q / CH, ch = q % CH;  // key row, 8-element chunk
     bf16x8 v;
     if (k0 + r < P) {
       v = __builtin_bit_cast(bf16x8, ld16(src + (int64_t)(d.cu_seqlens[img] + k0 + r) * ld_src +
-                                          col0 + h * 64 + ch * 8));
+                                          col0 + h * D + ch * 8));
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = f2bf(0.f);
@@ -329,13 +334,15 @@ __global__ __launch_bounds__(256) void tpack_kernel(const bf16* __restrict__ src
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < (N + 255) / 256; ++k) {
     const int q = threadIdx.x + 256 * k;
+    if (q >= N) break;
     const int e = q >> 3, ch = q & 7;  // destination row (dim), chunk of 8 slots
     bf16x8 v;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = tile[vt_key_slot(ch * 8 + j)][e];
-    st16(dst + (int64_t)(h * 64 + e) * ld + col + ch * 8, __builtin_bit_cast(u32x4, v));
+    for (int j = 0; j < 8; ++j)
+      v[j] = tile[K16 ? vt16_slot_key(ch * 8 + j) : vt_key_slot(ch * 8 + j)][e];
+    st16(dst + (int64_t)(h * D + e) * ld + col + ch * 8, __builtin_bit_cast(u32x4, v));
   }
 }
 
@@ -539,16 +546,21 @@ hipError_t launch_tpack(const void* src, int64_t ld_src, int64_t col0, const Var
   const int cols = d.kv_off[d.n_images];
   if (cols == 0) return hipSuccess;
   if (ld_src % 8 || col0 % 8 || ld % 8) return hipErrorInvalidValue;
-  tpack_kernel<<<dim3((unsigned)(cols / 64), (unsigned)n_heads), 256, 0, s>>>(
+  tpack_kernel<64, false><<<dim3((unsigned)(cols / 64), (unsigned)n_heads), 256, 0, s>>>(
       (const bf16*)src, ld_src, col0, d, (bf16*)dst, ld);
   return hipGetLastError();
 }
 
 hipError_t launch_vt_pack(const void* qkv, const VarlenDesc& d, int n_heads, int head_dim,
                           void* vt, int64_t vt_ld, hipStream_t s) {
-  if (head_dim != 64) return hipErrorInvalidValue;
-  const int64_t dm = (int64_t)n_heads * 64;
-  return launch_tpack(qkv, 3 * dm, 2 * dm, d, n_heads, vt, vt_ld, s);
+  const int64_t dm = (int64_t)n_heads * head_dim;
+  if (head_dim == 64) return launch_tpack(qkv, 3 * dm, 2 * dm, d, n_heads, vt, vt_ld, s);
+  if (head_dim != 72 || vt_ld % 8) return hipErrorInvalidValue;
+  const int cols = d.kv_off[d.n_images];
+  if (cols == 0) return hipSuccess;
+  tpack_kernel<72, true><<<dim3((unsigned)(cols / 64), (unsigned)n_heads), 256, 0, s>>>(
+      (const bf16*)qkv, 3 * dm, 2 * dm, d, (bf16*)vt, vt_ld);
+  return hipGetLastError();
 }
 
 hipError_t launch_layout(int grid_h, int grid_w, int merge, int32_t* perm, int32_t* nl_type,
