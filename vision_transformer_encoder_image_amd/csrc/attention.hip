@@ -20,7 +20,8 @@
 //        is needed) and V^T read from its LDS tile, one 16-byte read per
 //        fragment.
 // Softmax in base 2 with the 1/sqrt(D) scale folded into log2(e); fp32 state.
-// The next K/V tile is prefetched into registers during the current one.
+// Tile t+2 is fetched into registers and tile t+1 stored into the second LDS
+// buffer while tile t is computed; one barrier per tile.
 //
 // fp32 kernel (vector ALU): one thread per query, K/V tiles in LDS, same online
 // softmax in base e.  Used by the single-precision mode.
@@ -54,8 +55,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
   constexpr int VN = D * (BKV / 8);  // 16-byte chunks of a V^T tile (D rows of 64 keys)
   constexpr int KLD = (BKV * KCH + kThreads - 1) / kThreads;
   constexpr int VLD = (VN + kThreads - 1) / kThreads;
-  __shared__ __attribute__((aligned(16))) bf16 sK[BKV * KS];
-  __shared__ __attribute__((aligned(16))) bf16 sVt[DO * VS];
+  // two buffers of each: the tile after the current one is stored while the
+  // current one is read, so one barrier per tile orders both
+  __shared__ __attribute__((aligned(16))) bf16 sK2[2][BKV * KS];
+  __shared__ __attribute__((aligned(16))) bf16 sVt2[2][DO * VS];
 
   const int tile = blockIdx.x >> 1, h = blockIdx.y;  // two workgroups per descriptor tile
   int img = 0;
@@ -101,15 +104,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
       if (c < VN) rv[i] = ld16(Vb + (c >> 3) * vt_ld + (kv0) + (c & 7) * 8);     \
     }                                                                            \
   } while (0)
-#define VIT_LSTORE()                                                             \
+#define VIT_LSTORE(buf)                                                          \
   do {                                                                           \
     _Pragma("unroll") for (int i = 0; i < KLD; ++i) {                            \
       const int c = tid + kThreads * i;                                          \
-      if (c < BKV * KCH) st16(&sK[(c / KCH) * KS + (c % KCH) * 8], rk[i]);        \
+      if (c < BKV * KCH) st16(&sK2[buf][(c / KCH) * KS + (c % KCH) * 8], rk[i]);  \
     }                                                                            \
     _Pragma("unroll") for (int i = 0; i < VLD; ++i) {                            \
       const int c = tid + kThreads * i;                                          \
-      if (c < VN) st16(&sVt[(c >> 3) * VS + (c & 7) * 8], rv[i]);                \
+      if (c < VN) st16(&sVt2[buf][(c >> 3) * VS + (c & 7) * 8], rv[i]);          \
     }                                                                            \
   } while (0)
 
@@ -123,11 +126,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
 
   const int nkv = (seq1 - seq0 + BKV - 1) / BKV;
   VIT_GLOAD(seq0);
-  VIT_LSTORE();
+  VIT_LSTORE(0);
+  if (nkv > 1) VIT_GLOAD(seq0 + BKV);
   __syncthreads();
   for (int t = 0; t < nkv; ++t) {
     const int kv0 = seq0 + t * BKV;
-    if (t + 1 < nkv) VIT_GLOAD(kv0 + BKV);
+    // tile t+1 (in registers) into the other buffer, whose last reader (tile
+    // t-1) finished before the previous barrier; then fetch tile t+2
+    if (t + 1 < nkv) {
+      VIT_LSTORE((t + 1) & 1);
+      if (t + 2 < nkv) VIT_GLOAD(kv0 + 2 * BKV);
+    }
+    const bf16* sK = sK2[t & 1];
+    const bf16* sVt = sVt2[t & 1];
 
     f32x4 s[4][2];
 #pragma unroll
@@ -218,10 +229,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
       }
     }
     __syncthreads();
-    if (t + 1 < nkv) {
-      VIT_LSTORE();
-      __syncthreads();
-    }
   }
 
   const int64_t ldo = (int64_t)H * D;
