@@ -5,7 +5,7 @@
 // the P_i x P_i score matrix never leaves registers.
 //
 // head_dim 72 bf16 kernel (gfx950 MFMA; head_dim 64 takes attn_vt_kernel below).
-// One workgroup = 128 queries of one (image, head), 4 waves x 32 queries.  V
+// One workgroup = 256 queries of one (image, head), 8 waves x 32 queries.  V
 // comes transposed per head, [H*72, kv_total] with images at 64-aligned
 // columns, keys ordered inside each 64-key tile by vt16_slot_key and zero past
 // the image (a pack pass before the kernel).  Per 64-key tile:
@@ -33,14 +33,14 @@
 
 namespace {
 
-constexpr int BQ = 128, BKV = 64;
-// q-tile of the bf16 varlen descriptor: one transposed-V workgroup (8 waves x 32
-// queries), or two workgroups of the generic bf16 kernel
+constexpr int BQ = 256, BKV = 64;
+// q-tile of the bf16 varlen descriptor: one workgroup (8 waves x 32 queries) of
+// either bf16 kernel
 constexpr int BQ_DESC = 256;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __restrict__ qkv,
+__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const bf16* __restrict__ qkv,
                                                                 const bf16* __restrict__ vt,
                                                                 int64_t vt_ld, VarlenDesc desc,
                                                                 int H, bf16* __restrict__ out,
@@ -60,11 +60,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const bf16* __re
   __shared__ __attribute__((aligned(16))) bf16 sK2[2][BKV * KS];
   __shared__ __attribute__((aligned(16))) bf16 sVt2[2][DO * VS];
 
-  const int tile = blockIdx.x >> 1, h = blockIdx.y;  // two workgroups per descriptor tile
+  // 1D grid over (head, q-tile), dealt so that every XCD gets a contiguous
+  // range: the q-tiles of one (image, head) then share that XCD's L2 copy of
+  // the image's K and V^T
+  const int ntiles = desc.cu_tiles[desc.n_images];
+  const int nitems = ntiles * H;
+  const int per = nitems / 8, rem = nitems % 8;
+  const int xcd = blockIdx.x % 8;
+  const int item = xcd * per + min(xcd, rem) + (int)blockIdx.x / 8;
+  const int h = item / ntiles, tile = item % ntiles;
   int img = 0;
   while (img + 1 < desc.n_images && tile >= desc.cu_tiles[img + 1]) ++img;
   const int seq0 = desc.cu_seqlens[img], seq1 = desc.cu_seqlens[img + 1];
-  const int q0 = seq0 + (tile - desc.cu_tiles[img]) * BQ_DESC + (blockIdx.x & 1) * BQ;
+  const int q0 = seq0 + (tile - desc.cu_tiles[img]) * BQ;
   const int64_t ld = 3 * (int64_t)H * D;
   const bf16* Qb = qkv + h * D;
   const bf16* Kb = qkv + (int64_t)H * D + h * D;
@@ -584,7 +592,7 @@ int attention_q_tile(int dtype, int /*head_dim*/) { return dtype == VIT_BF16 ? B
 hipError_t launch_attention_vt(const void* qk, int64_t ld_qk, const void* vt, int64_t vt_ld,
                                const VarlenDesc& d, int n_heads, void* out, hipStream_t s,
                                float* lse2) {
-  static_assert(VT_BQ == BQ_DESC && 2 * BQ == BQ_DESC, "both bf16 kernels share the q-tile descriptor");
+  static_assert(VT_BQ == BQ_DESC && BQ == BQ_DESC, "both bf16 kernels share the q-tile descriptor");
   const int tiles = d.cu_tiles[d.n_images];
   if (tiles == 0) return hipSuccess;
   const float c = (float)(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
@@ -598,15 +606,14 @@ hipError_t launch_attention(int dtype, const void* qkv, const void* vt, int64_t 
                             hipStream_t s) {
   const int tiles = d.cu_tiles[d.n_images];
   if (tiles == 0) return hipSuccess;
-  // bf16: two 128-query workgroups per 256-query descriptor tile
-  const dim3 grid((unsigned)(dtype == VIT_BF16 ? 2 * tiles : tiles), (unsigned)n_heads);
   if (dtype == VIT_BF16) {
     const float sl2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
     if (head_dim != 72 || !vt || vt_ld < d.kv_off[d.n_images] || vt_ld % 8)
       return hipErrorInvalidValue;
-    attn_bf16_kernel<72><<<grid, kThreads, 0, s>>>((const bf16*)qkv, (const bf16*)vt, vt_ld, d,
-                                                   n_heads, (bf16*)out, sl2);
+    attn_bf16_kernel<72><<<dim3((unsigned)(tiles * n_heads)), kThreads, 0, s>>>(
+        (const bf16*)qkv, (const bf16*)vt, vt_ld, d, n_heads, (bf16*)out, sl2);
   } else {
+    const dim3 grid((unsigned)tiles, (unsigned)n_heads);
     const float sc = (float)(1.0 / sqrt((double)head_dim));
     if (head_dim == 64)
       attn_f32_kernel<64><<<grid, FQ, 0, s>>>((const float*)qkv, d, n_heads, (float*)out, sc);
