@@ -20,8 +20,8 @@
 //        is needed) and V^T read from its LDS tile, one 16-byte read per
 //        fragment.
 // Softmax in base 2 with the 1/sqrt(D) scale folded into log2(e); fp32 state.
-// Tile t+2 is fetched into registers and tile t+1 stored into the second LDS
-// buffer while tile t is computed; one barrier per tile.
+// K and V^T tiles are DMA'd into a 3-stage LDS ring two tiles ahead; one
+// barrier per tile.
 //
 // fp32 kernel (vector ALU): one thread per query, K/V tiles in LDS, same online
 // softmax in base e.  Used by the single-precision mode.
@@ -49,16 +49,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const bf16* __re
   constexpr int DO = (D + 15) / 16 * 16;  // output rows padded to the MFMA block
   constexpr int NDS = DP / 32;
   constexpr int NDB = DO / 16;
-  constexpr int KS = DP + 8;    // LDS row stride of K (elements), skews banks
-  constexpr int VS = BKV + 8;   // LDS row stride of V^T
-  constexpr int KCH = DP / 8;   // 16-byte chunks per K row (zero beyond D)
-  constexpr int VN = D * (BKV / 8);  // 16-byte chunks of a V^T tile (D rows of 64 keys)
-  constexpr int KLD = (BKV * KCH + kThreads - 1) / kThreads;
-  constexpr int VLD = (VN + kThreads - 1) / kThreads;
-  // two buffers of each: the tile after the current one is stored while the
-  // current one is read, so one barrier per tile orders both
-  __shared__ __attribute__((aligned(16))) bf16 sK2[2][BKV * KS];
-  __shared__ __attribute__((aligned(16))) bf16 sVt2[2][DO * VS];
+  // K and V^T tiles are DMA'd global -> LDS (global_load_lds_dwordx4) into a
+  // ring of STAGES buffers.  K tile: 64 keys x D/8 16-byte chunks, rows of D
+  // elements (an odd number of 16-byte chunks, so 16 lanes reading 16 rows hit
+  // distinct banks); V^T tile: D rows x 8 chunks, chunk c of row r stored at
+  // c ^ (r & 7).  Both are D/8 copies of 64 lanes; wave w issues copies w,
+  // w + 8, ... of the NB per tile.
+  static_assert(D % 8 == 0, "16-byte chunks");
+  constexpr int STAGES = 3;
+  constexpr int KCH = D / 8;         // 16-byte chunks per K row
+  constexpr int VOFF = BKV * D;      // V^T after K inside a stage (elements)
+  constexpr int NB = D / 4;          // 64-lane copies per tile (K and V^T)
+  constexpr int WAVES = kThreads / 64;
+  __shared__ __attribute__((aligned(16))) bf16 sKV[STAGES][2 * BKV * D];
 
   // 1D grid over (head, q-tile), dealt so that every XCD gets a contiguous
   // range: the q-tiles of one (image, head) then share that XCD's L2 copy of
@@ -94,35 +97,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const bf16* __re
     }
   }
 
-  // K/V staging registers (fully unrolled; KLD, VLD <= 3)
-  u32x4 rk[KLD], rv[VLD];
-#define VIT_GLOAD(kv0)                                                           \
-  do {                                                                           \
-    _Pragma("unroll") for (int i = 0; i < KLD; ++i) {                            \
-      const int c = tid + kThreads * i;                                          \
-      const int key = c / KCH, kc = c % KCH;                                     \
-      const int kidx = (kv0) + key;                                              \
-      if (c < BKV * KCH && kidx < seq1 && kc * 8 < D)                            \
-        rk[i] = ld16(Kb + kidx * ld + kc * 8);                                   \
-      else                                                                       \
-        rk[i] = u32x4{0, 0, 0, 0};                                               \
-    }                                                                            \
-    _Pragma("unroll") for (int i = 0; i < VLD; ++i) {                            \
-      const int c = tid + kThreads * i;                                          \
-      if (c < VN) rv[i] = ld16(Vb + (c >> 3) * vt_ld + (kv0) + (c & 7) * 8);     \
-    }                                                                            \
+  const int ncp = NB / WAVES + (wave < NB % WAVES ? 1 : 0);  // copies per tile, this wave
+#define VIT_ISSUE(t)                                                                  \
+  do {                                                                                \
+    const int kv0_ = seq0 + (t) * BKV;                                                \
+    bf16* st_ = sKV[(t) % STAGES];                                                    \
+    _Pragma("unroll") for (int i = 0; i < (NB + WAVES - 1) / WAVES; ++i) {            \
+      const int j_ = wave + WAVES * i;                                                \
+      if (j_ < NB) {                                                                  \
+        const bf16* src_;                                                             \
+        if (j_ < NB / 2) {                                                            \
+          const int c_ = j_ * 64 + lane, key_ = c_ / KCH;                             \
+          src_ = Kb + (int64_t)min(kv0_ + key_, seq1 - 1) * ld + (c_ % KCH) * 8;       \
+        } else {                                                                      \
+          const int c_ = (j_ - NB / 2) * 64 + lane, r_ = c_ >> 3;                     \
+          src_ = Vb + r_ * vt_ld + kv0_ + (((c_ & 7) ^ (r_ & 7)) << 3);               \
+        }                                                                             \
+        copy16_to_lds(src_, st_ + j_ * 512);                                          \
+      }                                                                               \
+    }                                                                                 \
   } while (0)
-#define VIT_LSTORE(buf)                                                          \
-  do {                                                                           \
-    _Pragma("unroll") for (int i = 0; i < KLD; ++i) {                            \
-      const int c = tid + kThreads * i;                                          \
-      if (c < BKV * KCH) st16(&sK2[buf][(c / KCH) * KS + (c % KCH) * 8], rk[i]);  \
-    }                                                                            \
-    _Pragma("unroll") for (int i = 0; i < VLD; ++i) {                            \
-      const int c = tid + kThreads * i;                                          \
-      if (c < VN) st16(&sVt2[buf][(c >> 3) * VS + (c & 7) * 8], rv[i]);          \
-    }                                                                            \
-  } while (0)
+  // all of tile t's copies of this wave done; the next tile's may be in flight
+  auto wait_tile = [&](bool next_in_flight) {
+    if (!next_in_flight)
+      wait_vmcnt<0>();
+    else if (ncp == NB / WAVES + 1)
+      wait_vmcnt<NB / WAVES + 1>();
+    else
+      wait_vmcnt<NB / WAVES>();
+  };
 
   f32x4 o[NDB][2];
 #pragma unroll
@@ -133,20 +136,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const bf16* __re
   float lsum[2] = {0.f, 0.f};
 
   const int nkv = (seq1 - seq0 + BKV - 1) / BKV;
-  VIT_GLOAD(seq0);
-  VIT_LSTORE(0);
-  if (nkv > 1) VIT_GLOAD(seq0 + BKV);
-  __syncthreads();
+  VIT_ISSUE(0);
+  if (nkv > 1) VIT_ISSUE(1);
   for (int t = 0; t < nkv; ++t) {
     const int kv0 = seq0 + t * BKV;
-    // tile t+1 (in registers) into the other buffer, whose last reader (tile
-    // t-1) finished before the previous barrier; then fetch tile t+2
-    if (t + 1 < nkv) {
-      VIT_LSTORE((t + 1) & 1);
-      if (t + 2 < nkv) VIT_GLOAD(kv0 + 2 * BKV);
-    }
-    const bf16* sK = sK2[t & 1];
-    const bf16* sVt = sVt2[t & 1];
+    wait_tile(t + 1 < nkv);
+    // tile t in LDS for every wave, and every wave is done with tile t-1, whose
+    // stage tile t+2 reuses
+    lds_barrier();
+    if (t + 2 < nkv) VIT_ISSUE(t + 2);
+    const bf16* sK = sKV[t % STAGES];
+    const bf16* sV = sK + VOFF;
 
     f32x4 s[4][2];
 #pragma unroll
@@ -157,8 +157,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const bf16* __re
     for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&sK[(kb * 16 + fr) * KS + ds * 32 + fk * 8]);
+        // chunks past D/8 (the zero-padded part of Q) reread the last one: finite
+        // K values times zero Q fragments
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+            &sK[(kb * 16 + fr) * D + min(ds * 4 + fk, KCH - 1) * 8]);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ds], s[kb][qb], 0, 0, 0);
@@ -229,14 +231,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const bf16* __re
       for (int db = 0; db < NDB; ++db) {
         // V^T slots 8 fk .. 8 fk + 7 of this 32-key half hold keys 4 fk .. 4 fk + 3
         // and 16 + 4 fk .. 16 + 4 fk + 3, the k-slots of pf (vt16_slot_key)
+        // rows past D (padding of the last 16-row block, discarded) reread row D-1
+        const int vr = min(db * 16 + fr, D - 1);
         const bf16x8 vf =
-            *reinterpret_cast<const bf16x8*>(&sVt[(db * 16 + fr) * VS + ks * 32 + fk * 8]);
+            *reinterpret_cast<const bf16x8*>(&sV[vr * BKV + (((ks * 4 + fk) ^ (vr & 7)) << 3)]);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], o[db][qb], 0, 0, 0);
       }
     }
-    __syncthreads();
   }
 
   const int64_t ldo = (int64_t)H * D;
@@ -258,8 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const bf16* __re
       *reinterpret_cast<bf16x4*>(out + query * ldo + h * D + d) = v;
     }
   }
-#undef VIT_GLOAD
-#undef VIT_LSTORE
+#undef VIT_ISSUE
 }
 
 
