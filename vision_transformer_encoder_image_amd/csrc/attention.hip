@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const bf16* __re
   // c ^ (r & 7).  Both are D/8 copies of 64 lanes; wave w issues copies w,
   // w + 8, ... of the NB per tile.
   static_assert(D % 8 == 0, "16-byte chunks");
-  constexpr int STAGES = 3;
+  constexpr int STAGES = 4;  // tiles t-1 .. t+2 (see the late waves below)
   constexpr int KCH = D / 8;         // 16-byte chunks per K row
   constexpr int VOFF = BKV * D;      // V^T after K inside a stage (elements)
   constexpr int NB = D / 4;          // 64-lane copies per tile (K and V^T)
@@ -135,18 +135,40 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const bf16* __re
   float mrow[2] = {-INFINITY, -INFINITY};
   float lsum[2] = {0.f, 0.f};
 
+  // The two waves that share a SIMD (w and w + 4) run out of phase: waves 4-7
+  // ("late") add tile t-1's O^T MFMAs at the start of step t, before tile t's
+  // S^T MFMAs, so their softmax meets the other wave's MFMAs.  Tile t-1's stage
+  // stays intact through step t (tile t+2 lands in a different one of the 4).
+  const bool late = wave >= WAVES / 2;
+  bf16x8 pf[BKV / 32][2];
+#define VIT_PV(sV_)                                                                   \
+  do {                                                                                \
+    const bf16* sv_ = (sV_);                                                          \
+    _Pragma("unroll") for (int ks = 0; ks < BKV / 32; ++ks)                           \
+    _Pragma("unroll") for (int db = 0; db < NDB; ++db) {                              \
+      /* V^T slots 8 fk .. 8 fk + 7 of this 32-key half hold keys 4 fk .. 4 fk + 3    \
+         and 16 + 4 fk .. 16 + 4 fk + 3, the k-slots of pf (vt16_slot_key); rows     \
+         past D (padding of the last 16-row block, discarded) reread row D-1 */      \
+      const int vr = min(db * 16 + fr, D - 1);                                        \
+      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(                             \
+          &sv_[vr * BKV + (((ks * 4 + fk) ^ (vr & 7)) << 3)]);                        \
+      _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) o[db][qb] =                    \
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[ks][qb], o[db][qb], 0, 0, 0); \
+    }                                                                                 \
+  } while (0)
+
   const int nkv = (seq1 - seq0 + BKV - 1) / BKV;
   VIT_ISSUE(0);
   if (nkv > 1) VIT_ISSUE(1);
   for (int t = 0; t < nkv; ++t) {
     const int kv0 = seq0 + t * BKV;
     wait_tile(t + 1 < nkv);
-    // tile t in LDS for every wave, and every wave is done with tile t-1, whose
+    // tile t in LDS for every wave, and every wave is done with tile t-2, whose
     // stage tile t+2 reuses
     lds_barrier();
     if (t + 2 < nkv) VIT_ISSUE(t + 2);
+    if (late && t > 0) VIT_PV(sKV[(t - 1) % STAGES] + VOFF);
     const bf16* sK = sKV[t % STAGES];
-    const bf16* sV = sK + VOFF;
 
     f32x4 s[4][2];
 #pragma unroll
@@ -207,40 +229,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const bf16* __re
           s[kb][qb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][i], scale_log2, nm));
     }
 
+    // probabilities as the bf16 B operand of O^T += V^T P^T; the sum adds the
+    // bf16 values the MFMAs use, two per dot2
 #pragma unroll
-    for (int ks = 0; ks < BKV / 32; ++ks) {
-      bf16x8 pf[2];
+    for (int ks = 0; ks < BKV / 32; ++ks)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pf[qb][i] = f2bf(s[2 * ks][qb][i]);
-          pf[qb][4 + i] = f2bf(s[2 * ks + 1][qb][i]);
+          pf[ks][qb][i] = f2bf(s[2 * ks][qb][i]);
+          pf[ks][qb][4 + i] = f2bf(s[2 * ks + 1][qb][i]);
         }
-        // the sum adds the bf16 probabilities the P.V MFMAs use, two per dot2
         const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
-        const bf16x8 q8 = pf[qb];
-        float t = lsum[qb];
-        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q8, q8, 0, 1), one2, t, false);
-        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q8, q8, 2, 3), one2, t, false);
-        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q8, q8, 4, 5), one2, t, false);
-        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q8, q8, 6, 7), one2, t, false);
-        lsum[qb] = t;
+        const bf16x8 q8 = pf[ks][qb];
+        float u = lsum[qb];
+        u = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q8, q8, 0, 1), one2, u, false);
+        u = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q8, q8, 2, 3), one2, u, false);
+        u = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q8, q8, 4, 5), one2, u, false);
+        u = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q8, q8, 6, 7), one2, u, false);
+        lsum[qb] = u;
       }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        // V^T slots 8 fk .. 8 fk + 7 of this 32-key half hold keys 4 fk .. 4 fk + 3
-        // and 16 + 4 fk .. 16 + 4 fk + 3, the k-slots of pf (vt16_slot_key)
-        // rows past D (padding of the last 16-row block, discarded) reread row D-1
-        const int vr = min(db * 16 + fr, D - 1);
-        const bf16x8 vf =
-            *reinterpret_cast<const bf16x8*>(&sV[vr * BKV + (((ks * 4 + fk) ^ (vr & 7)) << 3)]);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], o[db][qb], 0, 0, 0);
-      }
-    }
+    if (!late) VIT_PV(sKV[t % STAGES] + VOFF);
   }
+  if (late && nkv > 0) VIT_PV(sKV[(nkv - 1) % STAGES] + VOFF);
+#undef VIT_PV
 
   const int64_t ldo = (int64_t)H * D;
 #pragma unroll
