@@ -412,9 +412,14 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
     }
     if (!fuse_rope) {
       ProfScope ps(VIT_K_ROPE, s);
-      VIT_HIP(launch_rope(dt, qkv, table, P, c.n_heads, c.head_dim, s), "rope");
-      if (vt)
-        VIT_HIP(launch_vt_pack(qkv, desc, c.n_heads, c.head_dim, vt, p.kv_total, s), "pack V");
+      if (p.pack_vt) {  // one launch: rotary of q, k and the V^T pack
+        VIT_HIP(launch_vt_pack(qkv, desc, c.n_heads, c.head_dim, vt, p.kv_total, s, table),
+                "rope + pack V");
+      } else {
+        VIT_HIP(launch_rope(dt, qkv, table, P, c.n_heads, c.head_dim, s), "rope");
+        if (vt)
+          VIT_HIP(launch_vt_pack(qkv, desc, c.n_heads, c.head_dim, vt, p.kv_total, s), "pack V");
+      }
     }
     {
       ProfScope ps(VIT_K_ATTN, s);

@@ -238,8 +238,12 @@ hipError_t launch_patchify(int dtype, const void* pix, const VarlenDesc& d, int 
 hipError_t launch_vpos(const VarlenDesc& d, int32_t* vpos, hipStream_t s);
 hipError_t launch_vt_zero_pads(const VarlenDesc& d, int64_t rows, void* vt, int64_t vt_ld,
                                hipStream_t s);
+// V of a packed qkv buffer transposed into the attention kernels' V^T layout
+// (head_dim 64 or 72); for head_dim 72 with rope_table, the same launch also
+// applies the rotary to q and k in place.
 hipError_t launch_vt_pack(const void* qkv, const VarlenDesc& d, int n_heads, int head_dim,
-                          void* vt, int64_t vt_ld, hipStream_t s);
+                          void* vt, int64_t vt_ld, hipStream_t s,
+                          const void* rope_table = nullptr);
 hipError_t launch_gather(int dtype, const void* x, const VarlenDesc& d, int dim, int merge,
                          void* G, hipStream_t s);
 hipError_t launch_pad_rows(int dtype, const void* src, int64_t rows, int64_t cols, int64_t ld_dst,

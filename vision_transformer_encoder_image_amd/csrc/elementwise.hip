@@ -303,10 +303,15 @@ __global__ __launch_bounds__(kThreads) void encode_prep_kernel(PrepArgs a) {
 // vt16_slot_key for the 16x16x32 layout of head_dim 72).  One block per
 // (64-key tile of an image span, head): 64 source rows of D elements into
 // LDS, then D destination rows of 64 slots.
+// With a rotary table (head_dim 72 encode, src = the packed qkv buffer, col0 =
+// its V part), the block also applies the half-split 2D rotary to the q and k
+// rows of its keys and head in place, as rope_kernel does (fp32 math, pairs
+// (i, i + D/4) of each half, two pairs per access).
 template <int D, bool K16>
 __global__ __launch_bounds__(256) void tpack_kernel(const bf16* __restrict__ src, int64_t ld_src,
                                                     int64_t col0, VarlenDesc d,
-                                                    bf16* __restrict__ dst, int64_t ld) {
+                                                    bf16* __restrict__ dst, int64_t ld,
+                                                    const float2* __restrict__ rope_table) {
   constexpr int CH = D / 8;  // 16-byte chunks per source row
   constexpr int N = 64 * CH;  // chunks per tile, both ways
   __shared__ bf16 tile[64][D + 2];
@@ -331,6 +336,31 @@ __global__ __launch_bounds__(256) void tpack_kernel(const bf16* __restrict__ src
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) tile[r][ch * 8 + e] = v[e];
+  }
+  if (rope_table) {
+    static_assert(D % 8 == 0, "two pairs per access");
+    constexpr int q4 = D / 4, qv = q4 / 2;
+    const int64_t dm = (int64_t)gridDim.y * D;
+    for (int it = threadIdx.x; it < 64 * 4 * qv; it += 256) {
+      const int r = it / (4 * qv);
+      int j = it % (4 * qv);
+      const int kk = (j % qv) * 2;
+      j /= qv;
+      const int half = j & 1, part = j >> 1;  // part 0 = q, 1 = k
+      if (k0 + r >= P) continue;
+      const int64_t p = d.cu_seqlens[img] + k0 + r;
+      bf16* row = const_cast<bf16*>(src) + p * ld_src + part * dm + h * D + half * (D / 2);
+      const float4 cs = *reinterpret_cast<const float4*>(rope_table + p * (D / 2) + half * q4 + kk);
+      bf16x2 x1 = *reinterpret_cast<const bf16x2*>(row + kk);
+      bf16x2 x2 = *reinterpret_cast<const bf16x2*>(row + kk + q4);
+      const float a0 = bf2f(x1[0]), a1 = bf2f(x1[1]), b0 = bf2f(x2[0]), b1 = bf2f(x2[1]);
+      x1[0] = f2bf(a0 * cs.x - b0 * cs.y);
+      x2[0] = f2bf(b0 * cs.x + a0 * cs.y);
+      x1[1] = f2bf(a1 * cs.z - b1 * cs.w);
+      x2[1] = f2bf(b1 * cs.z + a1 * cs.w);
+      *reinterpret_cast<bf16x2*>(row + kk) = x1;
+      *reinterpret_cast<bf16x2*>(row + kk + q4) = x2;
+    }
   }
   __syncthreads();
 #pragma unroll
@@ -547,19 +577,21 @@ hipError_t launch_tpack(const void* src, int64_t ld_src, int64_t col0, const Var
   if (cols == 0) return hipSuccess;
   if (ld_src % 8 || col0 % 8 || ld % 8) return hipErrorInvalidValue;
   tpack_kernel<64, false><<<dim3((unsigned)(cols / 64), (unsigned)n_heads), 256, 0, s>>>(
-      (const bf16*)src, ld_src, col0, d, (bf16*)dst, ld);
+      (const bf16*)src, ld_src, col0, d, (bf16*)dst, ld, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_vt_pack(const void* qkv, const VarlenDesc& d, int n_heads, int head_dim,
-                          void* vt, int64_t vt_ld, hipStream_t s) {
+                          void* vt, int64_t vt_ld, hipStream_t s, const void* rope_table) {
   const int64_t dm = (int64_t)n_heads * head_dim;
-  if (head_dim == 64) return launch_tpack(qkv, 3 * dm, 2 * dm, d, n_heads, vt, vt_ld, s);
+  if (head_dim == 64 && !rope_table) return launch_tpack(qkv, 3 * dm, 2 * dm, d, n_heads, vt, vt_ld, s);
   if (head_dim != 72 || vt_ld % 8) return hipErrorInvalidValue;
+  if (rope_table && (((uintptr_t)qkv & 3) || ((uintptr_t)rope_table & 15)))
+    return hipErrorInvalidValue;
   const int cols = d.kv_off[d.n_images];
   if (cols == 0) return hipSuccess;
   tpack_kernel<72, true><<<dim3((unsigned)(cols / 64), (unsigned)n_heads), 256, 0, s>>>(
-      (const bf16*)qkv, 3 * dm, 2 * dm, d, (bf16*)vt, vt_ld);
+      (const bf16*)qkv, 3 * dm, 2 * dm, d, (bf16*)vt, vt_ld, (const float2*)rope_table);
   return hipGetLastError();
 }
 
