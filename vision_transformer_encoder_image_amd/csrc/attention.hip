@@ -20,8 +20,9 @@
 //        is needed) and V^T read from its LDS tile, one 16-byte read per
 //        fragment.
 // Softmax in base 2 with the 1/sqrt(D) scale folded into log2(e); fp32 state.
-// K and V^T tiles are DMA'd into a 3-stage LDS ring two tiles ahead; one
-// barrier per tile.
+// K and V^T tiles are DMA'd into a 4-stage LDS ring two tiles ahead; one
+// barrier per tile; waves 4-7 run each tile's O^T MFMAs one step late, out of
+// phase with waves 0-3 on the same SIMDs.
 //
 // fp32 kernel (vector ALU): one thread per query, K/V tiles in LDS, same online
 // softmax in base e.  Used by the single-precision mode.
