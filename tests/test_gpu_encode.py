@@ -277,3 +277,28 @@ def test_random_ragged_batches_match_oracle(seed):
     err = rowwise_rel_err(got, ref)
     print(f"seed {seed} grids {grids} aligner {aligner}: row-wise rel err {err:.3e}")
     assert err < TOL["bf16"], err
+
+
+@pytest.mark.parametrize("seed", list(range(4)))
+def test_random_ragged_batches_head_dim_72(seed):
+    """Randomised batches through the head_dim-72 path (width 576 = 8 heads of 72,
+    the rotary applied by the V^T pack launch, the 16x16x32 attention kernel):
+    1-6 images of grids 1..24 x 1..24, hidden 192, 2 blocks, 4x4 patches, the
+    aligner on or off; the whole path against the oracle at the workload bar."""
+    rng = np.random.Generator(np.random.PCG64(3000 + seed))
+    n = int(rng.integers(1, 7))
+    grids = tuple((int(rng.integers(1, 25)), int(rng.integers(1, 25))) for _ in range(n))
+    aligner = bool(seed % 2 == 0)
+    cfg = configs.VitConfig(f"random72_{seed}", grids, 576, 8, 192, 2, 256 if aligner else 0,
+                            "bf16", patch_size=4)
+    assert cfg.head_dim == 72
+    inp = synth.make_inputs(cfg, seed=4000 + seed)
+    w = api.DeviceWeights(cfg, inp["weights"])
+    x = torch.from_numpy(inp["patches"]).to("cuda", torch.bfloat16)
+    got = to_np(api.encode_varlen(x, list(grids), w, aligner=aligner, pad_odd=aligner))
+    ref = oracle.encode_varlen(inp["patches"], list(grids), inp["weights"], cfg.n_heads,
+                               cfg.rms_eps, cfg.rope_theta, with_aligner=aligner, pad_odd=aligner)
+    assert got.shape == ref.shape
+    err = rowwise_rel_err(got, ref)
+    print(f"seed {seed} grids {grids} aligner {aligner}: row-wise rel err {err:.3e}")
+    assert err < TOL["bf16"], err
