@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import oracle
-from parity_util import TOL, rowwise_rel_err, to_np
+from parity_util import TOL, frob_rel_err, rowwise_rel_err, to_np
 from vision_transformer_encoder_image_amd import _lib, api, synth
 
 pytestmark = pytest.mark.gpu
@@ -29,6 +29,28 @@ def _run(x, w, wg, wu, wd, dy, eps=1e-6):
     return [to_np(t) for t in out]
 
 
+# Whole-matrix bars: ||g - r||_F / ||r||_F per gradient.  Error model: every bf16
+# rounding of an operand perturbs it by a relative error uniform in [-u, u],
+# u = 2^-9, i.e. RMS u/sqrt(3) = 1.13e-3; products and sums over many terms of
+# random sign keep that relative size in the Frobenius norm, and independent
+# roundings along a gradient's path add in quadrature.  With k roundings on the
+# path the expected error is sqrt(k) * 1.13e-3; the bars allow 4x that (and 2x more
+# where a cancellation amplifies it):
+#   MLP half: dy, n (-> g, u), the SwiGLU output a or its gradient dg / du, the
+#     weight-gradient operand: k = 4 -> 2.3e-3 expected, bar 1e-2 (measured
+#     <= 3.4e-3);
+#   attention half: n, q, k, v, P, dO, dS, dqkv: k = 8 -> 3.2e-3, and
+#     dS = P (dP - rowsum(dO o)) cancels by ~2x -> 6.4e-3 expected, bar 2e-2
+#     (measured <= 8.3e-3);
+#   whole tower: a block's gradients add the incoming gradient's error (the later
+#     halves' dx, each ~5e-3 at most measured) and the bf16 forward's residual
+#     error (~5e-3 at four blocks) in quadrature to its own half's: ~1e-2 at
+#     most, bar 2e-2 (measured <= 6.0e-3).
+MLP_GRAD_FROB = 1e-2
+ATTN_GRAD_FROB = 2e-2
+TOWER_GRAD_FROB = 2e-2
+
+
 def _check(got, ref, tag, whole_matrix_weights=False):
     """Row-wise relative error (the encoder's bar).  With a single row every weight
     gradient row is one product scaled by one entry of da = dy W_down, whose bf16
@@ -41,8 +63,10 @@ def _check(got, ref, tag, whole_matrix_weights=False):
         if whole_matrix_weights and name.startswith("d_w_"):
             g2, r2 = g2.reshape(1, -1), r2.reshape(1, -1)
         err = rowwise_rel_err(g2, r2)
-        print(f"{tag} {name}: row-wise rel err {err:.3e}")
+        fro = frob_rel_err(g, r)
+        print(f"{tag} {name}: row-wise rel err {err:.3e}, whole-matrix (Frobenius) {fro:.3e}")
         assert err < TOL["bf16"], (name, err)
+        assert fro < MLP_GRAD_FROB, (name, fro)
 
 
 @pytest.mark.parametrize("P,d,h", [(300, 256, 512), (64, 128, 192), (1, 64, 64)])
@@ -126,8 +150,10 @@ def _attn_check(got, ref, tag, whole_matrix_weights=False):
         if whole_matrix_weights and name in ("d_wqkv", "d_wo"):
             g2, r2 = g2.reshape(1, -1), r2.reshape(1, -1)
         err = rowwise_rel_err(g2, r2)
-        print(f"{tag} {name}: row-wise rel err {err:.3e}")
+        fro = frob_rel_err(g, r)
+        print(f"{tag} {name}: row-wise rel err {err:.3e}, whole-matrix (Frobenius) {fro:.3e}")
         assert err < ATTN_GRAD_TOL, (name, err)
+        assert fro < ATTN_GRAD_FROB, (name, fro)
 
 
 @pytest.mark.parametrize("grids", [[(4, 6), (3, 5), (8, 8)], [(1, 1), (2, 3)], [(4, 17)]])
@@ -160,12 +186,14 @@ def test_attn_backward_deterministic_and_errors():
 
 
 # ------------------------------------------------------------- whole tower
-# Bar of the whole-tower gradients: one half's bar (ATTN_GRAD_TOL, 3e-2) plus the
-# forward's own bar (2e-2): each half's input is the residual stream of the bf16
-# forward, not the exact one, and each half's incoming gradient already carries
-# the later halves' error.  Measured: 2e-4 - 7e-3 for the norms, the patch
-# embedding and the MLP weights; 1.5e-2 - 4.2e-2 for wqkv and wo, whose rows are
-# sums over the patches of products with near-cancelling attention outputs.
+# Row-wise bar of the whole-tower gradients.  The row-wise measure divides each
+# row's error by that row's largest entry, so rows of W_qkv and W_o whose
+# entries are sums over the patches of products with near-cancelling attention
+# outputs see their error inflated by that row's cancellation (measured: 2e-4 -
+# 1e-2 for the norms, the patch embedding and the MLP weights, 1.5e-2 - 4.2e-2
+# for W_qkv and W_o, whose Frobenius errors are <= 6e-3 like the others).  The
+# whole-matrix bar above is the discriminating check; this one bounds the worst
+# row at 2.5x the half's row-wise bar of the forward (2e-2).
 TOWER_GRAD_TOL = 5e-2
 
 
@@ -199,8 +227,10 @@ def _tower_check(cfg, got, patches, weights, dy, tag):
         assert g.shape == r.shape, name
         g2, r2 = (g[None], r[None]) if g.ndim == 1 else (g, r)
         err = rowwise_rel_err(g2, r2)
-        print(f"{tag} {name}: row-wise rel err {err:.3e}")
+        fro = frob_rel_err(g, r)
+        print(f"{tag} {name}: row-wise rel err {err:.3e}, whole-matrix (Frobenius) {fro:.3e}")
         assert err < TOWER_GRAD_TOL, (name, err)
+        assert fro < TOWER_GRAD_FROB, (name, fro)
 
 
 @pytest.mark.parametrize("grids,n_blocks", [([(4, 6), (3, 5), (8, 8)], 2),

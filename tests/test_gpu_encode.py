@@ -47,27 +47,48 @@ def test_workload_full_parity(idx):
 
 
 def test_highres_full_tower_against_stored_oracle():
-    """64x64 grid, 32 blocks, head_dim 72: rows sampled from the stored oracle run."""
+    """64x64 grid, 32 blocks, head_dim 72: every aligner output row against the stored
+    oracle run (tests/golden/make_expected.py), whose inputs must be the ones the
+    seeded generator gives today."""
+    import sys
+
+    sys.path.insert(0, GOLDEN)
+    import make_expected
+
     path = os.path.join(GOLDEN, "expected_highres_64x64_full_tower.npz")
     ref = np.load(path)
     cfg, inp, w, x = _setup(3)
+    assert str(ref["fingerprint"]) == make_expected.fingerprint(inp), "stored oracle inputs drifted"
     got = to_np(api.Encoder(cfg, w, cfg.grids, aligner=True)(x))
     assert tuple(ref["shape"]) == got.shape
-    err = rowwise_rel_err(got[ref["rows"]], ref["values"])
-    print(f"{cfg.name}: row-wise rel err {err:.3e} on {len(ref['rows'])} rows")
+    rows = ref["rows"]
+    assert len(rows) == got.shape[0], "the stored run covers every output row"
+    per_row = np.abs(got[rows] - ref["values"]).max(1) / np.abs(ref["values"]).max(1)
+    err = float(per_row.max())
+    print(f"{cfg.name}: row-wise rel err max {err:.3e} (row {int(rows[per_row.argmax()])}), "
+          f"median {float(np.median(per_row)):.3e}, margin to the bar {TOL['bf16'] - err:.3e}, "
+          f"{len(rows)} rows")
     assert err < TOL["bf16"], err
 
 
-def test_throughput_batch_sampled_images():
-    """16 x 48x48 images: images are independent, so the oracle runs on two of them."""
+@pytest.fixture(scope="module")
+def throughput_out():
     cfg, inp, w, x = _setup(4)
-    got = to_np(api.Encoder(cfg, w, cfg.grids, aligner=True)(x))
+    return to_np(api.Encoder(cfg, w, cfg.grids, aligner=True)(x)), inp
+
+
+@pytest.mark.parametrize("image", [0, 5, 10, 15])
+def test_throughput_batch_sampled_images(throughput_out, image):
+    """16 x 48x48 images: images are independent, so the oracle runs on four of them
+    (first, two in the middle, last), each against its rows of the whole-batch call."""
+    cfg = configs.get(4)
+    got, inp = throughput_out
     P, T = 48 * 48, 24 * 24
-    for i in (0, 15):
-        ref = _oracle(cfg, inp, grids=[(48, 48)], patches=inp["patches"][i * P:(i + 1) * P])
-        err = rowwise_rel_err(got[i * T:(i + 1) * T], ref)
-        print(f"{cfg.name} image {i}: row-wise rel err {err:.3e}")
-        assert err < TOL["bf16"], err
+    i = image
+    ref = _oracle(cfg, inp, grids=[(48, 48)], patches=inp["patches"][i * P:(i + 1) * P])
+    err = rowwise_rel_err(got[i * T:(i + 1) * T], ref)
+    print(f"{cfg.name} image {i}: row-wise rel err {err:.3e}")
+    assert err < TOL["bf16"], err
 
 
 def test_single_image_entry_matches_varlen_bitwise():
