@@ -476,26 +476,44 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
   if constexpr (EPI == VIT_EPI_STORE_ROPE || EPI == VIT_EPI_QKV_VT) {
     // each pair of 32-wide blocks (2h, 2h+1) is one 64-wide head: block 2h
     // holds the row-angle half, block 2h+1 the column-angle half; the
-    // rotate_half partners (columns c and c+16 of a block) sit in one lane
+    // rotate_half partners (columns c and c+16 of a block) sit in one lane.
+    // The lane's table entries (16 cos/sin pairs per row: its 4-column groups
+    // c4 + 8 gq + 16 half) are all loaded before any is used, so the loads of
+    // every row block are in flight together.
+    if (n0 + wn * TN < g.rope_cols) {
+      f32x4 cs[BI][2][2][2];
 #pragma unroll
-    for (int i = 0; i < BI; ++i) {
-      const int m = min(m0 + wm * TM + i * 32 + fr, M - 1);
-      const float2* tab = (const float2*)g.rope_table + (int64_t)m * 32;
-#pragma unroll
-      for (int h = 0; h < BJ / 2; ++h) {
-        if (n0 + wn * TN + h * 64 >= g.rope_cols) continue;
+      for (int i = 0; i < BI; ++i) {
+        const int m = min(m0 + wm * TM + i * 32 + fr, M - 1);
+        const float* tab = (const float*)g.rope_table + (int64_t)m * 64;
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int gq = 0; gq < 2; ++gq)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float2 cs = tab[half * 16 + 8 * gq + c4 + r];
-              const float a1 = acc[i][2 * h + half][4 * gq + r];
-              const float a2 = acc[i][2 * h + half][4 * (gq + 2) + r];
-              acc[i][2 * h + half][4 * gq + r] = a1 * cs.x - a2 * cs.y;
-              acc[i][2 * h + half][4 * (gq + 2) + r] = a2 * cs.x + a1 * cs.y;
-            }
+            for (int q = 0; q < 2; ++q)
+              cs[i][half][gq][q] = *reinterpret_cast<const f32x4*>(
+                  tab + 2 * (half * 16 + 8 * gq + c4) + 4 * q);
+      }
+#pragma unroll
+      for (int i = 0; i < BI; ++i) {
+#pragma unroll
+        for (int h = 0; h < BJ / 2; ++h) {
+          if (n0 + wn * TN + h * 64 >= g.rope_cols) continue;
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int gq = 0; gq < 2; ++gq)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float c = cs[i][half][gq][r / 2][2 * (r % 2)];
+                const float sn = cs[i][half][gq][r / 2][2 * (r % 2) + 1];
+                const float a1 = acc[i][2 * h + half][4 * gq + r];
+                const float a2 = acc[i][2 * h + half][4 * (gq + 2) + r];
+                acc[i][2 * h + half][4 * gq + r] = a1 * c - a2 * sn;
+                acc[i][2 * h + half][4 * (gq + 2) + r] = a2 * c + a1 * sn;
+              }
+        }
       }
     }
   }
