@@ -149,6 +149,26 @@ vit_status vit_encode_varlen(const vit_config* cfg, const vit_weights* w, const 
                              const int32_t* grid_hw_host, int32_t n_images, int32_t flags,
                              void* out, void* ws, size_t ws_bytes, void* stream);
 
+/* vit_encode_varlen for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and output, with the workspace taken from a fixed array that
+ * the library holds on every GPU it runs on (VIT_NOALLOC_WORKSPACE_MAX bytes,
+ * from the library's load until the process ends) instead of a caller buffer.
+ * The call itself allocates nothing and launches the same kernels.
+ *   Limits: calls whose vit_workspace_bytes() exceeds the maximum return
+ *   VIT_E_WORKSPACE (with a message naming both sizes) and enqueue nothing.
+ *   Sharing: every call on one GPU uses that GPU's one array, which keeps the last
+ *   call's contents (each call initialises what it needs); calls that overlap on
+ *   one GPU (other streams or threads) race and must be serialised by the caller.
+ *   The stream must belong to the calling thread's current device.
+ * Other arguments and errors as vit_encode_varlen. */
+#define VIT_NOALLOC_WORKSPACE_MAX ((size_t)160 << 20)
+vit_status vit_encode_varlen_noalloc(const vit_config* cfg, const vit_weights* w, const void* in,
+                                     const int32_t* grid_hw_host, int32_t n_images,
+                                     int32_t flags, void* out, void* stream);
+/* VIT_NOALLOC_WORKSPACE_MAX as built into the library. */
+size_t vit_noalloc_workspace_limit(void);
+
 /* Index arrays of one image's aligner layout (the "permutation" and "N-layout"
  * columns of the PR #3772 parity table).  All device int32:
  *   perm    [grid_h*grid_w]: slot 4t+s of merged token t holds patch perm[4t+s];

@@ -77,6 +77,9 @@ SIGNATURES = {
                            c_i32, c_i32, c_vp, c_vp, c_size, c_vp]),
     "vit_encode_varlen": (c_i32, [ctypes.POINTER(VitConfig), ctypes.POINTER(VitWeights), c_vp,
                                   P_i32, c_i32, c_i32, c_vp, c_vp, c_size, c_vp]),
+    "vit_encode_varlen_noalloc": (c_i32, [ctypes.POINTER(VitConfig), ctypes.POINTER(VitWeights),
+                                          c_vp, P_i32, c_i32, c_i32, c_vp, c_vp]),
+    "vit_noalloc_workspace_limit": (c_size, []),
     "vit_aligner_layout": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "vit_rmsnorm": (c_i32, [c_vp, c_vp, c_f32, c_i64, c_i32, c_i32, c_vp, c_vp]),
     "vit_rope_table": (c_i32, [P_i32, c_i32, c_i32, c_f32, c_vp, c_vp]),

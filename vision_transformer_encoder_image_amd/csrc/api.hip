@@ -679,6 +679,36 @@ MergerPlan merger_plan(const vit_merger& m, const VarlenDesc& d) {
 
 }  // namespace
 
+// Workspace of vit_encode_varlen_noalloc: one array in the library's device
+// image, so every GPU the library runs on holds its own copy (from module load
+// until the process ends) and no call allocates.  Host code never uses the
+// array's name as a device address: its address on each device is taken once
+// with hipGetSymbolAddress (device current) and kept per device.
+static constexpr size_t kScratchBytes = (size_t)160 << 20;
+static_assert(kScratchBytes == VIT_NOALLOC_WORKSPACE_MAX, "header and library agree");
+static __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first
+// call on that device).
+static vit_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  VIT_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) return fail(VIT_E_ARG, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    VIT_TRY(hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch address"));
+    if (!p) return fail(VIT_E_HIP, "scratch address is NULL on device %d", dev);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VIT_OK;
+}
+
 extern "C" {
 
 const char* vit_status_str(int32_t st) {
@@ -727,6 +757,26 @@ vit_status vit_encode_varlen(const vit_config* cfg, const vit_weights* w, const 
   return encode_impl(cfg, w, in, grid_hw_host, n_images, flags, out, ws, ws_bytes,
                      (hipStream_t)stream);
 }
+
+vit_status vit_encode_varlen_noalloc(const vit_config* cfg, const vit_weights* w, const void* in,
+                                     const int32_t* grid_hw_host, int32_t n_images,
+                                     int32_t flags, void* out, void* stream) {
+  const size_t need = vit_workspace_bytes(cfg, grid_hw_host, n_images, flags);
+  if (need == 0)  // invalid arguments: encode_impl reports which
+    return encode_impl(cfg, w, in, grid_hw_host, n_images, flags, out, nullptr, 0,
+                       (hipStream_t)stream);
+  if (need > kScratchBytes)
+    return fail(VIT_E_WORKSPACE,
+                "this call needs %zu bytes of workspace; vit_encode_varlen_noalloc holds at "
+                "most %zu (call vit_encode_varlen with a workspace instead)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  VIT_TRY(scratch_on_current_device(&ws));
+  return encode_impl(cfg, w, in, grid_hw_host, n_images, flags, out, ws, kScratchBytes,
+                     (hipStream_t)stream);
+}
+
+size_t vit_noalloc_workspace_limit(void) { return kScratchBytes; }
 
 vit_status vit_aligner_layout(int32_t grid_h, int32_t grid_w, int32_t merge, int32_t* perm,
                               int32_t* nl_type, int32_t* nl_src, void* stream) {
