@@ -148,8 +148,9 @@ vit_status build_desc(const int32_t* grid_hw, int32_t n_images, int q_tile, bool
 struct Plan {
   int64_t P = 0, tokens = 0, Kp = 0, hp = 0;
   size_t table = 0, xpad = 0, wpe = 0, x = 0, n = 0, qkv = 0, act = 0, G = 0, rowmap = 0;
-  size_t vt = 0, vpos = 0, u = 0, ss = 0;
+  size_t vt = 0, vpos = 0, u = 0, ss = 0, arows = 0;
   int64_t kv_total = 0;
+  bool fuse_gather = false;  // bf16 aligner reads its 2x2 groups straight from n
   bool use_vt = false;  // bf16, head_dim 64: V written transposed by the wqkv GEMM
   bool pack_vt = false;  // bf16, head_dim 72: V transposed by a pack pass after the rotary
   bool fuse_norm = false;  // bf16, vision_dim % 64 == 0: RMSNorm folded into the GEMMs
@@ -184,7 +185,9 @@ Plan make_plan(const vit_config& c, const VarlenDesc& desc, int flags) {
     p.xpad = take((size_t)P * p.Kp * es);  // fp32 patches cut from the pixels
   }
   p.x = take((size_t)P * d * sizeof(float));
-  p.n = take((size_t)P * d * es);  // also holds the attention output
+  // also holds the attention output; one more row stays zero for the padded
+  // 2x2 groups of the aligner's gathered operand
+  p.n = take((size_t)(P + 1) * d * es);
   p.qkv = take((size_t)P * 3 * d * es);
   p.act = take((size_t)P * p.hp * es);
   p.use_vt = c.dtype == VIT_BF16 && c.head_dim == 64;
@@ -199,6 +202,13 @@ Plan make_plan(const vit_config& c, const VarlenDesc& desc, int flags) {
     p.u = take((size_t)P * d * es);                     // bf16(x * norm weight)
     p.ss = take((size_t)P * round_up(d / 64, 4) * sizeof(float));  // partial sums of x^2
   }
+  // bf16 with 64-multiple widths: the aligner GEMM gathers each merged token's
+  // four patch rows itself (source rows per token); otherwise a gather pass
+  // writes G [tokens, 4d] first
+  // (G stays reserved for operands the GEMM's loader cannot take: unaligned
+  // aligner weight or output)
+  p.fuse_gather = aligner && c.dtype == VIT_BF16 && c.merge == 2 && d % 64 == 0;
+  if (p.fuse_gather) p.arows = take((size_t)p.tokens * 4 * sizeof(int32_t));
   if (aligner) p.G = take((size_t)p.tokens * m2 * d * es);
   if (aligner && (flags & VIT_OUT_NLAYOUT)) p.rowmap = take((size_t)p.tokens * sizeof(int32_t));
   p.total = off;
@@ -355,6 +365,9 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
       pa.vt = vt;
       pa.vt_rows = p.use_vt ? d : 0;
       pa.vt_ld = p.kv_total;
+      pa.a_rows = p.fuse_gather ? (int32_t*)(base + p.arows) : nullptr;
+      pa.tokens = p.tokens;
+      pa.zrow = p.fuse_gather ? (char*)n + (size_t)P * d * 2 : nullptr;
       VIT_HIP(launch_encode_prep(pa, s), "encode preparation");
       GemmArgs g = gemm_args(xpad, p.Kp, wpe, nullptr, p.Kp, x, d, P, d, p.Kp, nullptr);
       if (fuse) producer(g, w->norm1[0]);
@@ -475,16 +488,31 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
   }
   if (!aligner) return VIT_OK;
 
-  void* G = base + p.G;
   const int64_t m2 = (int64_t)c.merge * c.merge;
-  {
-    ProfScope ps(VIT_K_GATHER, s);
-    VIT_HIP(launch_gather(dt, n, desc, (int)d, c.merge, G, s), "aligner gather");
-  }
   int32_t* rowmap = nullptr;
   if (flags & VIT_OUT_NLAYOUT) {
     rowmap = (int32_t*)(base + p.rowmap);
     VIT_HIP(launch_nl_rowmap(desc, c.merge, rowmap, s), "newline row map");
+  }
+  if (p.fuse_gather) {
+    // the A operand's row t is the final-normed patch rows a_rows[4t .. 4t+3]
+    // (TL, TR, BL, BR; row P of n is zero for padded groups), read by the GEMM's
+    // own loader: no G buffer and no gather pass
+    GemmArgs g = gemm_args(n, d, w->aligner, nullptr, m2 * d, out, c.llm_dim, p.tokens,
+                           c.llm_dim, m2 * d, rowmap);
+    g.a_rows = (const int32_t*)(base + p.arows);
+    g.a_seg = d;
+    g.a_src_rows = P + 1;
+    if (gemm_bf16_mfma_eligible(g)) {
+      ProfScope ps(VIT_K_ALIGNER, s);
+      VIT_HIP(launch_gemm_bf16(VIT_EPI_STORE_GATHER, g, s), "aligner gemm");
+      return VIT_OK;
+    }
+  }
+  void* G = base + p.G;
+  {
+    ProfScope ps(VIT_K_GATHER, s);
+    VIT_HIP(launch_gather(dt, n, desc, (int)d, c.merge, G, s), "aligner gather");
   }
   {
     ProfScope ps(VIT_K_ALIGNER, s);

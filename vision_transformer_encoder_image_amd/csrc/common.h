@@ -167,6 +167,12 @@ struct GemmArgs {
   float rms_inv_dim;
   // fp32 per-column bias of VIT_EPI_BIAS / VIT_EPI_BIAS_GELU ([N])
   const float* bias;
+  // Gathered A rows (VIT_EPI_STORE_GATHER): A is a [a_src_rows, lda] source
+  // matrix and logical row m of the GEMM's A operand is the concatenation of
+  // source rows a_rows[4m + s], s = 0..3, each a_seg columns wide (K = 4 a_seg).
+  const int32_t* a_rows;
+  int64_t a_seg;
+  int64_t a_src_rows;
 };
 
 // Largest number of 64-column groups (vision_dim / 64) the folded RMSNorm takes.
@@ -178,6 +184,10 @@ constexpr int VIT_EPI_STORE_ROPE = 16;
 // Internal epilogue: as VIT_EPI_STORE_ROPE for the q, k columns (C holds [M, rope_cols])
 // while the v columns are written transposed, one row per (head, dim), into vt.
 constexpr int VIT_EPI_QKV_VT = 17;
+// Internal epilogue: bf16 store (as VIT_EPI_STORE) of a GEMM whose A operand is
+// gathered row by row from four source rows (the aligner's 2x2 merge read
+// straight from the normed patch rows; GemmArgs::a_rows).
+constexpr int VIT_EPI_STORE_GATHER = 18;
 
 hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s);
 // two independent GEMMs with one epilogue, in one launch when both take the MFMA path
@@ -229,7 +239,12 @@ struct PrepArgs {
   int32_t* vpos;        // [P]
   void* vt;             // [vt_rows, vt_ld]
   int64_t vt_rows, vt_ld;
-  int64_t b[5];
+  // merged-token source rows for the aligner's gathered A operand ([tokens, 4],
+  // source row P = the zero row zrow) and that zero row ([d] bf16)
+  int32_t* a_rows;
+  int64_t tokens;
+  void* zrow;
+  int64_t b[7];
 };
 hipError_t launch_encode_prep(PrepArgs a, hipStream_t s);
 // pixel images (see VIT_IN_PIXELS) -> patches [P, ld_dst] (zero past 3*ps^2)

@@ -265,10 +265,32 @@ __global__ void patchify_kernel(const T* __restrict__ pix, VarlenDesc d, int ps,
   patchify_elem(pix, d, ps, ld_dst, dst, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
+// Source rows of merged token t's 2x2 group for the aligner's gathered A
+// operand: a_rows[4t + s] = patch row of the group's s-th patch (TL, TR, BL, BR;
+// the aligner's row-major order inside the group), or `zero_row` where an odd
+// grid is zero-padded to even (VIT_ALIGN_PAD).
+VIT_DEV void aligner_rows_elem(const VarlenDesc& d, int32_t zero_row, int32_t* a_rows,
+                               int64_t idx) {
+  const int64_t tokens = d.cu_tokens[d.n_images];
+  if (idx >= tokens * 4) return;
+  const int64_t t = idx / 4;
+  const int s = (int)(idx % 4);
+  int img = 0;
+  while (img + 1 < d.n_images && t >= d.cu_tokens[img + 1]) ++img;
+  const int tl = (int)(t - d.cu_tokens[img]);
+  const int gw = d.grid_w[img];
+  const int gh = (d.cu_seqlens[img + 1] - d.cu_seqlens[img]) / gw;
+  const int wq = (gw + 1) / 2;  // merged columns (odd grids zero-padded)
+  const int r = 2 * (tl / wq) + s / 2, c = 2 * (tl % wq) + s % 2;
+  a_rows[idx] = (r < gh && c < gw) ? d.cu_seqlens[img] + r * gw + c : zero_row;
+}
+
 // Everything an encode call prepares before the patch embedding, in one
 // launch: block ranges [0, b[0]) pad the patches, [b[0], b[1]) pad the
 // patch-embedding weight, [b[1], b[2]) build the rotary table, [b[2], b[3])
-// the transposed-V positions and [b[3], b[4]) zero the transposed-V padding.
+// the transposed-V positions, [b[3], b[4]) zero the transposed-V padding,
+// [b[4], b[5]) the aligner's merged-token source rows and [b[5], b[6]) zero the
+// row those name for padding.
 __global__ __launch_bounds__(kThreads) void encode_prep_kernel(PrepArgs a) {
   const int64_t b = blockIdx.x;
   const int t = threadIdx.x;
@@ -293,6 +315,11 @@ __global__ __launch_bounds__(kThreads) void encode_prep_kernel(PrepArgs a) {
     const int64_t i = (b - a.b[3]) * kThreads + t;
     vt_zero_pads_elem(a.desc, a.vt_rows, (bf16*)a.vt, a.vt_ld, i / (VT_ALIGN + 16),
                       (int)(i % (VT_ALIGN + 16)));
+  } else if (b < a.b[5]) {
+    aligner_rows_elem(a.desc, (int32_t)a.P, a.a_rows, (b - a.b[4]) * kThreads + t);
+  } else if (b < a.b[6]) {
+    const int64_t i = (b - a.b[5]) * kThreads + t;  // 8 bf16 per thread
+    if (i < a.d / 8) reinterpret_cast<u32x4*>(a.zrow)[i] = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -528,14 +555,17 @@ hipError_t launch_encode_prep(PrepArgs a, hipStream_t s) {
   if (a.table && a.head_dim / 4 > kRopeMaxFreqs) return hipErrorInvalidValue;
   a.pix_rows = a.pixel_ps > 0 && a.pixel_ps % 2 == 0 && a.Kp % 2 == 0 &&
                ((uintptr_t)a.patches & 3) == 0 && ((uintptr_t)a.xpad & 3) == 0;
-  const int64_t n[5] = {a.patches ? a.P * (a.pix_rows ? 3 * a.pixel_ps + 1
+  const int64_t n[7] = {a.patches ? a.P * (a.pix_rows ? 3 * a.pixel_ps + 1
                                            : a.pixel_ps > 0 ? a.Kp : a.Kp / 4) : 0,
                         a.w_pe ? a.d * (a.Kp / 4) : 0,
                         a.table ? (int64_t)a.desc.total * (a.head_dim / 2) : 0,
                         a.vpos ? (int64_t)a.desc.total : 0,
-                        a.vt ? a.vt_rows * (VT_ALIGN + 16) : 0};
+                        a.vt ? a.vt_rows * (VT_ALIGN + 16) : 0,
+                        a.a_rows ? a.tokens * 4 : 0,
+                        a.zrow ? a.d / 8 : 0};
+  if (a.zrow && (a.d % 8 || ((uintptr_t)a.zrow & 15))) return hipErrorInvalidValue;
   int64_t acc = 0;
-  for (int i = 0; i < 5; ++i) {
+  for (int i = 0; i < 7; ++i) {
     acc += (n[i] + kThreads - 1) / kThreads;
     a.b[i] = acc;
   }

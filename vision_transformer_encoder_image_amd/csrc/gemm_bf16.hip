@@ -241,9 +241,14 @@ bool pipe_eligible(const GemmArgs& g) {
                        (uintptr_t)g.C;
   // the copies address A and B with 32-bit byte offsets from the matrix base
   const int64_t lim = (int64_t)1 << 32;
+  // a gathered A operand: four source segments of a_seg columns (multiples of the
+  // K-tile), rows addressed inside its a_src_rows x lda source matrix
+  const bool gather_ok = !g.a_rows || (g.a_seg > 0 && g.a_seg % 64 == 0 && g.K == 4 * g.a_seg &&
+                                       g.lda >= g.a_seg && ((uintptr_t)g.a_rows & 15) == 0 &&
+                                       g.a_src_rows > 0 && g.a_src_rows * g.lda * 2 < lim);
   return g.K % 64 == 0 && g.kb % 8 == 0 && g.kb <= g.K && g.N % 4 == 0 && g.ldc % 4 == 0 &&
-         g.lda % 8 == 0 && g.ldb % 8 == 0 && (al & 15) == 0 && g.M * g.lda * 2 < lim &&
-         g.N * g.ldb * 2 < lim;
+         g.lda % 8 == 0 && g.ldb % 8 == 0 && (al & 15) == 0 &&
+         (g.a_rows || g.M * g.lda * 2 < lim) && g.N * g.ldb * 2 < lim && gather_ok;
 }
 
 }  // namespace
@@ -328,7 +333,8 @@ GemmSplit gemm_mfma_split(int epilogue, bool norm_producer, int64_t M, int64_t N
   best.cfg_main = best_tile(epilogue, norm_producer, M, N, &best_cost);
   best.n_main = N;
   best.cfg_tail = -1;
-  const bool col_free = epilogue == VIT_EPI_STORE || epilogue == VIT_EPI_STORE_F32 ||
+  const bool col_free = epilogue == VIT_EPI_STORE || epilogue == VIT_EPI_STORE_GATHER ||
+                        epilogue == VIT_EPI_STORE_F32 ||
                         epilogue == VIT_EPI_ADD_F32 || epilogue == VIT_EPI_SWIGLU ||
                         epilogue == VIT_EPI_BIAS || epilogue == VIT_EPI_BIAS_GELU;
   if (!col_free || norm_producer) return best;
@@ -398,7 +404,9 @@ hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s) {
   const bool rope = epilogue == VIT_EPI_STORE_ROPE || epilogue == VIT_EPI_QKV_VT;
   const bool norm = g.norm_w != nullptr || g.ss_in != nullptr;
   const bool bias = epilogue == VIT_EPI_BIAS || epilogue == VIT_EPI_BIAS_GELU;
-  if ((rope || norm || bias) && !pipe_eligible(g)) return hipErrorInvalidValue;
+  const bool gather = epilogue == VIT_EPI_STORE_GATHER;
+  if (gather != (g.a_rows != nullptr)) return hipErrorInvalidValue;
+  if ((rope || norm || bias || gather) && !pipe_eligible(g)) return hipErrorInvalidValue;
   if (bias && (!g.bias || norm)) return hipErrorInvalidValue;
   if (g.ss_in && (g.ss_groups < 1 || g.ss_groups > kMaxNormGroups)) return hipErrorInvalidValue;
   if (g.norm_w && (g.N % 64 != 0 || !g.norm_out || !g.ss_out ||

@@ -116,7 +116,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
   // row, because B's K index is clamped to its valid width per K-tile.
   constexpr int NIA = BM / (RPC * NW);
   static_assert(BM % (RPC * NW) == 0, "A/B copy split");
+  // gathered A (the aligner's 2x2 merge): A row m is source rows a_rows[4m + s],
+  // s = 0..3, side by side; every K-tile lies in one a_seg-wide segment s, so a
+  // copy slot keeps the byte offsets of its four source rows and picks one per
+  // K-tile
+  constexpr bool kGather = EPI == VIT_EPI_STORE_GATHER;
   uint32_t voff[NI];
+  uint32_t vga[kGather ? NIA : 1][4];
   int kcol[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -124,7 +130,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
     const int row = RPC * q + lane / CPR;
     kcol[i] = ((lane % CPR) ^ chunk_swz<BK>(row)) * 8;
     if (i < NIA) {
-      voff[i] = (uint32_t)(((int64_t)min(m0 + row, M - 1) * g.lda + kcol[i]) * 2);
+      if constexpr (kGather) {
+        const int4 r4 = *reinterpret_cast<const int4*>(g.a_rows + 4 * (int64_t)min(m0 + row, M - 1));
+        const int src[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+        for (int sg = 0; sg < 4; ++sg)
+          vga[i < NIA ? i : 0][sg] = (uint32_t)(((int64_t)src[sg] * g.lda + kcol[i]) * 2);
+        voff[i] = 0;
+      } else {
+        voff[i] = (uint32_t)(((int64_t)min(m0 + row, M - 1) * g.lda + kcol[i]) * 2);
+      }
     } else {
       const int r = row - BM;
       int brow = n0 + r;
@@ -135,12 +150,26 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
   // copy K-tile kt_ into LDS buffer `stage` (a constant).  A may be zero-padded
   // past B's valid K (KB); B's K index is clamped into [0, KB) so its reads
   // stay inside its rows (the products with A's zero columns vanish).
+  // segment seg_ of the gathered A operand holding K offset k0_, and the offset
+  // kin_ inside it (unused without the gather)
+  const int segk = kGather ? (int)g.a_seg : 1;
+#define W_SEG(k0_)                                                                      \
+  const int seg_ = kGather ? __builtin_amdgcn_readfirstlane((k0_) / segk) : 0;          \
+  const int kin_ = (k0_) - seg_ * segk;                                                 \
+  (void)seg_;                                                                           \
+  (void)kin_
   // copy i of K-tile k0_/BK (k0_ a scalar) into the LDS buffer at dst_
 #define W_COPY1(k0_, dst_, i)                                                           \
   do {                                                                                  \
     const int q_ = wave + NW * (i);                                                     \
     if ((i) < NIA) {                                                                    \
-      copy16_to_lds((const char*)A + 2 * (int64_t)(k0_) + voff[i], (dst_) + q_ * 512);  \
+      if constexpr (kGather) {                                                          \
+        const uint32_t* v_ = vga[(i) < NIA ? (i) : 0];                                  \
+        const uint32_t o_ = seg_ == 0 ? v_[0] : seg_ == 1 ? v_[1] : seg_ == 2 ? v_[2] : v_[3]; \
+        copy16_to_lds((const char*)A + 2 * (int64_t)kin_ + o_, (dst_) + q_ * 512);       \
+      } else {                                                                          \
+        copy16_to_lds((const char*)A + 2 * (int64_t)(k0_) + voff[i], (dst_) + q_ * 512); \
+      }                                                                                 \
     } else {                                                                            \
       const char* b_ = (const char*)((DUAL && ((RPC * q_ - BM) % TN) >= TN / 2) ? B2 : B); \
       copy16_to_lds(b_ + (voff[i] + 2u * (uint32_t)min((k0_) + kcol[i], KB - 8)),        \
@@ -153,6 +182,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
     /* readfirstlane keeps the K offset a scalar: strength reduction would */           \
     /* otherwise turn every copy address into a 64-bit vector induction variable */     \
     const int k0_ = __builtin_amdgcn_readfirstlane((kt_) * BK);                         \
+    W_SEG(k0_);                                                                         \
     bf16* dst_ = smem + (stage) * ROWS * BK;                                            \
     _Pragma("unroll") for (int i = 0; i < NI; ++i) W_COPY1(k0_, dst_, i);               \
   } while (0)
@@ -222,6 +252,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
     constexpr int NM_ = BI * BJ;                                                        \
     const bool iss_ = (kt_) < nk;                                                       \
     const int k0_ = __builtin_amdgcn_readfirstlane((kt_) * BK);                         \
+    W_SEG(k0_);                                                                         \
     bf16* dst_ = smem + (stage) * ROWS * BK;                                            \
     _Pragma("unroll") for (int x = 0; x < NM_; ++x) {                                   \
       acc[x / BJ][x % BJ] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                    \
@@ -329,6 +360,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
 #undef W_PRELOAD
 #undef W_ISSUE
 #undef W_COPY1
+#undef W_SEG
 
   // ---- epilogue: acc[i][j] lane holds row (lane & 31) of block i and, for
   // gq = 0..3, columns 8gq + 4*(lane >> 5) .. +3 of block j ----
@@ -774,6 +806,8 @@ template <int BM, int BN, int BK, int WM, int WN, int STAGES>
 hipError_t mfma_epi(int epi, const GemmArgs& g, hipStream_t s, const GemmArgs* g1 = nullptr) {
   switch (epi) {
     case VIT_EPI_STORE: return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_STORE, false>(g, s, g1);
+    case VIT_EPI_STORE_GATHER:
+      return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_STORE_GATHER, false>(g, s, g1);
     case VIT_EPI_STORE_F32:
       return mfma_cfg<BM, BN, BK, WM, WN, STAGES, VIT_EPI_STORE_F32, false>(g, s, g1);
     case VIT_EPI_ADD_F32:
