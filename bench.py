@@ -32,7 +32,7 @@ KERNEL_SOURCE = {"qkv": _GEMM_SRC, "outproj": _GEMM_SRC, "gateup": _GEMM_SRC, "d
                  "embed": _GEMM_SRC, "aligner": _GEMM_SRC, "attn": ("common.h", "attention.hip"),
                  "rmsnorm": ("common.h", "elementwise.hip"), "rope": ("common.h", "elementwise.hip"),
                  "gather": ("common.h", "elementwise.hip"), "merge": ("common.h", "merge.hip"),
-                 "proj1": _GEMM_SRC}
+                 "proj1": _GEMM_SRC, "attn72": ("common.h", "attention.hip")}
 
 
 def class_flops(cfg):
@@ -47,10 +47,17 @@ def class_flops(cfg):
 
 
 def class_bytes(cfg):
-    """Algorithmic HBM bytes per launch of the bandwidth-bound classes (bf16 activations)."""
+    """Algorithmic HBM bytes per launch of the bandwidth-bound classes (bf16 activations).
+    With head_dim 72 the rotary class is one pass that rotates q and k in place and
+    writes V transposed: q, k read and written, V read, V^T written (each image's keys
+    padded to a multiple of 64), the table read."""
     P, d, D, H = cfg.total_patches, cfg.vision_dim, cfg.head_dim, cfg.n_heads
+    rope = 2 * (2 * P * H * D * 2) + P * (D // 2) * 8
+    if D == 72 and cfg.dtype == "bf16":
+        kv = sum((p + 63) // 64 * 64 for p in cfg.seqlens)
+        rope += P * d * 2 + kv * d * 2
     return {"rmsnorm": P * d * 4 + P * d * 2 + d * 4,        # fp32 residual in, bf16 out, scale
-            "rope": 2 * (2 * P * H * D * 2) + P * (D // 2) * 8,  # q,k read+write, table read
+            "rope": rope,
             "gather": 2 * P * d * 2}
 
 
@@ -75,6 +82,7 @@ def counter_traffic(kernel_class, workload):
 # kernel-name patterns of each class in rocprofv3 output (SwiGLU is the only
 # dual-B GEMM instantiation, i.e. the template argument list ends in "true>")
 KERNEL_NAME_PATTERN = {"gateup": ("gemm_", ", true>("), "attn": ("attn_vt_kernel", ""),
+                       "attn72": ("attn_bf16_kernel<72", ""), "rope": ("tpack_kernel<72, true>", ""),
                        "rmsnorm": ("rmsnorm_kernel", ""), "merge": ("merge_copy_kernel", ""),
                        "proj1": ("gemm_mfma_kernel", ", 5, false>(")}
 
@@ -116,10 +124,44 @@ def pmc_summary(fetch_dir, write_dir, kernel, workload, copy_mb, out_path=None):
         out[counter.lower() + "_launches"] = sum(len(v) for v in by_name.values())
         out[counter.lower() + "_kernels_per_call"] = len(by_name)
     out["hbm_bytes_per_launch"] = out["fetch_size_bytes_per_launch"] + out["write_size_bytes_per_launch"]
+    try:
+        from vision_transformer_encoder_image_amd import configs
+        alg = class_bytes(configs.get(workload)).get(kernel)
+    except (KeyError, ValueError):
+        alg = None
+    if alg:
+        out["algorithmic_bytes_per_launch"] = alg
+        out["ratio_hbm_to_algorithmic"] = out["hbm_bytes_per_launch"] / alg
     path = out_path or os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+
+
+def trace_summary(trace_dir, out_path, title, command):
+    """Per-kernel table (calls, average / min / max duration, share of GPU time) from a
+    rocprofv3 --kernel-trace --stats run's kernel_stats.csv."""
+    import csv
+    import glob
+
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    if not rows:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"# rocprofv3 kernel statistics — {title}", "",
+             "Command (repo root, MI355X, `export TMPDIR=/tmp`):", "", "```", command, "```", "",
+             "| Kernel | Calls | Avg (us) | Min (us) | Max (us) | Share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        n = r["Name"].replace("void (anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+        lines.append(f"| `{n[:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def mfma_util_summary(pmc_dir, out_path):
@@ -732,7 +774,13 @@ def main():
                     help="summarise a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE run "
                          "of this script into a per-kernel MFMA-utilisation table and exit")
     ap.add_argument("--pmc-out", default=None, help="output path for --pmc-summary")
+    ap.add_argument("--trace-summary", nargs=4, metavar=("TRACE_DIR", "OUT", "TITLE", "COMMAND"),
+                    help="summarise a rocprofv3 --kernel-trace --stats run into a markdown table "
+                         "and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
+        return
     if args.mfma_summary:
         mfma_util_summary(args.mfma_summary[0], args.mfma_summary[1])
         return

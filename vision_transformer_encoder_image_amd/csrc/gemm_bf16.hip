@@ -269,17 +269,26 @@ struct TileOpt {
   int cfg, bm, bn;
   double eff;
   bool ok;
+  int per_cu;  // workgroups that fit on one CU at once (LDS)
 };
 
 constexpr int kCUs = 256;
+constexpr int kTileOpts = 5;
 
+// The 2-wave 64x64 tile (64 KB of LDS, two workgroups per CU) is ~0.33x as
+// efficient per flop, fitted to the 784-row encoder GEMMs of one 28x28 image:
+// out-projection 15.8 -> 12.4 us, down-projection 27.0 -> 20.9 us, aligner
+// (196 x 4096 x 4096) 29.2 -> 24.0 us, patch embedding 11.6 -> 10.2 us against
+// the 128x128 tile; on the ragged batch's shapes it loses (out-projection 25.4
+// against 20.7 us), which the model reproduces.
 int tile_opts(int epilogue, bool norm_producer, TileOpt* o) {
   const bool rmw = epilogue == VIT_EPI_ADD_F32;
-  o[0] = {GEMM_MFMA_128x128, 128, 128, rmw ? 1.04 : 1.13, true};
-  o[1] = {GEMM_MFMA_256x128_W8, 256, 128, rmw ? 1.1 : 1.18, true};
-  o[2] = {GEMM_MFMA_256x256_W8, 256, 256, 1.57, !rmw};
-  o[3] = {GEMM_MFMA_192x256, 192, 256, rmw ? 1.2 : 1.26, !norm_producer};
-  return 4;
+  o[0] = {GEMM_MFMA_128x128, 128, 128, rmw ? 1.04 : 1.13, true, 1};
+  o[1] = {GEMM_MFMA_256x128_W8, 256, 128, rmw ? 1.1 : 1.18, true, 1};
+  o[2] = {GEMM_MFMA_256x256_W8, 256, 256, 1.57, !rmw, 1};
+  o[3] = {GEMM_MFMA_192x256, 192, 256, rmw ? 1.2 : 1.26, !norm_producer, 1};
+  o[4] = {GEMM_MFMA_64x64_W2, 64, 64, rmw ? 0.33 : 0.34, true, 2};
+  return kTileOpts;
 }
 
 // output columns of one tile (the SwiGLU tile holds gate and up halves)
@@ -290,11 +299,12 @@ int64_t tile_cols(const TileOpt& o, int epilogue) {
 double tile_cost(const TileOpt& o, int epilogue, int64_t M, int64_t N) {
   const int64_t bno = tile_cols(o, epilogue);
   const int64_t tiles = ((M + o.bm - 1) / o.bm) * ((N + bno - 1) / bno);
-  return (double)((tiles + kCUs - 1) / kCUs) * o.bm * o.bn / o.eff;
+  const int64_t slots = (int64_t)kCUs * o.per_cu;
+  return (double)((tiles + slots - 1) / slots) * o.bm * o.bn / o.eff;
 }
 
 int best_tile(int epilogue, bool norm_producer, int64_t M, int64_t N, double* cost) {
-  TileOpt opts[4];
+  TileOpt opts[kTileOpts];
   const int n = tile_opts(epilogue, norm_producer, opts);
   int best = GEMM_MFMA_128x128;
   double best_cost = 1e300;
@@ -338,7 +348,7 @@ GemmSplit gemm_mfma_split(int epilogue, bool norm_producer, int64_t M, int64_t N
                         epilogue == VIT_EPI_ADD_F32 || epilogue == VIT_EPI_SWIGLU ||
                         epilogue == VIT_EPI_BIAS || epilogue == VIT_EPI_BIAS_GELU;
   if (!col_free || norm_producer) return best;
-  TileOpt opts[4];
+  TileOpt opts[kTileOpts];
   tile_opts(epilogue, norm_producer, opts);
   // largest tiles first: at equal cost the large-tile launch is the main one
   for (const int i : {2, 3, 1, 0}) {
@@ -377,7 +387,7 @@ hipError_t launch_gemm_bf16_pair(int epilogue, const GemmArgs& g0, const GemmArg
     if (e != hipSuccess) return e;
     return launch_gemm_bf16(epilogue, g1, s);
   }
-  TileOpt opts[4];
+  TileOpt opts[kTileOpts];
   tile_opts(epilogue, false, opts);
   int best = GEMM_MFMA_128x128;
   double best_cost = 1e300;
@@ -386,7 +396,8 @@ hipError_t launch_gemm_bf16_pair(int epilogue, const GemmArgs& g0, const GemmArg
     const int64_t bno = tile_cols(o, epilogue);
     const int64_t tiles = ((g0.M + o.bm - 1) / o.bm) * ((g0.N + bno - 1) / bno) +
                           ((g1.M + o.bm - 1) / o.bm) * ((g1.N + bno - 1) / bno);
-    const double c = (double)((tiles + kCUs - 1) / kCUs) * o.bm * o.bn / o.eff;
+    const int64_t slots = (int64_t)kCUs * o.per_cu;
+    const double c = (double)((tiles + slots - 1) / slots) * o.bm * o.bn / o.eff;
     if (c < best_cost) {
       best_cost = c;
       best = o.cfg;

@@ -8,7 +8,8 @@ enum GemmMfmaCfg {
   GEMM_MFMA_256x128_W8 = 1,  // 8 waves of 64x64, 3 stages of BK 64 (144 KB)
   GEMM_MFMA_256x256_W8 = 2,  // 8 waves of 128x64, 4 stages of BK 32 (128 KB)
   GEMM_MFMA_192x256 = 3,     // 4 waves of 96x128 (accumulators in AGPRs), 4 stages of BK 32 (112 KB)
-  GEMM_MFMA_NCFG = 4,
+  GEMM_MFMA_64x64_W2 = 4,    // 2 waves of 32x64, 4 stages of BK 64 (64 KB: two workgroups per CU)
+  GEMM_MFMA_NCFG = 5,
 };
 
 // g1 (optional): a second GEMM of the same configuration and epilogue in the

@@ -152,20 +152,30 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
   // stay inside its rows (the products with A's zero columns vanish).
   // segment seg_ of the gathered A operand holding K offset k0_, and the offset
   // kin_ inside it (unused without the gather)
+  // (k0_ / a_seg as a multiply-high by ceil(2^32 / a_seg), exact for k0_ * a_seg
+  // < 2^32; the segment's four offset masks select a copy slot's source row
+  // without branches)
   const int segk = kGather ? (int)g.a_seg : 1;
+  const uint32_t seg_magic = kGather ? (uint32_t)(((1ull << 32) + segk - 1) / segk) : 0u;
 #define W_SEG(k0_)                                                                      \
-  const int seg_ = kGather ? __builtin_amdgcn_readfirstlane((k0_) / segk) : 0;          \
+  const int seg_ = kGather ? (int)(((uint64_t)(uint32_t)(k0_) * seg_magic) >> 32) : 0;  \
   const int kin_ = (k0_) - seg_ * segk;                                                 \
-  (void)seg_;                                                                           \
-  (void)kin_
+  const uint32_t sm0_ = seg_ == 0 ? ~0u : 0u, sm1_ = seg_ == 1 ? ~0u : 0u;              \
+  const uint32_t sm2_ = seg_ == 2 ? ~0u : 0u, sm3_ = seg_ == 3 ? ~0u : 0u;              \
+  (void)kin_;                                                                           \
+  (void)sm0_;                                                                           \
+  (void)sm1_;                                                                           \
+  (void)sm2_;                                                                           \
+  (void)sm3_
   // copy i of K-tile k0_/BK (k0_ a scalar) into the LDS buffer at dst_
 #define W_COPY1(k0_, dst_, i)                                                           \
   do {                                                                                  \
     const int q_ = wave + NW * (i);                                                     \
     if ((i) < NIA) {                                                                    \
       if constexpr (kGather) {                                                          \
-        const uint32_t* v_ = vga[(i) < NIA ? (i) : 0];                                  \
-        const uint32_t o_ = seg_ == 0 ? v_[0] : seg_ == 1 ? v_[1] : seg_ == 2 ? v_[2] : v_[3]; \
+        const int ia_ = (i) < NIA ? (i) : 0;                                            \
+        const uint32_t o_ = (vga[ia_][0] & sm0_) | (vga[ia_][1] & sm1_) |               \
+                            (vga[ia_][2] & sm2_) | (vga[ia_][3] & sm3_);                \
         copy16_to_lds((const char*)A + 2 * (int64_t)kin_ + o_, (dst_) + q_ * 512);       \
       } else {                                                                          \
         copy16_to_lds((const char*)A + 2 * (int64_t)(k0_) + voff[i], (dst_) + q_ * 512); \
@@ -840,6 +850,7 @@ hipError_t launch_gemm_mfma(int cfg, int epi, const GemmArgs& g, hipStream_t s,
     case GEMM_MFMA_256x128_W8: return mfma_epi<256, 128, 64, 4, 2, 3>(epi, g, s, g1);
     case GEMM_MFMA_256x256_W8: return mfma_epi<256, 256, 32, 2, 4, 4>(epi, g, s, g1);
     case GEMM_MFMA_192x256: return mfma_epi<192, 256, 32, 2, 2, 4>(epi, g, s, g1);
+    case GEMM_MFMA_64x64_W2: return mfma_epi<64, 64, 64, 2, 1, 4>(epi, g, s, g1);
   }
   return hipErrorInvalidValue;
 }
