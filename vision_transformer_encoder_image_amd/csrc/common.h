@@ -161,6 +161,10 @@ struct GemmArgs {
   const float* norm_w;
   void* norm_out;
   float* ss_out;
+  // row strides of norm_out (elements) and ss_out (floats) when they differ from
+  // this launch's N and round4(N/64): a launch over a column range of a wider
+  // GEMM (norm_w, norm_out and ss_out then point at the range's first column)
+  int64_t ld_norm_out, ld_ss_out;
   const float* ss_in;
   int32_t ss_groups;
   float rms_eps;

@@ -335,8 +335,9 @@ int gemm_mfma_choice(int epilogue, bool norm_producer, int64_t M, int64_t N) {
 // second 256x256 round holding 52 of 308 tiles), one launch of large tiles
 // covers the columns that fill exactly one round and a second launch of
 // smaller tiles covers the rest.  Only epilogues whose arithmetic does not
-// depend on the absolute column take it (not the rotary, transposed-V or
-// folded-norm producer forms).
+// depend on the absolute column take it (not the rotary or transposed-V forms;
+// the folded-norm producer's second launch gets its columns' norm weights and
+// its columns of u and of the partial sums, with the full rows' strides).
 GemmSplit gemm_mfma_split(int epilogue, bool norm_producer, int64_t M, int64_t N) {
   GemmSplit best{};
   double best_cost;
@@ -347,7 +348,7 @@ GemmSplit gemm_mfma_split(int epilogue, bool norm_producer, int64_t M, int64_t N
                         epilogue == VIT_EPI_STORE_F32 ||
                         epilogue == VIT_EPI_ADD_F32 || epilogue == VIT_EPI_SWIGLU ||
                         epilogue == VIT_EPI_BIAS || epilogue == VIT_EPI_BIAS_GELU;
-  if (!col_free || norm_producer) return best;
+  if (!col_free) return best;
   TileOpt opts[kTileOpts];
   tile_opts(epilogue, norm_producer, opts);
   // largest tiles first: at equal cost the large-tile launch is the main one
@@ -439,6 +440,13 @@ hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s) {
     if (g.B2) b.B2 = (const bf16*)g.B2 + sp.n_main * g.ldb;
     b.C = (char*)g.C + sp.n_main * out_bytes;
     if (g.bias) b.bias = g.bias + sp.n_main;
+    if (g.norm_w) {  // folded-norm producer: the tail writes its columns of u and ss
+      a.ld_norm_out = b.ld_norm_out = g.ld_norm_out ? g.ld_norm_out : g.N;
+      a.ld_ss_out = b.ld_ss_out = g.ld_ss_out ? g.ld_ss_out : (g.N / 64 + 3) & ~3;
+      b.norm_w = g.norm_w + sp.n_main;
+      b.norm_out = (bf16*)g.norm_out + sp.n_main;
+      b.ss_out = g.ss_out + sp.n_main / 64;
+    }
     const hipError_t e = launch_gemm_mfma(sp.cfg_main, epilogue, a, s);
     if (e != hipSuccess) return e;
     return launch_gemm_mfma(sp.cfg_tail, epilogue, b, s);

@@ -407,6 +407,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
     constexpr bool kStageX = TM * (UROWB + XROWB) * NW <= STAGES * ROWS * BK * 2;
     const int n = n0 + wn * TN;
     const bool cols_ok = n < N;
+    const int64_t ld_nout = g.ld_norm_out ? g.ld_norm_out : N;
+    const int64_t ld_ss = g.ld_ss_out ? g.ld_ss_out : ((N / 64 + 3) & ~3);
     char* st = (char*)smem + wave * (TM * UROWB);
     char* xs = (char*)smem + NW * TM * UROWB + wave * (TM * XROWB);
     auto produce = [&](auto with_rowmap, auto with_pre) __attribute__((always_inline)) {
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
               *reinterpret_cast<bf16x4*>(st + r * UROWB + ((c16 ^ sw) << 4) + (hh << 3)) = u;
             }
           ssum = xor32_sum(ssum);
-          if (ok && fh == 0) g.ss_out[(int64_t)m * ((N / 64 + 3) & ~3) + n / 64] = ssum;
+          if (ok && fh == 0) g.ss_out[(int64_t)m * ld_ss + n / 64] = ssum;
         }
         sched_fence();
       }
@@ -511,7 +513,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
         dd[0] = dd[2]; dd[1] = dd[3]; dd[2] = t0; dd[3] = t1;
       }
       if (!cols_ok || m >= M) continue;
-      *reinterpret_cast<u32x4*>((bf16*)g.norm_out + (int64_t)m * N + n + cl * 8) = dd;
+      *reinterpret_cast<u32x4*>((bf16*)g.norm_out + (int64_t)m * ld_nout + n + cl * 8) = dd;
     }
     return;
   }
