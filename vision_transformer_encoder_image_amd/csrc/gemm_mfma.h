@@ -17,6 +17,12 @@ enum GemmMfmaCfg {
 hipError_t launch_gemm_mfma(int cfg, int epi, const GemmArgs& g, hipStream_t s,
                             const GemmArgs* g1 = nullptr);
 
+// Two GEMMs with different tile configurations (of one workgroup size) in one
+// launch: g0's tiles (cfg0) take the lower workgroup ids.  hipErrorNotSupported
+// when that pair of configurations is not built.
+hipError_t launch_gemm_mfma_pair(int cfg0, int cfg1, int epi, const GemmArgs& g0,
+                                 const GemmArgs& g1, hipStream_t s);
+
 // Launch plan of one GEMM: cfg_main over columns [0, n_main), and when
 // n_main < N a second launch of cfg_tail over [n_main, N).
 struct GemmSplit {

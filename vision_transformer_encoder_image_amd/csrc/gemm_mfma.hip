@@ -58,14 +58,9 @@ VIT_DEV float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 // GELU in its erf form, x * Phi(x)
 VIT_DEV float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
-// One launch computes one GEMM, or two independent GEMMs of the same tile
-// configuration and epilogue (a grouped launch: workgroups below tiles0 take
-// g0, the rest g1), which fills the CUs when each alone would leave many idle.
+// One output tile of GEMM g: tile L of its grid (before the XCD remap below).
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool DUAL>
-__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0, GemmArgs g1,
-                                                                    int tiles0) {
-  const bool second = (int)blockIdx.x >= tiles0;
-  const GemmArgs& g = second ? g1 : g0;
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int L) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;  // wave sub-tile
   constexpr int BI = TM / 32, BJ = TN / 32;  // 32x32 blocks per wave
@@ -93,7 +88,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
   // Workgroup ids go round-robin over the 8 XCDs; give each XCD a contiguous
   // run of the grouped tile order (kGroupM tile rows share a column band), so
   // the A rows and B columns one XCD touches stay in its own L2.
-  int L = second ? (int)blockIdx.x - tiles0 : (int)blockIdx.x;
   {
     const int per = ntiles / kXcds, rem = ntiles % kXcds;
     const int xcd = L % kXcds, idx = L / kXcds;
@@ -794,6 +788,35 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0,
     direct(std::false_type{}, std::false_type{});
 }
 
+// One launch computes one GEMM, or two independent GEMMs of the same tile
+// configuration and epilogue (a grouped launch: workgroups below tiles0 take
+// g0, the rest g1), which fills the CUs when each alone would leave many idle.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool DUAL>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(GemmArgs g0, GemmArgs g1,
+                                                                    int tiles0) {
+  if ((int)blockIdx.x < tiles0)
+    gemm_tile<BM, BN, BK, WM, WN, STAGES, EPI, DUAL>(g0, (int)blockIdx.x);
+  else
+    gemm_tile<BM, BN, BK, WM, WN, STAGES, EPI, DUAL>(g1, (int)blockIdx.x - tiles0);
+}
+
+// The two launches of a column split as one launch with two tile
+// configurations of the same thread count: workgroups below tiles0 run tiles of
+// configuration 0 over g0's columns, the rest tiles of configuration 1 over
+// g1's.  The dispatcher starts workgroups in id order, so the many short tiles
+// go first and their CUs then take the remaining long ones; the launch saves
+// the boundary between the two launches.
+template <int BM0, int BN0, int BK0, int WM0, int WN0, int S0, int BM1, int BN1, int BK1, int WM1,
+          int WN1, int S1, int EPI, bool DUAL>
+__global__ __launch_bounds__(WM0 * WN0 * 64, 1) void gemm_mfma_pair_kernel(GemmArgs g0, GemmArgs g1,
+                                                                         int tiles0) {
+  static_assert(WM0 * WN0 == WM1 * WN1, "one workgroup size");
+  if ((int)blockIdx.x < tiles0)
+    gemm_tile<BM0, BN0, BK0, WM0, WN0, S0, EPI, DUAL>(g0, (int)blockIdx.x);
+  else
+    gemm_tile<BM1, BN1, BK1, WM1, WN1, S1, EPI, DUAL>(g1, (int)blockIdx.x - tiles0);
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool DUAL>
 hipError_t mfma_cfg(const GemmArgs& g, hipStream_t s, const GemmArgs* g1 = nullptr) {
   constexpr int BNO = DUAL ? BN / 2 : BN;
@@ -855,4 +878,45 @@ hipError_t launch_gemm_mfma(int cfg, int epi, const GemmArgs& g, hipStream_t s,
     case GEMM_MFMA_64x64_W2: return mfma_epi<64, 64, 64, 2, 1, 4>(epi, g, s, g1);
   }
   return hipErrorInvalidValue;
+}
+
+namespace {
+
+template <int BM, int BN, int BK, int STAGES, bool DUAL>
+constexpr size_t gemm_lds_bytes(int epi) {
+  return (size_t)STAGES * (BM + BN) * BK * sizeof(bf16) +
+         ((epi == VIT_EPI_STORE_F32 || epi == VIT_EPI_ADD_F32) ? 0 : BM * sizeof(float));
+}
+
+template <int BM0, int BN0, int BK0, int WM0, int WN0, int S0, int BM1, int BN1, int BK1, int WM1,
+          int WN1, int S1, int EPI, bool DUAL>
+hipError_t mfma_pair_cfg(const GemmArgs& g0, const GemmArgs& g1, hipStream_t s) {
+  constexpr int BNO0 = DUAL ? BN0 / 2 : BN0, BNO1 = DUAL ? BN1 / 2 : BN1;
+  constexpr size_t l0 = gemm_lds_bytes<BM0, BN0, BK0, S0, DUAL>(EPI);
+  constexpr size_t l1 = gemm_lds_bytes<BM1, BN1, BK1, S1, DUAL>(EPI);
+  constexpr size_t lds = l0 > l1 ? l0 : l1;
+  auto kern = gemm_mfma_pair_kernel<BM0, BN0, BK0, WM0, WN0, S0, BM1, BN1, BK1, WM1, WN1, S1, EPI,
+                                    DUAL>;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int64_t tiles0 = ((g0.M + BM0 - 1) / BM0) * ((g0.N + BNO0 - 1) / BNO0);
+  const int64_t tiles1 = ((g1.M + BM1 - 1) / BM1) * ((g1.N + BNO1 - 1) / BNO1);
+  kern<<<dim3((unsigned)(tiles0 + tiles1)), dim3(WM0 * WN0 * 64), lds, s>>>(g0, g1, (int)tiles0);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_mfma_pair(int cfg0, int cfg1, int epi, const GemmArgs& g0,
+                                 const GemmArgs& g1, hipStream_t s) {
+  // the SwiGLU split of the encoder (short 128x128 tiles first, then 256x256)
+  if (cfg0 == GEMM_MFMA_128x128 && cfg1 == GEMM_MFMA_256x256_W8 && epi == VIT_EPI_SWIGLU)
+    return mfma_pair_cfg<128, 128, 64, 4, 2, 4, 256, 256, 32, 2, 4, 4, VIT_EPI_SWIGLU, true>(g0, g1,
+                                                                                           s);
+  return hipErrorNotSupported;
 }
