@@ -91,7 +91,9 @@ def test_gemm_tile_configs_sampled_rows(shape, epi):
     C = _dev(C0) if epi == "add_f32" else None
     got = to_np(api.gemm(_dev(A, "bf16"), _dev(B, "bf16"), code,
                          B2=_dev(B2, "bf16") if epi == "swiglu" else None, C=C))
-    rows = np.r_[0:3, 127:131, 191:194, 255:258, M // 2:M // 2 + 3, M - 70:M:7, M - 2:M]
+    # every third row of the first two 192-row tiles (every 32-row block of every
+    # wave of the tallest tile), then tile edges, the middle and the ragged end
+    rows = np.r_[0:384:3, 127:131, 191:194, 255:258, M // 2:M // 2 + 3, M - 70:M:7, M - 2:M]
     if epi == "swiglu":
         ref = oracle.mlp(A[rows], B, B2, np.eye(N))
     else:

@@ -286,7 +286,7 @@ int tile_opts(int epilogue, bool norm_producer, TileOpt* o) {
   o[0] = {GEMM_MFMA_128x128, 128, 128, rmw ? 1.04 : 1.13, true, 1};
   o[1] = {GEMM_MFMA_256x128_W8, 256, 128, rmw ? 1.1 : 1.18, true, 1};
   o[2] = {GEMM_MFMA_256x256_W8, 256, 256, 1.57, !rmw, 1};
-  o[3] = {GEMM_MFMA_192x256, 192, 256, rmw ? 1.2 : 1.26, !norm_producer, 1};
+  o[3] = {GEMM_MFMA_192x256, 192, 256, rmw ? 1.2 : 1.26, true, 1};
   o[4] = {GEMM_MFMA_64x64_W2, 64, 64, rmw ? 0.33 : 0.34, true, 2};
   return kTileOpts;
 }

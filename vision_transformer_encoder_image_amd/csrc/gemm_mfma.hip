@@ -65,6 +65,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int L) {
   constexpr int TM = BM / WM, TN = BN / WN;  // wave sub-tile
   constexpr int BI = TM / 32, BJ = TN / 32;  // 32x32 blocks per wave
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
+  static_assert(BI >= 1 && BJ >= 1, "wave tile");
   constexpr int KSTEPS = BK / 16;
   constexpr int CPR = BK / 8;    // 16-byte chunks per LDS row
   constexpr int RPC = 64 / CPR;  // LDS rows filled by one 1 KB wave copy
@@ -385,10 +386,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int L) {
   // load under a branch makes the compiler wait for all stores at its use).
   const bool has_rowmap = g.rowmap != nullptr;
 
-  if constexpr (kF32Out && TN == 64) if (g.norm_w) {
-    // RMSNorm producer (64-column wave sub-tiles only; the dispatcher picks
-    // such a tile).  The wave's 64 columns are one group; lanes l and l^32
-    // hold the two halves of a row's group.  x_new goes straight back to the
+  if constexpr (kF32Out && TN % 64 == 0) if (g.norm_w) {
+    // RMSNorm producer (wave sub-tiles of whole 64-column groups; the
+    // dispatcher picks such a tile).  Blocks 2q and 2q+1 of the wave are
+    // group q; lanes l and l^32 hold the two halves of a row's group.  x_new goes straight back to the
     // fp32 stream; u = bf16(x_new * w) is staged through the idle LDS ring (as
     // the bf16 outputs below) and written as row-contiguous 16-byte stores.
     constexpr int UROWB = TN * 2;            // bytes per staged u row
@@ -419,7 +420,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int L) {
         for (int gq = 0; gq < 4; ++gq)
           w[j][gq] = *reinterpret_cast<const f32x4*>(g.norm_w + min(n + j * 32 + 8 * gq + c4, N - 4));
       lds_barrier();  // every wave is done reading the ring
-      constexpr int GI = BI < 2 ? BI : 2;  // row blocks per load/store group
+      constexpr int GI = BI % 2 == 0 ? 2 : 1;  // row blocks per load/store group (divides BI)
 #pragma unroll
       for (int i0 = 0; i0 < BI; i0 += GI) {
         // loads of the group (unconditional, clamped in bounds) before its stores
@@ -446,7 +447,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int L) {
           const int m = m0 + wm * TM + r;
           const bool ok = cols_ok && m < M;
           const int sw = (r / URPL) % UCPR;
-          float ssum = 0.f;
+          float ssum[TN / 64] = {};
 #pragma unroll
           for (int j = 0; j < BJ; ++j)
 #pragma unroll
@@ -463,13 +464,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int L) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 u[e] = f2bf(v[ii][j][gq][e] * w[j][gq][e]);
-                ssum += v[ii][j][gq][e] * v[ii][j][gq][e];
+                ssum[j / 2] += v[ii][j][gq][e] * v[ii][j][gq][e];
               }
               const int c16 = j * 4 + gq, hh = fh ^ ((r >> 4) & 1);
               *reinterpret_cast<bf16x4*>(st + r * UROWB + ((c16 ^ sw) << 4) + (hh << 3)) = u;
             }
-          ssum = xor32_sum(ssum);
-          if (ok && fh == 0) g.ss_out[(int64_t)m * ld_ss + n / 64] = ssum;
+#pragma unroll
+          for (int q = 0; q < TN / 64; ++q) {
+            const float sq = xor32_sum(ssum[q]);
+            if (ok && fh == 0) g.ss_out[(int64_t)m * ld_ss + n / 64 + q] = sq;
+          }
         }
         sched_fence();
       }
@@ -697,7 +701,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int L) {
       if constexpr (EPI == VIT_EPI_QKV_VT) vpos_i[i] = g.vpos[m];
     }
     if constexpr (EPI == VIT_EPI_ADD_F32) {
-      constexpr int GI = BI < 2 ? BI : 2;  // row blocks per load/store group
+      constexpr int GI = BI % 2 == 0 ? 2 : 1;  // row blocks per load/store group (divides BI)
 #pragma unroll
       for (int i0 = 0; i0 < BI; i0 += GI) {
         // loads of the group (unconditional, clamped in bounds) before its stores
