@@ -447,8 +447,11 @@ hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s) {
       b.norm_out = (bf16*)g.norm_out + sp.n_main;
       b.ss_out = g.ss_out + sp.n_main / 64;
     }
-    // one launch when that pair of tile configurations is built (tail tiles first)
-    const hipError_t ep = launch_gemm_mfma_pair(sp.cfg_tail, sp.cfg_main, epilogue, b, a, s);
+    // one launch when that pair of tile configurations is built, whichever of the
+    // two covers the main columns (the built pair puts the 128x128 tiles first)
+    hipError_t ep = launch_gemm_mfma_pair(sp.cfg_tail, sp.cfg_main, epilogue, b, a, s);
+    if (ep == hipErrorNotSupported)
+      ep = launch_gemm_mfma_pair(sp.cfg_main, sp.cfg_tail, epilogue, a, b, s);
     if (ep != hipErrorNotSupported) return ep;
     const hipError_t e = launch_gemm_mfma(sp.cfg_main, epilogue, a, s);
     if (e != hipSuccess) return e;
