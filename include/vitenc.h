@@ -293,8 +293,9 @@ vit_status vit_gemm_bias(int32_t epilogue, const void* A, int64_t lda, const voi
  * chain rule of the forward (the SwiGLU pre-activations are recomputed from x).
  * Rows are independent (patches of any images).  bf16 GEMM operands (x's
  * normalised rows, dy, the activations and their gradients are rounded to
- * bf16), fp32 accumulation and fp32 outputs.  dim and hidden multiples of 64,
- * dim <= 2048.  Every pointer 16-byte aligned, all device memory.
+ * bf16), fp32 accumulation and fp32 outputs.  dim a multiple of 64 and at most
+ * 2048, hidden a multiple of 16 (4304 for the 1152-wide tower).  Every pointer
+ * 16-byte aligned, all device memory.
  * ------------------------------------------------------------------------- */
 typedef struct {
   int64_t rows;        /* sum of patches                                  */
@@ -323,11 +324,12 @@ vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, vo
  * bidirectional attention per image and head, out-projection wo).  Given dy,
  * computes dL/dx, dL/dnorm_w, dL/dwqkv and dL/dwo by the chain rule; q, k, v
  * and each query's softmax log-sum-exp are recomputed by a forward pass.  bf16
- * GEMM and attention operands, fp32 accumulation and outputs; head_dim 64
- * (dim = 64 * n_heads), dim <= 2048.  Images as in vit_encode_varlen (rows of
- * x / dy concatenated in image order).  Every pointer 16-byte aligned, device. */
+ * GEMM and attention operands, fp32 accumulation and outputs; head_dim 64 or
+ * 72 (dim = 64 or 72 times n_heads), dim a multiple of 64 and at most 2048.
+ * Images as in vit_encode_varlen (rows of x / dy concatenated in image order).
+ * Every pointer 16-byte aligned, device. */
 typedef struct {
-  int32_t dim;         /* vision_dim d = 64 * n_heads                     */
+  int32_t dim;         /* vision_dim d = head_dim (64 or 72) * n_heads    */
   int32_t n_heads;
   float rope_theta;
   float eps;           /* RMSNorm eps                                     */
@@ -355,8 +357,9 @@ vit_status vit_attn_backward(const vit_attn_grad* a, const int32_t* grid_hw_host
  * fp32 residual stream at the input of each residual branch; then the final
  * norm's gradient, the blocks in reverse (each as vit_mlp_backward then
  * vit_attn_backward) and the patch embedding's weight gradient dx0^T . patches.
- * bf16 weights and patches, fp32 gradients; head_dim 64, vision_dim <= 2048 and
- * mlp_hidden multiples of 64, patch_dim a multiple of 4.  Images as in
+ * bf16 weights and patches, fp32 gradients; head_dim 64 or 72, vision_dim a
+ * multiple of 64 and at most 2048, mlp_hidden a multiple of 16, patch_dim a
+ * multiple of 4.  Images as in
  * vit_encode_varlen (patches [sum P, patch_dim], rows of dy in the same order).
  * The per-block arrays are HOST arrays of n_blocks device pointers (as in
  * vit_weights).  Every device pointer 16-byte aligned; the workspace must not

@@ -158,9 +158,9 @@ def test_workspace_grows_with_patches(lib):
 
 
 def test_tower_backward_workspace_host_checks(lib):
-    """Host-side sizing of vit_tower_backward: bf16 with head_dim 64 only; the
-    workspace holds at least the forward's plus 2 n_blocks + 1 fp32 residual
-    checkpoints."""
+    """Host-side sizing of vit_tower_backward: bf16 with head_dim 64 or 72, hidden a
+    multiple of 16; the workspace holds at least the forward's plus 2 n_blocks + 1
+    fp32 residual checkpoints."""
     c = configs.get(2)
     grids = list(c.grids)
     need = api.tower_backward_workspace_bytes(c, grids)
@@ -169,8 +169,11 @@ def test_tower_backward_workspace_host_checks(lib):
     g = _lib.grid_array(grids)
     for bad in (configs.VitConfig("f", c.grids, 1024, 16, 2816, 4, 0, "f32"),
                 configs.VitConfig("h", c.grids, 1024, 8, 2816, 4, 0, "bf16"),
-                configs.VitConfig("m", c.grids, 1024, 16, 2800, 4, 0, "bf16")):
+                configs.VitConfig("m", c.grids, 1024, 16, 2808, 4, 0, "bf16")):
         assert lib.vit_tower_backward_workspace_bytes(ctypes.byref(api.c_config(bad)), g, 4) == 0
+    # the 64x64 tower's widths (head_dim 72, hidden 4304) are taken
+    c4 = configs.get(3)
+    assert api.tower_backward_workspace_bytes(c4, list(c4.grids)) > 0
     one = api.tower_backward_workspace_bytes(
         configs.VitConfig("b1", c.grids, 1024, 16, 2816, 1, 0, "bf16"), grids)
     assert need - one >= 6 * P * d * 4

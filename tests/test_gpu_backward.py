@@ -69,7 +69,7 @@ def _check(got, ref, tag, whole_matrix_weights=False):
         assert fro < MLP_GRAD_FROB, (name, fro)
 
 
-@pytest.mark.parametrize("P,d,h", [(300, 256, 512), (64, 128, 192), (1, 64, 64)])
+@pytest.mark.parametrize("P,d,h", [(300, 256, 512), (64, 128, 192), (1, 64, 64), (200, 128, 208)])
 def test_mlp_backward_small_matches_oracle(P, d, h):
     args = _case(P, d, h, seed=70 + P)
     _check(_run(*args), oracle.mlp_half_backward(*args), f"P={P} d={d} h={h}",
@@ -82,6 +82,13 @@ def test_mlp_backward_ragged_batch_shape_matches_oracle():
     _check(_run(*args), oracle.mlp_half_backward(*args), "3562x1024x2816")
 
 
+def test_mlp_backward_tower_width_matches_oracle():
+    """The 64x64 tower's widths: 1152, hidden 4304 (not a multiple of 64: the gate
+    and up halves are padded apart internally), 1000 rows."""
+    args = _case(1000, 1152, 4304, seed=85)
+    _check(_run(*args), oracle.mlp_half_backward(*args), "1000x1152x4304")
+
+
 def test_mlp_backward_deterministic():
     args = _case(777, 256, 320, seed=90)
     a, b = _run(*args), _run(*args)
@@ -92,7 +99,7 @@ def test_mlp_backward_deterministic():
 def test_mlp_backward_error_paths():
     lib = _lib.load()
     assert lib.vit_mlp_backward_workspace_bytes(100, 96, 128) == 0  # dim % 64
-    assert lib.vit_mlp_backward_workspace_bytes(100, 128, 100) == 0  # hidden % 64
+    assert lib.vit_mlp_backward_workspace_bytes(100, 128, 100) == 0  # hidden % 16
     assert lib.vit_mlp_backward_workspace_bytes(0, 128, 128) == 0
     assert lib.vit_mlp_backward(None, None, 0, None) == _lib.VIT_E_ARG
     t = torch.zeros(64 * 64, device="cuda")
@@ -171,6 +178,26 @@ def test_attn_backward_ragged_batch_matches_oracle():
     H, d = 16, 1024
     args = _attn_case(grids, d, seed=120)
     _attn_check(_attn_run(*args, grids, H), _attn_oracle(*args, grids, H), "ragged batch")
+
+
+@pytest.mark.parametrize("grids,seed", [([(4, 6), (3, 5), (8, 8)], 0), ([(1, 1), (2, 3)], 1),
+                                        ([(4, 17), (9, 9)], 2)])
+def test_attn_backward_head_dim_72_small_grids_match_oracle(grids, seed):
+    """head_dim 72 (8 heads, width 576): the padded 32x32x16 kernels, the fused
+    rotary + V^T pack of the recomputed forward, and the rotary's inverse pass."""
+    H, d = 8, 576
+    args = _attn_case(grids, d, seed=210 + seed)
+    rows = sum(h * w for h, w in grids)
+    _attn_check(_attn_run(*args, grids, H), _attn_oracle(*args, grids, H), f"D=72 {grids}",
+                whole_matrix_weights=rows < 64)
+
+
+def test_attn_backward_head_dim_72_ragged_batch_matches_oracle():
+    """The ragged 4-image batch at the 64x64 tower's widths: 16 heads x 72 (1152)."""
+    grids = [(27, 37), (37, 27), (10, 78), (112, 7)]
+    H, d = 16, 1152
+    args = _attn_case(grids, d, seed=220)
+    _attn_check(_attn_run(*args, grids, H), _attn_oracle(*args, grids, H), "D=72 ragged batch")
 
 
 def test_attn_backward_deterministic_and_errors():
@@ -263,6 +290,23 @@ def test_tower_backward_ragged_batch_matches_oracle():
     dy = synth.random_array((cfg.total_patches, cfg.vision_dim), 181, std=1.0)
     got = _tower_run(cfg, inp["patches"], inp["weights"], dy)
     _tower_check(cfg, got, inp["patches"], inp["weights"], dy, "ragged batch x4")
+
+
+@pytest.mark.parametrize("grids,n_blocks", [([(4, 6), (3, 5), (8, 8)], 2), ([(1, 1), (2, 3), (1, 70)], 1)])
+def test_tower_backward_head_dim_72_small_matches_oracle(grids, n_blocks):
+    """head_dim 72 (8 heads, width 576, hidden 704), 4x4 patches, ragged grids."""
+    cfg, patches, weights, dy = _tower_case(grids, 576, 8, 704, n_blocks, seed=250 + n_blocks)
+    got = _tower_run(cfg, patches, weights, dy)
+    _tower_check(cfg, got, patches, weights, dy, f"D=72 {grids} x{n_blocks}")
+
+
+def test_tower_backward_head_dim_72_tower_width_matches_oracle():
+    """The 64x64 tower's widths (1152, 16 heads of 72, hidden 4304, 14x14 patches) on a
+    32x32 and a 12x20 grid through two blocks: every gradient."""
+    cfg, patches, weights, dy = _tower_case([(32, 32), (12, 20)], 1152, 16, 4304, 2, seed=260,
+                                            patch_size=14)
+    got = _tower_run(cfg, patches, weights, dy)
+    _tower_check(cfg, got, patches, weights, dy, "D=72 32x32+12x20 x2")
 
 
 def test_tower_backward_deterministic_and_errors():

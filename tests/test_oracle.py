@@ -736,11 +736,13 @@ def test_mlp_half_backward_zero_branch_passes_dy():
     np.testing.assert_allclose(dwd, dy.T @ (g / (1 + np.exp(-g)) * u), rtol=1e-13, atol=1e-13)
 
 
-def test_attn_half_backward_matches_finite_differences():
+@pytest.mark.parametrize("D", [4, 12])
+def test_attn_half_backward_matches_finite_differences(D):
     """Central differences of L = sum(dy * (x + attn(norm1(x)))) built from the pinned
-    forward steps (rmsnorm, linear, apply_rope, attention) on a 2x3 grid, 2 heads."""
-    rng = _rng(37)
-    gh, gw, H, D = 2, 3, 2, 4
+    forward steps (rmsnorm, linear, apply_rope, attention) on a 2x3 grid, 2 heads; head
+    dims 4 and 12 (one and three rotated pairs per quarter; the 1152-wide tower has 18)."""
+    rng = _rng(37 + D)
+    gh, gw, H = 2, 3, 2
     P, d = gh * gw, H * D
     x = rng.standard_normal((P, d))
     w = 1.0 + 0.3 * rng.standard_normal(d)

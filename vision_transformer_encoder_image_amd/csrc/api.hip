@@ -522,9 +522,12 @@ vit_status encode_impl(const vit_config* cfg, const vit_weights* w, const void* 
   return VIT_OK;
 }
 
-// Backward of the MLP half: workspace layout
+// Backward of the MLP half: workspace layout.  The gate and up halves of g|u,
+// dg|du and the transposed weights sit hp = round64(h) columns apart, the
+// columns between zero, so the dn GEMM's K (2 hp) is whole K-tiles.
 struct MlpGradPlan {
   int64_t Pp = 0;  // rows rounded up to 64 (K of the weight-gradient GEMMs)
+  int64_t hp = 0;  // hidden width rounded up to 64
   size_t n = 0, dy16 = 0, gu = 0, da = 0, a = 0, dgdu = 0, dn = 0, wdT = 0, wguT = 0;
   size_t dyT = 0, aT = 0, dgduT = 0, nT = 0, partial = 0, total = 0;
 };
@@ -532,6 +535,8 @@ struct MlpGradPlan {
 MlpGradPlan mlp_grad_plan(int64_t P, int64_t d, int64_t h) {
   MlpGradPlan p;
   p.Pp = round_up(P, 64);
+  p.hp = round_up(h, 64);
+  const int64_t hp = p.hp;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -540,16 +545,16 @@ MlpGradPlan mlp_grad_plan(int64_t P, int64_t d, int64_t h) {
   };
   p.n = take(P * d * 2);
   p.dy16 = take(P * d * 2);
-  p.gu = take(P * 2 * h * 4);
+  p.gu = take(P * 2 * hp * 4);
   p.da = take(P * h * 4);
   p.a = take(P * h * 2);
-  p.dgdu = take(P * 2 * h * 2);
+  p.dgdu = take(P * 2 * hp * 2);
   p.dn = take(P * d * 4);
   p.wdT = take(h * d * 2);
-  p.wguT = take(d * 2 * h * 2);
+  p.wguT = take(d * 2 * hp * 2);
   p.dyT = take(d * p.Pp * 2);
   p.aT = take(h * p.Pp * 2);
-  p.dgduT = take(2 * h * p.Pp * 2);
+  p.dgduT = take(2 * hp * p.Pp * 2);
   p.nT = take(d * p.Pp * 2);
   p.partial = take((size_t)rmsnorm_bwd_blocks(P) * d * 4);
   p.total = off;
@@ -560,7 +565,7 @@ vit_status check_mlp_grad_sizes(int64_t rows, int32_t dim, int32_t hidden) {
   if (rows < 1 || rows > (1 << 24)) return fail(VIT_E_SHAPE, "rows %lld out of range", (long long)rows);
   if (dim <= 0 || dim % 64 || dim > 2048)
     return fail(VIT_E_SHAPE, "dim %d: need a multiple of 64, at most 2048", dim);
-  if (hidden <= 0 || hidden % 64) return fail(VIT_E_SHAPE, "hidden %d: need a multiple of 64", hidden);
+  if (hidden <= 0 || hidden % 16) return fail(VIT_E_SHAPE, "hidden %d: need a multiple of 16", hidden);
   return VIT_OK;
 }
 
@@ -573,6 +578,7 @@ struct AttnGradPlan {
 };
 
 AttnGradPlan attn_grad_plan(const VarlenDesc& desc, int64_t d, int64_t H) {
+  const int64_t D = d / H;
   AttnGradPlan p;
   p.P = desc.total;
   p.Pp = round_up(p.P, 64);
@@ -586,7 +592,7 @@ AttnGradPlan attn_grad_plan(const VarlenDesc& desc, int64_t d, int64_t H) {
   };
   p.n = take(P * d * 2);
   p.qkv = take(P * 3 * d * 2);
-  p.table = take(P * 32 * 8);
+  p.table = take(P * (D / 2) * 8);
   p.vt = take(d * p.kv * 2);
   p.o = take(P * d * 2);
   p.lse = take(H * P * 4);
@@ -611,9 +617,11 @@ AttnGradPlan attn_grad_plan(const VarlenDesc& desc, int64_t d, int64_t H) {
 
 vit_status check_attn_grad(const vit_attn_grad* a) {
   if (!a) return fail(VIT_E_ARG, "arguments are NULL");
-  if (a->n_heads <= 0 || a->dim != 64 * a->n_heads || a->dim > 2048)
-    return fail(VIT_E_SHAPE, "dim %d, n_heads %d: need head_dim 64 and dim <= 2048", a->dim,
-                a->n_heads);
+  if (a->n_heads <= 0 || (a->dim != 64 * a->n_heads && a->dim != 72 * a->n_heads) ||
+      a->dim > 2048 || a->dim % 64)
+    return fail(VIT_E_SHAPE,
+                "dim %d, n_heads %d: need head_dim 64 or 72, dim a multiple of 64, dim <= 2048",
+                a->dim, a->n_heads);
   if (!(a->eps >= 0.f) || !(a->rope_theta > 0.f)) return fail(VIT_E_ARG, "bad eps / theta");
   return VIT_OK;
 }
@@ -635,11 +643,13 @@ vit_status tower_setup(const vit_config* cfg, const int32_t* grid_hw, int32_t n_
   VIT_TRY(check_config(cfg));
   const vit_config& c = *cfg;
   if (c.dtype != VIT_BF16) return fail(VIT_E_ARG, "tower backward: bf16 only");
-  if (c.head_dim != 64 || c.vision_dim % 64 || c.vision_dim > 2048)
-    return fail(VIT_E_SHAPE, "tower backward: head_dim 64 and vision_dim <= 2048 (got %d, %d)",
+  if ((c.head_dim != 64 && c.head_dim != 72) || c.vision_dim % 64 || c.vision_dim > 2048)
+    return fail(VIT_E_SHAPE,
+                "tower backward: head_dim 64 or 72, vision_dim a multiple of 64 and <= 2048 "
+                "(got %d, %d)",
                 c.head_dim, c.vision_dim);
-  if (c.mlp_hidden % 64)
-    return fail(VIT_E_SHAPE, "tower backward: mlp_hidden %d not a multiple of 64", c.mlp_hidden);
+  if (c.mlp_hidden % 16)
+    return fail(VIT_E_SHAPE, "tower backward: mlp_hidden %d not a multiple of 16", c.mlp_hidden);
   if (c.patch_dim % 4)
     return fail(VIT_E_SHAPE, "tower backward: patch_dim %d not a multiple of 4", c.patch_dim);
   VarlenDesc fdesc, bdesc;
@@ -1039,6 +1049,7 @@ vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, vo
   }
   const int64_t P = a->rows, d = a->dim, h = a->hidden;
   const MlpGradPlan p = mlp_grad_plan(P, d, h);
+  const int64_t hp = p.hp;
   if (!ws || ws_bytes < p.total || misaligned16(ws))
     return fail(VIT_E_WORKSPACE, "workspace %zu < %zu (or misaligned)", ws ? ws_bytes : (size_t)0,
                 p.total);
@@ -1073,8 +1084,8 @@ vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, vo
     ProfScope ps(VIT_K_BWD_PASS, s);
     VIT_HIP(launch_rmsnorm(a->x, a->norm_w, a->eps, P, (int)d, VIT_BF16, n, s), "norm");
   }
-  VIT_TRY(mm(n, d, a->w_gate, d, gu, 2 * h, P, h, d));
-  VIT_TRY(mm(n, d, a->w_up, d, gu + h, 2 * h, P, h, d));
+  VIT_TRY(mm(n, d, a->w_gate, d, gu, 2 * hp, P, h, d));
+  VIT_TRY(mm(n, d, a->w_up, d, gu + hp, 2 * hp, P, h, d));
   // da = dy . W_down
   {
     ProfScope ps(VIT_K_BWD_PASS, s);
@@ -1088,18 +1099,18 @@ vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, vo
   // SwiGLU gradient (and the activation for dW_down)
   {
     ProfScope ps(VIT_K_BWD_PASS, s);
-    VIT_HIP(launch_swiglu_bwd(gu, da, P, (int)h, act, dgdu, s), "swiglu backward");
+    VIT_HIP(launch_swiglu_bwd(gu, da, P, (int)h, (int)hp, act, dgdu, s), "swiglu backward");
   }
-  // dn = dg . W_gate + du . W_up
+  // dn = dg . W_gate + du . W_up (columns h .. hp-1 of each half zero on both sides)
   {
     ProfScope ps(VIT_K_BWD_PASS, s);
-    VIT_HIP(launch_transpose_bf16(a->w_gate, h, d, d, wguT, h, 2 * h, s), "transpose W_gate");
+    VIT_HIP(launch_transpose_bf16(a->w_gate, h, d, d, wguT, hp, 2 * hp, s), "transpose W_gate");
   }
   {
     ProfScope ps(VIT_K_BWD_PASS, s);
-    VIT_HIP(launch_transpose_bf16(a->w_up, h, d, d, wguT + h, h, 2 * h, s), "transpose W_up");
+    VIT_HIP(launch_transpose_bf16(a->w_up, h, d, d, wguT + hp, hp, 2 * hp, s), "transpose W_up");
   }
-  VIT_TRY(mm(dgdu, 2 * h, wguT, 2 * h, dn, d, P, d, 2 * h, true));
+  VIT_TRY(mm(dgdu, 2 * hp, wguT, 2 * hp, dn, d, P, d, 2 * hp, true));
   // RMSNorm gradient + residual, and the norm scale gradient
   {
     ProfScope ps(VIT_K_BWD_PASS, s);
@@ -1114,7 +1125,7 @@ vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, vo
   }
   {
     ProfScope ps(VIT_K_BWD_PASS, s);
-    VIT_HIP(launch_transpose_bf16(dgdu, P, 2 * h, 2 * h, dgduT, p.Pp, p.Pp, s), "transpose dg, du");
+    VIT_HIP(launch_transpose_bf16(dgdu, P, 2 * hp, 2 * hp, dgduT, p.Pp, p.Pp, s), "transpose dg, du");
   }
   {
     ProfScope ps(VIT_K_BWD_PASS, s);
@@ -1122,7 +1133,7 @@ vit_status vit_mlp_backward(const vit_mlp_grad* a, void* ws, size_t ws_bytes, vo
   }
   VIT_TRY(mm(dyT, p.Pp, aT, p.Pp, a->d_w_down, h, d, h, p.Pp));
   VIT_TRY(mm(dgduT, p.Pp, nT, p.Pp, a->d_w_gate, d, h, d, p.Pp));
-  return mm(dgduT + h * p.Pp, p.Pp, nT, p.Pp, a->d_w_up, d, h, d, p.Pp);
+  return mm(dgduT + hp * p.Pp, p.Pp, nT, p.Pp, a->d_w_up, d, h, d, p.Pp);
 }
 
 size_t vit_attn_backward_workspace_bytes(const vit_attn_grad* a, const int32_t* grid_hw_host,
@@ -1142,10 +1153,11 @@ vit_status vit_attn_backward(const vit_attn_grad* a, const int32_t* grid_hw_host
     if (!q) return fail(VIT_E_ARG, "NULL pointer");
     if (misaligned16(q)) return fail(VIT_E_ARG, "buffers must be 16-byte aligned");
   }
-  VarlenDesc fwd, bwd;  // q-tiles of the forward attention and of the backward kernels
-  VIT_TRY(build_desc(grid_hw_host, n_images, attention_q_tile(VIT_BF16, 64), false, 2, &fwd));
-  VIT_TRY(build_desc(grid_hw_host, n_images, attention_bwd_tile(), false, 2, &bwd));
   const int64_t d = a->dim, H = a->n_heads;
+  const int D = (int)(d / H);  // head_dim, 64 or 72
+  VarlenDesc fwd, bwd;  // q-tiles of the forward attention and of the backward kernels
+  VIT_TRY(build_desc(grid_hw_host, n_images, attention_q_tile(VIT_BF16, D), false, 2, &fwd));
+  VIT_TRY(build_desc(grid_hw_host, n_images, attention_bwd_tile(), false, 2, &bwd));
   const AttnGradPlan p = attn_grad_plan(bwd, d, H);
   const int64_t P = p.P;
   if (!ws || ws_bytes < p.total || misaligned16(ws))
@@ -1184,35 +1196,45 @@ vit_status vit_attn_backward(const vit_attn_grad* a, const int32_t* grid_hw_host
   };
   // forward recomputation: n, rotated q, k and v, attention output and lse
   VIT_HIP(launch_rmsnorm(a->x, a->norm_w, a->eps, P, (int)d, VIT_BF16, n, s), "norm");
-  VIT_HIP(launch_rope_table(fwd, 64, a->rope_theta, table, s), "rope table");
-  {
+  VIT_HIP(launch_rope_table(fwd, D, a->rope_theta, table, s), "rope table");
+  if (D == 64) {
     // qkv = n . Wqkv^T with the rotary applied to the q and k columns in the epilogue
     GemmArgs g = gemm_args(n, d, a->wqkv, nullptr, d, qkv, 3 * d, P, 3 * d, d, nullptr);
     g.rope_table = table;
     g.rope_cols = 2 * d;
     if (!gemm_bf16_can_fuse_rope(g)) return fail(VIT_E_SHAPE, "wqkv GEMM too large");
-    ProfScope all(VIT_K_BWD_GEMM, s);
-    VIT_HIP(launch_gemm_bf16(VIT_EPI_STORE_ROPE, g, s), "qkv + rotary gemm");
-  }
-  VIT_HIP(launch_vt_pack(qkv, fwd, (int)H, 64, vt, p.kv, s), "pack V");
-  {
+    {
+      ProfScope all(VIT_K_BWD_GEMM, s);
+      VIT_HIP(launch_gemm_bf16(VIT_EPI_STORE_ROPE, g, s), "qkv + rotary gemm");
+    }
+    VIT_HIP(launch_vt_pack(qkv, fwd, (int)H, 64, vt, p.kv, s), "pack V");
     ProfScope ps(VIT_K_ATTN, s);
     VIT_HIP(launch_attention_vt(qkv, 3 * d, vt, p.kv, fwd, (int)H, o, s, lse), "attention");
+  } else {
+    // as the encoder's head_dim-72 path: qkv = n . Wqkv^T, then one launch rotates
+    // q and k in place and packs V^T for the 16x16x32 attention kernel
+    VIT_TRY(mm(VIT_EPI_STORE, n, d, a->wqkv, d, qkv, 3 * d, P, 3 * d, d));
+    VIT_HIP(launch_vt_pack(qkv, fwd, (int)H, D, vt, p.kv, s, table), "rotary + pack V");
+    ProfScope ps(VIT_K_ATTN, s);
+    VIT_HIP(launch_attention(VIT_BF16, qkv, vt, p.kv, fwd, (int)H, D, o, s, lse), "attention");
   }
   // dO = dy . Wo, Dq = rowsum(dO o), transposed operands of the attention gradient
   VIT_HIP(launch_cast_transpose(a->dy, P, d, dy16, dyT, p.Pp, p.Pp, s), "cast + transpose dy");
   VIT_HIP(launch_transpose_bf16(a->wo, d, d, d, woT, d, d, s), "transpose wo");
   VIT_TRY(mm(VIT_EPI_STORE, dy16, d, woT, d, dO, d, P, d, d));
-  VIT_HIP(launch_rowdot(dO, o, P, (int)H, Dq, s), "rowsum(dO o)");
-  VIT_HIP(launch_tpack(qkv, 3 * d, 0, fwd, (int)H, qt, p.kv, s), "pack Q^T");
-  VIT_HIP(launch_tpack(qkv, 3 * d, d, fwd, (int)H, kt, p.kv, s), "pack K^T");
-  VIT_HIP(launch_tpack(dO, d, 0, fwd, (int)H, dot, p.kv, s), "pack dO^T");
+  VIT_HIP(launch_rowdot(dO, o, P, (int)H, D, Dq, s), "rowsum(dO o)");
+  VIT_HIP(launch_tpack(qkv, 3 * d, 0, fwd, (int)H, D, qt, p.kv, s), "pack Q^T");
+  VIT_HIP(launch_tpack(qkv, 3 * d, d, fwd, (int)H, D, kt, p.kv, s), "pack K^T");
+  VIT_HIP(launch_tpack(dO, d, 0, fwd, (int)H, D, dot, p.kv, s), "pack dO^T");
   {
     ProfScope ps(VIT_K_BWD_ATTN, s);
-    VIT_HIP(launch_attention_bwd(qkv, 3 * d, dO, qt, kt, dot, p.kv, lse, Dq, table, bwd, (int)H,
+    VIT_HIP(launch_attention_bwd(qkv, 3 * d, dO, qt, kt, dot, p.kv, lse, Dq, table, bwd, (int)H, D,
                                  dqkv, 3 * d, s),
             "attention backward");
   }
+  // head_dim 72: dq and dk come out in the rotated space; the rotation by the
+  // opposite angles gives the gradients with respect to wqkv's q and k outputs
+  if (D != 64) VIT_HIP(launch_rope_inverse(dqkv, table, P, (int)H, D, s), "rotary backward");
   // dn = dqkv . Wqkv, then the norm gradient and the residual
   VIT_HIP(launch_transpose_bf16(a->wqkv, 3 * d, d, d, wqkvT, 3 * d, 3 * d, s), "transpose wqkv");
   VIT_TRY(mm(VIT_EPI_STORE_F32, dqkv, 3 * d, wqkvT, 3 * d, dn, d, P, d, 3 * d));

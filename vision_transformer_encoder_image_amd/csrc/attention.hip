@@ -45,7 +45,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const bf16* __re
                                                                 const bf16* __restrict__ vt,
                                                                 int64_t vt_ld, VarlenDesc desc,
                                                                 int H, bf16* __restrict__ out,
-                                                                float scale_log2) {
+                                                                float scale_log2,
+                                                                float* __restrict__ lse2) {
   constexpr int DP = (D + 31) / 32 * 32;  // QK contraction length padded to the MFMA k
   constexpr int DO = (D + 15) / 16 * 16;  // output rows padded to the MFMA block
   constexpr int NDS = DP / 32;
@@ -264,6 +265,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const bf16* __re
     const float inv = 1.0f / l;
     const int query = q0 + wave * 32 + qb * 16 + fr;
     if (query >= seq1) continue;
+    // base-2 log-sum-exp of the scaled scores (mrow is already scaled), for the backward
+    if (lse2 && fk == 0) lse2[(int64_t)h * desc.total + query] = mrow[qb] + __log2f(l);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int d = db * 16 + fk * 4;
@@ -618,7 +621,7 @@ hipError_t launch_attention_vt(const void* qk, int64_t ld_qk, const void* vt, in
 
 hipError_t launch_attention(int dtype, const void* qkv, const void* vt, int64_t vt_ld,
                             const VarlenDesc& d, int n_heads, int head_dim, void* out,
-                            hipStream_t s) {
+                            hipStream_t s, float* lse2) {
   const int tiles = d.cu_tiles[d.n_images];
   if (tiles == 0) return hipSuccess;
   if (dtype == VIT_BF16) {
@@ -626,8 +629,9 @@ hipError_t launch_attention(int dtype, const void* qkv, const void* vt, int64_t 
     if (head_dim != 72 || !vt || vt_ld < d.kv_off[d.n_images] || vt_ld % 8)
       return hipErrorInvalidValue;
     attn_bf16_kernel<72><<<dim3((unsigned)(tiles * n_heads)), kThreads, 0, s>>>(
-        (const bf16*)qkv, (const bf16*)vt, vt_ld, d, n_heads, (bf16*)out, sl2);
+        (const bf16*)qkv, (const bf16*)vt, vt_ld, d, n_heads, (bf16*)out, sl2, lse2);
   } else {
+    if (lse2) return hipErrorInvalidValue;
     const dim3 grid((unsigned)tiles, (unsigned)n_heads);
     const float sc = (float)(1.0 / sqrt((double)head_dim));
     if (head_dim == 64)

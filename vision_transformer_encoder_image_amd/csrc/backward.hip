@@ -90,21 +90,28 @@ __global__ __launch_bounds__(kThreads) void transpose_bf16_kernel(
   }
 }
 
-// SwiGLU gradient: g, u = gu[:, :h], gu[:, h:] (fp32), da (fp32, [rows, h]) ->
-// a = silu(g) u (bf16, [rows, h]), dg = da u (s + g s (1 - s)), du = da g s
-// (bf16, side by side in dgdu [rows, 2h]); s = sigmoid(g)
+// SwiGLU gradient: g, u = gu[:, :h], gu[:, hp:hp+h] (fp32, rows of 2 hp, hp >= h
+// the padded half width), da (fp32, [rows, h]) -> a = silu(g) u (bf16, [rows, h]),
+// dg = da u (s + g s (1 - s)), du = da g s (bf16, side by side in dgdu [rows, 2 hp],
+// columns h .. hp-1 of each half written zero); s = sigmoid(g)
 __global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(const float* __restrict__ gu,
                                                               const float* __restrict__ da,
-                                                              int64_t rows, int h,
+                                                              int64_t rows, int h, int hp,
                                                               bf16* __restrict__ a,
                                                               bf16* __restrict__ dgdu) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // group of 4 columns
-  const int h4 = h / 4;
+  const int h4 = hp / 4;
   if (i >= rows * h4) return;
   const int64_t r = i / h4;
   const int c = (int)(i % h4) * 4;
-  const f32x4 g = *reinterpret_cast<const f32x4*>(gu + r * 2 * h + c);
-  const f32x4 u = *reinterpret_cast<const f32x4*>(gu + r * 2 * h + h + c);
+  if (c >= h) {  // padding of the K dimension of the dn GEMM
+    const bf16x4 z = {f2bf(0.f), f2bf(0.f), f2bf(0.f), f2bf(0.f)};
+    *reinterpret_cast<bf16x4*>(dgdu + r * 2 * hp + c) = z;
+    *reinterpret_cast<bf16x4*>(dgdu + r * 2 * hp + hp + c) = z;
+    return;
+  }
+  const f32x4 g = *reinterpret_cast<const f32x4*>(gu + r * 2 * hp + c);
+  const f32x4 u = *reinterpret_cast<const f32x4*>(gu + r * 2 * hp + hp + c);
   const f32x4 d = *reinterpret_cast<const f32x4*>(da + r * h + c);
   bf16x4 av, dgv, duv;
 #pragma unroll
@@ -115,8 +122,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(const float* __res
     duv[e] = f2bf(d[e] * g[e] * s);
   }
   *reinterpret_cast<bf16x4*>(a + r * h + c) = av;
-  *reinterpret_cast<bf16x4*>(dgdu + r * 2 * h + c) = dgv;
-  *reinterpret_cast<bf16x4*>(dgdu + r * 2 * h + h + c) = duv;
+  *reinterpret_cast<bf16x4*>(dgdu + r * 2 * hp + c) = dgv;
+  *reinterpret_cast<bf16x4*>(dgdu + r * 2 * hp + hp + c) = duv;
 }
 
 // RMSNorm gradient plus the residual: per row, r = (mean(x^2) + eps)^-1/2,
@@ -267,12 +274,12 @@ hipError_t launch_cast_transpose(const float* src, int64_t R, int64_t C, void* c
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_bwd(const float* gu, const float* da, int64_t rows, int h, void* a,
-                             void* dgdu, hipStream_t s) {
-  if (h % 4) return hipErrorInvalidValue;
+hipError_t launch_swiglu_bwd(const float* gu, const float* da, int64_t rows, int h, int hp,
+                             void* a, void* dgdu, hipStream_t s) {
+  if (h % 4 || hp % 4 || hp < h) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
-  swiglu_bwd_kernel<<<blocks_of(rows * (h / 4)), kThreads, 0, s>>>(gu, da, rows, h, (bf16*)a,
-                                                                   (bf16*)dgdu);
+  swiglu_bwd_kernel<<<blocks_of(rows * (hp / 4)), kThreads, 0, s>>>(gu, da, rows, h, hp, (bf16*)a,
+                                                                    (bf16*)dgdu);
   return hipGetLastError();
 }
 

@@ -207,10 +207,16 @@ hipError_t launch_rope_table(const VarlenDesc& d, int head_dim, float theta, voi
                              hipStream_t s);
 hipError_t launch_rope(int dtype, void* qkv, const void* table, int64_t P, int n_heads,
                        int head_dim, hipStream_t s);
-// fp32: vt unused.  bf16: head_dim 72 only, with vt from launch_vt_pack.
+// the rotation by the opposite angles on the q and k parts (bf16): gradients with
+// respect to the rotated q, k back to gradients with respect to q, k
+hipError_t launch_rope_inverse(void* qkv, const void* table, int64_t P, int n_heads, int head_dim,
+                               hipStream_t s);
+// fp32: vt unused.  bf16: head_dim 72 only, with vt from launch_vt_pack; lse2
+// (optional, bf16 only, [n_heads, total] fp32): each query's log2(sum over keys of
+// 2^(s c)), s the raw q.k score and c = log2(e)/sqrt(72)
 hipError_t launch_attention(int dtype, const void* qkv, const void* vt, int64_t vt_ld,
                             const VarlenDesc& d, int n_heads, int head_dim, void* out,
-                            hipStream_t s);
+                            hipStream_t s, float* lse2 = nullptr);
 int attention_q_tile(int dtype, int head_dim);
 // lse2 (optional, [n_heads, total] fp32): each query's log2(sum over keys of 2^(s c)),
 // s the raw q.k score and c = log2(e)/sqrt(64)
@@ -289,27 +295,33 @@ hipError_t launch_cast_transpose(const float* src, int64_t R, int64_t C, void* c
 int64_t mfma_peak_out_floats();
 double mfma_peak_flops(int iters);
 hipError_t launch_mfma_peak(int iters, float* out, hipStream_t s);
-hipError_t launch_swiglu_bwd(const float* gu, const float* da, int64_t rows, int h, void* a,
-                             void* dgdu, hipStream_t s);
+// gu [rows, 2 hp] (g, u at columns 0 and hp), dgdu [rows, 2 hp] likewise, its
+// columns h .. hp-1 of each half zero
+hipError_t launch_swiglu_bwd(const float* gu, const float* da, int64_t rows, int h, int hp,
+                             void* a, void* dgdu, hipStream_t s);
 int rmsnorm_bwd_blocks(int64_t rows);
 hipError_t launch_rmsnorm_bwd(const float* x, const float* w, const float* dn, const float* dy,
                               int64_t rows, int d, float eps, float* dx, float* partial,
                               float* dw, hipStream_t s);
-// backward of the attention (attention_bwd.hip), bf16, head_dim 64
+// backward of the attention (attention_bwd.hip), bf16, head_dim D = 64 or 72
 int attention_bwd_tile();  // queries / keys per workgroup: the q-tile of its descriptor
-// dst [H*64, ld] = columns col0 .. col0+H*64 of src, transposed into the forward's
-// V^T layout (64-aligned image spans, keys permuted by vt_key_slot, zero padding)
+// dst [H*D, ld] = columns col0 .. col0+H*D of src, transposed into the V^T layout
+// of the 32x32x16 MFMAs (64-aligned image spans, keys permuted by vt_key_slot,
+// zero padding)
 hipError_t launch_tpack(const void* src, int64_t ld_src, int64_t col0, const VarlenDesc& d,
-                        int n_heads, void* dst, int64_t ld, hipStream_t s);
-hipError_t launch_rowdot(const void* dO, const void* O, int64_t P, int n_heads, float* Dq,
-                         hipStream_t s);
-// dq -> columns [0, H*64) of dqkv, dk, dv -> [H*64, 3*H*64), dq and dk rotated back
-// with the rotary table (the gradients before the rotary); q, k, v read from qkv
-// ([P, ldq], rotated q, k); qt, kt, dot in the tpack layout
+                        int n_heads, int head_dim, void* dst, int64_t ld, hipStream_t s);
+hipError_t launch_rowdot(const void* dO, const void* O, int64_t P, int n_heads, int head_dim,
+                         float* Dq, hipStream_t s);
+// dq -> columns [0, H*D) of dqkv, dk, dv -> [H*D, 3*H*D); q, k, v read from qkv
+// ([P, ldq], rotated q, k); qt, kt, dot in the tpack layout.  D = 64: dq and dk
+// rotated back with the rotary table in the kernels (the gradients before the
+// rotary); D = 72: dq and dk left in the rotated space (table unused), for
+// launch_rope_inverse.
 hipError_t launch_attention_bwd(const void* qkv, int64_t ldq, const void* dO, const void* qt,
                                 const void* kt, const void* dot, int64_t t_ld, const float* lse2,
                                 const float* Dq, const void* table, const VarlenDesc& d,
-                                int n_heads, void* dqkv, int64_t ld_out, hipStream_t s);
+                                int n_heads, int head_dim, void* dqkv, int64_t ld_out,
+                                hipStream_t s);
 // image tokens and sentinel rows into a text embedding stream (merge.hip)
 size_t merge_workspace_bytes(int64_t positions);
 // group counts of IMAGE positions, scanned in place in ws; total to n_image (optional)

@@ -79,7 +79,9 @@ struct alignas(sizeof(T) * V) RopeVec {
   T v[V];
 };
 
-template <typename T, int V>
+// With INV the rotation is by the opposite angles (the transpose), which maps a
+// gradient with respect to the rotated q, k back to one with respect to q, k.
+template <typename T, int V, bool INV>
 __global__ void rope_kernel(T* qkv, const float2* __restrict__ table, int64_t P, int H, int D) {
   const int q4 = D / 4, qv = q4 / V;
   const int per_row = 4 * H * qv;  // 2 parts * H heads * 2 halves * D/(4V)
@@ -102,8 +104,9 @@ __global__ void rope_kernel(T* qkv, const float2* __restrict__ table, int64_t P,
 #pragma unroll
   for (int e = 0; e < V; ++e) {
     const float a1 = to_f32(x1.v[e]), a2 = to_f32(x2.v[e]);
-    x1.v[e] = from_f32<T>(a1 * c.v[e].x - a2 * c.v[e].y);
-    x2.v[e] = from_f32<T>(a2 * c.v[e].x + a1 * c.v[e].y);
+    const float sn = INV ? -c.v[e].y : c.v[e].y;
+    x1.v[e] = from_f32<T>(a1 * c.v[e].x - a2 * sn);
+    x2.v[e] = from_f32<T>(a2 * c.v[e].x + a1 * sn);
   }
   *reinterpret_cast<RopeVec<T, V>*>(row + kk) = x1;
   *reinterpret_cast<RopeVec<T, V>*>(row + kk + q4) = x2;
@@ -488,7 +491,7 @@ hipError_t launch_rope_table(const VarlenDesc& d, int head_dim, float theta, voi
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool INV = false>
 hipError_t launch_rope_t(T* qkv, const float2* table, int64_t P, int H, int D, hipStream_t s) {
   const int q4 = D / 4;
   auto fits = [&](int v) {
@@ -497,11 +500,11 @@ hipError_t launch_rope_t(T* qkv, const float2* table, int64_t P, int H, int D, h
   };
   const int64_t pairs = P * H * D;  // 2 parts * 2 halves * D/4 pairs per head
   if (fits(4))
-    rope_kernel<T, 4><<<blocks_for(pairs / 4), kThreads, 0, s>>>(qkv, table, P, H, D);
+    rope_kernel<T, 4, INV><<<blocks_for(pairs / 4), kThreads, 0, s>>>(qkv, table, P, H, D);
   else if (fits(2))
-    rope_kernel<T, 2><<<blocks_for(pairs / 2), kThreads, 0, s>>>(qkv, table, P, H, D);
+    rope_kernel<T, 2, INV><<<blocks_for(pairs / 2), kThreads, 0, s>>>(qkv, table, P, H, D);
   else
-    rope_kernel<T, 1><<<blocks_for(pairs), kThreads, 0, s>>>(qkv, table, P, H, D);
+    rope_kernel<T, 1, INV><<<blocks_for(pairs), kThreads, 0, s>>>(qkv, table, P, H, D);
   return hipGetLastError();
 }
 
@@ -511,6 +514,11 @@ hipError_t launch_rope(int dtype, void* qkv, const void* table, int64_t P, int n
   if (dtype == VIT_BF16)
     return launch_rope_t((bf16*)qkv, (const float2*)table, P, n_heads, head_dim, s);
   return launch_rope_t((float*)qkv, (const float2*)table, P, n_heads, head_dim, s);
+}
+hipError_t launch_rope_inverse(void* qkv, const void* table, int64_t P, int n_heads, int head_dim,
+                               hipStream_t s) {
+  if (P * n_heads * head_dim == 0) return hipSuccess;
+  return launch_rope_t<bf16, true>((bf16*)qkv, (const float2*)table, P, n_heads, head_dim, s);
 }
 
 hipError_t launch_gather(int dtype, const void* x, const VarlenDesc& d, int dim, int merge,
@@ -602,19 +610,26 @@ hipError_t launch_vt_zero_pads(const VarlenDesc& d, int64_t rows, void* vt, int6
 }
 
 hipError_t launch_tpack(const void* src, int64_t ld_src, int64_t col0, const VarlenDesc& d,
-                        int n_heads, void* dst, int64_t ld, hipStream_t s) {
+                        int n_heads, int head_dim, void* dst, int64_t ld, hipStream_t s) {
   const int cols = d.kv_off[d.n_images];
   if (cols == 0) return hipSuccess;
   if (ld_src % 8 || col0 % 8 || ld % 8) return hipErrorInvalidValue;
-  tpack_kernel<64, false><<<dim3((unsigned)(cols / 64), (unsigned)n_heads), 256, 0, s>>>(
-      (const bf16*)src, ld_src, col0, d, (bf16*)dst, ld, nullptr);
+  const dim3 grid((unsigned)(cols / 64), (unsigned)n_heads);
+  if (head_dim == 64)
+    tpack_kernel<64, false><<<grid, 256, 0, s>>>((const bf16*)src, ld_src, col0, d, (bf16*)dst, ld,
+                                                 nullptr);
+  else if (head_dim == 72)
+    tpack_kernel<72, false><<<grid, 256, 0, s>>>((const bf16*)src, ld_src, col0, d, (bf16*)dst, ld,
+                                                 nullptr);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_vt_pack(const void* qkv, const VarlenDesc& d, int n_heads, int head_dim,
                           void* vt, int64_t vt_ld, hipStream_t s, const void* rope_table) {
   const int64_t dm = (int64_t)n_heads * head_dim;
-  if (head_dim == 64 && !rope_table) return launch_tpack(qkv, 3 * dm, 2 * dm, d, n_heads, vt, vt_ld, s);
+  if (head_dim == 64 && !rope_table) return launch_tpack(qkv, 3 * dm, 2 * dm, d, n_heads, 64, vt, vt_ld, s);
   if (head_dim != 72 || vt_ld % 8) return hipErrorInvalidValue;
   if (rope_table && (((uintptr_t)qkv & 3) || ((uintptr_t)rope_table & 15)))
     return hipErrorInvalidValue;

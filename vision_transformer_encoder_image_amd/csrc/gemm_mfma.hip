@@ -210,17 +210,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int L) {
 #pragma unroll
     for (int j = 0; j < BJ; ++j) acc[i][j] = f32x16{};
 
-  // fp32 residual add: the rows to add to are loaded into registers right
-  // after the copies of the last K-tile are issued, so their reads overlap the
-  // MFMAs of the last STAGES-1 K-tiles instead of following them.  Those
-  // loads are younger than every copy; the waits of the last K-tiles count
-  // them (kPreLoads).  Needs the last copies issued inside the loop (nk >=
-  // STAGES), no row map, and at most 32 registers of rows per lane (more
-  // would spill with two waves per SIMD).
+  // fp32 residual add: the rows to add to, and the folded-norm producer's norm
+  // weights, are loaded into registers right after the copies of the last
+  // K-tile are issued, so their reads overlap the MFMAs of the last STAGES-1
+  // K-tiles instead of following them.  Those loads are younger than every
+  // copy; the waits of the last K-tiles count them (kPreLoads).  Needs the last
+  // copies issued inside the loop (nk >= STAGES), no row map, and at most
+  // 32 + 8 registers per lane (more would spill with two waves per SIMD).
+  // Every wave issues the same loads (without norm weights the first row of C
+  // stands in), so the counts hold for all.
   constexpr bool kPre = EPI == VIT_EPI_ADD_F32 && BI * BJ <= 2 && STAGES <= 4;
-  constexpr int kPreLoads = kPre ? BI * BJ * 4 : 0;
+  constexpr int kPreLoads = kPre ? BI * BJ * 4 + BJ * 4 : 0;
   const bool pre_on = kPre && nk >= STAGES && g.rowmap == nullptr;
   f32x4 pre[kPre ? BI : 1][kPre ? BJ : 1][4];
+  f32x4 wpre[kPre ? BJ : 1][4];
   const int c4 = 4 * (lane >> 5);
 #define W_PRELOAD()                                                                     \
   do {                                                                                  \
@@ -230,6 +233,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int L) {
       _Pragma("unroll") for (int gq = 0; gq < 4; ++gq) pre[i][j][gq] =                  \
           *reinterpret_cast<const f32x4*>((const float*)g.C + (int64_t)m_ * g.ldc +     \
                                           min(n0 + wn * TN + j * 32 + 8 * gq + c4, N - 4)); \
+    }                                                                                   \
+    if constexpr (kPre) {                                                               \
+      const float* w_ = g.norm_w ? g.norm_w : (const float*)g.C;                        \
+      _Pragma("unroll") for (int j = 0; j < BJ; ++j)                                    \
+      _Pragma("unroll") for (int gq = 0; gq < 4; ++gq) wpre[j][gq] =                    \
+          *reinterpret_cast<const f32x4*>(w_ + min(n0 + wn * TN + j * 32 + 8 * gq + c4, N - 4)); \
     }                                                                                   \
   } while (0)
 
@@ -417,8 +426,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int L) {
 #pragma unroll
       for (int j = 0; j < BJ; ++j)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq)
-          w[j][gq] = *reinterpret_cast<const f32x4*>(g.norm_w + min(n + j * 32 + 8 * gq + c4, N - 4));
+        for (int gq = 0; gq < 4; ++gq) {
+          if constexpr (with_pre)
+            w[j][gq] = wpre[kPre ? j : 0][gq];
+          else
+            w[j][gq] = *reinterpret_cast<const f32x4*>(g.norm_w + min(n + j * 32 + 8 * gq + c4, N - 4));
+        }
       lds_barrier();  // every wave is done reading the ring
       constexpr int GI = BI % 2 == 0 ? 2 : 1;  // row blocks per load/store group (divides BI)
 #pragma unroll
