@@ -663,19 +663,21 @@ def tower_backward_flops(cfg, grids):
 
 def bench_tower_backward(args):
     """vit_tower_backward on the ragged 4-image batch (27x37, 37x27, 10x78, 112x7;
-    vision_dim 1024, 16 heads x 64, hidden 2816, 4 blocks; synthetic bf16 patches and
-    weights, fp32 dy).  One step is one call: the forward with residual checkpoints,
-    the final norm's gradient, the four blocks' halves in reverse and the patch
-    embedding's gradient."""
+    vision_dim 1024, 16 heads x 64, hidden 2816, 4 blocks), or with --workload on
+    another workload's grids and widths (the 64x64 tower: 1152, 16 heads x 72,
+    hidden 4304, 32 blocks); synthetic bf16 patches and weights, fp32 dy.  One step
+    is one call: the forward with residual checkpoints, the final norm's gradient,
+    every block's halves in reverse and the patch embedding's gradient."""
     import torch
 
     from vision_transformer_encoder_image_amd import api, configs, synth
 
     dev = "cuda:0"
-    cfg = configs.get("ragged_varlen_4img")
+    cfg = configs.get(args.workload)
     grids = list(cfg.grids)
     P, d, h, L = cfg.total_patches, cfg.vision_dim, cfg.mlp_hidden, cfg.n_blocks
     Pp = (P + 63) // 64 * 64
+    hp = (h + 63) // 64 * 64  # the MLP backward's padded hidden width
     inp = synth.make_inputs(cfg, seed=2)
     w = api.DeviceWeights(cfg, inp["weights"], device=dev)
     x = torch.from_numpy(inp["patches"]).to(dev, torch.bfloat16)
@@ -685,7 +687,7 @@ def bench_tower_backward(args):
     # FLOPs the backward GEMM class executes per call (with the halves' recomputed
     # forward GEMMs and the weight gradients' row padding)
     gemm_exec = L * (6.0 * P * d * d + 2.0 * P * d * d + 6.0 * P * d * d + 8.0 * d * d * Pp +
-                     4.0 * P * d * h + 2.0 * P * d * h + 4.0 * P * d * h + 6.0 * d * h * Pp)
+                     4.0 * P * d * h + 2.0 * P * d * h + 4.0 * P * d * hp + 6.0 * d * h * Pp)
     for _ in range(max(args.warmup, 1)):
         api.tower_backward(x, grids, w, dy, ws=ws)
     torch.cuda.synchronize()
@@ -708,7 +710,7 @@ def bench_tower_backward(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "tower_backward_ragged_varlen_4img", "grids": [list(g) for g in grids],
+        "config": {"workload": f"tower_backward_{cfg.name}", "grids": [list(g) for g in grids],
                    "patches": P, "dim": d, "heads": cfg.n_heads, "mlp_hidden": h, "blocks": L,
                    "flops_per_step": total},
         "roofline": {"kernel": "bwd_gemm", "bound": "mfma", "achieved": round(achieved, 1),
@@ -726,21 +728,31 @@ def bench_tower_backward(args):
 
         info = threadpoolctl.threadpool_info()
         cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-        sub = [grids[2]]  # the 10x78 image: 780 patches, all four blocks
-        off = grids[0][0] * grids[0][1] + grids[1][0] * grids[1][1]
+        wts = inp["weights"]
+        if cfg.name == "ragged_varlen_4img":
+            sub = [grids[2]]  # the 10x78 image: 780 patches, all four blocks
+            off = grids[0][0] * grids[0][1] + grids[1][0] * grids[1][1]
+            scfg, what = cfg, f"the 10x78 image (780 patches, {L} blocks)"
+        else:
+            # the first 16x16 patches of the first image (rows of its top 16 x 16
+            # corner are not contiguous, so the sample is a 16x16 grid of the image's
+            # first 256 patches) through the first two blocks
+            sub, off = [(16, 16)], 0
+            scfg = configs.VitConfig(cfg.name, tuple(sub), d, cfg.n_heads, h, min(L, 2), 0,
+                                     cfg.dtype)
+            wts = dict(wts, blocks=wts["blocks"][:scfg.n_blocks])
+            what = f"a 16x16 grid of the first 256 patches, the first {scfg.n_blocks} blocks"
         Pi = sub[0][0] * sub[0][1]
         pt = inp["patches"][off:off + Pi]
         dyh = synth.random_array((P, d), 180)[off:off + Pi]
         runs, t0 = 0, time.perf_counter()
         while time.perf_counter() - t0 < 10.0:
-            oracle.tower_backward(pt, sub, inp["weights"], cfg.n_heads, dyh, cfg.rms_eps,
-                                  cfg.rope_theta)
+            oracle.tower_backward(pt, sub, wts, cfg.n_heads, dyh, cfg.rms_eps, cfg.rope_theta)
             runs += 1
         dt = time.perf_counter() - t0
-        result["cpu_baseline"] = {"value": round(tower_backward_flops(cfg, sub) * runs / dt / 1e12, 4),
+        result["cpu_baseline"] = {"value": round(tower_backward_flops(scfg, sub) * runs / dt / 1e12, 4),
                                   "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-                                  "sample": f"the 10x78 image ({Pi} patches, 4 blocks), {runs} "
-                                            f"float64 oracle passes in {dt:.1f} s"}
+                                  "sample": f"{what}, {runs} float64 oracle passes in {dt:.1f} s"}
     print(json.dumps(result), flush=True)
 
 
