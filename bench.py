@@ -756,6 +756,84 @@ def bench_tower_backward(args):
     print(json.dumps(result), flush=True)
 
 
+GEMM_LIB_METRIC = "TFLOP/s of the encoder's GEMM shapes, library kernel vs vendor BLAS (bf16)"
+
+
+def bench_gemm_library(args):
+    """The block GEMM shapes of a workload (wqkv, out-projection, gate and up side
+    by side, down) plus a large square one, each timed as C = A B^T with a plain
+    bf16 store: through vit_gemm (the library's MFMA kernel and tile choice) and
+    through torch.nn.functional.linear (the vendor BLAS, hipBLASLt), same inputs
+    and stream.  Median of per-call HIP events; the outputs are compared.  The
+    BLAS leg is a reference point for the hand-written kernel, not part of the
+    encoder."""
+    import statistics
+
+    import torch
+
+    from vision_transformer_encoder_image_amd import _lib, api, configs
+
+    dev = "cuda:0"
+    cfg = configs.get(args.workload)
+    P, d, h = cfg.total_patches, cfg.vision_dim, cfg.mlp_hidden
+    shapes = [("wqkv", P, 3 * d, d), ("outproj", P, d, d), ("gateup", P, 2 * h, d),
+              ("down", P, d, h), ("square8192", 8192, 8192, 8192)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+
+    def med_us(fn):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(args.steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        return statistics.median(ts)
+
+    rows = []
+    for name, M, N, K in shapes:
+        A = (torch.rand(M, K, device=dev, generator=gen) * 2 - 1).bfloat16()
+        B = (torch.randn(N, K, device=dev, generator=gen) * 0.02).bfloat16()
+        C = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+        t_lib = med_us(lambda: api.gemm(A, B, _lib.VIT_EPI_STORE, C=C))
+        ref = torch.nn.functional.linear(A, B)
+        t_blas = med_us(lambda: torch.nn.functional.linear(A, B))
+        diff = float((C.float() - ref.float()).abs().max() / ref.float().abs().max())
+        fl = 2.0 * M * N * K
+        rows.append({"gemm": name, "M": M, "N": N, "K": K,
+                     "library_us": round(t_lib, 2), "library_tflops": round(fl / t_lib / 1e6, 1),
+                     "blas_us": round(t_blas, 2), "blas_tflops": round(fl / t_blas / 1e6, 1),
+                     "max_rel_diff": float(f"{diff:.3e}")})
+        del A, B, C, ref
+    enc = [r for r in rows if r["gemm"] != "square8192"]
+    fl_enc = sum(2.0 * r["M"] * r["N"] * r["K"] for r in enc)
+    t_enc = sum(r["library_us"] for r in enc)
+    result = {
+        "metric": GEMM_LIB_METRIC,
+        "value": round(fl_enc / t_enc / 1e6, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "higher_is_better": True,
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"gemm_library_{cfg.name}", "shapes": rows,
+                   "blas_tflops_encoder_shapes": round(
+                       fl_enc / sum(r["blas_us"] for r in enc) / 1e6, 1)},
+        "note": "value: the library kernel over the encoder shapes (plain bf16 store, no fused "
+                "epilogue); per-call events include the launch; blas = torch.nn.functional.linear",
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -763,12 +841,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--stage", choices=("encode", "merge", "projector", "mlp_backward",
-                                        "attn_backward", "tower_backward"),
+                                        "attn_backward", "tower_backward", "gemm_library"),
                     default="encode",
                     help="encode: the encoder step; merge: image tokens into the LLM stream; "
                          "projector: the PatchMerger projector; mlp_backward / attn_backward: "
                          "the backward of a block's MLP / attention half; tower_backward: the "
-                         "backward of the whole tower")
+                         "backward of the whole tower; gemm_library: the library GEMM against "
+                         "the vendor BLAS on the workload's GEMM shapes")
     ap.add_argument("--pixels", action="store_true",
                     help="encode stage: pixel images in (the library cuts the patches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -820,6 +899,9 @@ def main():
         return
     if args.stage == "tower_backward":
         bench_tower_backward(args)
+        return
+    if args.stage == "gemm_library":
+        bench_gemm_library(args)
         return
 
     import torch
