@@ -533,42 +533,51 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int L) {
     // holds the row-angle half, block 2h+1 the column-angle half; the
     // rotate_half partners (columns c and c+16 of a block) sit in one lane.
     // The lane's table entries (16 cos/sin pairs per row: its 4-column groups
-    // c4 + 8 gq + 16 half) are all loaded before any is used, so the loads of
-    // every row block are in flight together.
+    // c4 + 8 gq + 16 half) for a group of RG row blocks are all loaded before
+    // any is used, so those loads are in flight together. RG is every row
+    // block when a wave has 512 registers per lane (one wave per SIMD) and two
+    // with 256 (the 8-wave tiles, whose accumulators already take half).
     if (n0 + wn * TN < g.rope_cols) {
-      f32x4 cs[BI][2][2][2];
+      constexpr int RG = (WM * WN > 4 && BI > 2) ? 2 : BI;
+      static_assert(BI % RG == 0, "row block groups");
 #pragma unroll
-      for (int i = 0; i < BI; ++i) {
-        const int m = min(m0 + wm * TM + i * 32 + fr, M - 1);
-        const float* tab = (const float*)g.rope_table + (int64_t)m * 64;
+      for (int i0 = 0; i0 < BI; i0 += RG) {
+        f32x4 cs[RG][2][2][2];
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int gq = 0; gq < 2; ++gq)
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-              cs[i][half][gq][q] = *reinterpret_cast<const f32x4*>(
-                  tab + 2 * (half * 16 + 8 * gq + c4) + 4 * q);
-      }
-#pragma unroll
-      for (int i = 0; i < BI; ++i) {
-#pragma unroll
-        for (int h = 0; h < BJ / 2; ++h) {
-          if (n0 + wn * TN + h * 64 >= g.rope_cols) continue;
+        for (int ii = 0; ii < RG; ++ii) {
+          const int m = min(m0 + wm * TM + (i0 + ii) * 32 + fr, M - 1);
+          const float* tab = (const float*)g.rope_table + (int64_t)m * 64;
 #pragma unroll
           for (int half = 0; half < 2; ++half)
 #pragma unroll
             for (int gq = 0; gq < 2; ++gq)
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const float c = cs[i][half][gq][r / 2][2 * (r % 2)];
-                const float sn = cs[i][half][gq][r / 2][2 * (r % 2) + 1];
-                const float a1 = acc[i][2 * h + half][4 * gq + r];
-                const float a2 = acc[i][2 * h + half][4 * (gq + 2) + r];
-                acc[i][2 * h + half][4 * gq + r] = a1 * c - a2 * sn;
-                acc[i][2 * h + half][4 * (gq + 2) + r] = a2 * c + a1 * sn;
-              }
+              for (int q = 0; q < 2; ++q)
+                cs[ii][half][gq][q] = *reinterpret_cast<const f32x4*>(
+                    tab + 2 * (half * 16 + 8 * gq + c4) + 4 * q);
         }
+#pragma unroll
+        for (int ii = 0; ii < RG; ++ii) {
+          const int i = i0 + ii;
+#pragma unroll
+          for (int h = 0; h < BJ / 2; ++h) {
+            if (n0 + wn * TN + h * 64 >= g.rope_cols) continue;
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+              for (int gq = 0; gq < 2; ++gq)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const float c = cs[ii][half][gq][r / 2][2 * (r % 2)];
+                  const float sn = cs[ii][half][gq][r / 2][2 * (r % 2) + 1];
+                  const float a1 = acc[i][2 * h + half][4 * gq + r];
+                  const float a2 = acc[i][2 * h + half][4 * (gq + 2) + r];
+                  acc[i][2 * h + half][4 * gq + r] = a1 * c - a2 * sn;
+                  acc[i][2 * h + half][4 * (gq + 2) + r] = a2 * c + a1 * sn;
+                }
+          }
+        }
+        sched_fence();  // one group's table entries live at a time
       }
     }
   }
