@@ -77,10 +77,11 @@ def throughput_out():
     return to_np(api.Encoder(cfg, w, cfg.grids, aligner=True)(x)), inp
 
 
-@pytest.mark.parametrize("image", [0, 5, 10, 15])
-def test_throughput_batch_sampled_images(throughput_out, image):
-    """16 x 48x48 images: images are independent, so the oracle runs on four of them
-    (first, two in the middle, last), each against its rows of the whole-batch call."""
+@pytest.mark.parametrize("image", range(16))
+def test_throughput_batch_every_image(throughput_out, image):
+    """16 x 48x48 images: images are independent, so the oracle runs one image at a
+    time, each against its rows of the whole-batch call; together the 16 cases cover
+    every output row."""
     cfg = configs.get(4)
     got, inp = throughput_out
     P, T = 48 * 48, 24 * 24
