@@ -117,6 +117,33 @@ def test_rmsnorm(dim, out_dtype):
     assert rowwise_rel_err(got, ref) < (1e-5 if out_dtype == "f32" else 8e-3)
 
 
+@pytest.mark.parametrize("dim", [4, 200, 256, 1024, 1152, 2048, 2052])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_rmsnorm_register_rows_match_streamed_rows(dim, out_dtype):
+    """Rows up to 2048 wide are held in registers and stored 4 elements at a time when
+    the output is aligned for that; an output one element off that alignment takes
+    the streaming kernel.  Both must give the same bits (same arithmetic, same order)."""
+    rows = 301
+    x = synth.random_array((rows, dim), 17)
+    x *= np.exp(synth.random_array((rows, 1), 18)).astype(np.float32)
+    w = 1 + synth.random_array((dim,), 19, std=0.02)
+    xd, wd = _dev(x), _dev(w)
+    td = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    buf = torch.zeros(2, rows * dim + 8, dtype=td, device="cuda")
+    lib = _lib.load()
+    s = torch.cuda.current_stream().cuda_stream
+    code = _lib.VIT_BF16 if out_dtype == "bf16" else _lib.VIT_F32
+    for k, off in enumerate((0, 1)):  # 16-byte aligned base, then one element past it
+        st = lib.vit_rmsnorm(xd.data_ptr(), wd.data_ptr(), 1e-6, rows, dim, code,
+                             buf[k, off:].data_ptr(), s)
+        assert st == 0, st
+    a = buf[0, :rows * dim]
+    b = buf[1, 1:rows * dim + 1]
+    assert torch.equal(a, b)
+    assert rowwise_rel_err(to_np(a.view(rows, dim)), oracle.rmsnorm(x, w, 1e-6)) < \
+        (1e-5 if out_dtype == "f32" else 8e-3)
+
+
 def test_rmsnorm_zero_rows_are_zero():
     x = np.zeros((4, 256), dtype=np.float32)
     got = to_np(api.rmsnorm(_dev(x), _dev(np.ones(256)), 1e-6, "f32"))

@@ -11,6 +11,15 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------------------
+// ss + v.x^2 + v.y^2 + v.z^2 + v.w^2 as four FMAs in this order (spelled out so
+// that both RMSNorm kernels round the sum of squares identically)
+VIT_DEV float sumsq4(float4 v, float ss) {
+  ss = fmaf(v.x, v.x, ss);
+  ss = fmaf(v.y, v.y, ss);
+  ss = fmaf(v.z, v.z, ss);
+  return fmaf(v.w, v.w, ss);
+}
+
 // RMSNorm (NeMo Automodel vision page, DeepseekV4VisionRMSNorm: fp32 scale,
 // eps 1e-6): one wavefront per row, fp32 sum of squares reduced across the
 // wave, then y = w * (x * rsqrt(mean + eps)) cast once to the output type.
@@ -28,7 +37,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const float* __restri
   float ss = 0.f;
   for (int c = lane; c < n4; c += 64) {
     float4 v = xr[c];
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    ss = sumsq4(v, ss);
   }
   ss = wave_sum(ss);
   const float rstd = 1.0f / sqrtf(ss / (float)dim + eps);
@@ -40,6 +49,47 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const float* __restri
     o[1] = from_f32<TO>(s.y * (v.y * rstd));
     o[2] = from_f32<TO>(s.z * (v.z * rstd));
     o[3] = from_f32<TO>(s.w * (v.w * rstd));
+  }
+}
+
+// The same for dim <= 256 * NV: the lane's NV float4s of the row stay in
+// registers between the two passes (x is read once), and each float4 of output
+// leaves as one vector store.  Same arithmetic, in the same order.
+template <typename TO, int NV>
+__global__ __launch_bounds__(kThreads) void rmsnorm_reg_kernel(const float* __restrict__ x,
+                                                               const float* __restrict__ w,
+                                                               float eps, int64_t rows, int dim,
+                                                               TO* __restrict__ out) {
+  typedef TO TO4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float4* xr = reinterpret_cast<const float4*>(x + row * dim);
+  const float4* w4 = reinterpret_cast<const float4*>(w);
+  const int n4 = dim >> 2;
+  float4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = c < n4 ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (lane + 64 * i < n4) ss = sumsq4(v[i], ss);
+  ss = wave_sum(ss);
+  const float rstd = 1.0f / sqrtf(ss / (float)dim + eps);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= n4) continue;
+    const float4 s = w4[c];
+    TO4 o;
+    o[0] = from_f32<TO>(s.x * (v[i].x * rstd));
+    o[1] = from_f32<TO>(s.y * (v[i].y * rstd));
+    o[2] = from_f32<TO>(s.z * (v[i].z * rstd));
+    o[3] = from_f32<TO>(s.w * (v[i].w * rstd));
+    *reinterpret_cast<TO4*>(out + row * dim + 4 * c) = o;
   }
 }
 
@@ -467,6 +517,24 @@ hipError_t launch_rmsnorm(const float* x, const float* w, float eps, int64_t row
                           int out_dtype, void* out, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const unsigned grid = (unsigned)((rows + 3) / 4);
+  const size_t osz = out_dtype == VIT_BF16 ? 2 : 4;
+  // register-resident rows for dim <= 2048 when the output takes 4-element stores
+  const int nv = dim <= 256 ? 1 : dim <= 512 ? 2 : dim <= 1024 ? 4 : dim <= 2048 ? 8 : 0;
+  if (nv && (uintptr_t)out % (4 * osz) == 0) {
+#define VIT_RMS_REG(NV_)                                                                        \
+  if (out_dtype == VIT_BF16)                                                                    \
+    rmsnorm_reg_kernel<bf16, NV_><<<grid, kThreads, 0, s>>>(x, w, eps, rows, dim, (bf16*)out);  \
+  else                                                                                          \
+    rmsnorm_reg_kernel<float, NV_><<<grid, kThreads, 0, s>>>(x, w, eps, rows, dim, (float*)out)
+    switch (nv) {
+      case 1: VIT_RMS_REG(1); break;
+      case 2: VIT_RMS_REG(2); break;
+      case 4: VIT_RMS_REG(4); break;
+      default: VIT_RMS_REG(8); break;
+    }
+#undef VIT_RMS_REG
+    return hipGetLastError();
+  }
   if (out_dtype == VIT_BF16)
     rmsnorm_kernel<bf16><<<grid, kThreads, 0, s>>>(x, w, eps, rows, dim, (bf16*)out);
   else
