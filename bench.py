@@ -83,7 +83,7 @@ def counter_traffic(kernel_class, workload):
 # dual-B GEMM instantiation, i.e. the template argument list ends in "true>")
 KERNEL_NAME_PATTERN = {"gateup": ("gemm_", ", true>("), "attn": ("attn_vt_kernel", ""),
                        "attn72": ("attn_bf16_kernel<72", ""), "rope": ("tpack_kernel<72, true>", ""),
-                       "rmsnorm": ("rmsnorm_kernel", ""), "merge": ("merge_copy_kernel", ""),
+                       "rmsnorm": ("rmsnorm_", ""), "merge": ("merge_copy_kernel", ""),
                        "proj1": ("gemm_mfma_kernel", ", 5, false>(")}
 
 
