@@ -324,3 +324,24 @@ def test_random_ragged_batches_head_dim_72(seed):
     err = rowwise_rel_err(got, ref)
     print(f"seed {seed} grids {grids} aligner {aligner}: row-wise rel err {err:.3e}")
     assert err < TOL["bf16"], err
+
+
+@pytest.mark.parametrize("width,heads", [(128, 2), (576, 8)], ids=["head_dim64", "head_dim72"])
+def test_large_image_long_sequence(width, heads):
+    """One 96x96 image (9,216 patches: 145 key tiles per query, rotary positions up
+    to 95) beside a 3x5 image, one block, the aligner on (the odd grid zero-padded),
+    through the head_dim-64 and head_dim-72 paths; the whole output against the
+    oracle at the workload bar."""
+    grids = ((96, 96), (3, 5))
+    cfg = configs.VitConfig(f"large_{width}", grids, width, heads, 192, 1, 256, "bf16", patch_size=4)
+    assert cfg.head_dim in (64, 72)
+    inp = synth.make_inputs(cfg, seed=77)
+    w = api.DeviceWeights(cfg, inp["weights"])
+    x = torch.from_numpy(inp["patches"]).to("cuda", torch.bfloat16)
+    got = to_np(api.encode_varlen(x, list(grids), w, aligner=True, pad_odd=True))
+    ref = oracle.encode_varlen(inp["patches"], list(grids), inp["weights"], cfg.n_heads,
+                               cfg.rms_eps, cfg.rope_theta, with_aligner=True, pad_odd=True)
+    assert got.shape == ref.shape
+    err = rowwise_rel_err(got, ref)
+    print(f"{cfg.name}: row-wise rel err {err:.3e}")
+    assert err < TOL["bf16"], err
