@@ -261,8 +261,8 @@ bool pipe_eligible(const GemmArgs& g) {
 // the 8-wave 256x256 tile ~1.57x as efficient; with the fp32 read-modify-write
 // epilogue, whose traffic grows with the tile, 1.04x / 1.1x / 1.2x, and the
 // 256x256 tile (which spills with it) is not used.  The 4-wave 128x128 tile is
-// not built: the 8-wave one was never slower.  The folded-RMSNorm producer
-// needs 64-column wave sub-tiles (not 192x256).
+// not built: the 8-wave one was never slower.  Every tile takes the
+// folded-RMSNorm producer (its wave sub-tiles are whole 64-column groups).
 namespace {
 
 struct TileOpt {
@@ -281,7 +281,7 @@ constexpr int kTileOpts = 5;
 // (196 x 4096 x 4096) 29.2 -> 24.0 us, patch embedding 11.6 -> 10.2 us against
 // the 128x128 tile; on the ragged batch's shapes it loses (out-projection 25.4
 // against 20.7 us), which the model reproduces.
-int tile_opts(int epilogue, bool norm_producer, TileOpt* o) {
+int tile_opts(int epilogue, TileOpt* o) {
   const bool rmw = epilogue == VIT_EPI_ADD_F32;
   o[0] = {GEMM_MFMA_128x128, 128, 128, rmw ? 1.04 : 1.13, true, 1};
   o[1] = {GEMM_MFMA_256x128_W8, 256, 128, rmw ? 1.1 : 1.18, true, 1};
@@ -303,9 +303,9 @@ double tile_cost(const TileOpt& o, int epilogue, int64_t M, int64_t N) {
   return (double)((tiles + slots - 1) / slots) * o.bm * o.bn / o.eff;
 }
 
-int best_tile(int epilogue, bool norm_producer, int64_t M, int64_t N, double* cost) {
+int best_tile(int epilogue, int64_t M, int64_t N, double* cost) {
   TileOpt opts[kTileOpts];
-  const int n = tile_opts(epilogue, norm_producer, opts);
+  const int n = tile_opts(epilogue, opts);
   int best = GEMM_MFMA_128x128;
   double best_cost = 1e300;
   for (int i = 0; i < n; ++i) {
@@ -326,8 +326,8 @@ constexpr double kSplitPenalty = 1.3e3;
 
 }  // namespace
 
-int gemm_mfma_choice(int epilogue, bool norm_producer, int64_t M, int64_t N) {
-  return best_tile(epilogue, norm_producer, M, N, nullptr);
+int gemm_mfma_choice(int epilogue, int64_t M, int64_t N) {
+  return best_tile(epilogue, M, N, nullptr);
 }
 
 // Column split: when a wide GEMM's best single tile leaves a ragged last round
@@ -338,10 +338,10 @@ int gemm_mfma_choice(int epilogue, bool norm_producer, int64_t M, int64_t N) {
 // depend on the absolute column take it (not the rotary or transposed-V forms;
 // the folded-norm producer's second launch gets its columns' norm weights and
 // its columns of u and of the partial sums, with the full rows' strides).
-GemmSplit gemm_mfma_split(int epilogue, bool norm_producer, int64_t M, int64_t N) {
+GemmSplit gemm_mfma_split(int epilogue, int64_t M, int64_t N) {
   GemmSplit best{};
   double best_cost;
-  best.cfg_main = best_tile(epilogue, norm_producer, M, N, &best_cost);
+  best.cfg_main = best_tile(epilogue, M, N, &best_cost);
   best.n_main = N;
   best.cfg_tail = -1;
   const bool col_free = epilogue == VIT_EPI_STORE || epilogue == VIT_EPI_STORE_GATHER ||
@@ -350,7 +350,7 @@ GemmSplit gemm_mfma_split(int epilogue, bool norm_producer, int64_t M, int64_t N
                         epilogue == VIT_EPI_BIAS || epilogue == VIT_EPI_BIAS_GELU;
   if (!col_free) return best;
   TileOpt opts[kTileOpts];
-  tile_opts(epilogue, norm_producer, opts);
+  tile_opts(epilogue, opts);
   // largest tiles first: at equal cost the large-tile launch is the main one
   for (const int i : {2, 3, 1, 0}) {
     const TileOpt& o = opts[i];
@@ -360,7 +360,7 @@ GemmSplit gemm_mfma_split(int epilogue, bool norm_producer, int64_t M, int64_t N
     const int64_t n_main = (kCUs / row_tiles) * bno;
     if (n_main <= 0 || n_main >= N) continue;
     double tail_cost;
-    const int tail = best_tile(epilogue, norm_producer, M, N - n_main, &tail_cost);
+    const int tail = best_tile(epilogue, M, N - n_main, &tail_cost);
     const double c = o.bm * o.bn / o.eff + tail_cost + kSplitPenalty;
     if (c < best_cost) {
       best_cost = c;
@@ -389,7 +389,7 @@ hipError_t launch_gemm_bf16_pair(int epilogue, const GemmArgs& g0, const GemmArg
     return launch_gemm_bf16(epilogue, g1, s);
   }
   TileOpt opts[kTileOpts];
-  tile_opts(epilogue, false, opts);
+  tile_opts(epilogue, opts);
   int best = GEMM_MFMA_128x128;
   double best_cost = 1e300;
   for (const TileOpt& o : opts) {
@@ -426,10 +426,10 @@ hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& g, hipStream_t s) {
     return hipErrorInvalidValue;
   if (pipe_eligible(g)) {
     if (rope) {
-      const int cfg = gemm_mfma_choice(VIT_EPI_STORE, g.norm_w != nullptr, g.M, g.N);
+      const int cfg = gemm_mfma_choice(VIT_EPI_STORE, g.M, g.N);
       return launch_gemm_mfma(cfg, epilogue, g, s);
     }
-    const GemmSplit sp = gemm_mfma_split(epilogue, g.norm_w != nullptr, g.M, g.N);
+    const GemmSplit sp = gemm_mfma_split(epilogue, g.M, g.N);
     if (sp.n_main == g.N) return launch_gemm_mfma(sp.cfg_main, epilogue, g, s);
     GemmArgs a = g, b = g;
     a.N = sp.n_main;

@@ -591,7 +591,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int L) {
   constexpr int OTN = DUAL ? TN / 2 : TN;      // output columns per wave
   constexpr int ROWB = OTN * OB;               // bytes per staged row
   constexpr int CPRW = ROWB / 16;              // 16-byte chunks per staged row
-  constexpr int RPL = 256 / ROWB;              // staged rows per 256-byte bank line
+  constexpr int RPL = ROWB <= 256 ? 256 / ROWB : 1;  // staged rows per 256-byte bank line
   constexpr int EPC = 16 / OB;                 // elements per chunk
   constexpr bool kStaged = EPI != VIT_EPI_ADD_F32 && (ROWB == 64 || ROWB == 128 || ROWB == 256) &&
                            TM * ROWB * NW <= STAGES * ROWS * BK * 2;
