@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from parity_util import TOL, rowwise_rel_err, to_np
+from parity_util import rowwise_rel_err, to_np
 from vision_transformer_encoder_image_amd import _lib, api, synth
 
 pytestmark = pytest.mark.gpu

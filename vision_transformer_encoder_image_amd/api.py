@@ -7,7 +7,7 @@ encoder runs inside ``libvitenc.so``.  Names follow the C ABI in
 from __future__ import annotations
 
 import ctypes
-from typing import Dict, List, Optional, Sequence, Tuple
+from typing import Dict, Optional, Sequence, Tuple
 
 import numpy as np
 import torch
