@@ -138,11 +138,14 @@ def pmc_summary(fetch_dir, write_dir, kernel, workload, copy_mb, out_path=None):
     print(json.dumps(out))
 
 
-def trace_summary(trace_dir, out_path, title, command):
+def trace_summary(trace_dir, out_path, title, command, per_call=0):
     """Per-kernel table (calls, average / min / max duration, share of GPU time) from a
-    rocprofv3 --kernel-trace --stats run's kernel_stats.csv."""
+    rocprofv3 --kernel-trace --stats run's kernel_stats.csv.  With per_call = the number
+    of calls of the entry point in the trace, the table gives each kernel's time per call
+    of the entry point instead, and their sum."""
     import csv
     import glob
+    import shlex
 
     rows = []
     for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True):
@@ -150,15 +153,32 @@ def trace_summary(trace_dir, out_path, title, command):
     if not rows:
         raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    cmds = command if not per_call else (
+        command + "\npython3 bench.py --trace-summary " + " ".join(
+            shlex.quote(a) for a in (trace_dir, out_path, title, command)) + f" --per-call {per_call}")
     lines = [f"# rocprofv3 kernel statistics — {title}", "",
-             "Command (repo root, MI355X, `export TMPDIR=/tmp`):", "", "```", command, "```", "",
-             "| Kernel | Calls | Avg (us) | Min (us) | Max (us) | Share of GPU time |",
-             "|---|---|---|---|---|---|"]
+             "Command (repo root, MI355X, `export TMPDIR=/tmp`):", "", "```", cmds, "```", ""]
+    if per_call:
+        lines += [f"({per_call} calls of the entry point in the trace)", "",
+                  "| Kernel | Calls | Avg (us) | Per call of the entry point (us) |",
+                  "|---|---|---|---|"]
+    else:
+        lines += ["| Kernel | Calls | Avg (us) | Min (us) | Max (us) | Share of GPU time |",
+                  "|---|---|---|---|---|---|"]
+    total = 0.0
     for r in rows:
         n = r["Name"].replace("void (anonymous namespace)::", "").replace("(anonymous namespace)::", "")
-        lines.append(f"| `{n[:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
-                     f"{float(r['Percentage']):.1f}% |")
+        avg = float(r["AverageNs"]) / 1e3
+        if per_call:
+            each = int(r["Calls"]) * avg / per_call
+            total += each
+            lines.append(f"| `{n[:100]}` | {r['Calls']} | {avg:.2f} | {each:.1f} |")
+        else:
+            lines.append(f"| `{n[:100]}` | {r['Calls']} | {avg:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{float(r['Percentage']):.1f}% |")
+    if per_call:
+        lines += ["", f"Kernel time per call of the entry point: {total / 1e3:.3f} ms."]
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -868,9 +888,12 @@ def main():
     ap.add_argument("--trace-summary", nargs=4, metavar=("TRACE_DIR", "OUT", "TITLE", "COMMAND"),
                     help="summarise a rocprofv3 --kernel-trace --stats run into a markdown table "
                          "and exit")
+    ap.add_argument("--per-call", type=int, default=0,
+                    help="with --trace-summary: calls of the entry point in the trace (the table "
+                         "then gives each kernel's time per call)")
     args = ap.parse_args()
     if args.trace_summary:
-        trace_summary(*args.trace_summary)
+        trace_summary(*args.trace_summary, per_call=args.per_call)
         return
     if args.mfma_summary:
         mfma_util_summary(args.mfma_summary[0], args.mfma_summary[1])
